@@ -1,0 +1,205 @@
+"""ctypes front of the fp64 CPU oracle (``liboracle.so``) of the HashEvict path.
+
+TEST INFRASTRUCTURE ONLY.  Only the test-suite, the package smoke check and the
+CPU-baseline leg of the benchmark may import this package.  It shares no code
+with the GPU library: it decodes bf16 storage itself, slices query heads into
+GQA groups itself, and runs the eviction rule of the HashEvict summary page
+("Technical framework", stages 1-5; abstract) in plain C.
+
+Functions with no pin of their own: none -- see tests/test_oracle_*.py for the
+brute-force, invariant, closed-form (Charikar) and exact-attention pins.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SOURCES = [os.path.join(_HERE, "hkv_oracle.c")]
+
+STREAM = 0
+TRUNCATE = 1
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the oracle with the host C compiler (plain -O2, one thread)."""
+    cmd = ["gcc", "-std=c11", "-O2", "-mpopcnt", "-fPIC", "-shared", "-Wall", "-Wextra",
+           "-o", LIB_PATH + ".tmp"] + SOURCES + ["-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(LIB_PATH + ".tmp", LIB_PATH)
+    return LIB_PATH
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        L = C.CDLL(LIB_PATH)
+        P = C.c_void_p
+        L.orc_create.restype = P
+        L.orc_create.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, P]
+        L.orc_destroy.argtypes = [P]
+        L.orc_encode.argtypes = [P, P, P, P]
+        L.orc_encode_many.argtypes = [P, C.c_int, P, P, P]
+        L.orc_prefill.restype = C.c_int
+        L.orc_prefill.argtypes = [P, C.c_int, C.c_int, P, P, P]
+        L.orc_decode_step.restype = C.c_int
+        L.orc_decode_step.argtypes = [P] * 3 + [P] * 8 + [P]
+        L.orc_scores.argtypes = [P, P, P]
+        L.orc_attend.argtypes = [P, P, P]
+        L.orc_get_state.argtypes = [P] * 7
+        L.orc_set_state.argtypes = [P, P, P, P, P, C.c_int32, C.c_int64]
+        L.orc_words.restype = C.c_int
+        L.orc_words.argtypes = [P]
+        _lib = L
+    return _lib
+
+
+def bf16_bits_to_f64(u: np.ndarray) -> np.ndarray:
+    """Widen raw bf16 bits (uint16) to float64 (exact)."""
+    w = np.ascontiguousarray(u, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return w.view(np.float32).astype(np.float64)
+
+
+def widen(x: np.ndarray) -> np.ndarray:
+    """fp32 values or raw bf16 bits -> float64."""
+    if x.dtype == np.uint16:
+        return bf16_bits_to_f64(x)
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float64)
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _u32(a) -> Optional[np.ndarray]:
+    return None if a is None else np.ascontiguousarray(a, dtype=np.uint32)
+
+
+class OracleHead:
+    """One eviction domain: the cache of one (sequence, KV head) pair."""
+
+    def __init__(self, R: np.ndarray, budget: int, group: int):
+        R = _f64(widen(R) if R.dtype != np.float64 else R)
+        self.d, self.nbits = R.shape
+        self.budget, self.group = int(budget), int(group)
+        self.W = (self.nbits + 31) // 32
+        self._R = R
+        self._h = lib().orc_create(self.d, self.nbits, self.budget, self.group, _p(R))
+        if not self._h:
+            raise ValueError("orc_create rejected its arguments")
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and _lib is not None:
+            _lib.orc_destroy(h)
+            self._h = None
+
+    def encode(self, X: np.ndarray):
+        """Codes and flags, [n][W] uint32 each, for vectors X[n][d] (or one vector)."""
+        X = _f64(X)
+        one = X.ndim == 1
+        X = X.reshape(-1, self.d)
+        codes = np.zeros((X.shape[0], self.W), np.uint32)
+        flags = np.zeros((X.shape[0], self.W), np.uint32)
+        lib().orc_encode_many(self._h, X.shape[0], _p(X), _p(codes), _p(flags))
+        return (codes[0], flags[0]) if one else (codes, flags)
+
+    def prefill(self, K: np.ndarray, V: np.ndarray, policy: int = STREAM,
+                inj_codes: Optional[np.ndarray] = None):
+        K, V = _f64(K), _f64(V)
+        n = K.shape[0]
+        inj = _u32(inj_codes)
+        if inj is not None:
+            assert inj.shape == (n, self.W)
+        rc = lib().orc_prefill(self._h, int(policy), n, _p(K), _p(V), _p(inj))
+        if rc != 0:
+            raise RuntimeError("orc_prefill failed (cache not empty?)")
+
+    def decode_step(self, q, k, v, inj_qcodes=None, inj_kcode=None):
+        q, k, v = _f64(q).reshape(self.group, self.d), _f64(k), _f64(v)
+        out = np.zeros((self.group, self.d), np.float64)
+        ev = np.zeros(1, np.int32)
+        qc = np.zeros((self.group, self.W), np.uint32)
+        qf = np.zeros_like(qc)
+        kc = np.zeros(self.W, np.uint32)
+        kf = np.zeros_like(kc)
+        iq, ik = _u32(inj_qcodes), _u32(inj_kcode)
+        rc = lib().orc_decode_step(self._h, _p(q), _p(k), _p(v), _p(iq), _p(ik), _p(out),
+                                   _p(ev), _p(qc), _p(qf), _p(kc), _p(kf))
+        if rc != 0:
+            raise RuntimeError("orc_decode_step failed (zero budget?)")
+        return {"out": out, "evicted": int(ev[0]), "qcodes": qc, "qflags": qf,
+                "kcode": kc, "kflag": kf}
+
+    def scores(self, qcodes) -> np.ndarray:
+        qc = _u32(qcodes).reshape(self.group, self.W)
+        sc = np.zeros(self.budget, np.int32)
+        lib().orc_scores(self._h, _p(qc), _p(sc))
+        return sc
+
+    def attend(self, q) -> np.ndarray:
+        q = _f64(q).reshape(self.group, self.d)
+        out = np.zeros((self.group, self.d), np.float64)
+        lib().orc_attend(self._h, _p(q), _p(out))
+        return out
+
+    def state(self) -> dict:
+        S = max(self.budget, 0)
+        K = np.zeros((S, self.d)); V = np.zeros((S, self.d))
+        code = np.zeros((S, self.W), np.uint32)
+        tok = np.zeros(S, np.int64)
+        n = np.zeros(1, np.int32); t = np.zeros(1, np.int64)
+        lib().orc_get_state(self._h, _p(K), _p(V), _p(code), _p(tok), _p(n), _p(t))
+        return {"K": K, "V": V, "code": code, "tok": tok, "n": int(n[0]), "t": int(t[0])}
+
+    def set_state(self, st: dict):
+        K, V = _f64(st["K"]), _f64(st["V"])
+        code = _u32(st["code"])
+        tok = np.ascontiguousarray(st["tok"], dtype=np.int64)
+        lib().orc_set_state(self._h, _p(K), _p(V), _p(code), _p(tok), int(st["n"]), int(st["t"]))
+
+
+class OracleCache:
+    """All eviction domains of a batch: heads[b][h] for b < B, h < Hkv.
+
+    Query head hq belongs to KV head hq // G (contiguous groups)."""
+
+    def __init__(self, R, budgets, n_q_heads: int, n_kv_heads: int, heads=None):
+        self.B = len(budgets)
+        self.Hq, self.Hkv = int(n_q_heads), int(n_kv_heads)
+        self.G = self.Hq // self.Hkv
+        self.sel = heads if heads is not None else [(b, h) for b in range(self.B) for h in range(self.Hkv)]
+        self.heads = {(b, h): OracleHead(R, int(budgets[b]), self.G) for (b, h) in self.sel}
+
+    def prefill(self, K, V, prompt_lens, policy=STREAM, inj_codes=None):
+        for (b, h), o in self.heads.items():
+            n = int(prompt_lens[b])
+            inj = None if inj_codes is None else inj_codes[b, h, :n]
+            o.prefill(widen(K[b, h, :n]), widen(V[b, h, :n]), policy, inj)
+
+    def decode_step(self, q, k, v, inj_qcodes=None, inj_kcodes=None):
+        """q [B][Hq][d] fp32; k, v [B][Hkv][d]; returns per-head dicts keyed (b, h)."""
+        res = {}
+        G = self.G
+        for (b, h), o in self.heads.items():
+            iq = None if inj_qcodes is None else inj_qcodes[b, h * G:(h + 1) * G]
+            ik = None if inj_kcodes is None else inj_kcodes[b, h]
+            res[(b, h)] = o.decode_step(widen(q[b, h * G:(h + 1) * G]), widen(k[b, h]),
+                                        widen(v[b, h]), iq, ik)
+        return res

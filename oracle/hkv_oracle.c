@@ -1,0 +1,270 @@
+/*
+ * hkv_oracle.c -- plain, slow, single-threaded fp64 CPU oracle of the
+ * HashEvict decode path.
+ *
+ * TEST INFRASTRUCTURE ONLY: loaded by the test-suite, the package smoke check
+ * and the CPU-baseline leg of the benchmark, never by the GPU library.
+ *
+ * Each function follows the HashEvict summary page ("HashEvict: A
+ * Pre-Attention KV Cache Eviction Strategy using Locality-Sensitive Hashing",
+ * arXiv 2412.16187): section "Technical framework", stages 1-5, and the
+ * English abstract.  Readings of points the page leaves open are marked
+ * READING below.  No blocking, fusion or reordering: every sum runs over its
+ * index in ascending order.
+ */
+#include "hkv_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+struct orc_head {
+    int d, nbits, words, budget, group;
+    double* R;        /* [d][nbits] */
+    double* rnorm;    /* [nbits]  Euclidean norm of column j of R */
+    double* K;        /* [budget][d] */
+    double* V;        /* [budget][d] */
+    uint32_t* code;   /* [budget][words] */
+    int64_t* tok;     /* [budget]  token position held by the slot, -1 if empty */
+    int n;            /* occupancy: slots 0 .. n-1 hold tokens */
+    int64_t t;        /* position of the next token */
+};
+
+int orc_words(const orc_head* h) { return h->words; }
+
+orc_head* orc_create(int d, int n_bits, int budget, int group, const double* R)
+{
+    if (d <= 0 || n_bits <= 0 || budget < 0 || group <= 0 || !R) return NULL;
+    orc_head* h = (orc_head*)calloc(1, sizeof(orc_head));
+    h->d = d;
+    h->nbits = n_bits;
+    h->words = (n_bits + 31) / 32;
+    h->budget = budget;
+    h->group = group;
+    h->R = (double*)malloc(sizeof(double) * (size_t)d * n_bits);
+    memcpy(h->R, R, sizeof(double) * (size_t)d * n_bits);
+    h->rnorm = (double*)malloc(sizeof(double) * n_bits);
+    for (int j = 0; j < n_bits; ++j) {
+        double s = 0.0;
+        for (int i = 0; i < d; ++i) s += R[(size_t)i * n_bits + j] * R[(size_t)i * n_bits + j];
+        h->rnorm[j] = sqrt(s);
+    }
+    size_t slots = budget > 0 ? (size_t)budget : 1;
+    h->K = (double*)calloc(slots * d, sizeof(double));
+    h->V = (double*)calloc(slots * d, sizeof(double));
+    h->code = (uint32_t*)calloc(slots * h->words, sizeof(uint32_t));
+    h->tok = (int64_t*)malloc(slots * sizeof(int64_t));
+    for (size_t s = 0; s < slots; ++s) h->tok[s] = -1;
+    h->n = 0;
+    h->t = 0;
+    return h;
+}
+
+void orc_destroy(orc_head* h)
+{
+    if (!h) return;
+    free(h->R); free(h->rnorm); free(h->K); free(h->V); free(h->code); free(h->tok);
+    free(h);
+}
+
+/* Stages 1-2 of the technical framework: Gaussian random projection of the
+ * vector to n_bits coordinates, then binarisation.  READING: the
+ * binarisation threshold is 0 (a bit is set when the projection is strictly
+ * positive) -- the page names the threshold as a design knob without a value,
+ * and the sign is the plain binarisation of a Gaussian projection. */
+void orc_encode(const orc_head* h, const double* x, uint32_t* code, uint32_t* flag)
+{
+    double xn = 0.0;
+    for (int i = 0; i < h->d; ++i) xn += x[i] * x[i];
+    xn = sqrt(xn);
+    for (int w = 0; w < h->words; ++w) { code[w] = 0u; flag[w] = 0u; }
+    for (int j = 0; j < h->nbits; ++j) {
+        double y = 0.0;
+        for (int i = 0; i < h->d; ++i) y += x[i] * h->R[(size_t)i * h->nbits + j];
+        if (y > 0.0) code[j >> 5] |= 1u << (j & 31);
+        if (fabs(y) < 1e-5 * xn * h->rnorm[j]) flag[j >> 5] |= 1u << (j & 31);
+    }
+}
+
+void orc_encode_many(const orc_head* h, int n, const double* X, uint32_t* codes, uint32_t* flags)
+{
+    for (int t = 0; t < n; ++t)
+        orc_encode(h, X + (size_t)t * h->d, codes + (size_t)t * h->words, flags + (size_t)t * h->words);
+}
+
+static int popcount32(uint32_t v) { return __builtin_popcount(v); }
+
+/* Stage 3: Hamming distance between two codes (number of differing bits). */
+static int hamming(const uint32_t* a, const uint32_t* b, int words)
+{
+    int s = 0;
+    for (int w = 0; w < words; ++w) s += popcount32(a[w] ^ b[w]);
+    return s;
+}
+
+/* Stage 3 under grouped-query attention: the score of a slot is the sum of
+ * its Hamming distances to the codes of the query heads that share the KV
+ * head. */
+static int gqa_score(const orc_head* h, const uint32_t* qcodes, int ngroup, int slot)
+{
+    int s = 0;
+    for (int g = 0; g < ngroup; ++g)
+        s += hamming(qcodes + (size_t)g * h->words, h->code + (size_t)slot * h->words, h->words);
+    return s;
+}
+
+/* Stage 4: the slot to evict is the occupied slot whose code is farthest in
+ * Hamming distance from the query code(s) -- the most cosine-dissimilar key,
+ * hence the lowest expected attention.  READING: ties go to the lowest slot. */
+static int pick_victim(const orc_head* h, const uint32_t* qcodes, int ngroup)
+{
+    int best = -1, e = -1;
+    for (int s = 0; s < h->n; ++s) {
+        int sc = gqa_score(h, qcodes, ngroup, s);
+        if (sc > best) { best = sc; e = s; }
+    }
+    return e;
+}
+
+/* Stage 5: the token's key, value and key code take the slot. */
+static void write_slot(orc_head* h, int e, const double* k, const double* v, const uint32_t* kc,
+                       int64_t pos)
+{
+    memcpy(h->K + (size_t)e * h->d, k, sizeof(double) * h->d);
+    memcpy(h->V + (size_t)e * h->d, v, sizeof(double) * h->d);
+    memcpy(h->code + (size_t)e * h->words, kc, sizeof(uint32_t) * h->words);
+    h->tok[e] = pos;
+}
+
+/* Slot a new token goes to: the lowest empty slot while the cache is not
+ * full (READING: nothing is evicted then), else the stage-4 victim. */
+static int place(orc_head* h, const uint32_t* qcodes, int ngroup)
+{
+    if (h->n < h->budget) return h->n++;
+    return pick_victim(h, qcodes, ngroup);
+}
+
+/* READING of the prefill rule (the page does not describe prefill): STREAM
+ * feeds the prompt through the decode rule one token at a time, scoring the
+ * cache against the token's own key code because no query accompanies a
+ * prompt key; TRUNCATE keeps the first `budget` prompt tokens. */
+int orc_prefill(orc_head* h, int policy, int n, const double* K, const double* V,
+                const uint32_t* inj_codes)
+{
+    if (h->n != 0 || n < 0) return -1;
+    uint32_t* c = (uint32_t*)malloc(sizeof(uint32_t) * h->words);
+    uint32_t* f = (uint32_t*)malloc(sizeof(uint32_t) * h->words);
+    for (int t = 0; t < n; ++t) {
+        const double* kt = K + (size_t)t * h->d;
+        const uint32_t* ct;
+        if (inj_codes) {
+            ct = inj_codes + (size_t)t * h->words;
+        } else {
+            orc_encode(h, kt, c, f);
+            ct = c;
+        }
+        int e;
+        if (policy == ORC_PREFILL_TRUNCATE) {
+            if (h->n >= h->budget) break;
+            e = h->n++;
+        } else {
+            e = place(h, ct, 1);
+            if (e < 0) continue;
+        }
+        write_slot(h, e, kt, V + (size_t)t * h->d, ct, (int64_t)t);
+    }
+    free(c);
+    free(f);
+    h->t = n;
+    return 0;
+}
+
+/* Attention over the occupied slots: softmax(q . K^T / sqrt(d)) V, with the
+ * maximum logit subtracted before exponentiation. */
+void orc_attend(const orc_head* h, const double* q, double* out)
+{
+    double* lg = (double*)malloc(sizeof(double) * (h->n > 0 ? h->n : 1));
+    const double scale = 1.0 / sqrt((double)h->d);
+    for (int g = 0; g < h->group; ++g) {
+        const double* qg = q + (size_t)g * h->d;
+        double* og = out + (size_t)g * h->d;
+        double m = -INFINITY;
+        for (int s = 0; s < h->n; ++s) {
+            double dot = 0.0;
+            for (int i = 0; i < h->d; ++i) dot += qg[i] * h->K[(size_t)s * h->d + i];
+            lg[s] = dot * scale;
+            if (lg[s] > m) m = lg[s];
+        }
+        double den = 0.0;
+        for (int i = 0; i < h->d; ++i) og[i] = 0.0;
+        for (int s = 0; s < h->n; ++s) {
+            double p = exp(lg[s] - m);
+            den += p;
+            for (int i = 0; i < h->d; ++i) og[i] += p * h->V[(size_t)s * h->d + i];
+        }
+        for (int i = 0; i < h->d; ++i) og[i] = h->n > 0 ? og[i] / den : 0.0;
+    }
+    free(lg);
+}
+
+/* One decode step: encode the query heads and the new key (stages 1-2),
+ * choose the slot (stages 3-4) before any attention is computed, write the
+ * new token there (stage 5), then attend over the updated cache. */
+int orc_decode_step(orc_head* h, const double* q, const double* k, const double* v,
+                    const uint32_t* inj_qcodes, const uint32_t* inj_kcode,
+                    double* out, int32_t* evicted,
+                    uint32_t* qcodes, uint32_t* qflags, uint32_t* kcode, uint32_t* kflag)
+{
+    const int W = h->words, G = h->group;
+    uint32_t* qc = (uint32_t*)calloc((size_t)G * W, sizeof(uint32_t));
+    uint32_t* qf = (uint32_t*)calloc((size_t)G * W, sizeof(uint32_t));
+    uint32_t* kc = (uint32_t*)calloc((size_t)W, sizeof(uint32_t));
+    uint32_t* kf = (uint32_t*)calloc((size_t)W, sizeof(uint32_t));
+    for (int g = 0; g < G; ++g)
+        orc_encode(h, q + (size_t)g * h->d, qc + (size_t)g * W, qf + (size_t)g * W);
+    orc_encode(h, k, kc, kf);
+    if (inj_qcodes) memcpy(qc, inj_qcodes, sizeof(uint32_t) * (size_t)G * W);
+    if (inj_kcode) memcpy(kc, inj_kcode, sizeof(uint32_t) * (size_t)W);
+
+    int e = place(h, qc, G);
+    if (e >= 0) write_slot(h, e, k, v, kc, h->t);
+    h->t += 1;
+    if (out) orc_attend(h, q, out);
+    if (evicted) *evicted = e;
+    if (qcodes) memcpy(qcodes, qc, sizeof(uint32_t) * (size_t)G * W);
+    if (qflags) memcpy(qflags, qf, sizeof(uint32_t) * (size_t)G * W);
+    if (kcode) memcpy(kcode, kc, sizeof(uint32_t) * (size_t)W);
+    if (kflag) memcpy(kflag, kf, sizeof(uint32_t) * (size_t)W);
+    free(qc); free(qf); free(kc); free(kf);
+    return e >= 0 ? 0 : -1;
+}
+
+void orc_scores(const orc_head* h, const uint32_t* qcodes, int32_t* scores)
+{
+    for (int s = 0; s < h->budget; ++s)
+        scores[s] = s < h->n ? gqa_score(h, qcodes, h->group, s) : -1;
+}
+
+void orc_get_state(const orc_head* h, double* K, double* V, uint32_t* code, int64_t* tok,
+                   int32_t* occupancy, int64_t* next_pos)
+{
+    size_t S = (size_t)h->budget;
+    if (K) memcpy(K, h->K, sizeof(double) * S * h->d);
+    if (V) memcpy(V, h->V, sizeof(double) * S * h->d);
+    if (code) memcpy(code, h->code, sizeof(uint32_t) * S * h->words);
+    if (tok) memcpy(tok, h->tok, sizeof(int64_t) * S);
+    if (occupancy) *occupancy = h->n;
+    if (next_pos) *next_pos = h->t;
+}
+
+void orc_set_state(orc_head* h, const double* K, const double* V, const uint32_t* code,
+                   const int64_t* tok, int32_t occupancy, int64_t next_pos)
+{
+    size_t S = (size_t)h->budget;
+    memcpy(h->K, K, sizeof(double) * S * h->d);
+    memcpy(h->V, V, sizeof(double) * S * h->d);
+    memcpy(h->code, code, sizeof(uint32_t) * S * h->words);
+    memcpy(h->tok, tok, sizeof(int64_t) * S);
+    h->n = occupancy;
+    h->t = next_pos;
+}

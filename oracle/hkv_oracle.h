@@ -1,0 +1,82 @@
+/*
+ * hkv_oracle.h -- plain, slow, single-threaded CPU oracle of the HashEvict
+ * decode path (test infrastructure).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the package smoke check and
+ * the CPU-baseline leg of the benchmark may load this library.  It shares no
+ * code, header, table or helper with the GPU library and the GPU library never
+ * calls it.
+ *
+ * Source of the method: "HashEvict: A Pre-Attention KV Cache Eviction
+ * Strategy using Locality-Sensitive Hashing" (arXiv 2412.16187, summary page),
+ * sections "Technical framework" (the five stages: Gaussian projection,
+ * binarisation, Hamming distance, eviction decision, dynamic in-place update)
+ * and the English abstract (query code against cached key codes, decision made
+ * before attention, the current token replaces the evicted one at every decode
+ * step, a binary code table kept in GPU memory).
+ *
+ * One handle is one eviction domain: the cache of one (sequence, KV head)
+ * pair, attended by the `group` query heads that share that KV head.
+ * All arithmetic is fp64; K/V are passed already widened to double (bf16 and
+ * fp32 inputs are exactly representable).
+ *
+ * Codes: W = ceil(n_bits / 32) uint32 words per code, bit j of the code is bit
+ * (j mod 32) of word j / 32 (LSB first).  Unused high bits are zero.
+ */
+#ifndef HKV_ORACLE_H
+#define HKV_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct orc_head orc_head;
+
+enum { ORC_PREFILL_STREAM = 0, ORC_PREFILL_TRUNCATE = 1 };
+
+/* R: [d][n_bits] fp32 values widened to double; copied. NULL on bad args. */
+orc_head* orc_create(int d, int n_bits, int budget, int group, const double* R);
+void orc_destroy(orc_head* h);
+
+/* E: project x (length d), sign-binarise, pack.  flag bit j is set when
+ * |y_j| < 1e-5 * ||x|| * ||R[:, j]|| (a sign too close to call in fp32). */
+void orc_encode(const orc_head* h, const double* x, uint32_t* code, uint32_t* flag);
+/* E over n vectors X[n][d] -> codes[n][W], flags[n][W]. */
+void orc_encode_many(const orc_head* h, int n, const double* X, uint32_t* codes, uint32_t* flags);
+
+/* P: prefill from an empty cache with the prompt K[n][d], V[n][d].
+ * inj_codes (may be NULL): [n][W] codes used instead of E(K[t]).
+ * Returns 0 on success, -1 if the cache is not empty or n < 0. */
+int orc_prefill(orc_head* h, int policy, int n, const double* K, const double* V,
+                const uint32_t* inj_codes);
+
+/* D + A: one decode step.  q: [group][d], k, v: [d].
+ * inj_qcodes [group][W] / inj_kcode [W] (may be NULL) replace E's output.
+ * Outputs (may be NULL): out [group][d], evicted slot, the codes and flags used. */
+int orc_decode_step(orc_head* h, const double* q, const double* k, const double* v,
+                    const uint32_t* inj_qcodes, const uint32_t* inj_kcode,
+                    double* out, int32_t* evicted,
+                    uint32_t* qcodes, uint32_t* qflags, uint32_t* kcode, uint32_t* kflag);
+
+/* GQA Hamming score of every occupied slot against qcodes [group][W];
+ * scores[s] for s < occupancy, -1 beyond. */
+void orc_scores(const orc_head* h, const uint32_t* qcodes, int32_t* scores);
+
+/* A alone over the current cache: out [group][d] for q [group][d]. */
+void orc_attend(const orc_head* h, const double* q, double* out);
+
+/* state export / import (checkpoint).  K, V: [budget][d]; code [budget][W];
+ * tok [budget] (-1 for an empty slot); occupancy; next token position. */
+void orc_get_state(const orc_head* h, double* K, double* V, uint32_t* code, int64_t* tok,
+                   int32_t* occupancy, int64_t* next_pos);
+void orc_set_state(orc_head* h, const double* K, const double* V, const uint32_t* code,
+                   const int64_t* tok, int32_t occupancy, int64_t next_pos);
+
+int orc_words(const orc_head* h);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
