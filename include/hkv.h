@@ -1,0 +1,172 @@
+/*
+ * hkv.h -- C ABI of libhkv.so: HashEvict LSH eviction and decode attention
+ * over a fixed-budget KV cache, on one MI355X (gfx950).
+ *
+ * The method (HashEvict summary page, "HashEvict: A Pre-Attention KV Cache
+ * Eviction Strategy using Locality-Sensitive Hashing", arXiv 2412.16187;
+ * section "Technical framework" stages 1-5 and the abstract): at every decode
+ * step, for every (sequence, KV head),
+ *   1. project the current query through a fixed Gaussian matrix R (d x b),
+ *   2. binarise the projection to a b-bit code,
+ *   3. take the Hamming distance between that code and the code of every
+ *      cached key (codes kept in a packed table in GPU memory),
+ *   4. pick the cached token farthest from the query (cosine-dissimilar, so
+ *      expected to get the lowest attention) -- before any attention score,
+ *   5. overwrite that slot with the new token's key, value and key code,
+ * and then attend over the cache, which therefore never grows past its budget.
+ *
+ * Readings taken where the page is silent (the GPU path and the CPU oracle
+ * both follow them):
+ *   - binarisation threshold 0: bit j is set iff (x . R[:, j]) > 0;
+ *   - bit j of a code is bit (j % 32) of uint32 word j / 32 (LSB first);
+ *   - grouped-query attention: the score of a slot is the SUM over the G query
+ *     heads of the KV head of their Hamming distances; query head hq belongs
+ *     to KV head hq / G;
+ *   - ties go to the lowest slot index;
+ *   - while the cache is not full a new token goes to the lowest empty slot
+ *     and nothing is evicted;
+ *   - the new token is not a candidate for eviction; attention runs over the
+ *     cache after the write, with logits q.k / sqrt(d), no mask, no rotary;
+ *   - prefill (HKV_PREFILL_STREAM, default): the prompt tokens enter one at a
+ *     time by the decode rule, each scored against its own key code (prefill
+ *     has no query); HKV_PREFILL_TRUNCATE keeps the first `budget` tokens.
+ *
+ * Conventions for every call:
+ *   - all device pointers are HIP device memory of the current device; `stream`
+ *     is a hipStream_t (NULL = the null stream).  Calls only enqueue work on
+ *     `stream` and return; inputs and outputs must stay alive until the work
+ *     has completed.  Introspection calls (hkv_get_state, hkv_debug_*) enqueue
+ *     copies as well; synchronise the stream before reading their results.
+ *   - the caller owns the workspace and every buffer it passes; the handle
+ *     owns only host metadata.  R is copied into the workspace at create.
+ *   - a handle is not safe for concurrent use from several host threads.
+ *   - errors are returned, never thrown.  Arguments are validated before
+ *     anything is enqueued, so a call that fails validation has no effect.  A
+ *     launch failure poisons the handle: every later call returns
+ *     HKV_ERR_STATE.  hkv_last_error() gives a one-line reason.
+ *   - supported: n_bits in {16, 32, 64}; head_dim in {64, 128};
+ *     n_q_heads % n_kv_heads == 0 with G = n_q_heads / n_kv_heads <= 16;
+ *     kv dtype fp32 or bf16; 1 <= budget <= 2^22 per sequence (a prefill
+ *     with HKV_PREFILL_STREAM needs budget * ceil(b/8) <= 128 KiB, its code
+ *     table lives in on-chip LDS); 1 <= batch <= 4096.
+ */
+#ifndef HKV_H
+#define HKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    HKV_OK = 0,
+    HKV_ERR_INVALID_ARG = 1,   /* null pointer, bad size, misaligned buffer */
+    HKV_ERR_UNSUPPORTED = 2,   /* a value outside the supported set above */
+    HKV_ERR_STATE = 3,         /* wrong call order, or a poisoned handle */
+    HKV_ERR_DEVICE = 4         /* a HIP runtime call failed */
+} hkv_status;
+
+enum { HKV_F32 = 0, HKV_BF16 = 1 };                        /* kv_dtype */
+enum { HKV_PREFILL_STREAM = 0, HKV_PREFILL_TRUNCATE = 1 };  /* prefill_policy */
+/* decode_schedule: FUSED = one launch per step (score, hold-out attention,
+ * merge, write); SPLIT = the separate kernels lsh_encode, hamming_argmax,
+ * evict_write, split-K attention and LSE merge (five launches). */
+enum { HKV_DECODE_FUSED = 0, HKV_DECODE_SPLIT = 1 };
+
+typedef struct {
+    int32_t batch;           /* B sequences */
+    int32_t n_q_heads;       /* Hq */
+    int32_t n_kv_heads;      /* Hkv, divides Hq */
+    int32_t head_dim;        /* d */
+    int32_t n_bits;          /* b, LSH code length */
+    int32_t kv_dtype;        /* HKV_F32 or HKV_BF16: storage of K, V, k, v */
+    int32_t prefill_policy;  /* HKV_PREFILL_* */
+    int32_t decode_schedule; /* HKV_DECODE_* */
+    int32_t max_prompt;      /* largest n_max a prefill will be given (>= 0) */
+    int32_t chunk;           /* slots per attention split; 0 = library default;
+                                otherwise a multiple of 64 in [64, 65536] */
+    const int32_t* budgets;  /* host [batch]: cache slots S_b of each sequence */
+} hkv_config;
+
+typedef struct hkv_cache hkv_cache;   /* opaque handle */
+
+/* Host-only checks of a configuration (no GPU needed).  HKV_OK if supported. */
+hkv_status hkv_validate_config(const hkv_config* cfg);
+
+/* Device workspace bytes a cache with this configuration needs (host-only).
+ * Sizes: K and V caches [B][Hkv][Smax][d] of kv dtype, code table, slot->token
+ * map, per-split partial results and the prefill code buffer; Smax = max_b S_b. */
+hkv_status hkv_workspace_bytes(const hkv_config* cfg, size_t* bytes);
+
+/* Create a cache in `workspace` (device, 256-byte aligned, >= the bytes
+ * hkv_workspace_bytes reported; owned by the caller and not touched by
+ * anyone else while the handle lives).  R_host: host fp32 [head_dim][n_bits]
+ * row-major, the Gaussian projection shared by queries and keys (method stage
+ * 1); copied.  The cache starts empty.  Synchronises `stream` once. */
+hkv_status hkv_create(const hkv_config* cfg, const float* R_host, void* workspace,
+                      size_t ws_bytes, void* stream, hkv_cache** out);
+
+/* Fill an empty cache from a prompt.  K, V: device [B][Hkv][n_max][d] kv dtype
+ * (row t of sequence b is valid for t < prompt_lens[b]); prompt_lens: host [B],
+ * 0 <= prompt_lens[b] <= n_max <= cfg.max_prompt.  Builds the b-bit code of
+ * every prompt key (method stages 1-2; an MFMA projection), applies the
+ * prefill policy, and leaves occupancy min(N_b, S_b) and next position N_b.
+ * HKV_ERR_STATE if the cache is not empty. */
+hkv_status hkv_prefill(hkv_cache* c, const void* K, const void* V, const int32_t* prompt_lens,
+                       int32_t n_max, void* stream);
+
+/* One decode step for every sequence (method stages 1-5, then attention).
+ * q: device fp32 [B][Hq][d]; k, v: device kv dtype [B][Hkv][d], the new token;
+ * out: device fp32 [B][Hq][d] = softmax(q K^T / sqrt(d)) V over the cache
+ * after the write; evicted_slot: device int32 [B][Hkv], the slot the new token
+ * was written to (the evicted one once the cache is full).  State (occupancy,
+ * next position) lives on the device, so a sequence of steps can be captured
+ * in a HIP graph and replayed.  HKV_ERR_STATE before a prefill. */
+hkv_status hkv_decode_step(hkv_cache* c, const float* q, const void* k, const void* v,
+                           float* out, int32_t* evicted_slot, void* stream);
+
+/* Free the handle (host metadata only; the workspace stays the caller's). */
+hkv_status hkv_destroy(hkv_cache* c);
+
+const char* hkv_status_str(hkv_status s);
+/* Last error detail of this handle ("" if none); c may be NULL (then the
+ * detail of the last failed hkv_create / hkv_validate_config of this thread). */
+const char* hkv_last_error(const hkv_cache* c);
+
+/* Checkpoint export (device -> caller device buffers; any may be NULL):
+ * K, V [B][Hkv][Smax][d] kv dtype; codes [B][Hkv][Smax][W] uint32 with
+ * W = ceil(b/32) (unused high bits zero); slot_token [B][Hkv][Smax] int32
+ * (-1 = empty slot); head_state [B][Hkv][2] int32 = (occupancy, next position). */
+hkv_status hkv_get_state(const hkv_cache* c, void* K, void* V, uint32_t* codes,
+                         int32_t* slot_token, int32_t* head_state, void* stream);
+/* Checkpoint import, same layouts; all five buffers required.  Marks the
+ * cache as prefilled. */
+hkv_status hkv_set_state(hkv_cache* c, const void* K, const void* V, const uint32_t* codes,
+                         const int32_t* slot_token, const int32_t* head_state, void* stream);
+
+/* Codes the last decode step computed: qcodes [B][Hq][W], kcodes [B][Hkv][W]
+ * (uint32 device buffers). */
+hkv_status hkv_debug_last_codes(const hkv_cache* c, uint32_t* qcodes, uint32_t* kcodes,
+                                void* stream);
+/* Codes the last prefill computed for every prompt key:
+ * codes [B][Hkv][n_max][W] (uint32 device buffer; rows t >= prompt_lens[b] are
+ * unspecified). */
+hkv_status hkv_debug_prefill_codes(const hkv_cache* c, uint32_t* codes, void* stream);
+/* GQA Hamming score of every slot against the given query codes
+ * qcodes [B][Hq][W] (device): scores [B][Hkv][Smax] int32 (device), -1 for
+ * slots at or beyond the occupancy. */
+hkv_status hkv_debug_scores(const hkv_cache* c, const uint32_t* qcodes, int32_t* scores,
+                            void* stream);
+
+/* Stand-alone encoder (method stages 1-2): codes [n][W] uint32 (device) of the
+ * rows X [n][d] (device, fp32 if x_dtype == HKV_F32 else bf16) under the
+ * cache's R. */
+hkv_status hkv_encode(const hkv_cache* c, const void* X, int32_t x_dtype, int32_t n,
+                      uint32_t* codes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HKV_H */

@@ -1,0 +1,280 @@
+// hkv_api.cpp -- the C ABI of libhkv.so: handle, validation before any
+// enqueue, workspace carving, launch sequencing, checkpoint and introspection.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "hkv.h"
+#include "hkv_kernels.h"
+#include "hkv_layout.h"
+
+struct hkv_cache {
+    hkv::Layout lay;
+    hkv::DevCache dev;
+    std::vector<int32_t> budgets;
+    std::vector<int32_t> plens;
+    int device = 0;
+    int last_n_max = 0;
+    bool prefilled = false;
+    bool stepped = false;
+    bool poisoned = false;
+    bool debug_sync = false;
+    std::string err;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+hkv_status fail(hkv_cache* c, hkv_status s, const std::string& msg)
+{
+    if (c)
+        c->err = msg;
+    else
+        g_err = msg;
+    return s;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Checks a launch; a failure poisons the handle.
+hkv_status check_launch(hkv_cache* c, hipError_t e, hipStream_t st, const char* what)
+{
+    if (e == hipSuccess && c->debug_sync) e = hipStreamSynchronize(st);
+    if (e == hipSuccess && c->debug_sync) e = hipGetLastError();
+    if (e != hipSuccess) {
+        c->poisoned = true;
+        return fail(c, HKV_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
+    }
+    return HKV_OK;
+}
+
+hkv_status usable(hkv_cache* c)
+{
+    if (!c) return HKV_ERR_INVALID_ARG;
+    if (c->poisoned) return fail(c, HKV_ERR_STATE, "handle poisoned by an earlier device error");
+    return HKV_OK;
+}
+
+}  // namespace
+
+extern "C" const char* hkv_last_error(const hkv_cache* c) { return c ? c->err.c_str() : g_err.c_str(); }
+
+extern "C" hkv_status hkv_create(const hkv_config* cfg, const float* R_host, void* workspace,
+                                 size_t ws_bytes, void* stream, hkv_cache** out)
+{
+    char msg[256] = {0};
+    if (!out) return fail(nullptr, HKV_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    hkv::Layout L;
+    hkv_status s = hkv::compute_layout(cfg, &L, msg, sizeof(msg));
+    if (s != HKV_OK) return fail(nullptr, s, msg);
+    if (!R_host) return fail(nullptr, HKV_ERR_INVALID_ARG, "R is NULL");
+    if (!workspace) return fail(nullptr, HKV_ERR_INVALID_ARG, "workspace is NULL");
+    if (!aligned(workspace, hkv::kAlign)) return fail(nullptr, HKV_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+    if (ws_bytes < L.total) {
+        snprintf(msg, sizeof(msg), "workspace has %zu bytes, %zu needed", ws_bytes, L.total);
+        return fail(nullptr, HKV_ERR_INVALID_ARG, msg);
+    }
+    hipStream_t st = (hipStream_t)stream;
+    hkv_cache* c = new hkv_cache();
+    c->lay = L;
+    c->budgets.assign(cfg->budgets, cfg->budgets + cfg->batch);
+    c->plens.assign(cfg->batch, 0);
+    const char* dbg = getenv("HKV_DEBUG");
+    c->debug_sync = dbg && dbg[0] == '1';
+    if (hipGetDevice(&c->device) != hipSuccess) c->device = 0;
+
+    char* ws = (char*)workspace;
+    hkv::DevCache& d = c->dev;
+    d.R = (const float*)(ws + L.off_R);
+    d.budget = (const int*)(ws + L.off_budget);
+    d.plen = (const int*)(ws + L.off_plen);
+    d.state = (int*)(ws + L.off_state);
+    d.K = ws + L.off_K;
+    d.V = ws + L.off_V;
+    d.code = ws + L.off_code;
+    d.tok = (int*)(ws + L.off_tok);
+    d.dbg_q = (uint32_t*)(ws + L.off_dbg_q);
+    d.dbg_k = (uint32_t*)(ws + L.off_dbg_k);
+    d.part = (float*)(ws + L.off_part);
+    d.cand_key = (unsigned long long*)(ws + L.off_cand_key);
+    d.cand_lg = (float*)(ws + L.off_cand_lg);
+    d.count = (unsigned*)(ws + L.off_count);
+    d.evict = (int*)(ws + L.off_evict);
+    d.pcode = ws + L.off_pcode;
+    d.B = L.B; d.Hq = L.Hq; d.Hkv = L.Hkv; d.G = L.G; d.d = L.d; d.bits = L.bits; d.W = L.W;
+    d.Smax = L.Smax; d.chunk = L.chunk; d.nsplit = L.nsplit; d.cstride = L.cstride;
+    d.kv_bf16 = L.kv_dtype == HKV_BF16;
+    d.code_slots = (long long)L.code_slots;
+    d.pcode_slots = (long long)L.pcode_slots;
+
+    hipError_t e = hipMemcpyAsync((void*)d.R, R_host, (size_t)L.d * L.bits * sizeof(float),
+                                  hipMemcpyHostToDevice, st);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync((void*)d.budget, cfg->budgets, (size_t)L.B * sizeof(int32_t),
+                           hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hkv::launch_reset(d, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) {
+        std::string m = std::string("hkv_create: ") + hipGetErrorString(e);
+        delete c;
+        return fail(nullptr, HKV_ERR_DEVICE, m);
+    }
+    *out = c;
+    return HKV_OK;
+}
+
+extern "C" hkv_status hkv_destroy(hkv_cache* c)
+{
+    if (!c) return HKV_ERR_INVALID_ARG;
+    delete c;
+    return HKV_OK;
+}
+
+extern "C" hkv_status hkv_prefill(hkv_cache* c, const void* K, const void* V, const int32_t* prompt_lens,
+                                  int32_t n_max, void* stream)
+{
+    hkv_status s = usable(c);
+    if (s != HKV_OK) return s;
+    if (c->prefilled) return fail(c, HKV_ERR_STATE, "hkv_prefill: cache is not empty");
+    if (!prompt_lens) return fail(c, HKV_ERR_INVALID_ARG, "hkv_prefill: prompt_lens is NULL");
+    if (n_max < 0 || n_max > c->lay.max_prompt)
+        return fail(c, HKV_ERR_INVALID_ARG,
+                    "hkv_prefill: n_max " + std::to_string(n_max) + " outside [0, max_prompt = " +
+                        std::to_string(c->lay.max_prompt) + "]");
+    for (int b = 0; b < c->lay.B; ++b)
+        if (prompt_lens[b] < 0 || prompt_lens[b] > n_max)
+            return fail(c, HKV_ERR_INVALID_ARG,
+                        "hkv_prefill: prompt_lens[" + std::to_string(b) + "] outside [0, n_max]");
+    if (n_max > 0 && (!K || !V)) return fail(c, HKV_ERR_INVALID_ARG, "hkv_prefill: K or V is NULL");
+    if (n_max > 0 && (!aligned(K, 16) || !aligned(V, 16)))
+        return fail(c, HKV_ERR_INVALID_ARG, "hkv_prefill: K and V must be 16-byte aligned");
+    hipStream_t st = (hipStream_t)stream;
+    c->plens.assign(prompt_lens, prompt_lens + c->lay.B);
+    hipError_t e = hipMemcpyAsync((void*)c->dev.plen, c->plens.data(), (size_t)c->lay.B * sizeof(int32_t),
+                                  hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);   // plens is host memory of the handle
+    if (e == hipSuccess) e = hkv::launch_prefill(c->dev, K, V, n_max, c->lay.prefill_policy, st);
+    s = check_launch(c, e, st, "hkv_prefill");
+    if (s != HKV_OK) return s;
+    c->last_n_max = n_max;
+    c->prefilled = true;
+    return HKV_OK;
+}
+
+extern "C" hkv_status hkv_decode_step(hkv_cache* c, const float* q, const void* k, const void* v,
+                                      float* out, int32_t* evicted_slot, void* stream)
+{
+    hkv_status s = usable(c);
+    if (s != HKV_OK) return s;
+    if (!c->prefilled) return fail(c, HKV_ERR_STATE, "hkv_decode_step: call hkv_prefill or hkv_set_state first");
+    if (!q || !k || !v || !out || !evicted_slot)
+        return fail(c, HKV_ERR_INVALID_ARG, "hkv_decode_step: NULL buffer");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+        return fail(c, HKV_ERR_INVALID_ARG, "hkv_decode_step: q, k, v must be 16-byte aligned");
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = c->lay.schedule == HKV_DECODE_FUSED
+                       ? hkv::launch_decode_fused(c->dev, q, k, v, out, evicted_slot, st)
+                       : hkv::launch_decode_split(c->dev, q, k, v, out, evicted_slot, st);
+    s = check_launch(c, e, st, "hkv_decode_step");
+    if (s == HKV_OK) c->stepped = true;
+    return s;
+}
+
+extern "C" hkv_status hkv_get_state(const hkv_cache* cc, void* K, void* V, uint32_t* codes,
+                                    int32_t* slot_token, int32_t* head_state, void* stream)
+{
+    hkv_cache* c = const_cast<hkv_cache*>(cc);
+    hkv_status s = usable(c);
+    if (s != HKV_OK) return s;
+    const hkv::Layout& L = c->lay;
+    hipStream_t st = (hipStream_t)stream;
+    const size_t heads = (size_t)L.B * L.Hkv;
+    const size_t kv = heads * L.Smax * L.d * L.es;
+    hipError_t e = hipSuccess;
+    if (K) e = hipMemcpyAsync(K, c->dev.K, kv, hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess && V) e = hipMemcpyAsync(V, c->dev.V, kv, hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess && codes) e = hkv::launch_export_codes(c->dev, codes, st);
+    if (e == hipSuccess && slot_token)
+        e = hipMemcpyAsync(slot_token, c->dev.tok, heads * L.Smax * 4, hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess && head_state)
+        e = hipMemcpyAsync(head_state, c->dev.state, heads * 8, hipMemcpyDeviceToDevice, st);
+    return check_launch(c, e, st, "hkv_get_state");
+}
+
+extern "C" hkv_status hkv_set_state(hkv_cache* c, const void* K, const void* V, const uint32_t* codes,
+                                    const int32_t* slot_token, const int32_t* head_state, void* stream)
+{
+    hkv_status s = usable(c);
+    if (s != HKV_OK) return s;
+    if (!K || !V || !codes || !slot_token || !head_state)
+        return fail(c, HKV_ERR_INVALID_ARG, "hkv_set_state: all five buffers are required");
+    const hkv::Layout& L = c->lay;
+    hipStream_t st = (hipStream_t)stream;
+    const size_t heads = (size_t)L.B * L.Hkv;
+    const size_t kv = heads * L.Smax * L.d * L.es;
+    hipError_t e = hipMemcpyAsync(c->dev.K, K, kv, hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(c->dev.V, V, kv, hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess) e = hkv::launch_import_codes(c->dev, codes, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(c->dev.tok, slot_token, heads * L.Smax * 4, hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(c->dev.state, head_state, heads * 8, hipMemcpyDeviceToDevice, st);
+    s = check_launch(c, e, st, "hkv_set_state");
+    if (s == HKV_OK) c->prefilled = true;
+    return s;
+}
+
+extern "C" hkv_status hkv_debug_last_codes(const hkv_cache* cc, uint32_t* qcodes, uint32_t* kcodes, void* stream)
+{
+    hkv_cache* c = const_cast<hkv_cache*>(cc);
+    hkv_status s = usable(c);
+    if (s != HKV_OK) return s;
+    if (!c->stepped) return fail(c, HKV_ERR_STATE, "hkv_debug_last_codes: no decode step yet");
+    const hkv::Layout& L = c->lay;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = hipSuccess;
+    if (qcodes) e = hipMemcpyAsync(qcodes, c->dev.dbg_q, (size_t)L.B * L.Hq * L.W * 4, hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess && kcodes)
+        e = hipMemcpyAsync(kcodes, c->dev.dbg_k, (size_t)L.B * L.Hkv * L.W * 4, hipMemcpyDeviceToDevice, st);
+    return check_launch(c, e, st, "hkv_debug_last_codes");
+}
+
+extern "C" hkv_status hkv_debug_prefill_codes(const hkv_cache* cc, uint32_t* codes, void* stream)
+{
+    hkv_cache* c = const_cast<hkv_cache*>(cc);
+    hkv_status s = usable(c);
+    if (s != HKV_OK) return s;
+    if (!c->prefilled) return fail(c, HKV_ERR_STATE, "hkv_debug_prefill_codes: no prefill yet");
+    if (!codes) return fail(c, HKV_ERR_INVALID_ARG, "hkv_debug_prefill_codes: codes is NULL");
+    hipStream_t st = (hipStream_t)stream;
+    return check_launch(c, hkv::launch_export_pcodes(c->dev, codes, c->last_n_max, st), st,
+                        "hkv_debug_prefill_codes");
+}
+
+extern "C" hkv_status hkv_debug_scores(const hkv_cache* cc, const uint32_t* qcodes, int32_t* scores, void* stream)
+{
+    hkv_cache* c = const_cast<hkv_cache*>(cc);
+    hkv_status s = usable(c);
+    if (s != HKV_OK) return s;
+    if (!qcodes || !scores) return fail(c, HKV_ERR_INVALID_ARG, "hkv_debug_scores: NULL buffer");
+    hipStream_t st = (hipStream_t)stream;
+    return check_launch(c, hkv::launch_scores(c->dev, qcodes, scores, st), st, "hkv_debug_scores");
+}
+
+extern "C" hkv_status hkv_encode(const hkv_cache* cc, const void* X, int32_t x_dtype, int32_t n,
+                                 uint32_t* codes, void* stream)
+{
+    hkv_cache* c = const_cast<hkv_cache*>(cc);
+    hkv_status s = usable(c);
+    if (s != HKV_OK) return s;
+    if (n < 0) return fail(c, HKV_ERR_INVALID_ARG, "hkv_encode: n < 0");
+    if (x_dtype != HKV_F32 && x_dtype != HKV_BF16) return fail(c, HKV_ERR_UNSUPPORTED, "hkv_encode: x_dtype");
+    if (n > 0 && (!X || !codes)) return fail(c, HKV_ERR_INVALID_ARG, "hkv_encode: NULL buffer");
+    hipStream_t st = (hipStream_t)stream;
+    return check_launch(c, hkv::launch_encode_rows(c->dev, X, x_dtype == HKV_BF16, n, codes, st), st,
+                        "hkv_encode");
+}

@@ -1,0 +1,6 @@
+// hkv_consts.h -- constants shared by the host layout code and the kernels.
+#pragma once
+
+namespace hkv {
+constexpr int kScoreChunk = 4096;   // slots per block of the stand-alone hamming_argmax
+}  // namespace hkv

@@ -1,0 +1,54 @@
+// hkv_kernels.h -- device-side view of a cache and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace hkv {
+
+// Pointers into the caller's workspace plus the sizes every kernel needs.
+struct DevCache {
+    const float* R;                 // [d][bits] fp32
+    const int* budget;              // [B]
+    const int* plen;                // [B] prompt lengths of the last prefill
+    int* state;                     // [B][Hkv][2]: occupancy, next position
+    void* K;                        // [B][Hkv][Smax][d] kv dtype
+    void* V;
+    void* code;                     // [B][Hkv][code_slots] codes of cb bytes
+    int* tok;                       // [B][Hkv][Smax] token held by a slot, -1 empty
+    uint32_t* dbg_q;                // [B][Hq][W] query codes of the last step
+    uint32_t* dbg_k;                // [B][Hkv][W] key codes of the last step
+    float* part;                    // [B][Hq][nsplit][d + 4]: acc[d], m, l
+    unsigned long long* cand_key;   // [B][Hkv][cstride] (score << 32) | ~slot, 0 = none
+    float* cand_lg;                 // [B][Hkv][cstride][G] logits (base 2) of the candidate
+    unsigned* count;                // [B][Hkv] blocks of the step that have finished
+    int* evict;                     // [B][Hkv] slot chosen this step (split schedule)
+    void* pcode;                    // [B][Hkv][pcode_slots] prompt key codes
+    int B, Hq, Hkv, G, d, bits, W, Smax, chunk, nsplit;
+    int cstride;                    // candidates per head in cand_key / cand_lg
+    int kv_bf16;
+    long long code_slots, pcode_slots;
+};
+
+// decode, fused schedule: one launch
+hipError_t launch_decode_fused(const DevCache& c, const float* q, const void* k, const void* v,
+                               float* out, int* evicted, hipStream_t st);
+// decode, split schedule: lsh_encode, hamming_argmax, evict_write, attention, merge
+hipError_t launch_decode_split(const DevCache& c, const float* q, const void* k, const void* v,
+                               float* out, int* evicted, hipStream_t st);
+hipError_t launch_scores(const DevCache& c, const uint32_t* qcodes, int* scores, hipStream_t st);
+hipError_t launch_encode_rows(const DevCache& c, const void* X, int x_bf16, int n,
+                              uint32_t* codes, hipStream_t st);
+
+// prefill
+hipError_t launch_reset(const DevCache& c, hipStream_t st);
+hipError_t launch_prefill(const DevCache& c, const void* K, const void* V, int n_max, int policy,
+                          hipStream_t st);
+// checkpoint
+hipError_t launch_export_codes(const DevCache& c, uint32_t* codes, hipStream_t st);
+hipError_t launch_import_codes(const DevCache& c, const uint32_t* codes, hipStream_t st);
+hipError_t launch_export_pcodes(const DevCache& c, uint32_t* codes, int n_max, hipStream_t st);
+
+}  // namespace hkv

@@ -1,0 +1,37 @@
+// hkv_layout.h -- host-side configuration checks and the workspace layout.
+// Host-only: no HIP types, so the validation can be compiled and tested
+// without a GPU.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "hkv.h"
+#include "hkv_consts.h"
+
+namespace hkv {
+
+constexpr int kMaxGroup = 16;
+constexpr int kMaxBudget = 1 << 22;
+constexpr int kMaxBatch = 4096;
+constexpr size_t kLdsTableBytes = 128 * 1024;   // prefill code table in LDS
+constexpr int kDefaultChunk = 512;
+constexpr size_t kAlign = 256;
+
+struct Layout {
+    int B, Hq, Hkv, G, d, bits, W, cb, es;   // cb: code bytes, es: kv element bytes
+    int kv_dtype, prefill_policy, schedule;
+    int Smax, chunk, nsplit, cstride, max_prompt;
+    size_t code_slots;     // slots per head in the code table (padded)
+    size_t pcode_slots;    // prompt positions per head in the prefill code buffer (padded)
+    // byte offsets into the workspace
+    size_t off_R, off_budget, off_plen, off_state, off_K, off_V, off_code, off_tok;
+    size_t off_dbg_q, off_dbg_k, off_part, off_cand_key, off_cand_lg, off_count;
+    size_t off_evict, off_pcode;
+    size_t total;
+};
+
+// Fills `lay` and returns HKV_OK, or an error code with a reason in `err`.
+hkv_status compute_layout(const hkv_config* cfg, Layout* lay, char* err, size_t errlen);
+
+}  // namespace hkv

@@ -1,0 +1,130 @@
+// hkv_validate.cpp -- host-only configuration checks and workspace layout.
+#include <cstdio>
+#include <cstring>
+
+#include "hkv_layout.h"
+
+namespace hkv {
+
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+hkv_status compute_layout(const hkv_config* cfg, Layout* L, char* err, size_t errlen)
+{
+#define FAIL(code, ...)                                  \
+    do {                                                 \
+        if (err && errlen) snprintf(err, errlen, __VA_ARGS__); \
+        return code;                                     \
+    } while (0)
+    if (!cfg) FAIL(HKV_ERR_INVALID_ARG, "config is NULL");
+    if (!cfg->budgets) FAIL(HKV_ERR_INVALID_ARG, "budgets is NULL");
+    if (cfg->batch < 1 || cfg->batch > kMaxBatch)
+        FAIL(HKV_ERR_UNSUPPORTED, "batch %d outside [1, %d]", cfg->batch, kMaxBatch);
+    if (cfg->n_kv_heads < 1 || cfg->n_q_heads < 1)
+        FAIL(HKV_ERR_INVALID_ARG, "head counts must be positive");
+    if (cfg->n_q_heads % cfg->n_kv_heads != 0)
+        FAIL(HKV_ERR_UNSUPPORTED, "n_q_heads %d not a multiple of n_kv_heads %d", cfg->n_q_heads,
+             cfg->n_kv_heads);
+    const int G = cfg->n_q_heads / cfg->n_kv_heads;
+    if (G > kMaxGroup) FAIL(HKV_ERR_UNSUPPORTED, "group size %d > %d", G, kMaxGroup);
+    if (cfg->head_dim != 64 && cfg->head_dim != 128)
+        FAIL(HKV_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", cfg->head_dim);
+    if (cfg->n_bits != 16 && cfg->n_bits != 32 && cfg->n_bits != 64)
+        FAIL(HKV_ERR_UNSUPPORTED, "n_bits %d not in {16, 32, 64}", cfg->n_bits);
+    if (cfg->kv_dtype != HKV_F32 && cfg->kv_dtype != HKV_BF16)
+        FAIL(HKV_ERR_UNSUPPORTED, "kv_dtype %d unknown", cfg->kv_dtype);
+    if (cfg->prefill_policy != HKV_PREFILL_STREAM && cfg->prefill_policy != HKV_PREFILL_TRUNCATE)
+        FAIL(HKV_ERR_UNSUPPORTED, "prefill_policy %d unknown", cfg->prefill_policy);
+    if (cfg->decode_schedule != HKV_DECODE_FUSED && cfg->decode_schedule != HKV_DECODE_SPLIT)
+        FAIL(HKV_ERR_UNSUPPORTED, "decode_schedule %d unknown", cfg->decode_schedule);
+    if (cfg->max_prompt < 0 || cfg->max_prompt > (1 << 24))
+        FAIL(HKV_ERR_UNSUPPORTED, "max_prompt %d outside [0, 2^24]", cfg->max_prompt);
+    if (cfg->chunk != 0 && (cfg->chunk < 64 || cfg->chunk > 65536 || cfg->chunk % 64 != 0))
+        FAIL(HKV_ERR_UNSUPPORTED, "chunk %d must be 0 or a multiple of 64 in [64, 65536]",
+             cfg->chunk);
+    const int cb = cfg->n_bits / 8;
+    int Smax = 0;
+    for (int b = 0; b < cfg->batch; ++b) {
+        const int s = cfg->budgets[b];
+        if (s < 1 || s > kMaxBudget)
+            FAIL(HKV_ERR_UNSUPPORTED, "budget[%d] = %d outside [1, %d]", b, s, kMaxBudget);
+        if (cfg->prefill_policy == HKV_PREFILL_STREAM && (size_t)s * cb > kLdsTableBytes)
+            FAIL(HKV_ERR_UNSUPPORTED,
+                 "budget[%d] = %d: its %d-byte code table exceeds the %zu-byte on-chip table of "
+                 "the STREAM prefill", b, s, s * cb, kLdsTableBytes);
+        if (s > Smax) Smax = s;
+    }
+
+    Layout& l = *L;
+    memset(&l, 0, sizeof(l));
+    l.B = cfg->batch; l.Hq = cfg->n_q_heads; l.Hkv = cfg->n_kv_heads; l.G = G;
+    l.d = cfg->head_dim; l.bits = cfg->n_bits; l.W = (cfg->n_bits + 31) / 32; l.cb = cb;
+    l.es = cfg->kv_dtype == HKV_BF16 ? 2 : 4;
+    l.kv_dtype = cfg->kv_dtype; l.prefill_policy = cfg->prefill_policy;
+    l.schedule = cfg->decode_schedule;
+    l.Smax = Smax;
+    l.chunk = cfg->chunk ? cfg->chunk : kDefaultChunk;
+    l.nsplit = (Smax + l.chunk - 1) / l.chunk;
+    {
+        const int nscore = (Smax + kScoreChunk - 1) / kScoreChunk;
+        l.cstride = l.nsplit > nscore ? l.nsplit : nscore;
+    }
+    l.max_prompt = cfg->max_prompt;
+    l.code_slots = align_up((size_t)Smax, 64);
+    l.pcode_slots = align_up((size_t)(cfg->max_prompt > 0 ? cfg->max_prompt : 1), 64);
+
+    const size_t heads = (size_t)l.B * l.Hkv;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off = align_up(off + bytes, kAlign);
+        return o;
+    };
+    l.off_R = take((size_t)l.d * l.bits * 4);
+    l.off_budget = take((size_t)l.B * 4);
+    l.off_plen = take((size_t)l.B * 4);
+    l.off_state = take(heads * 2 * 4);
+    l.off_K = take(heads * Smax * l.d * l.es);
+    l.off_V = take(heads * Smax * l.d * l.es);
+    l.off_code = take(heads * l.code_slots * cb);
+    l.off_tok = take(heads * Smax * 4);
+    l.off_dbg_q = take((size_t)l.B * l.Hq * l.W * 4);
+    l.off_dbg_k = take(heads * l.W * 4);
+    l.off_part = take((size_t)l.B * l.Hq * l.nsplit * (l.d + 4) * 4);
+    l.off_cand_key = take(heads * l.cstride * 8);
+    l.off_cand_lg = take(heads * l.cstride * G * 4);
+    l.off_count = take(heads * 4);
+    l.off_evict = take(heads * 4);
+    l.off_pcode = take(heads * l.pcode_slots * cb);
+    l.total = off;
+    return HKV_OK;
+#undef FAIL
+}
+
+}  // namespace hkv
+
+extern "C" hkv_status hkv_validate_config(const hkv_config* cfg)
+{
+    hkv::Layout l;
+    return hkv::compute_layout(cfg, &l, nullptr, 0);
+}
+
+extern "C" hkv_status hkv_workspace_bytes(const hkv_config* cfg, size_t* bytes)
+{
+    if (!bytes) return HKV_ERR_INVALID_ARG;
+    hkv::Layout l;
+    hkv_status s = hkv::compute_layout(cfg, &l, nullptr, 0);
+    if (s == HKV_OK) *bytes = l.total;
+    return s;
+}
+
+extern "C" const char* hkv_status_str(hkv_status s)
+{
+    switch (s) {
+    case HKV_OK: return "HKV_OK";
+    case HKV_ERR_INVALID_ARG: return "HKV_ERR_INVALID_ARG";
+    case HKV_ERR_UNSUPPORTED: return "HKV_ERR_UNSUPPORTED";
+    case HKV_ERR_STATE: return "HKV_ERR_STATE";
+    case HKV_ERR_DEVICE: return "HKV_ERR_DEVICE";
+    }
+    return "HKV_UNKNOWN_STATUS";
+}

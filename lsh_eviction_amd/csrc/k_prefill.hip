@@ -1,0 +1,325 @@
+// k_prefill.hip -- prompt code build and prefill selection on gfx950.
+//
+// Method stages 1-2 (HashEvict summary page, "Technical framework"): every
+// prompt key is projected through the Gaussian matrix R and sign-binarised.
+// Projecting N keys is a dense N x d x b contraction, so it runs on the
+// matrix cores (fp32 MFMA 16x16x4: fp32 semantics, so the signs agree with an
+// fp64 reference outside the flagged band).
+//
+// Prefill rule (the page does not describe prefill; reading used here): with
+// the STREAM policy the prompt enters the cache one token at a time by the
+// decode rule, each token scored against its own key code; TRUNCATE keeps
+// the first `budget` tokens.  The sequential selection keeps the whole code
+// table of one (sequence, KV head) in LDS.
+#include <type_traits>
+
+#include "hkv.h"
+#include "hkv_device.h"
+
+namespace hkv {
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// slot -> token map and per-head state before a prefill
+__global__ void k_prefill_init(DevCache c)
+{
+    const int h = blockIdx.y, b = blockIdx.z, head = b * c.Hkv + h;
+    const int N = c.plen[b], S = c.budget[b];
+    const int occ = min(N, S);
+    const int s = blockIdx.x * blockDim.x + threadIdx.x;
+    if (s < c.Smax) c.tok[(size_t)head * c.Smax + s] = s < occ ? s : -1;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        c.state[2 * head] = occ;
+        c.state[2 * head + 1] = N;
+        c.count[head] = 0;
+    }
+}
+
+// reset of an empty cache (create)
+__global__ void k_reset(DevCache c)
+{
+    const int h = blockIdx.y, b = blockIdx.z, head = b * c.Hkv + h;
+    const int s = blockIdx.x * blockDim.x + threadIdx.x;
+    if (s < c.Smax) c.tok[(size_t)head * c.Smax + s] = -1;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        c.state[2 * head] = 0;
+        c.state[2 * head + 1] = 0;
+        c.count[head] = 0;
+    }
+}
+
+// Codes of prompt keys [64 * blockIdx.x, +64) of one head on the matrix
+// cores.  Wave w takes 16 keys; lane l feeds key row (l % 16) and the quarter
+// (l / 16) of the head dimension, so MFMA step s contracts dimension
+// (l / 16) * D/4 + s.  The 16 x 16 result tile of bit columns nt*16 .. +15 is
+// sign-packed by a wave ballot per accumulator register.
+template <int D, int BITS, typename KT>
+__global__ __launch_bounds__(256) void k_project_mfma(DevCache c, const KT* __restrict__ Kp, int n_max)
+{
+    using CT = typename CodeT<BITS>::T;
+    constexpr int DQ = D / 4;          // dimensions fed by one lane
+    constexpr int NT = BITS / 16;      // bit tiles
+    __shared__ float sR[D * BITS];
+    const int h = blockIdx.y, b = blockIdx.z, head = b * c.Hkv + h;
+    const int N = c.plen[b];
+    const int t0 = blockIdx.x * 64;
+    if (t0 >= N) return;
+    for (int i = threadIdx.x; i < D * BITS; i += blockDim.x) sR[i] = c.R[i];
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int row = t0 + wave * 16 + (lane & 15);
+    const int qd = lane >> 4;
+
+    float x[DQ];
+    if (row < N) {
+        const KT* src = Kp + ((size_t)head * n_max + row) * D + qd * DQ;
+        constexpr int EPL = Vec16<KT>::EPL;
+#pragma unroll
+        for (int v = 0; v < DQ / EPL; ++v) {
+            const uint4 raw = *reinterpret_cast<const uint4*>(src + v * EPL);
+            float f[EPL];
+            Vec16<KT>::cvt(raw, f);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) x[v * EPL + e] = f[e];
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < DQ; ++s) x[s] = 0.f;
+    }
+
+    unsigned long long mk[NT][4];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const float* rcol = sR + (size_t)(qd * DQ) * BITS + nt * 16 + (lane & 15);
+#pragma unroll
+        for (int s = 0; s < DQ; ++s)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[s], rcol[s * BITS], acc, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mk[nt][r] = __ballot(acc[r] > 0.f);
+    }
+    // result row i = 4 * (lane / 16) + r sits in register r of lanes 16 * (i / 4) + col
+    if (lane < 16) {
+        const int a = lane >> 2, r = lane & 3;
+        unsigned long long cde = 0;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const unsigned long long m = r == 0 ? mk[nt][0] : r == 1 ? mk[nt][1] : r == 2 ? mk[nt][2] : mk[nt][3];
+            cde |= ((m >> (16 * a)) & 0xFFFFull) << (16 * nt);
+        }
+        const int t = t0 + wave * 16 + lane;
+        if (t < N) reinterpret_cast<CT*>(c.pcode)[(size_t)head * c.pcode_slots + t] = (CT)cde;
+    }
+}
+
+__device__ __forceinline__ unsigned wave_max_u32(unsigned v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        const unsigned o = __shfl_xor(v, m);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+// STREAM selection for one (sequence, KV head): prompt tokens t >= S evict,
+// one after the other, the slot whose code is farthest from their own code
+// (ties to the lowest slot).  The code table stays in LDS; tok[] records the
+// token of every slot.
+template <int BITS>
+__global__ __launch_bounds__(1024) void k_prefill_select(DevCache c)
+{
+    using CT = typename CodeT<BITS>::T;
+    constexpr int VS = 16 / sizeof(CT);
+    extern __shared__ uint4 dyn_lds[];
+    CT* table = reinterpret_cast<CT*>(dyn_lds);
+    __shared__ unsigned s_red[16];
+    const int h = blockIdx.x, b = blockIdx.y, head = b * c.Hkv + h;
+    const int N = c.plen[b], S = c.budget[b];
+    if (N <= S) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const CT* pc = reinterpret_cast<const CT*>(c.pcode) + (size_t)head * c.pcode_slots;
+    int* tok = c.tok + (size_t)head * c.Smax;
+    const int Sp = (S + 63) & ~63;
+    for (int s = tid; s < Sp; s += blockDim.x) table[s] = s < S ? pc[s] : (CT)0;
+    __syncthreads();
+    for (int t = S; t < N; ++t) {
+        const CT cq = pc[t];
+        unsigned best = 0;
+        for (int s = tid * VS; s < S; s += 1024 * VS) {
+            const uint4 raw = *reinterpret_cast<const uint4*>(table + s);
+            CT cs[VS];
+            __builtin_memcpy(cs, &raw, 16);
+#pragma unroll
+            for (int u = 0; u < VS; ++u) {
+                const unsigned k = (s + u < S)
+                                       ? (((unsigned)popc((CT)(cq ^ cs[u])) << 24) | (0xFFFFFFu - (unsigned)(s + u)))
+                                       : 0u;
+                best = k > best ? k : best;
+            }
+        }
+        best = wave_max_u32(best);
+        if (lane == 0) s_red[wave] = best;
+        __syncthreads();
+        if (wave == 0) {
+            unsigned v = lane < 16 ? s_red[lane] : 0u;
+            v = wave_max_u32(v);
+            if (lane == 0) {
+                const int e = (int)(0xFFFFFFu - (v & 0xFFFFFFu));
+                table[e] = cq;
+                tok[e] = t;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// K, V and codes of the kept tokens into their slots; 16 lanes per row.
+template <int D, int BITS, typename KT>
+__global__ __launch_bounds__(256) void k_prefill_gather(DevCache c, const KT* __restrict__ Kp,
+                                                        const KT* __restrict__ Vp, int n_max)
+{
+    using CT = typename CodeT<BITS>::T;
+    constexpr int CH = D * (int)sizeof(KT) / 16;   // 16-byte chunks per row
+    const int h = blockIdx.y, b = blockIdx.z, head = b * c.Hkv + h;
+    const int occ = min(c.plen[b], c.budget[b]);
+    const int s = blockIdx.x * 16 + threadIdx.x / 16;
+    const int j = threadIdx.x % 16;
+    if (s >= occ) return;
+    const size_t rowbase = (size_t)head * c.Smax;
+    const int t = c.tok[rowbase + s];
+    const uint4* ks = reinterpret_cast<const uint4*>(Kp + ((size_t)head * n_max + t) * D);
+    const uint4* vs = reinterpret_cast<const uint4*>(Vp + ((size_t)head * n_max + t) * D);
+    uint4* kd = reinterpret_cast<uint4*>(reinterpret_cast<KT*>(c.K) + (rowbase + s) * D);
+    uint4* vd = reinterpret_cast<uint4*>(reinterpret_cast<KT*>(c.V) + (rowbase + s) * D);
+    for (int q = j; q < CH; q += 16) {
+        kd[q] = ks[q];
+        vd[q] = vs[q];
+    }
+    if (j == 0)
+        reinterpret_cast<CT*>(c.code)[(size_t)head * c.code_slots + s] =
+            reinterpret_cast<const CT*>(c.pcode)[(size_t)head * c.pcode_slots + t];
+}
+
+template <int BITS>
+__global__ void k_export_codes(DevCache c, uint32_t* __restrict__ out)
+{
+    using CT = typename CodeT<BITS>::T;
+    const int h = blockIdx.y, b = blockIdx.z, head = b * c.Hkv + h;
+    const int s = blockIdx.x * blockDim.x + threadIdx.x;
+    if (s >= c.Smax) return;
+    const unsigned long long v = reinterpret_cast<const CT*>(c.code)[(size_t)head * c.code_slots + s];
+    store_words(out + ((size_t)head * c.Smax + s) * c.W, c.W, v);
+}
+
+template <int BITS>
+__global__ void k_import_codes(DevCache c, const uint32_t* __restrict__ in)
+{
+    using CT = typename CodeT<BITS>::T;
+    const int h = blockIdx.y, b = blockIdx.z, head = b * c.Hkv + h;
+    const int s = blockIdx.x * blockDim.x + threadIdx.x;
+    if (s >= c.Smax) return;
+    const uint32_t* p = in + ((size_t)head * c.Smax + s) * c.W;
+    unsigned long long v = p[0];
+    if (c.W > 1) v |= (unsigned long long)p[1] << 32;
+    reinterpret_cast<CT*>(c.code)[(size_t)head * c.code_slots + s] = (CT)v;
+}
+
+template <int BITS>
+__global__ void k_export_pcodes(DevCache c, uint32_t* __restrict__ out, int n_max)
+{
+    using CT = typename CodeT<BITS>::T;
+    const int h = blockIdx.y, b = blockIdx.z, head = b * c.Hkv + h;
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= n_max) return;
+    const unsigned long long v = reinterpret_cast<const CT*>(c.pcode)[(size_t)head * c.pcode_slots + t];
+    store_words(out + ((size_t)head * n_max + t) * c.W, c.W, v);
+}
+
+template <typename F>
+hipError_t with_bits(const DevCache& c, F&& f)
+{
+    if (c.bits == 16) return f(std::integral_constant<int, 16>{});
+    if (c.bits == 32) return f(std::integral_constant<int, 32>{});
+    return f(std::integral_constant<int, 64>{});
+}
+
+template <typename F>
+hipError_t with_d_kv(const DevCache& c, F&& f)
+{
+    if (c.d == 64) {
+        if (c.kv_bf16) return f(std::integral_constant<int, 64>{}, bf16_t{});
+        return f(std::integral_constant<int, 64>{}, float{});
+    }
+    if (c.kv_bf16) return f(std::integral_constant<int, 128>{}, bf16_t{});
+    return f(std::integral_constant<int, 128>{}, float{});
+}
+
+}  // namespace
+
+hipError_t launch_reset(const DevCache& c, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_reset, dim3((c.Smax + 255) / 256, c.Hkv, c.B), dim3(256), 0, st, c);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill(const DevCache& c, const void* K, const void* V, int n_max, int policy,
+                          hipStream_t st)
+{
+    hipLaunchKernelGGL(k_prefill_init, dim3((c.Smax + 255) / 256, c.Hkv, c.B), dim3(256), 0, st, c);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    if (n_max <= 0) return hipSuccess;
+    return with_bits(c, [&](auto bb) {
+        constexpr int BITS = decltype(bb)::value;
+        return with_d_kv(c, [&](auto dd, auto kt) {
+            constexpr int D = decltype(dd)::value;
+            using KT = decltype(kt);
+            hipLaunchKernelGGL((k_project_mfma<D, BITS, KT>), dim3((n_max + 63) / 64, c.Hkv, c.B),
+                               dim3(256), 0, st, c, (const KT*)K, n_max);
+            if (policy == HKV_PREFILL_STREAM) {
+                using CT = typename CodeT<BITS>::T;
+                const size_t lds = (size_t)((c.Smax + 63) & ~63) * sizeof(CT);
+                hipError_t e2 = hipFuncSetAttribute((const void*)k_prefill_select<BITS>,
+                                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                if (e2 != hipSuccess) return e2;
+                hipLaunchKernelGGL((k_prefill_select<BITS>), dim3(c.Hkv, c.B), dim3(1024), lds, st, c);
+            }
+            hipLaunchKernelGGL((k_prefill_gather<D, BITS, KT>), dim3((c.Smax + 15) / 16, c.Hkv, c.B),
+                               dim3(256), 0, st, c, (const KT*)K, (const KT*)V, n_max);
+            return hipGetLastError();
+        });
+    });
+}
+
+hipError_t launch_export_codes(const DevCache& c, uint32_t* codes, hipStream_t st)
+{
+    return with_bits(c, [&](auto bb) {
+        hipLaunchKernelGGL((k_export_codes<decltype(bb)::value>), dim3((c.Smax + 255) / 256, c.Hkv, c.B),
+                           dim3(256), 0, st, c, codes);
+        return hipGetLastError();
+    });
+}
+
+hipError_t launch_import_codes(const DevCache& c, const uint32_t* codes, hipStream_t st)
+{
+    return with_bits(c, [&](auto bb) {
+        hipLaunchKernelGGL((k_import_codes<decltype(bb)::value>), dim3((c.Smax + 255) / 256, c.Hkv, c.B),
+                           dim3(256), 0, st, c, codes);
+        return hipGetLastError();
+    });
+}
+
+hipError_t launch_export_pcodes(const DevCache& c, uint32_t* codes, int n_max, hipStream_t st)
+{
+    if (n_max <= 0) return hipSuccess;
+    return with_bits(c, [&](auto bb) {
+        hipLaunchKernelGGL((k_export_pcodes<decltype(bb)::value>), dim3((n_max + 255) / 256, c.Hkv, c.B),
+                           dim3(256), 0, st, c, codes, n_max);
+        return hipGetLastError();
+    });
+}
+
+}  // namespace hkv

@@ -1,0 +1,146 @@
+"""Parity harness: run the HIP path through the C ABI and replay the CPU oracle.
+
+Rules (the readings are the same on both sides):
+* sign codes must agree bit for bit except on bits the oracle flags
+  (|projection| < 1e-5 * ||x|| * ||R[:, j]||, where fp32 and fp64 may round to
+  different signs);
+* the oracle is then replayed with the GPU's codes injected, and Hamming
+  scores, evicted slots, slot -> token maps, code tables and K/V bytes must be
+  bit-identical;
+* attention outputs: per (sequence, query head) row,
+  max_i |gpu_i - ref_i| / max_i |ref_i| <= 2e-3 against the fp64 oracle.
+"""
+from __future__ import annotations
+
+import sys
+import time
+from typing import Iterable, Optional, Sequence, Tuple
+
+import numpy as np
+
+import oracle
+from lsh_eviction_amd import datagen
+from lsh_eviction_amd.configs import Shape
+
+ATTN_TOL = 2e-3
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def words_u32(t) -> np.ndarray:
+    from lsh_eviction_amd import hkv
+    return hkv.to_numpy(t).view(np.uint32)
+
+
+def check_codes(gpu: np.ndarray, ref: np.ndarray, flags: np.ndarray, what: str) -> int:
+    """All unflagged bits equal; returns the number of (flagged) differing bits."""
+    diff = (gpu ^ ref).astype(np.uint32)
+    bad = diff & ~flags.astype(np.uint32)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"{what}: {int(np.count_nonzero(bad))} unflagged code words differ, "
+                             f"first at {idx.tolist()}")
+    return int(sum(bin(int(x)).count("1") for x in diff.ravel() if x))
+
+
+def rel_err_rows(out: np.ndarray, ref: np.ndarray) -> float:
+    """max over rows of max_i |o - r| / max_i |r| (rows = last axis)."""
+    num = np.abs(out - ref).max(axis=-1)
+    den = np.maximum(np.abs(ref).max(axis=-1), 1e-30)
+    return float((num / den).max())
+
+
+def kv_bytes_equal(gpu_rows: np.ndarray, ref_rows_f64: np.ndarray, kv_dtype: str) -> bool:
+    """Rows stored on the GPU (fp32 or raw bf16 bits) equal the oracle's fp64 copies."""
+    return bool(np.array_equal(oracle.widen(gpu_rows), ref_rows_f64))
+
+
+def run_case(shape: Shape, steps: int, schedule: int = 0, policy: int = 0, chunk: int = 0,
+             heads: Optional[Sequence[Tuple[int, int]]] = None, seed: Optional[int] = None,
+             check_every: int = 1, stats: Optional[dict] = None):
+    """Prefill + `steps` decode steps on the GPU, replayed on the oracle for `heads`
+    (all heads if None).  Raises AssertionError on any parity failure."""
+    import torch
+    from lsh_eviction_amd import hkv
+
+    t0 = time.time()
+    wl = datagen.workload(shape, steps=steps, seed=seed)
+    P, Dd = wl["prompt"], wl["decode"]
+    B, Hq, Hkv, d, bits = shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.n_bits
+    G, W = Hq // Hkv, (bits + 31) // 32
+    kvd = hkv.HKV_BF16 if shape.kv_dtype == "bf16" else hkv.HKV_F32
+    n_max = P.n_max
+    log(f"[{shape.name}] B={B} Hq={Hq} Hkv={Hkv} d={d} b={bits} N<={n_max} S<={P.budgets.max()} "
+        f"steps={steps} schedule={schedule} policy={policy} chunk={chunk} (data {time.time()-t0:.1f}s)")
+
+    cache = hkv.Cache(B, Hq, Hkv, d, bits, kvd, P.budgets, P.R, prefill_policy=policy,
+                      decode_schedule=schedule, max_prompt=n_max, chunk=chunk)
+    Kt, Vt = hkv.to_device(P.K), hkv.to_device(P.V)
+    cache.prefill(Kt, Vt, P.prompt_lens)
+    pcodes = words_u32(cache.prefill_codes())
+    torch.cuda.synchronize()
+    del Kt, Vt
+
+    sel = list(heads) if heads is not None else [(b, h) for b in range(B) for h in range(Hkv)]
+    orc = oracle.OracleCache(P.R, P.budgets, Hq, Hkv, heads=sel)
+    flagged = 0
+    for (b, h) in sel:
+        n = int(P.prompt_lens[b])
+        if n == 0:
+            continue
+        codes_o, flags_o = orc.heads[(b, h)].encode(oracle.widen(P.K[b, h, :n]))
+        flagged += check_codes(pcodes[b, h, :n], codes_o, flags_o, f"prefill codes b={b} h={h}")
+    # replay the oracle's prefill with the GPU codes
+    orc.prefill(P.K, P.V, P.prompt_lens, policy, inj_codes=pcodes)
+    log(f"  prefill codes ok ({flagged} flagged bits differ), {time.time()-t0:.1f}s")
+    compare_state(cache, orc, sel, shape, "after prefill")
+    log(f"  prefill state ok, {time.time()-t0:.1f}s")
+
+    worst = 0.0
+    for s in range(steps):
+        q = hkv.to_device(Dd.q[s]); k = hkv.to_device(Dd.k[s]); v = hkv.to_device(Dd.v[s])
+        out, ev = cache.decode_step(q, k, v)
+        qc, kc = cache.last_codes()
+        out = hkv.to_numpy(out); ev = hkv.to_numpy(ev)
+        qc = words_u32(qc); kc = words_u32(kc)
+        res = orc.decode_step(Dd.q[s], Dd.k[s], Dd.v[s], inj_qcodes=qc, inj_kcodes=kc)
+        for (b, h), r in res.items():
+            qo, qf = orc.heads[(b, h)].encode(oracle.widen(Dd.q[s, b, h * G:(h + 1) * G]))
+            ko, kf = orc.heads[(b, h)].encode(oracle.widen(Dd.k[s, b, h]))
+            check_codes(qc[b, h * G:(h + 1) * G], qo, qf, f"step {s} qcodes b={b} h={h}")
+            check_codes(kc[b, h], ko, kf, f"step {s} kcode b={b} h={h}")
+            assert ev[b, h] == r["evicted"], f"step {s} b={b} h={h}: evicted {ev[b, h]} != {r['evicted']}"
+            err = rel_err_rows(out[b, h * G:(h + 1) * G].astype(np.float64), r["out"])
+            worst = max(worst, err)
+            assert err <= ATTN_TOL, f"step {s} b={b} h={h}: attention rel err {err:.3e} > {ATTN_TOL}"
+        if check_every and (s + 1) % check_every == 0 or s == steps - 1:
+            compare_state(cache, orc, sel, shape, f"after step {s}")
+    log(f"  {steps} decode steps ok, worst attention rel err {worst:.2e}, {time.time()-t0:.1f}s")
+    if stats is not None:
+        stats.update(worst=worst, flagged=flagged)
+    cache.close()
+    return worst
+
+
+def compare_state(cache, orc, sel, shape: Shape, when: str):
+    from lsh_eviction_amd import hkv
+    st = cache.get_state()
+    tok = hkv.to_numpy(st["tok"])
+    codes = words_u32(st["codes"])
+    hs = hkv.to_numpy(st["state"])
+    K = hkv.to_numpy(st["K"]); V = hkv.to_numpy(st["V"])
+    for (b, h) in sel:
+        o = orc.heads[(b, h)].state()
+        S = orc.heads[(b, h)].budget
+        assert hs[b, h, 0] == o["n"] and hs[b, h, 1] == o["t"], \
+            f"{when} b={b} h={h}: head state {hs[b, h].tolist()} != ({o['n']}, {o['t']})"
+        np.testing.assert_array_equal(tok[b, h, :S], o["tok"].astype(np.int32),
+                                      err_msg=f"{when} b={b} h={h}: slot->token map")
+        n = o["n"]
+        np.testing.assert_array_equal(codes[b, h, :n], o["code"][:n],
+                                      err_msg=f"{when} b={b} h={h}: code table")
+        assert kv_bytes_equal(K[b, h, :n], o["K"][:n], shape.kv_dtype), f"{when} b={b} h={h}: K rows"
+        assert kv_bytes_equal(V[b, h, :n], o["V"][:n], shape.kv_dtype), f"{when} b={b} h={h}: V rows"

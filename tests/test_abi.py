@@ -1,0 +1,132 @@
+"""The C-ABI library loads, exports every symbol include/hkv.h declares, and
+rejects bad configurations on the host (no GPU needed: validation runs before
+any HIP call)."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def hkv():
+    from lsh_eviction_amd import build, hkv as H
+    if not os.path.exists(H.LIB_PATH):
+        build.build()
+    H.load()
+    return H
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "hkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hkv_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(hkv):
+    decl = declared_functions()
+    assert len(decl) >= 14
+    assert sorted(hkv.EXPORTS) == decl
+    lib = C.CDLL(hkv.LIB_PATH)
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+def _cfg(hkv, **kw):
+    base = dict(batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128, n_bits=32, kv_dtype=hkv.HKV_BF16,
+                budgets=[4096], max_prompt=8192)
+    base.update(kw)
+    return hkv.make_config(**base)
+
+
+def test_named_shapes_validate(hkv):
+    from lsh_eviction_amd import configs, datagen
+    for s in configs.ALL:
+        n, b = datagen.lengths(s)
+        cfg = hkv.make_config(s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim, s.n_bits,
+                              hkv.HKV_BF16 if s.kv_dtype == "bf16" else hkv.HKV_F32, b,
+                              max_prompt=int(n.max()))
+        assert hkv.hkv_validate_config(cfg) == hkv.HKV_OK, s.name
+        assert hkv.hkv_workspace_bytes(cfg) > 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_bits=24), "UNSUPPORTED"),
+    (dict(n_bits=128), "UNSUPPORTED"),
+    (dict(head_dim=96), "UNSUPPORTED"),
+    (dict(n_q_heads=30), "UNSUPPORTED"),
+    (dict(n_q_heads=256, n_kv_heads=8), "UNSUPPORTED"),   # group 32 > 16
+    (dict(budgets=[0]), "UNSUPPORTED"),
+    (dict(budgets=[1 << 23], prefill_policy=1), "UNSUPPORTED"),
+    (dict(budgets=[40000]), "UNSUPPORTED"),               # 160 KB code table > on-chip table
+    (dict(kv_dtype=7), "UNSUPPORTED"),
+    (dict(chunk=100), "UNSUPPORTED"),
+    (dict(chunk=32), "UNSUPPORTED"),
+    (dict(max_prompt=-1), "UNSUPPORTED"),
+    (dict(batch=0, budgets=[]), "UNSUPPORTED"),
+    (dict(n_kv_heads=0), "INVALID_ARG"),
+])
+def test_bad_configs(hkv, kw, status):
+    cfg = _cfg(hkv, **kw)
+    assert hkv.hkv_validate_config(cfg) == getattr(hkv, "HKV_ERR_" + status)
+
+
+def test_truncate_allows_large_budget(hkv):
+    cfg = _cfg(hkv, budgets=[40000], prefill_policy=hkv.HKV_PREFILL_TRUNCATE)
+    assert hkv.hkv_validate_config(cfg) == hkv.HKV_OK
+
+
+def test_null_pointers(hkv):
+    L = hkv.load()
+    assert L.hkv_validate_config(None) == hkv.HKV_ERR_INVALID_ARG
+    cfg = _cfg(hkv)
+    cfg.budgets = C.POINTER(C.c_int32)()
+    assert L.hkv_validate_config(C.byref(cfg)) == hkv.HKV_ERR_INVALID_ARG
+    assert L.hkv_workspace_bytes(C.byref(_cfg(hkv)), None) == hkv.HKV_ERR_INVALID_ARG
+    for f, n in (("hkv_prefill", 6), ("hkv_decode_step", 7), ("hkv_destroy", 1), ("hkv_get_state", 7),
+                 ("hkv_set_state", 7), ("hkv_debug_last_codes", 4), ("hkv_debug_prefill_codes", 3),
+                 ("hkv_debug_scores", 4)):
+        fn = getattr(L, f)
+        args = [0 if t is C.c_int32 else None for t in fn.argtypes]
+        assert len(args) == n
+        assert fn(*args) == hkv.HKV_ERR_INVALID_ARG, f
+
+
+def test_create_rejects_before_touching_the_gpu(hkv):
+    L = hkv.load()
+    cfg = _cfg(hkv)
+    R = np.zeros((128, 32), np.float32)
+    h = C.c_void_p()
+    # NULL workspace, misaligned workspace, too small workspace
+    assert L.hkv_create(C.byref(cfg), R.ctypes.data_as(C.c_void_p), None, 1 << 30, None,
+                        C.byref(h)) == hkv.HKV_ERR_INVALID_ARG
+    assert "workspace" in hkv.hkv_last_error(None)
+    assert L.hkv_create(C.byref(cfg), R.ctypes.data_as(C.c_void_p), C.c_void_p(0x1008), 1 << 30, None,
+                        C.byref(h)) == hkv.HKV_ERR_INVALID_ARG
+    assert L.hkv_create(C.byref(cfg), R.ctypes.data_as(C.c_void_p), C.c_void_p(0x100000), 16, None,
+                        C.byref(h)) == hkv.HKV_ERR_INVALID_ARG
+    assert L.hkv_create(C.byref(cfg), None, C.c_void_p(0x100000), 1 << 40, None,
+                        C.byref(h)) == hkv.HKV_ERR_INVALID_ARG
+    bad = _cfg(hkv, n_bits=20)
+    assert L.hkv_create(C.byref(bad), R.ctypes.data_as(C.c_void_p), C.c_void_p(0x100000), 1 << 40, None,
+                        C.byref(h)) == hkv.HKV_ERR_UNSUPPORTED
+    assert "n_bits" in hkv.hkv_last_error(None)
+    assert not h.value
+
+
+def test_workspace_grows_with_budget(hkv):
+    a = hkv.hkv_workspace_bytes(_cfg(hkv, budgets=[1000]))
+    b = hkv.hkv_workspace_bytes(_cfg(hkv, budgets=[2000]))
+    c = hkv.hkv_workspace_bytes(_cfg(hkv, budgets=[2000, 100], batch=2))
+    assert 0 < a < b < c
+    # K + V of 2 x 8 heads x 2000 slots x 128 x bf16 dominate
+    assert c >= 2 * 2 * 8 * 2000 * 128 * 2
+
+
+def test_status_strings(hkv):
+    assert hkv.status_str(0) == "HKV_OK"
+    assert hkv.status_str(3) == "HKV_ERR_STATE"
+    assert hkv.status_str(99) == "HKV_UNKNOWN_STATUS"
