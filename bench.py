@@ -1,0 +1,276 @@
+"""Decode-step throughput of the HashEvict path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config long_128k]
+
+One step = one decode step of one attention layer over all sequences and KV
+heads of the workload: encode the queries, score every cached key code,
+evict, write the new token, attend (the whole hot path).  Steps rotate over
+L independent layer caches so the rotating working set (>= 512 MB) does not
+fit the 256 MB last-level cache: every step reads its K/V from HBM.
+Inputs are synthetic (seeded), already resident in HBM when timing starts.
+
+Prints one JSON line (rank 0).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, AMD public spec
+MALL_BYTES = 256 << 20
+DEFAULT_WORKLOAD = "long_128k"
+
+
+def step_bytes(shape, budgets) -> int:
+    """Algorithmic HBM bytes of one decode step: per cached slot and KV head the
+    code (b/8 bytes) and the K and V rows (2 * d * kv bytes) are read; per KV
+    head the new k, v, code and position are written; q is read and out written
+    (fp32)."""
+    es = 2 if shape.kv_dtype == "bf16" else 4
+    cb = shape.n_bits // 8
+    H, d = shape.n_kv_heads, shape.head_dim
+    slots = int(sum(int(s) for s in budgets)) * H
+    per_slot = cb + 2 * d * es
+    writes = shape.batch * H * (2 * d * es + cb + 4)
+    qo = shape.batch * shape.n_q_heads * d * 4 * 2
+    return slots * per_slot + writes + qo
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("k_decode.hip", "hkv_device.h"):
+        with open(os.path.join(ROOT, "lsh_eviction_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, schedule: str):
+    """HBM traffic per launch from committed rocprofv3 counter runs, or None if the
+    kernel source changed since they were taken."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        data = json.load(open(p))
+        rec = data.get(f"{workload}/{schedule}")
+        if rec and rec.get("kernel_hash") == kernel_source_hash():
+            return rec.get("bytes_per_launch")
+    except Exception:
+        return None
+    return None
+
+
+def make_layer_inputs(shape, P, layer: int, seed: int):
+    """Prompt K, V of one layer on the GPU with the datagen recipe (R and the key
+    channel scales are the workload's; the draws come from a torch generator)."""
+    import torch
+    B, H, d = shape.batch, shape.n_kv_heads, shape.head_dim
+    n_max = int(P.prompt_lens.max())
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed * 1000 + layer)
+    dt = torch.bfloat16 if shape.kv_dtype == "bf16" else torch.float32
+    scale = torch.from_numpy(P.key_scale).cuda()
+    K = torch.randn((B, H, n_max, d), generator=g, device="cuda", dtype=torch.float32)
+    K.mul_(scale[None, :, None, :])
+    K = K.to(dt)
+    V = torch.randn((B, H, n_max, d), generator=g, device="cuda", dtype=torch.float32).to(dt)
+    return K, V
+
+
+def cpu_baseline(shape, budget_s: float = 15.0):
+    """The oracle's decode step timed on one host core on a bounded sample: the
+    first sequence of the workload with all its KV heads, its cache filled with
+    the first `budget` prompt tokens (the same slot count the GPU cache holds;
+    the time of a decode step does not depend on which tokens the slots hold)."""
+    import oracle
+    from lsh_eviction_amd import datagen
+    oracle.lib()
+    n, s = datagen.lengths(shape)
+    S1 = int(s[0])
+    one = shape.scaled(batch=1, prompt_range=None, budget_frac=None, prompt=S1, budget=S1)
+    P = datagen.prompt(one)
+    D = datagen.decode(one, steps=64, key_scale=P.key_scale if one.key_outliers else None)
+    orc = oracle.OracleCache(P.R, P.budgets, one.n_q_heads, one.n_kv_heads)
+    orc.prefill(P.K, P.V, P.prompt_lens, oracle.TRUNCATE)
+    t0 = time.perf_counter()
+    steps = 0
+    while steps < 64:
+        orc.decode_step(D.q[steps], D.k[steps], D.v[steps])
+        steps += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    per_seq_step = dt / steps
+    rate = 1.0 / (per_seq_step * shape.batch)   # a workload step covers `batch` sequences
+    return {"value": round(rate, 4), "unit": "decode steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"1 sequence x {one.n_kv_heads} KV heads x {S1} slots (G={one.group}, d={one.head_dim}), "
+                      f"{steps} decode steps in {dt:.1f} s on one thread, scaled to {shape.batch} "
+                      f"sequence(s) per workload step"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--config", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--schedule", default="fused", choices=["fused", "split"])
+    ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--layers", type=int, default=0, help="layer caches rotated (0 = enough to exceed the MALL twice)")
+    ap.add_argument("--graph", action="store_true", help="replay the steps of one rotation as a HIP graph")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from lsh_eviction_amd import configs, datagen, hkv
+
+    shape = configs.BY_NAME[args.config]
+    torch.cuda.set_device(0)
+    n, budgets = datagen.lengths(shape)
+    per_step = step_bytes(shape, budgets)
+    L = args.layers or max(1, math.ceil(2 * MALL_BYTES / per_step))
+    kvd = hkv.HKV_BF16 if shape.kv_dtype == "bf16" else hkv.HKV_F32
+    sched = hkv.HKV_DECODE_FUSED if args.schedule == "fused" else hkv.HKV_DECODE_SPLIT
+    P = datagen.prompt(shape.scaled(prompt=1, prompt_range=None, budget_frac=None, budget=1, batch=1))
+    P.prompt_lens, P.budgets = n, budgets
+    n_max = int(n.max())
+
+    caches, prefill_ms = [], []
+    for layer in range(L):
+        c = hkv.Cache(shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.n_bits, kvd,
+                      budgets, P.R, decode_schedule=sched, max_prompt=n_max, chunk=args.chunk)
+        K, V = make_layer_inputs(shape, P, layer, shape.index)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        c.prefill(K, V, n)
+        e1.record()
+        torch.cuda.synchronize()
+        prefill_ms.append(e0.elapsed_time(e1))
+        del K, V
+        caches.append(c)
+    torch.cuda.empty_cache()
+
+    # decode inputs: a pool of distinct steps, resident on the GPU
+    POOL = 16
+    g = torch.Generator(device="cuda")
+    g.manual_seed(shape.index + 7)
+    dt = torch.bfloat16 if shape.kv_dtype == "bf16" else torch.float32
+    scale = torch.from_numpy(P.key_scale).cuda()
+    qs = torch.randn((POOL, shape.batch, shape.n_q_heads, shape.head_dim), generator=g, device="cuda")
+    ks = (torch.randn((POOL, shape.batch, shape.n_kv_heads, shape.head_dim), generator=g, device="cuda")
+          * scale[None, None]).to(dt)
+    vs = torch.randn((POOL, shape.batch, shape.n_kv_heads, shape.head_dim), generator=g, device="cuda").to(dt)
+    outs = torch.empty((L, shape.batch, shape.n_q_heads, shape.head_dim), device="cuda")
+    evs = torch.empty((L, shape.batch, shape.n_kv_heads), dtype=torch.int32, device="cuda")
+
+    stream = torch.cuda.current_stream()
+
+    def one(i):
+        l = i % L
+        p = i % POOL
+        caches[l].decode_step(qs[p], ks[p], vs[p], outs[l], evs[l], stream)
+
+    graph = None
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(stream)
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(graph, stream=s):
+                for i in range(L):
+                    caches[i].decode_step(qs[i % POOL], ks[i % POOL], vs[i % POOL], outs[i], evs[i], s)
+        torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        one(i)
+    torch.cuda.synchronize()
+
+    K_ = args.steps
+    t_wall = time.perf_counter()
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if graph is not None:
+        reps = max(1, K_ // L)
+        K_ = reps * L
+        e_start.record(stream)
+        for r in range(reps):
+            graph.replay()
+        e_end.record(stream)
+        torch.cuda.synchronize()
+        total_ms = e_start.elapsed_time(e_end)
+        kern_ms = total_ms / K_
+    else:
+        # timed region 1: the steps back to back
+        e_start.record(stream)
+        for i in range(K_):
+            one(i)
+        e_end.record(stream)
+        torch.cuda.synchronize()
+        total_ms = e_start.elapsed_time(e_end)
+        # timed region 2: the same steps, each launch bracketed by events on its stream
+        K2 = min(K_, 1000)
+        a = [torch.cuda.Event(enable_timing=True) for _ in range(K2)]
+        b = [torch.cuda.Event(enable_timing=True) for _ in range(K2)]
+        for i in range(K2):
+            a[i].record(stream)
+            one(i)
+            b[i].record(stream)
+        torch.cuda.synchronize()
+        kern_ms = float(np.mean([a[i].elapsed_time(b[i]) for i in range(K2)]))
+    wall = time.perf_counter() - t_wall
+
+    ms_per_step = total_ms / K_
+    value = 1000.0 / ms_per_step
+    achieved = per_step / (kern_ms * 1e-3) / 1e9
+    traffic = load_traffic(args.config, args.schedule)
+    rec = {
+        "metric": "decode steps/s (LSH score+evict+attend) & % HBM peak, 8B-shape 128K ctx",
+        "value": round(value, 1),
+        "unit": "decode steps/s",
+        "n_gpus": 1,
+        "steps": K_,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": shape.name, "batch": shape.batch, "n_q_heads": shape.n_q_heads,
+                   "n_kv_heads": shape.n_kv_heads, "head_dim": shape.head_dim, "n_bits": shape.n_bits,
+                   "kv_storage": shape.kv_dtype, "budget_slots": int(budgets.sum()),
+                   "prompt_tokens": int(n.sum()), "layers_rotated": L, "schedule": args.schedule,
+                   "chunk": caches[0].cfg.chunk or 512, "graph": bool(args.graph)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "bytes_per_step": per_step,
+        "kernel_us": round(kern_ms * 1e3, 3),
+        "hbm_frac_of_step": round(per_step / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "prefill_ms_per_layer": round(float(np.mean(prefill_ms)), 2),
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu:
+        rec["cpu_baseline"] = cpu_baseline(shape, args.cpu_seconds)
+    for c in caches:
+        c.close()
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

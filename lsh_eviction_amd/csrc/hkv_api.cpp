@@ -104,8 +104,10 @@ extern "C" hkv_status hkv_create(const hkv_config* cfg, const float* R_host, voi
     d.part = (float*)(ws + L.off_part);
     d.cand_key = (unsigned long long*)(ws + L.off_cand_key);
     d.cand_lg = (float*)(ws + L.off_cand_lg);
+    d.cand_v = (float*)(ws + L.off_cand_v);
+    d.ekey = (unsigned long long*)(ws + L.off_ekey);
+    d.info = (int*)(ws + L.off_info);
     d.count = (unsigned*)(ws + L.off_count);
-    d.evict = (int*)(ws + L.off_evict);
     d.pcode = ws + L.off_pcode;
     d.B = L.B; d.Hq = L.Hq; d.Hkv = L.Hkv; d.G = L.G; d.d = L.d; d.bits = L.bits; d.W = L.W;
     d.Smax = L.Smax; d.chunk = L.chunk; d.nsplit = L.nsplit; d.cstride = L.cstride;
@@ -223,6 +225,7 @@ extern "C" hkv_status hkv_set_state(hkv_cache* c, const void* K, const void* V, 
     if (e == hipSuccess) e = hkv::launch_import_codes(c->dev, codes, st);
     if (e == hipSuccess) e = hipMemcpyAsync(c->dev.tok, slot_token, heads * L.Smax * 4, hipMemcpyDeviceToDevice, st);
     if (e == hipSuccess) e = hipMemcpyAsync(c->dev.state, head_state, heads * 8, hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess) e = hkv::launch_clear_step_scratch(c->dev, st);
     s = check_launch(c, e, st, "hkv_set_state");
     if (s == HKV_OK) c->prefilled = true;
     return s;

@@ -44,6 +44,15 @@ struct Vec16<float> {
     }
 };
 
+// Streaming 16-byte load: the non-temporal hint keeps rows that are read once
+// per step from displacing reusable lines in the caches.
+__device__ __forceinline__ uint4 ld_stream(const void* p)
+{
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(w.x, w.y, w.z, w.w);
+}
+
 // code of `BITS` bits held in the smallest unsigned type
 template <int BITS>
 struct CodeT;

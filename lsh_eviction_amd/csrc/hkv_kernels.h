@@ -23,8 +23,10 @@ struct DevCache {
     float* part;                    // [B][Hq][nsplit][d + 4]: acc[d], m, l
     unsigned long long* cand_key;   // [B][Hkv][cstride] (score << 32) | ~slot, 0 = none
     float* cand_lg;                 // [B][Hkv][cstride][G] logits (base 2) of the candidate
-    unsigned* count;                // [B][Hkv] blocks of the step that have finished
-    int* evict;                     // [B][Hkv] slot chosen this step (split schedule)
+    float* cand_v;                  // [B][Hkv][cstride][d] value row of the candidate (fp32)
+    unsigned long long* ekey;       // [B][Hkv][2] eviction key of the step, by parity of its position
+    int* info;                      // [B][Hkv][2] occupancy and position at the start of the step
+    unsigned* count;                // [B][Hkv] blocks of the current step that have published
     void* pcode;                    // [B][Hkv][pcode_slots] prompt key codes
     int B, Hq, Hkv, G, d, bits, W, Smax, chunk, nsplit;
     int cstride;                    // candidates per head in cand_key / cand_lg
@@ -50,5 +52,7 @@ hipError_t launch_prefill(const DevCache& c, const void* K, const void* V, int n
 hipError_t launch_export_codes(const DevCache& c, uint32_t* codes, hipStream_t st);
 hipError_t launch_import_codes(const DevCache& c, const uint32_t* codes, hipStream_t st);
 hipError_t launch_export_pcodes(const DevCache& c, uint32_t* codes, int n_max, hipStream_t st);
+// clears the per-step scratch (eviction keys) after a state import
+hipError_t launch_clear_step_scratch(const DevCache& c, hipStream_t st);
 
 }  // namespace hkv

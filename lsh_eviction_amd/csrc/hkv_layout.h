@@ -15,7 +15,7 @@ constexpr int kMaxGroup = 16;
 constexpr int kMaxBudget = 1 << 22;
 constexpr int kMaxBatch = 4096;
 constexpr size_t kLdsTableBytes = 128 * 1024;   // prefill code table in LDS
-constexpr int kDefaultChunk = 512;
+constexpr int kDefaultChunk = 1024;
 constexpr size_t kAlign = 256;
 
 struct Layout {
@@ -26,8 +26,8 @@ struct Layout {
     size_t pcode_slots;    // prompt positions per head in the prefill code buffer (padded)
     // byte offsets into the workspace
     size_t off_R, off_budget, off_plen, off_state, off_K, off_V, off_code, off_tok;
-    size_t off_dbg_q, off_dbg_k, off_part, off_cand_key, off_cand_lg, off_count;
-    size_t off_evict, off_pcode;
+    size_t off_dbg_q, off_dbg_k, off_part, off_cand_key, off_cand_lg, off_cand_v, off_ekey;
+    size_t off_info, off_count, off_pcode;
     size_t total;
 };
 

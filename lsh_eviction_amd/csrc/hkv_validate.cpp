@@ -92,8 +92,10 @@ hkv_status compute_layout(const hkv_config* cfg, Layout* L, char* err, size_t er
     l.off_part = take((size_t)l.B * l.Hq * l.nsplit * (l.d + 4) * 4);
     l.off_cand_key = take(heads * l.cstride * 8);
     l.off_cand_lg = take(heads * l.cstride * G * 4);
+    l.off_cand_v = take(heads * l.cstride * l.d * 4);
+    l.off_ekey = take(heads * 2 * 8);
+    l.off_info = take(heads * 2 * 4);
     l.off_count = take(heads * 4);
-    l.off_evict = take(heads * 4);
     l.off_pcode = take(heads * l.pcode_slots * cb);
     l.total = off;
     return HKV_OK;

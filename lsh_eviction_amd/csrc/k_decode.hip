@@ -7,17 +7,27 @@
 // any attention is computed, write the new token there, attend.
 //
 // Two schedules of the same step:
-//   FUSED (one launch).  Every block owns a chunk of slots of one (sequence,
-//   KV head).  It encodes the group's queries, finds its chunk's candidate
-//   (highest GQA score, lowest slot on ties), and accumulates softmax partials
-//   over its chunk with that candidate held out.  The last block of the head
-//   to finish picks the winner among the chunk candidates (the global argmax
-//   with lowest-index ties is always its own chunk's candidate), adds back the
-//   held-out candidates of the other chunks and the new token, merges by
-//   log-sum-exp, and writes the new token into the winner's slot.  The result
-//   equals "evict, write, then attend" with every K/V byte read once.
+//
+//   FUSED (two launches).  k_fused_attend: every block owns a chunk of slots
+//   of one (sequence, KV head).  It encodes the group's queries (matrix
+//   cores), finds its chunk's candidate (highest GQA score, lowest slot on
+//   ties), folds the candidate into the head's eviction key with a 64-bit
+//   atomic max, and accumulates softmax partials over its chunk with that
+//   candidate held out.  k_fused_merge: one block per query head takes the
+//   winner from the eviction key (the global argmax with lowest-index ties is
+//   always its own chunk's candidate), adds back the held-out candidates of
+//   the other chunks and the new token, merges by log-sum-exp, and the first
+//   query head of the group writes the new token into the winner's slot.  The
+//   result equals "evict, write, then attend" with every K/V byte read once
+//   and no grid-wide fence inside a kernel.
+//
 //   SPLIT (five launches): lsh_encode, hamming_argmax, evict_write, split-K
-//   attention, merge.
+//   attention, LSE merge.
+//
+// Eviction keys are double-buffered by the parity of the step's token
+// position: the step at position t folds into ekey[t & 1] and its merge
+// clears ekey[(t + 1) & 1] for the next step, so no block ever clears a key
+// another block of the same step may still read.
 #include <type_traits>
 
 #include "hkv_consts.h"
@@ -27,8 +37,9 @@ namespace hkv {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int D>
 __device__ __forceinline__ float qscale2()
@@ -39,37 +50,232 @@ __device__ __forceinline__ float qscale2()
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Shared memory of one attention block.
+// (m, l) <- log-sum-exp union of (m, l) and (mo, lo), base 2.
+__device__ __forceinline__ void lse_add(float& m, float& l, float mo, float lo)
+{
+    const float mx = fmaxf(m, mo);
+    if (mx == -INFINITY) return;
+    l = l * exp2_fast(m - mx) + lo * exp2_fast(mo - mx);
+    m = mx;
+}
+
+// ---------------------------------------------------------------------------
+// stages 1-2 on the matrix cores
+// ---------------------------------------------------------------------------
+
+// The calling wave computes bit columns [16 nt, 16 nt + 16) of the codes of
+// rows v < nvec <= 16 of X (row stride D): Y = X R on a 16x16x4 fp32 MFMA
+// (lane l feeds row l % 16 and the quarter l / 16 of the head dimension), one
+// ballot of (y > 0) per accumulator register.  Lane i < nvec returns the
+// 16-bit chunk of row i.
+// Operands of one wave's share of the encoder (see encode16_mfma).
+template <int D>
+struct EncOps {
+    float x[D / 4];    // the lane's quarter of its row of X
+    float rv[D / 4];   // the matching entries of R's column
+};
+
+template <int D, int BITS, typename XT>
+__device__ __forceinline__ void enc_load_x(EncOps<D>& op, const XT* __restrict__ X, int nvec)
+{
+    constexpr int DQ = D / 4;
+    constexpr int EPL = Vec16<XT>::EPL;
+    const int lane = threadIdx.x & 63;
+    const int m = lane & 15, qd = lane >> 4;
+    const XT* src = X + (size_t)(m < nvec ? m : 0) * D + qd * DQ;
+#pragma unroll
+    for (int v = 0; v < DQ / EPL; ++v) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(src + v * EPL);
+        float f[EPL];
+        Vec16<XT>::cvt(raw, f);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) op.x[v * EPL + e] = m < nvec ? f[e] : 0.f;
+    }
+}
+
+template <int D, int BITS>
+__device__ __forceinline__ void enc_load_r(EncOps<D>& op, const float* __restrict__ R, int nt)
+{
+    constexpr int DQ = D / 4;
+    const int lane = threadIdx.x & 63;
+    const int m = lane & 15, qd = lane >> 4;
+    const float* rc = R + (size_t)(qd * DQ) * BITS + nt * 16 + m;
+#pragma unroll
+    for (int s = 0; s < DQ; ++s) op.rv[s] = rc[s * BITS];
+}
+
+// The calling wave computes bit columns [16 nt, 16 nt + 16) of the codes of
+// up to 16 rows: Y = X R on a 16x16x4 fp32 MFMA (lane l feeds row l % 16 and
+// the quarter l / 16 of the head dimension), one ballot of (y > 0) per
+// accumulator register.  Lane i returns the 16-bit chunk of row i.
+template <int D>
+__device__ __forceinline__ uint32_t enc_compute(const EncOps<D>& op)
+{
+    constexpr int DQ = D / 4;
+    const int lane = threadIdx.x & 63;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < DQ; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(op.x[s], op.rv[s], acc, 0, 0, 0);
+    unsigned long long mk[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mk[r] = __ballot(acc[r] > 0.f);
+    // result row i = 4 a + r sits in register r of lanes 16 a + column
+    const int a = (lane & 15) >> 2, r = lane & 3;
+    const unsigned long long mm = r == 0 ? mk[0] : r == 1 ? mk[1] : r == 2 ? mk[2] : mk[3];
+    return (uint32_t)((mm >> (16 * a)) & 0xFFFFull);
+}
+
+template <int D, int BITS, typename XT>
+__device__ __forceinline__ uint32_t encode16_mfma(const XT* __restrict__ X, int nvec, const float* __restrict__ R,
+                                                  int nt)
+{
+    EncOps<D> op;
+    enc_load_x<D, BITS, XT>(op, X, nvec);
+    enc_load_r<D, BITS>(op, R, nt);
+    return enc_compute<D>(op);
+}
+
+// Codes of rows [0, nvec <= 16) of X into out16[nt][row] (LDS), waves 0 .. NT-1.
+template <int D, int BITS, typename XT>
+__device__ __forceinline__ void encode_block16(const XT* __restrict__ X, int nvec, const float* __restrict__ R,
+                                               uint32_t (*out16)[16])
+{
+    constexpr int NT = BITS / 16;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int nt = wave; nt < NT; nt += kWaves) {
+        const uint32_t c16 = encode16_mfma<D, BITS, XT>(X, nvec, R, nt);
+        if (lane < nvec) out16[nt][lane] = c16;
+    }
+}
+
+template <int BITS>
+__device__ __forceinline__ unsigned long long join16(const uint32_t (*c16)[16], int row)
+{
+    unsigned long long v = 0;
+#pragma unroll
+    for (int nt = 0; nt < BITS / 16; ++nt) v |= (unsigned long long)c16[nt][row] << (16 * nt);
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Hamming candidate of a slot range
+// ---------------------------------------------------------------------------
+template <int BITS, int GM>
+__device__ __forceinline__ unsigned long long thread_candidate(const typename CodeT<BITS>::T* __restrict__ code,
+                                                               const typename CodeT<BITS>::T (&qc)[GM], int G,
+                                                               int s0, int s1, uint4 first)
+{
+    using CT = typename CodeT<BITS>::T;
+    constexpr int VS = 16 / sizeof(CT);
+    unsigned long long best = 0;
+    uint4 raw = first;
+    for (int s = s0 + (int)threadIdx.x * VS; s < s1; s += kThreads * VS) {
+        const int sn = s + kThreads * VS;
+        uint4 nxt = make_uint4(0, 0, 0, 0);
+        if (sn < s1) nxt = *reinterpret_cast<const uint4*>(code + sn);
+        CT cs[VS];
+        __builtin_memcpy(cs, &raw, 16);
+#pragma unroll
+        for (int u = 0; u < VS; ++u) {
+            int sc = 0;
+#pragma unroll
+            for (int g = 0; g < GM; ++g)
+                if (g < G) sc += popc((CT)(cs[u] ^ qc[g]));
+            const unsigned long long k = (s + u < s1) ? cand_key(sc, s + u) : 0ull;
+            best = k > best ? k : best;
+        }
+        raw = nxt;
+    }
+    return best;
+}
+
+__device__ __forceinline__ unsigned long long block_max_u64(unsigned long long v, unsigned long long* red)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = wave_max_u64(v);
+    __syncthreads();
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    v = red[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) v = red[w] > v ? red[w] : v;
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// softmax partial over a slot range (VALU, 16-byte coalesced row loads)
+// ---------------------------------------------------------------------------
 template <int D, int GM>
 struct AttnSmem {
     float m[kWaves][GM];
     float l[kWaves][GM];
     float acc[kWaves][GM][D];
-    float candlg[GM];
 };
 
-// Softmax partial of the G query heads of one KV head over rows [r0, r1) of
-// Kh / Vh (row stride D), leaving out row `skip` (-1: none).  The base-2
-// logits of the skipped row go to sm.candlg.  On return (after a block
-// barrier) sm.m[0..3][g], sm.l, sm.acc hold one (max, sum, acc) per wave.
+template <int D, typename KT>
+struct Tile {
+    static constexpr int EPL = Vec16<KT>::EPL;   // elements per 16-byte load
+    static constexpr int LPR = D / EPL;          // lanes per row
+    static constexpr int RPW = 64 / LPR;         // rows per wave load
+    static constexpr int UNR = 2;                // wave loads per tile and lane
+    static constexpr int ROWS = RPW * UNR;       // rows of a wave's tile
+    uint4 k[UNR], v[UNR];
+
+    // tile `base` (row offset within the range of `len` rows, first row r0)
+    __device__ __forceinline__ void load(const KT* __restrict__ Kh, const KT* __restrict__ Vh, int r0, int len,
+                                         int base)
+    {
+        const int lane = threadIdx.x & 63;
+        const int rg = lane / LPR, cc = lane % LPR;
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int row = base + u * RPW + rg;
+            if (row < len) {
+                const size_t off = (size_t)(r0 + row) * D + cc * EPL;
+                k[u] = *reinterpret_cast<const uint4*>(Kh + off);
+                v[u] = *reinterpret_cast<const uint4*>(Vh + off);
+            } else {
+                k[u] = make_uint4(0, 0, 0, 0);
+                v[u] = make_uint4(0, 0, 0, 0);
+            }
+        }
+    }
+};
+
+// Softmax partial of the G query heads of one KV head over rows [r0, r0+len)
+// of Kh / Vh, leaving out row `skip` (-1: none), whose base-2 logits go to
+// sm.candlg.  `first` is the wave's first tile, already in flight.  The next
+// tile is loaded while the current one is computed.  On return (after a block
+// barrier) sm.m, sm.l, sm.acc hold one (max, sum, acc) per wave.
 template <int D, int GM, typename KT>
 __device__ __forceinline__ void attend_rows(const KT* __restrict__ Kh, const KT* __restrict__ Vh,
-                                            const float* __restrict__ qh, int G, int r0, int r1,
-                                            int skip, AttnSmem<D, GM>& sm)
+                                            const float* __restrict__ qh, int G, int r0, int len, int skip,
+                                            Tile<D, KT> cur, AttnSmem<D, GM>& sm)
 {
-    constexpr int EPL = Vec16<KT>::EPL;   // elements per 16-byte load
-    constexpr int LPR = D / EPL;          // lanes per row
-    constexpr int RPW = 64 / LPR;         // rows per wave load
-    constexpr int UNR = 4;                // wave loads in flight per lane
+    using T = Tile<D, KT>;
+    constexpr int EPL = T::EPL, LPR = T::LPR, RPW = T::RPW, UNR = T::UNR;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int rg = lane / LPR, cc = lane % LPR;
 
     float qr[GM][EPL];
     const float qs = qscale2<D>();
 #pragma unroll
-    for (int g = 0; g < GM; ++g)
+    for (int g = 0; g < GM; ++g) {
+        if (g < G) {
+            const float4* qp = reinterpret_cast<const float4*>(qh + g * D + cc * EPL);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) qr[g][e] = g < G ? qh[g * D + cc * EPL + e] * qs : 0.f;
+            for (int e4 = 0; e4 < EPL / 4; ++e4) {
+                const float4 f = qp[e4];
+                qr[g][4 * e4 + 0] = f.x * qs;
+                qr[g][4 * e4 + 1] = f.y * qs;
+                qr[g][4 * e4 + 2] = f.z * qs;
+                qr[g][4 * e4 + 3] = f.w * qs;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) qr[g][e] = 0.f;
+        }
+    }
 
     float m[GM], l[GM], acc[GM][EPL];
 #pragma unroll
@@ -80,26 +286,15 @@ __device__ __forceinline__ void attend_rows(const KT* __restrict__ Kh, const KT*
         for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
     }
 
-    const int len = r1 - r0;
-    for (int base = wave * UNR * RPW; base < len; base += kWaves * UNR * RPW) {
-        uint4 kr[UNR], vr[UNR];
-#pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-            const int row = base + u * RPW + rg;
-            if (row < len) {
-                const size_t off = (size_t)(r0 + row) * D + cc * EPL;
-                kr[u] = *reinterpret_cast<const uint4*>(Kh + off);
-                vr[u] = *reinterpret_cast<const uint4*>(Vh + off);
-            } else {
-                kr[u] = make_uint4(0, 0, 0, 0);
-                vr[u] = make_uint4(0, 0, 0, 0);
-            }
-        }
+    for (int base = wave * T::ROWS; base < len; base += kWaves * T::ROWS) {
+        T nxt;
+        const int nb = base + kWaves * T::ROWS;
+        if (nb < len) nxt.load(Kh, Vh, r0, len, nb);
         float lg[UNR][GM];
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
             float kf[EPL];
-            Vec16<KT>::cvt(kr[u], kf);
+            Vec16<KT>::cvt(cur.k[u], kf);
 #pragma unroll
             for (int g = 0; g < GM; ++g) {
                 float dot = 0.f;
@@ -109,10 +304,6 @@ __device__ __forceinline__ void attend_rows(const KT* __restrict__ Kh, const KT*
             }
             const int row = base + u * RPW + rg;
             const bool isc = (r0 + row) == skip;
-            if (isc && cc == 0) {
-#pragma unroll
-                for (int g = 0; g < GM; ++g) sm.candlg[g] = lg[u][g];
-            }
             if (row >= len || isc) {
 #pragma unroll
                 for (int g = 0; g < GM; ++g) lg[u][g] = -INFINITY;
@@ -140,12 +331,13 @@ __device__ __forceinline__ void attend_rows(const KT* __restrict__ Kh, const KT*
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
             float vf[EPL];
-            Vec16<KT>::cvt(vr[u], vf);
+            Vec16<KT>::cvt(cur.v[u], vf);
 #pragma unroll
             for (int g = 0; g < GM; ++g)
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(p[u][g], vf[e], acc[g][e]);
         }
+        cur = nxt;
     }
 
     // combine the row groups of the wave
@@ -181,10 +373,10 @@ __device__ __forceinline__ void attend_rows(const KT* __restrict__ Kh, const KT*
     __syncthreads();
 }
 
-// Writes the block's partial for query heads g < G: part[(hq, split)] = acc[D], m, l.
+// The block's partial for query heads g < G: part[(hq, split)] = acc[D], m, l.
 template <int D, int GM>
-__device__ __forceinline__ void store_partial(const AttnSmem<D, GM>& sm, float* __restrict__ part,
-                                              int hq0, int G, int nsplit, int split)
+__device__ __forceinline__ void store_partial(const AttnSmem<D, GM>& sm, float* __restrict__ part, int hq0, int G,
+                                              int nsplit, int split)
 {
     for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
         const int g = idx / D, i = idx % D;
@@ -208,52 +400,485 @@ __device__ __forceinline__ void store_partial(const AttnSmem<D, GM>& sm, float* 
     }
 }
 
-// GQA Hamming scores of slots [s0, s1) against qc[0..G); returns the block's
-// best candidate key (0 if the range is empty).  Uses red[kWaves].
-template <int BITS, int GM>
-__device__ __forceinline__ unsigned long long block_candidate(
-    const typename CodeT<BITS>::T* __restrict__ code, const typename CodeT<BITS>::T (&qc)[GM], int G,
-    int s0, int s1, unsigned long long* red)
-{
-    using CT = typename CodeT<BITS>::T;
-    constexpr int VS = 16 / sizeof(CT);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    unsigned long long best = 0;
-    for (int s = s0 + tid * VS; s < s1; s += kThreads * VS) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(code + s);
-        CT cs[VS];
-        __builtin_memcpy(cs, &raw, 16);
+// ---------------------------------------------------------------------------
+// softmax partial over a slot range, bf16 K/V: QK^T on the matrix cores
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// One wave's tile of TR rows: K in the A-operand layout of the 16x16x32 bf16
+// MFMA (lane l: row l % 16 of each 16-row half, the contiguous quarter
+// (l / 16) of the head dimension, 16 bytes per k-step), V in coalesced
+// 16-byte row segments (lane l: row group l / (D/8), segment l % (D/8)).
+// Rows at or beyond `len` are not loaded and read as zero.
+template <int D, int TR>
+struct MTile {
+    static constexpr int H = TR / 16;          // 16-row halves
+    static constexpr int KS = D / 32;          // k-steps of 32 per half
+    static constexpr int LPR = D / 8;          // V lanes per row
+    static constexpr int RPW = 64 / LPR;       // V rows per wave load
+    static constexpr int VU = TR / RPW;        // V loads per lane
+    uint4 k[H][KS];
+    uint4 v[VU];
+
+    // Rows beyond the range are clamped to its last row (loaded, then masked by
+    // the caller); len == 0 clamps to row 0 of the range, which is in bounds.
+    // No load sits in a branch, so the wait counters stay exact and the tile
+    // in flight is never waited for early.
+    __device__ __forceinline__ void load(const bf16_t* __restrict__ Kh, const bf16_t* __restrict__ Vh, int r0,
+                                         int len, int base)
+    {
+        const int lane = threadIdx.x & 63;
+        const int i = lane & 15, qd = lane >> 4;
+        const int last = len > 0 ? len - 1 : 0;
 #pragma unroll
-        for (int u = 0; u < VS; ++u) {
-            int sc = 0;
+        for (int h = 0; h < H; ++h) {
+            const int row = min(base + 16 * h + i, last);
+            const uint4* p = reinterpret_cast<const uint4*>(Kh + (size_t)(r0 + row) * D + qd * (D / 4));
 #pragma unroll
-            for (int g = 0; g < GM; ++g)
-                if (g < G) sc += popc((CT)(cs[u] ^ qc[g]));
-            const unsigned long long k = (s + u < s1) ? cand_key(sc, s + u) : 0ull;
-            best = k > best ? k : best;
+            for (int s = 0; s < KS; ++s) k[h][s] = p[s];
+        }
+        const int rg = lane / LPR, cc = lane % LPR;
+#pragma unroll
+        for (int u = 0; u < VU; ++u) {
+            const int row = min(base + u * RPW + rg, last);
+            v[u] = *reinterpret_cast<const uint4*>(Vh + (size_t)(r0 + row) * D + cc * 8);
         }
     }
-    best = wave_max_u64(best);
-    __syncthreads();
-    if (lane == 0) red[wave] = best;
-    __syncthreads();
-    best = red[0];
+};
+
+template <int GM>
+constexpr int pad_g()
+{
+    return GM < 4 ? 4 : GM;
+}
+
+// LDS hand-off from the MFMA lanes (logits, one head per lane) to the value
+// lanes (rows): probabilities and rescale factors of the wave's current tile.
+template <int GM, int TR>
+struct PSmem {
+    float p[kWaves][TR][pad_g<GM>()];
+    float alpha[kWaves][pad_g<GM>()];
+};
+
+// Running state of one wave's softmax partial (GM heads, padded heads carry
+// zero queries and are discarded by the caller).
+template <int GM>
+struct MState {
+    float m, lsum;          // MFMA view: head (lane % 16)
+    float acc[GM][8];       // value view: 8 elements of the lane's row segment
+};
+
+template <int D, int GM, int TR>
+__device__ __forceinline__ void mfma_tile(const MTile<D, TR>& tl, int base, int r0, int len, int skip,
+                                          const bf16x8 (&qhi)[D / 32], const bf16x8 (&qlo)[D / 32],
+                                          PSmem<GM, TR>& ps, MState<GM>& st)
+{
+    using T = MTile<D, TR>;
+    constexpr int H = T::H, KS = T::KS, LPR = T::LPR, RPW = T::RPW, VU = T::VU;
+    constexpr int GP = pad_g<GM>();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 15, qd = lane >> 4;
+    const int rg = lane / LPR;
+
+    f32x4 C[H];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) best = red[w] > best ? red[w] : best;
-    return best;
+    for (int h = 0; h < H; ++h) {
+        C[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const bf16x8 a = __builtin_bit_cast(bf16x8, tl.k[h][s]);
+            C[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qhi[s], C[h], 0, 0, 0);
+            C[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo[s], C[h], 0, 0, 0);
+        }
+    }
+    // logits of rows 16h + 4qd + r for head n; masked rows get -inf
+    float lg[H][4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < H; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = base + 16 * h + 4 * qd + r;
+            const bool ok = row < len && (r0 + row) != skip;
+            lg[h][r] = ok ? C[h][r] : -INFINITY;
+            tmax = fmaxf(tmax, lg[h][r]);
+        }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float mx = fmaxf(st.m, tmax);
+    const float ms = mx == -INFINITY ? 0.f : mx;
+    const float alpha = exp2_fast(st.m - ms);
+    st.m = mx;
+    float psum = 0.f;
+#pragma unroll
+    for (int h = 0; h < H; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float p = exp2_fast(lg[h][r] - ms);
+            psum += p;
+            if (n < GM) ps.p[wave][16 * h + 4 * qd + r][n] = p;
+        }
+    st.lsum = st.lsum * alpha + psum;
+    if (qd == 0 && n < GM) ps.alpha[wave][n] = alpha;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // value lanes: rescale, then accumulate p * v
+    float al[GP];
+#pragma unroll
+    for (int g4 = 0; g4 < GP / 4; ++g4) {
+        const float4 a4 = reinterpret_cast<const float4*>(ps.alpha[wave])[g4];
+        al[4 * g4] = a4.x;
+        al[4 * g4 + 1] = a4.y;
+        al[4 * g4 + 2] = a4.z;
+        al[4 * g4 + 3] = a4.w;
+    }
+#pragma unroll
+    for (int g = 0; g < GM; ++g)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st.acc[g][e] *= al[g];
+#pragma unroll
+    for (int u = 0; u < VU; ++u) {
+        const int trow = u * RPW + rg;
+        float pg[GP];
+#pragma unroll
+        for (int g4 = 0; g4 < GP / 4; ++g4) {
+            const float4 p4 = reinterpret_cast<const float4*>(ps.p[wave][trow])[g4];
+            pg[4 * g4] = p4.x;
+            pg[4 * g4 + 1] = p4.y;
+            pg[4 * g4 + 2] = p4.z;
+            pg[4 * g4 + 3] = p4.w;
+        }
+        float vf[8];
+        Vec16<bf16_t>::cvt(tl.v[u], vf);
+#pragma unroll
+        for (int g = 0; g < GM; ++g)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) st.acc[g][e] = fmaf(pg[g], vf[e], st.acc[g][e]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Same contract as attend_rows, for bf16 K/V.  Logits come from MFMA: the
+// query of head n is column n of the B operand, split into a bf16 high part
+// and a bf16 remainder (two MFMAs into one fp32 accumulator), so the products
+// keep fp32 accuracy while K stays exact.  Probabilities go through LDS to the
+// lanes that hold the value rows; P.V is accumulated in fp32 on the VALU.
+// Two tiles alternate: one is computed while the other is in flight.
+template <int D, int GM, int TR, int NB>
+__device__ __forceinline__ void attend_rows_mfma(const bf16_t* __restrict__ Kh, const bf16_t* __restrict__ Vh,
+                                                 const float* __restrict__ qh, int G, int r0, int len, int skip,
+                                                 MTile<D, TR> (&ring)[NB], AttnSmem<D, GM>& sm, PSmem<GM, TR>& ps)
+{
+    constexpr int KS = D / 32, LPR = D / 8;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 15, qd = lane >> 4;
+    const int rg = lane / LPR, cc = lane % LPR;
+
+    bf16x8 qhi[KS], qlo[KS];
+    {
+        const float qs = qscale2<D>();
+        const float* qp = qh + (size_t)(n < G ? n : 0) * D + qd * (D / 4);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = n < G ? qp[8 * s + e] * qs : 0.f;
+                const __bf16 hi = (__bf16)x;
+                qhi[s][e] = hi;
+                qlo[s][e] = (__bf16)(x - (float)hi);
+            }
+        }
+    }
+
+    MState<GM> st;
+    st.m = -INFINITY;
+    st.lsum = 0.f;
+#pragma unroll
+    for (int g = 0; g < GM; ++g)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st.acc[g][e] = 0.f;
+
+    // tiles of this wave: base = b0 + k * step, k < ntile.  Tiles 0 .. NB-1
+    // are in flight on entry; every buffer is reloaded with the tile NB ahead
+    // as soon as it has been computed.  In the main loop every reload is
+    // valid, so no load sits in a branch there and the wait counters stay
+    // exact; the last 2 NB tiles form the tail.
+    const int step = kWaves * TR;
+    const int b0 = wave * TR;
+    const int ntile = len > b0 ? (len - b0 + step - 1) / step : 0;
+    int k = 0;
+    for (; k + 2 * NB <= ntile; k += NB) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            mfma_tile<D, GM, TR>(ring[i], b0 + (k + i) * step, r0, len, skip, qhi, qlo, ps, st);
+            ring[i].load(Kh, Vh, r0, len, b0 + (k + i + NB) * step);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        if (k + i < ntile) {
+            mfma_tile<D, GM, TR>(ring[i], b0 + (k + i) * step, r0, len, skip, qhi, qlo, ps, st);
+            if (k + i + NB < ntile) ring[i].load(Kh, Vh, r0, len, b0 + (k + i + NB) * step);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+        if (k + NB + i < ntile) mfma_tile<D, GM, TR>(ring[i], b0 + (k + NB + i) * step, r0, len, skip, qhi, qlo, ps, st);
+
+    // the wave's rows share one running max per head: sums combine directly
+    float lsum = st.lsum;
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+        for (int g = 0; g < GM; ++g)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) st.acc[g][e] += __shfl_xor(st.acc[g][e], off);
+    if (qd == 0 && n < GM) {
+        sm.m[wave][n] = st.m;
+        sm.l[wave][n] = lsum;
+    }
+    if (rg == 0) {
+#pragma unroll
+        for (int g = 0; g < GM; ++g)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sm.acc[wave][g][cc * 8 + e] = st.acc[g][e];
+    }
+    __syncthreads();
+}
+
+// The held-out candidate of a chunk: its base-2 logits for the G heads (VALU
+// dot products, one head per wave) into clg[0 .. G) and its value row (fp32)
+// into candv.  kc / vc: the lane's two elements of the candidate's K and V
+// rows (every wave holds them).
+template <int D>
+__device__ __forceinline__ void candidate_terms(const float* __restrict__ qh, int G, float2 kc, float2 vc,
+                                                float* __restrict__ clg, float* __restrict__ candv)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int i0 = 2 * lane;
+    const bool in = i0 < D;
+    const float qs = qscale2<D>();
+    for (int g = wave; g < G; g += kWaves) {
+        float dot = 0.f;
+        if (in) dot = fmaf(qh[g * D + i0] * qs, kc.x, qh[g * D + i0 + 1] * qs * kc.y);
+        dot = wave_sum_f(dot);
+        if (lane == 0) clg[g] = dot;
+    }
+    if (wave == 0 && in) {
+        candv[i0] = vc.x;
+        candv[i0 + 1] = vc.y;
+    }
 }
 
 // ---------------------------------------------------------------------------
-// FUSED schedule
+// LSE merge of the partials of one query head
 // ---------------------------------------------------------------------------
+
+// (m, l, a) <- log-sum-exp union with (mo, lo, ao); a holds 4 output elements.
+__device__ __forceinline__ void lse_add4(float& m, float& l, float4& a, float mo, float lo, float4 ao)
+{
+    const float mx = fmaxf(m, mo);
+    if (mx == -INFINITY) return;
+    const float sa = exp2_fast(m - mx), sb = exp2_fast(mo - mx);
+    l = l * sa + lo * sb;
+    a.x = a.x * sa + ao.x * sb;
+    a.y = a.y * sa + ao.y * sb;
+    a.z = a.z * sa + ao.z * sb;
+    a.w = a.w * sa + ao.w * sb;
+    m = mx;
+}
+
+constexpr int kMergeThreads = 1024;
+
+template <int D>
+struct MergeSmem {
+    static constexpr int TPR = D / 4;                 // threads per record (4 outputs each)
+    static constexpr int RPI = kMergeThreads / TPR;   // records in flight per pass
+    float m[RPI], l[RPI];
+    float4 a[RPI][TPR];
+    float nlg;
+};
+
+// One block merges the nsb partial records rec(j) of one query head, in
+// hold-out mode also the candidate of every split j != js (base-2 logit and
+// fp32 value row from cand(j)), and, if has_new, the new token (logit *nlg,
+// value vnew4 of thread t: elements 4t .. 4t+3).  Every thread owns 4 output
+// elements of a subset of the records, so all record loads are independent.
+// Returns true in threads t < D/4, with outputs 4t .. 4t+3 in o.
+// Records j < nbound are loaded (nbound needs no device load, so the loads
+// are not held back by the ones that give nsb and js); those j >= nsb are
+// ignored.
+template <int D, typename RecF, typename CandF>
+__device__ __forceinline__ bool merge_head(MergeSmem<D>& sm, int nbound, int nsb, RecF rec, bool holdout, int js,
+                                           CandF cand, bool has_new, const float* nlg, float4 vnew4, float4& o)
+{
+    constexpr int TPR = MergeSmem<D>::TPR, RPI = MergeSmem<D>::RPI;
+    const int tid = threadIdx.x, c4 = tid % TPR, jr = tid / TPR;
+    float m = -INFINITY, l = 0.f;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+    for (int j = jr; j < nbound; j += RPI) {
+        const float* r = rec(j);
+        const float4 av = reinterpret_cast<const float4*>(r)[c4];
+        const float mj = r[D], lj = r[D + 1];
+        float cl = -INFINITY;
+        float4 cv4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (holdout) {
+            const float* cv;
+            cand(j, cl, cv);
+            cv4 = reinterpret_cast<const float4*>(cv)[c4];
+        }
+        if (j < nsb) {
+            if (lj > 0.f) lse_add4(m, l, a, mj, lj, av);
+            if (holdout && j != js) lse_add4(m, l, a, cl, 1.f, cv4);
+        }
+    }
+    if (c4 == 0) {
+        sm.m[jr] = m;
+        sm.l[jr] = l;
+    }
+    sm.a[jr][c4] = a;
+    __syncthreads();
+    if (tid >= TPR) return false;
+    float M = -INFINITY, L = 0.f;
+    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (has_new) {
+        M = *nlg;
+        L = 1.f;
+        A = vnew4;
+    }
+#pragma unroll
+    for (int k = 0; k < RPI; ++k) lse_add4(M, L, A, sm.m[k], sm.l[k], sm.a[k][tid]);
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    o = make_float4(A.x * inv, A.y * inv, A.z * inv, A.w * inv);
+    return true;
+}
+
+template <typename KT>
+__device__ __forceinline__ float4 load4_f32(const KT* p)
+{
+    return make_float4(to_f32(p[0]), to_f32(p[1]), to_f32(p[2]), to_f32(p[3]));
+}
+
+template <int GM>
+constexpr int tile_rows()
+{
+    return 16;   // rows of a wave's tile in the bf16 path
+}
+
+// tiles of a wave in flight at once in the bf16 path
+template <int GM>
+constexpr int ring_depth()
+{
+    return 2;
+}
+
+// ---------------------------------------------------------------------------
+// FUSED schedule (one launch)
+// ---------------------------------------------------------------------------
+
+// Device-coherent accesses for data one block hands to another inside a
+// launch.  Each XCD has its own L2 and those L2s are not coherent with each
+// other; agent-scope atomic loads and stores (the sc1 cache policy) write
+// through and re-fetch past them, so the data never sits stale in a writer's
+// or a reader's L2, and no L2-wide writeback fence is needed.
+__device__ __forceinline__ void st_dev(float* p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(unsigned long long* p, unsigned long long v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p)
+{
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dev(const uint32_t* p)
+{
+    return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long ld_dev(const unsigned long long* p)
+{
+    return __hip_atomic_load(const_cast<unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float4 ld_dev4(const float* p)
+{
+    return make_float4(ld_dev(p), ld_dev(p + 1), ld_dev(p + 2), ld_dev(p + 3));
+}
+
+// Every memory operation this thread issued has completed -- its write-through
+// stores have reached the coherence point -- before anything after it is
+// issued; the compiler may not move memory operations across either.
+__device__ __forceinline__ void own_stores_complete()
+{
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// The block's partial for query heads g < G, device-coherent:
+// part[(hq, split)] = acc[D], m, l.
+template <int D, int GM>
+__device__ __forceinline__ void publish_partial(const AttnSmem<D, GM>& sm, float* __restrict__ part, int hq0, int G,
+                                                int nsplit, int split)
+{
+    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+        const int g = idx / D, i = idx % D;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm.m[w][g]);
+        const float ms = mx == -INFINITY ? 0.f : mx;
+        float a = 0.f, ls = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float sc = exp2_fast(sm.m[w][g] - ms);
+            a += sm.acc[w][g][i] * sc;
+            ls += sm.l[w][g] * sc;
+        }
+        float* rec = part + ((size_t)(hq0 + g) * nsplit + split) * (D + 4);
+        st_dev(rec + i, a);
+        if (i == 0) {
+            st_dev(rec + D, mx);
+            st_dev(rec + D + 1, ls);
+        }
+    }
+}
+
+// Shared memory of the last block's merge: one (max, sum, 4 outputs) per
+// wave, head and 4-element column.
+template <int D, int GM>
+struct MergeBlockSmem {
+    float m[kWaves][GM];
+    float l[kWaves][GM];
+    float4 a[kWaves][GM][D / 4];
+};
+
+template <int D, int GM>
+union FusedSmem {
+    AttnSmem<D, GM> at;
+    MergeBlockSmem<D, GM> mg;
+};
+
 template <int D, int BITS, int GM, typename KT>
 __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const float* __restrict__ q,
-                                                           const KT* __restrict__ knew,
-                                                           const KT* __restrict__ vnew,
-                                                           float* __restrict__ out,
-                                                           int* __restrict__ evicted)
+                                                           const KT* __restrict__ knew, const KT* __restrict__ vnew,
+                                                           float* __restrict__ out, int* __restrict__ evicted)
 {
     using CT = typename CodeT<BITS>::T;
+    constexpr int VS = 16 / sizeof(CT);
+    constexpr bool kMfma = std::is_same<KT, bf16_t>::value;
+    constexpr int TR = tile_rows<GM>();
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int S = c.budget[b];
     const int nsb = (S + c.chunk - 1) / c.chunk;
@@ -261,161 +886,234 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     const int G = c.G;
     const int head = b * c.Hkv + h;
     const int n = c.state[2 * head];
+    const int t = c.state[2 * head + 1];
     const bool full = n >= S;
     const int s0 = split * c.chunk;
-    const int s1 = min(s0 + c.chunk, n);
+    const int len = max(min(s0 + c.chunk, n) - s0, 0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-    __shared__ AttnSmem<D, GM> sm;
-    __shared__ CT s_qc[GM];
-    __shared__ CT s_kc;
+    __shared__ FusedSmem<D, GM> u;
+    __shared__ PSmem<GM, TR> ps;
+    __shared__ uint32_t s_q16[BITS / 16][16];
+    __shared__ uint32_t s_k16[BITS / 16][16];
     __shared__ unsigned long long s_red[kWaves];
-    __shared__ float s_f[kWaves][GM];
-    __shared__ float s_M[GM], s_L[GM], s_nlg[GM];
+    __shared__ float s_nlg[GM];
     __shared__ int s_last;
+    AttnSmem<D, GM>& sm = u.at;
 
     const int hq0 = b * c.Hq + h * G;
     const float* qh = q + (size_t)hq0 * D;
     const size_t rowbase = (size_t)head * c.Smax;
     KT* Kh = reinterpret_cast<KT*>(c.K) + rowbase * D;
     KT* Vh = reinterpret_cast<KT*>(c.V) + rowbase * D;
-    CT* codeh = reinterpret_cast<CT*>(c.code) + (size_t)head * c.code_slots;
+    const CT* codeh = reinterpret_cast<const CT*>(c.code) + (size_t)head * c.code_slots;
+    const size_t crec = (size_t)head * c.cstride + split;
+    const KT* kh = knew + (size_t)head * D;
+    const KT* vh = vnew + (size_t)head * D;
 
-    // stages 1-2: the group's query codes
-    encode_rows<D, BITS>(qh, G, c.R, [&](int v, unsigned long long cd) { s_qc[v] = (CT)cd; });
-    if (tid < GM) sm.candlg[tid] = -INFINITY;
+    // Loads are issued in the order their data is needed (the vector memory
+    // counter completes in order): encoder operands, the new token's key and
+    // value, the chunk's codes, then the first tiles of every wave.
+    constexpr int NT = BITS / 16;
+    EncOps<D> eq, ek;
+    if (wave < NT) {
+        enc_load_x<D, BITS, float>(eq, qh, G);
+        if (split == 0) enc_load_x<D, BITS, KT>(ek, kh, 1);
+        enc_load_r<D, BITS>(eq, c.R, wave);
+    }
+    constexpr int NH = (GM + kWaves - 1) / kWaves;   // new-token logits per wave
+    float2 kn = make_float2(0.f, 0.f), qn[NH];
+#pragma unroll
+    for (int a = 0; a < NH; ++a) {
+        const int gn = min(wave + a * kWaves, G - 1);
+        qn[a] = 2 * lane < D ? make_float2(qh[gn * D + 2 * lane], qh[gn * D + 2 * lane + 1]) : make_float2(0.f, 0.f);
+    }
+    if (2 * lane < D) kn = make_float2(to_f32(kh[2 * lane]), to_f32(kh[2 * lane + 1]));
+    const int cvec = min(s0 + tid * VS, (int)c.code_slots - VS);
+    uint4 craw = *reinterpret_cast<const uint4*>(codeh + cvec);
+    constexpr int NB = ring_depth<GM>();
+    MTile<D, TR> ring[kMfma ? NB : 1];
+    Tile<D, KT> first;
+    if constexpr (kMfma) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) ring[i].load(Kh, Vh, s0, len, (wave + i * kWaves) * TR);
+    } else {
+        first.load(Kh, Vh, s0, len, wave * Tile<D, KT>::ROWS);
+    }
+
+    // stages 1-2: codes of the group's queries (and of the new key, once)
+    if (wave < NT) {
+        const uint32_t c16 = enc_compute<D>(eq);
+        if (lane < G) s_q16[wave][lane] = c16;
+        if (split == 0) {
+#pragma unroll
+            for (int s2 = 0; s2 < D / 4; ++s2) ek.rv[s2] = eq.rv[s2];
+            const uint32_t k16 = enc_compute<D>(ek);
+            if (lane == 0) s_k16[wave][0] = k16;
+        }
+    }
+    // base-2 logit of the new token for head `wave` (only the head's last
+    // block uses it)
+#pragma unroll
+    for (int a = 0; a < NH; ++a) {
+        const int g = wave + a * kWaves;
+        float dot = qn[a].x * qscale2<D>() * kn.x + qn[a].y * qscale2<D>() * kn.y;
+        dot = wave_sum_f(dot);
+        if (lane == 0 && g < G) s_nlg[g] = dot;
+    }
     __syncthreads();
-    if (split == 0 && tid < G) store_words(c.dbg_q + (size_t)(hq0 + tid) * c.W, c.W, s_qc[tid]);
+    if (split == 0) {
+        if (tid < G) store_words(c.dbg_q + (size_t)(hq0 + tid) * c.W, c.W, join16<BITS>(s_q16, tid));
+        if (tid == 0) {
+            const unsigned long long kc = join16<BITS>(s_k16, 0);
+            st_dev(c.dbg_k + (size_t)head * c.W, (uint32_t)kc);
+            if (c.W > 1) st_dev(c.dbg_k + (size_t)head * c.W + 1, (uint32_t)(kc >> 32));
+        }
+    }
 
-    // stages 3-4 inside the chunk
+    // stages 3-4 inside the chunk; the chunk's candidate joins the head's key
     int cand = -1;
     unsigned long long ckey = 0;
     if (full) {
         CT qc[GM];
 #pragma unroll
-        for (int g = 0; g < GM; ++g) qc[g] = g < G ? s_qc[g] : (CT)0;
-        ckey = block_candidate<BITS, GM>(codeh, qc, G, s0, s1, s_red);
+        for (int g = 0; g < GM; ++g) qc[g] = g < G ? (CT)join16<BITS>(s_q16, g) : (CT)0;
+        ckey = thread_candidate<BITS, GM>(codeh, qc, G, s0, s0 + len, craw);
+        ckey = block_max_u64(ckey, s_red);
         cand = ckey ? cand_slot(ckey) : -1;
+        if (tid == 0 && ckey) atomicMax(&c.ekey[2 * head + (t & 1)], ckey);
+    }
+
+    // the held-out candidate's K and V rows: fetched now, used after the loop
+    float2 kc2 = make_float2(0.f, 0.f), vc2 = make_float2(0.f, 0.f);
+    if (cand >= 0 && 2 * lane < D) {
+        kc2 = make_float2(to_f32(Kh[(size_t)cand * D + 2 * lane]), to_f32(Kh[(size_t)cand * D + 2 * lane + 1]));
+        vc2 = make_float2(to_f32(Vh[(size_t)cand * D + 2 * lane]), to_f32(Vh[(size_t)cand * D + 2 * lane + 1]));
     }
 
     // attention over the chunk with the candidate held out
-    attend_rows<D, GM, KT>(Kh, Vh, qh, G, s0, max(s1, s0), cand, sm);
-    store_partial<D, GM>(sm, c.part, hq0, G, c.nsplit, split);
-    const size_t crec = (size_t)head * c.cstride + split;
-    if (tid == 0) c.cand_key[crec] = ckey;
-    if (tid < G) c.cand_lg[crec * G + tid] = sm.candlg[tid];
+    if constexpr (kMfma)
+        attend_rows_mfma<D, GM, TR, NB>(Kh, Vh, qh, G, s0, len, cand, ring, sm, ps);
+    else
+        attend_rows<D, GM, KT>(Kh, Vh, qh, G, s0, len, cand, first, sm);
 
-    // the last block of this head merges and writes
-    __threadfence();
+    // publish this chunk: partial softmax, candidate logits and value row
+    publish_partial<D, GM>(sm, c.part, hq0, G, c.nsplit, split);
+    if (cand >= 0) {
+        const float qs = qscale2<D>();
+        const int i0 = 2 * lane;
+        for (int g = wave; g < G; g += kWaves) {
+            float dot = 0.f;
+            if (i0 < D) dot = fmaf(qh[g * D + i0] * qs, kc2.x, qh[g * D + i0 + 1] * qs * kc2.y);
+            dot = wave_sum_f(dot);
+            if (lane == 0) st_dev(c.cand_lg + crec * G + g, dot);
+        }
+        if (wave == 0 && i0 < D) {
+            st_dev(c.cand_v + crec * D + i0, vc2.x);
+            st_dev(c.cand_v + crec * D + i0 + 1, vc2.y);
+        }
+    }
+    if (tid == 0) st_dev(c.cand_key + crec, ckey);
+    own_stores_complete();
     __syncthreads();
     if (tid == 0) s_last = atomicAdd(&c.count[head], 1u) == (unsigned)(nsb - 1);
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
-    if (tid == 0) c.count[head] = 0;
 
-    int e;
-    if (full) {
-        unsigned long long best = 0;
-        for (int j = tid; j < nsb; j += kThreads) {
-            const unsigned long long k = c.cand_key[(size_t)head * c.cstride + j];
-            best = k > best ? k : best;
-        }
-        best = wave_max_u64(best);
-        if (lane == 0) s_red[wave] = best;
-        __syncthreads();
-        best = s_red[0];
-        for (int w = 1; w < kWaves; ++w) best = s_red[w] > best ? s_red[w] : best;
-        e = cand_slot(best);
-    } else {
-        e = n;
-    }
-    const int js = full ? e / c.chunk : -1;
-
-    // code of the new key; base-2 logits of the new token
-    const KT* kh = knew + (size_t)head * D;
-    const KT* vh = vnew + (size_t)head * D;
-    encode_rows<D, BITS>(kh, 1, c.R, [&](int, unsigned long long cd) { s_kc = (CT)cd; });
-    for (int g = wave; g < G; g += kWaves) {
-        float dot = 0.f;
-        for (int i = lane; i < D; i += 64) dot = fmaf(qh[g * D + i] * qscale2<D>(), to_f32(kh[i]), dot);
-        dot = wave_sum_f(dot);
-        if (lane == 0) s_nlg[g] = dot;
-    }
-    __syncthreads();
-
-    // M[g] = max over chunk maxima, added-back candidates and the new token
-    const float* part = c.part;
-    const float* clg = c.cand_lg + (size_t)head * c.cstride * G;
-    float mloc[GM];
-#pragma unroll
-    for (int g = 0; g < GM; ++g) mloc[g] = -INFINITY;
-    for (int j = tid; j < nsb; j += kThreads) {
-#pragma unroll
-        for (int g = 0; g < GM; ++g) {
-            if (g < G) {
-                const float* rec = part + ((size_t)(hq0 + g) * c.nsplit + j) * (D + 4);
-                if (rec[D + 1] > 0.f) mloc[g] = fmaxf(mloc[g], rec[D]);
-                if (full && j != js) mloc[g] = fmaxf(mloc[g], clg[(size_t)j * G + g]);
-            }
-        }
-    }
+    // ---- the last block of the head: winner, merge, write ----
+    // Every thread owns 4 output columns (c4) of every head for the splits
+    // j = r + RS * jj.  All loads of a batch of splits are issued before any
+    // of them is used, so the merge costs one round trip to memory per batch.
+    if (tid == 0) c.count[head] = 0u;
+    // Acquire: drop this XCD's cached lines so that the plain loads below see
+    // what the other blocks wrote through to memory.
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    constexpr int TPR = D / 4;
+    constexpr int RS = kThreads / TPR;
+    constexpr int JB = GM <= 4 ? 4 : (GM <= 8 ? 2 : 1);   // splits per thread and batch
+    const int c4 = tid % TPR, r = tid / TPR;
+    const unsigned long long wkey = ld_dev(&c.ekey[2 * head + (t & 1)]);
+    float Mt[GM], Lt[GM];
+    float4 At[GM];
 #pragma unroll
     for (int g = 0; g < GM; ++g) {
-        const float v = wave_max_f(mloc[g]);
-        if (lane == 0) s_f[wave][g] = v;
+        Mt[g] = -INFINITY;
+        Lt[g] = 0.f;
+        At[g] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    __syncthreads();
-    if (tid < G) {
-        float mx = s_nlg[tid];
-        for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, s_f[w][tid]);
-        s_M[tid] = mx;
-    }
-    __syncthreads();
-    float lloc[GM];
+    const float* partb = c.part + (size_t)hq0 * c.nsplit * (D + 4);
+    const float* clgb = c.cand_lg + (size_t)head * c.cstride * G;
+    const float* cvb = c.cand_v + (size_t)head * c.cstride * D;
+    int e = n, js = -1;
+    for (int j0 = 0; j0 < nsb; j0 += RS * JB) {
+        float4 av[JB][GM], cv[JB];
+        float mj[JB][GM], lj[JB][GM], cl[JB][GM];
 #pragma unroll
-    for (int g = 0; g < GM; ++g) lloc[g] = 0.f;
-    for (int j = tid; j < nsb; j += kThreads) {
+        for (int jj = 0; jj < JB; ++jj) {
+            const int j = min(j0 + r + RS * jj, nsb - 1);
+            cv[jj] = reinterpret_cast<const float4*>(cvb + (size_t)j * D)[c4];
+#pragma unroll
+            for (int g = 0; g < GM; ++g) {
+                const int gg = min(g, G - 1);
+                const float* rec = partb + ((size_t)gg * c.nsplit + j) * (D + 4);
+                av[jj][g] = reinterpret_cast<const float4*>(rec)[c4];
+                const float2 ml = *reinterpret_cast<const float2*>(rec + D);
+                mj[jj][g] = ml.x;
+                lj[jj][g] = ml.y;
+                cl[jj][g] = clgb[(size_t)j * G + gg];
+            }
+        }
+        if (full) {
+            e = cand_slot(wkey);
+            js = e / c.chunk;
+        }
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj) {
+            const int j = j0 + r + RS * jj;
+            if (j < nsb) {
+                const bool hold = full && j != js;
+#pragma unroll
+                for (int g = 0; g < GM; ++g) {
+                    if (lj[jj][g] > 0.f) lse_add4(Mt[g], Lt[g], At[g], mj[jj][g], lj[jj][g], av[jj][g]);
+                    if (hold) lse_add4(Mt[g], Lt[g], At[g], cl[jj][g], 1.f, cv[jj]);
+                }
+            }
+        }
+    }
+    MergeBlockSmem<D, GM>& mg = u.mg;
+    // lanes of a wave that share c4 (lane % TPR) combine, then one entry per wave
+#pragma unroll
+    for (int off = TPR; off < 64; off <<= 1) {
 #pragma unroll
         for (int g = 0; g < GM; ++g) {
-            if (g < G) {
-                const float* rec = part + ((size_t)(hq0 + g) * c.nsplit + j) * (D + 4);
-                if (rec[D + 1] > 0.f) lloc[g] += rec[D + 1] * exp2_fast(rec[D] - s_M[g]);
-                if (full && j != js) lloc[g] += exp2_fast(clg[(size_t)j * G + g] - s_M[g]);
-            }
+            const float mo = __shfl_xor(Mt[g], off), lo = __shfl_xor(Lt[g], off);
+            const float4 ao = make_float4(__shfl_xor(At[g].x, off), __shfl_xor(At[g].y, off),
+                                          __shfl_xor(At[g].z, off), __shfl_xor(At[g].w, off));
+            lse_add4(Mt[g], Lt[g], At[g], mo, lo, ao);
         }
     }
-    __syncthreads();
+    __syncthreads();   // the attention's shared memory is free from here on
+    if (lane < TPR) {
 #pragma unroll
-    for (int g = 0; g < GM; ++g) {
-        const float v = wave_sum_f(lloc[g]);
-        if (lane == 0) s_f[wave][g] = v;
-    }
-    __syncthreads();
-    if (tid < G) {
-        float ls = exp2_fast(s_nlg[tid] - s_M[tid]);
-        for (int w = 0; w < kWaves; ++w) ls += s_f[w][tid];
-        s_L[tid] = ls;
-    }
-    __syncthreads();
-
-    for (int idx = tid; idx < G * D; idx += kThreads) {
-        const int g = idx / D, i = idx % D;
-        const float Mg = s_M[g];
-        float a = 0.f;
-        for (int j = 0; j < nsb; ++j) {
-            const float* rec = part + ((size_t)(hq0 + g) * c.nsplit + j) * (D + 4);
-            const float lj = rec[D + 1];
-            if (lj > 0.f) a = fmaf(rec[i], exp2_fast(rec[D] - Mg), a);
-            if (full && j != js) {
-                const int cj = cand_slot(c.cand_key[(size_t)head * c.cstride + j]);
-                a = fmaf(exp2_fast(clg[(size_t)j * G + g] - Mg), to_f32(Vh[(size_t)cj * D + i]), a);
+        for (int g = 0; g < GM; ++g) {
+            mg.a[wave][g][c4] = At[g];
+            if (c4 == 0) {
+                mg.m[wave][g] = Mt[g];
+                mg.l[wave][g] = Lt[g];
             }
         }
-        a = fmaf(exp2_fast(s_nlg[g] - Mg), to_f32(vh[i]), a);
-        out[(size_t)(hq0 + g) * D + i] = a / s_L[g];
     }
     __syncthreads();
+    for (int idx = tid; idx < G * TPR; idx += kThreads) {
+        const int g = idx / TPR, cc = idx % TPR;
+        float M = s_nlg[g], L = 1.f;
+        float4 A = load4_f32(vh + 4 * cc);
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) lse_add4(M, L, A, mg.m[w][g], mg.l[w][g], mg.a[w][g][cc]);
+        const float inv = 1.f / L;
+        reinterpret_cast<float4*>(out + (size_t)(hq0 + g) * D)[cc] = make_float4(A.x * inv, A.y * inv, A.z * inv,
+                                                                               A.w * inv);
+    }
 
     // stage 5: the new token takes slot e
     for (int i = tid; i < D; i += kThreads) {
@@ -423,13 +1121,14 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
         Vh[(size_t)e * D + i] = vh[i];
     }
     if (tid == 0) {
-        const int t = c.state[2 * head + 1];
-        codeh[e] = s_kc;
+        unsigned long long kc = ld_dev(c.dbg_k + (size_t)head * c.W);
+        if (c.W > 1) kc |= (unsigned long long)ld_dev(c.dbg_k + (size_t)head * c.W + 1) << 32;
+        reinterpret_cast<CT*>(c.code)[(size_t)head * c.code_slots + e] = (CT)kc;
         c.tok[rowbase + e] = t;
         c.state[2 * head] = full ? n : n + 1;
         c.state[2 * head + 1] = t + 1;
+        c.ekey[2 * head + (t & 1)] = 0ull;
         evicted[head] = e;
-        store_words(c.dbg_k + (size_t)head * c.W, c.W, s_kc);
     }
 }
 
@@ -437,18 +1136,28 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
 // SPLIT schedule
 // ---------------------------------------------------------------------------
 
-// lsh_encode: codes of all query heads and new keys of sequence b.
+// lsh_encode: 16 query heads or 16 new keys of sequence b per block.
 template <int D, int BITS, typename KT>
 __global__ __launch_bounds__(kThreads) void k_lsh_encode(DevCache c, const float* __restrict__ q,
                                                          const KT* __restrict__ knew)
 {
-    const int b = blockIdx.x;
-    encode_rows<D, BITS>(q + (size_t)b * c.Hq * D, c.Hq, c.R, [&](int v, unsigned long long cd) {
-        store_words(c.dbg_q + ((size_t)b * c.Hq + v) * c.W, c.W, cd);
-    });
-    encode_rows<D, BITS>(knew + (size_t)b * c.Hkv * D, c.Hkv, c.R, [&](int v, unsigned long long cd) {
-        store_words(c.dbg_k + ((size_t)b * c.Hkv + v) * c.W, c.W, cd);
-    });
+    __shared__ uint32_t s16[BITS / 16][16];
+    const int b = blockIdx.y;
+    const int nqt = (c.Hq + 15) / 16;
+    const int tile = blockIdx.x;
+    const bool isq = tile < nqt;
+    const int r0 = (isq ? tile : tile - nqt) * 16;
+    const int nv = min(16, (isq ? c.Hq : c.Hkv) - r0);
+    if (isq)
+        encode_block16<D, BITS, float>(q + ((size_t)b * c.Hq + r0) * D, nv, c.R, s16);
+    else
+        encode_block16<D, BITS, KT>(knew + ((size_t)b * c.Hkv + r0) * D, nv, c.R, s16);
+    __syncthreads();
+    if ((int)threadIdx.x < nv) {
+        uint32_t* dst = isq ? c.dbg_q + ((size_t)b * c.Hq + r0 + threadIdx.x) * c.W
+                            : c.dbg_k + ((size_t)b * c.Hkv + r0 + threadIdx.x) * c.W;
+        store_words(dst, c.W, join16<BITS>(s16, threadIdx.x));
+    }
 }
 
 __device__ __forceinline__ unsigned long long load_code_words(const uint32_t* p, int W)
@@ -458,64 +1167,45 @@ __device__ __forceinline__ unsigned long long load_code_words(const uint32_t* p,
     return v;
 }
 
-// hamming_argmax: block candidates over kScoreChunk slots, the last block of
-// a head reduces them to the evicted slot.
+// hamming_argmax: every block folds the best (score, lowest slot) of its
+// kScoreChunk slots into the head's eviction key.
 template <int BITS, int GM>
-__global__ __launch_bounds__(kThreads) void k_hamming_argmax(DevCache c, int* __restrict__ evicted)
+__global__ __launch_bounds__(kThreads) void k_hamming_argmax(DevCache c)
 {
     using CT = typename CodeT<BITS>::T;
+    constexpr int VS = 16 / sizeof(CT);
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int S = c.budget[b];
-    const int nsb = (S + kScoreChunk - 1) / kScoreChunk;
-    if (split >= nsb) return;
-    const int G = c.G, head = b * c.Hkv + h, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int head = b * c.Hkv + h;
     const int n = c.state[2 * head];
-    const bool full = n >= S;
+    if (n < S) return;                    // not full: nothing is evicted
+    const int s0 = split * kScoreChunk;
+    if (s0 >= n) return;
+    const int s1 = min(s0 + kScoreChunk, n);
+    const int G = c.G;
     __shared__ unsigned long long s_red[kWaves];
-    __shared__ int s_last;
-    unsigned long long key = 0;
-    if (full) {
-        CT qc[GM];
+    CT qc[GM];
 #pragma unroll
-        for (int g = 0; g < GM; ++g)
-            qc[g] = g < G ? (CT)load_code_words(c.dbg_q + ((size_t)b * c.Hq + h * G + g) * c.W, c.W)
-                          : (CT)0;
-        const CT* codeh = reinterpret_cast<const CT*>(c.code) + (size_t)head * c.code_slots;
-        const int s0 = split * kScoreChunk;
-        key = block_candidate<BITS, GM>(codeh, qc, G, s0, min(s0 + kScoreChunk, n), s_red);
-    }
-    if (tid == 0) c.cand_key[(size_t)head * c.cstride + split] = key;
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&c.count[head], 1u) == (unsigned)(nsb - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    unsigned long long best = 0;
-    for (int j = tid; j < nsb; j += kThreads) {
-        const unsigned long long k = c.cand_key[(size_t)head * c.cstride + j];
-        best = k > best ? k : best;
-    }
-    best = wave_max_u64(best);
-    if (lane == 0) s_red[wave] = best;
-    __syncthreads();
-    if (tid == 0) {
-        for (int w = 1; w < kWaves; ++w) best = s_red[w] > best ? s_red[w] : best;
-        best = s_red[0] > best ? s_red[0] : best;
-        const int e = full ? cand_slot(best) : n;
-        c.evict[head] = e;
-        evicted[head] = e;
-        c.count[head] = 0;
-    }
+    for (int g = 0; g < GM; ++g)
+        qc[g] = g < G ? (CT)load_code_words(c.dbg_q + ((size_t)b * c.Hq + h * G + g) * c.W, c.W) : (CT)0;
+    const CT* codeh = reinterpret_cast<const CT*>(c.code) + (size_t)head * c.code_slots;
+    uint4 first = make_uint4(0, 0, 0, 0);
+    if (s0 + (int)threadIdx.x * VS < s1) first = *reinterpret_cast<const uint4*>(codeh + s0 + threadIdx.x * VS);
+    unsigned long long key = thread_candidate<BITS, GM>(codeh, qc, G, s0, s1, first);
+    key = block_max_u64(key, s_red);
+    if (threadIdx.x == 0 && key) atomicMax(&c.ekey[2 * head], key);
 }
 
 // evict_write: the new token's K, V, code and position take the chosen slot.
 template <int D, int BITS, typename KT>
-__global__ void k_evict_write(DevCache c, const KT* __restrict__ knew, const KT* __restrict__ vnew)
+__global__ void k_evict_write(DevCache c, const KT* __restrict__ knew, const KT* __restrict__ vnew,
+                              int* __restrict__ evicted)
 {
     using CT = typename CodeT<BITS>::T;
     const int h = blockIdx.x, b = blockIdx.y, head = b * c.Hkv + h;
-    const int e = c.evict[head];
+    const int n = c.state[2 * head], t = c.state[2 * head + 1];
+    const bool full = n >= c.budget[b];
+    const int e = full ? cand_slot(c.ekey[2 * head]) : n;
     const size_t rowbase = (size_t)head * c.Smax;
     KT* Kh = reinterpret_cast<KT*>(c.K) + rowbase * D;
     KT* Vh = reinterpret_cast<KT*>(c.V) + rowbase * D;
@@ -523,13 +1213,15 @@ __global__ void k_evict_write(DevCache c, const KT* __restrict__ knew, const KT*
         Kh[(size_t)e * D + i] = knew[(size_t)head * D + i];
         Vh[(size_t)e * D + i] = vnew[(size_t)head * D + i];
     }
+    __syncthreads();
     if (threadIdx.x == 0) {
-        const int n = c.state[2 * head], t = c.state[2 * head + 1];
         reinterpret_cast<CT*>(c.code)[(size_t)head * c.code_slots + e] =
             (CT)load_code_words(c.dbg_k + (size_t)head * c.W, c.W);
         c.tok[rowbase + e] = t;
-        c.state[2 * head] = n < c.budget[b] ? n + 1 : n;
+        c.state[2 * head] = full ? n : n + 1;
         c.state[2 * head + 1] = t + 1;
+        c.ekey[2 * head] = 0ull;
+        evicted[head] = e;
     }
 }
 
@@ -537,25 +1229,40 @@ __global__ void k_evict_write(DevCache c, const KT* __restrict__ knew, const KT*
 template <int D, int GM, typename KT>
 __global__ __launch_bounds__(kThreads) void k_attn_split(DevCache c, const float* __restrict__ q)
 {
+    constexpr bool kMfma = std::is_same<KT, bf16_t>::value;
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int head = b * c.Hkv + h;
     const int n = c.state[2 * head];
     const int nsb = max((n + c.chunk - 1) / c.chunk, 1);
     if (split >= nsb) return;
     __shared__ AttnSmem<D, GM> sm;
-    if (threadIdx.x < GM) sm.candlg[threadIdx.x] = -INFINITY;
+    __shared__ PSmem<GM, tile_rows<GM>()> ps;
     const int hq0 = b * c.Hq + h * c.G;
     const size_t rowbase = (size_t)head * c.Smax;
     const KT* Kh = reinterpret_cast<const KT*>(c.K) + rowbase * D;
     const KT* Vh = reinterpret_cast<const KT*>(c.V) + rowbase * D;
     const int s0 = split * c.chunk;
-    attend_rows<D, GM, KT>(Kh, Vh, q + (size_t)hq0 * D, c.G, s0, max(min(s0 + c.chunk, n), s0), -1, sm);
+    const int len = max(min(s0 + c.chunk, n) - s0, 0);
+    const int wave = threadIdx.x >> 6;
+    if constexpr (kMfma) {
+        constexpr int TR = tile_rows<GM>(), NB = ring_depth<GM>();
+        MTile<D, TR> ring[NB];
+        const int ntile = len > wave * TR ? (len - wave * TR + kWaves * TR - 1) / (kWaves * TR) : 0;
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+            if (i < ntile) ring[i].load(Kh, Vh, s0, len, (wave + i * kWaves) * TR);
+        attend_rows_mfma<D, GM, TR, NB>(Kh, Vh, q + (size_t)hq0 * D, c.G, s0, len, -1, ring, sm, ps);
+    } else {
+        Tile<D, KT> first;
+        first.load(Kh, Vh, s0, len, wave * Tile<D, KT>::ROWS);
+        attend_rows<D, GM, KT>(Kh, Vh, q + (size_t)hq0 * D, c.G, s0, len, -1, first, sm);
+    }
     store_partial<D, GM>(sm, c.part, hq0, c.G, c.nsplit, split);
 }
 
-// LSE merge of the chunk partials into the output.
+// LSE merge of the chunk partials of one query head into the output.
 template <int D>
-__global__ __launch_bounds__(kThreads) void k_attn_merge(DevCache c, float* __restrict__ out)
+__global__ __launch_bounds__(kMergeThreads) void k_attn_merge(DevCache c, float* __restrict__ out)
 {
     const int hq = blockIdx.x, b = blockIdx.y;
     const int head = b * c.Hkv + hq / c.G;
@@ -563,44 +1270,15 @@ __global__ __launch_bounds__(kThreads) void k_attn_merge(DevCache c, float* __re
     const int nsb = max((n + c.chunk - 1) / c.chunk, 1);
     const size_t row = (size_t)b * c.Hq + hq;
     const float* part = c.part + row * c.nsplit * (D + 4);
-    __shared__ float s_red[kWaves];
-    __shared__ float s_M, s_L;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    float mx = -INFINITY;
-    for (int j = tid; j < nsb; j += kThreads)
-        if (part[(size_t)j * (D + 4) + D + 1] > 0.f) mx = fmaxf(mx, part[(size_t)j * (D + 4) + D]);
-    mx = wave_max_f(mx);
-    if (lane == 0) s_red[wave] = mx;
-    __syncthreads();
-    if (tid == 0) {
-        float v = s_red[0];
-        for (int w = 1; w < kWaves; ++w) v = fmaxf(v, s_red[w]);
-        s_M = v == -INFINITY ? 0.f : v;
-    }
-    __syncthreads();
-    float ls = 0.f;
-    for (int j = tid; j < nsb; j += kThreads) {
-        const float* rec = part + (size_t)j * (D + 4);
-        if (rec[D + 1] > 0.f) ls += rec[D + 1] * exp2_fast(rec[D] - s_M);
-    }
-    ls = wave_sum_f(ls);
-    __syncthreads();
-    if (lane == 0) s_red[wave] = ls;
-    __syncthreads();
-    if (tid == 0) {
-        float v = 0.f;
-        for (int w = 0; w < kWaves; ++w) v += s_red[w];
-        s_L = v;
-    }
-    __syncthreads();
-    for (int i = tid; i < D; i += kThreads) {
-        float a = 0.f;
-        for (int j = 0; j < nsb; ++j) {
-            const float* rec = part + (size_t)j * (D + 4);
-            if (rec[D + 1] > 0.f) a = fmaf(rec[i], exp2_fast(rec[D] - s_M), a);
-        }
-        out[row * D + i] = s_L > 0.f ? a / s_L : 0.f;
-    }
+    __shared__ MergeSmem<D> sm;
+    auto rec = [&](int j) { return part + (size_t)j * (D + 4); };
+    auto cand = [&](int, float& cl, const float*& cv) {
+        cl = -INFINITY;
+        cv = nullptr;
+    };
+    float4 o;
+    if (merge_head<D>(sm, c.nsplit, nsb, rec, false, -1, cand, false, nullptr, make_float4(0.f, 0.f, 0.f, 0.f), o))
+        reinterpret_cast<float4*>(out + row * D)[threadIdx.x] = o;
 }
 
 // GQA scores of every slot (introspection).
@@ -622,15 +1300,17 @@ __global__ void k_scores(DevCache c, const uint32_t* __restrict__ qcodes, int* _
     scores[(size_t)head * c.Smax + s] = sc;
 }
 
+// stand-alone encoder: 16 rows per block
 template <int D, int BITS, typename XT>
 __global__ __launch_bounds__(kThreads) void k_encode_rows(DevCache c, const XT* __restrict__ X, int n,
                                                           uint32_t* __restrict__ codes)
 {
-    constexpr int PER = 64;   // rows per block
-    const int r0 = blockIdx.x * PER;
-    encode_rows<D, BITS>(X + (size_t)r0 * D, min(PER, n - r0), c.R, [&](int v, unsigned long long cd) {
-        store_words(codes + (size_t)(r0 + v) * c.W, c.W, cd);
-    });
+    __shared__ uint32_t s16[BITS / 16][16];
+    const int r0 = blockIdx.x * 16;
+    const int nv = min(16, n - r0);
+    encode_block16<D, BITS, XT>(X + (size_t)r0 * D, nv, c.R, s16);
+    __syncthreads();
+    if ((int)threadIdx.x < nv) store_words(codes + (size_t)(r0 + threadIdx.x) * c.W, c.W, join16<BITS>(s16, threadIdx.x));
 }
 
 // ---------------------------------------------------------------------------
@@ -670,27 +1350,8 @@ hipError_t with_gm(const DevCache& c, F&& f)
 
 }  // namespace
 
-hipError_t launch_decode_fused(const DevCache& c, const float* q, const void* k, const void* v,
-                               float* out, int* evicted, hipStream_t st)
-{
-    return with_kv(c, [&](auto kt) {
-        using KT = decltype(kt);
-        return with_d(c, [&](auto dd) {
-            return with_bits(c, [&](auto bb) {
-                return with_gm(c, [&](auto gg) {
-                    dim3 grid(c.nsplit, c.Hkv, c.B);
-                    hipLaunchKernelGGL((k_decode_fused<decltype(dd)::value, decltype(bb)::value, decltype(gg)::value, KT>), grid,
-                                       dim3(kThreads), 0, st, c, q, (const KT*)k, (const KT*)v, out,
-                                       evicted);
-                    return hipGetLastError();
-                });
-            });
-        });
-    });
-}
-
-hipError_t launch_decode_split(const DevCache& c, const float* q, const void* k, const void* v,
-                               float* out, int* evicted, hipStream_t st)
+hipError_t launch_decode_fused(const DevCache& c, const float* q, const void* k, const void* v, float* out,
+                               int* evicted, hipStream_t st)
 {
     return with_kv(c, [&](auto kt) {
         using KT = decltype(kt);
@@ -698,17 +1359,34 @@ hipError_t launch_decode_split(const DevCache& c, const float* q, const void* k,
             return with_bits(c, [&](auto bb) {
                 return with_gm(c, [&](auto gg) {
                     constexpr int D = decltype(dd)::value, BITS = decltype(bb)::value, GM = decltype(gg)::value;
-                    hipLaunchKernelGGL((k_lsh_encode<D, BITS, KT>), dim3(c.B), dim3(kThreads), 0, st, c,
-                                       q, (const KT*)k);
+                    hipLaunchKernelGGL((k_decode_fused<D, BITS, GM, KT>), dim3(c.nsplit, c.Hkv, c.B), dim3(kThreads),
+                                       0, st, c, q, (const KT*)k, (const KT*)v, out, evicted);
+                    return hipGetLastError();
+                });
+            });
+        });
+    });
+}
+
+hipError_t launch_decode_split(const DevCache& c, const float* q, const void* k, const void* v, float* out,
+                               int* evicted, hipStream_t st)
+{
+    return with_kv(c, [&](auto kt) {
+        using KT = decltype(kt);
+        return with_d(c, [&](auto dd) {
+            return with_bits(c, [&](auto bb) {
+                return with_gm(c, [&](auto gg) {
+                    constexpr int D = decltype(dd)::value, BITS = decltype(bb)::value, GM = decltype(gg)::value;
+                    const int ntiles = (c.Hq + 15) / 16 + (c.Hkv + 15) / 16;
+                    hipLaunchKernelGGL((k_lsh_encode<D, BITS, KT>), dim3(ntiles, c.B), dim3(kThreads), 0, st, c, q,
+                                       (const KT*)k);
                     const int nsh = (c.Smax + kScoreChunk - 1) / kScoreChunk;
-                    hipLaunchKernelGGL((k_hamming_argmax<BITS, GM>), dim3(nsh, c.Hkv, c.B),
-                                       dim3(kThreads), 0, st, c, evicted);
-                    hipLaunchKernelGGL((k_evict_write<D, BITS, KT>), dim3(c.Hkv, c.B), dim3(128), 0, st,
-                                       c, (const KT*)k, (const KT*)v);
-                    hipLaunchKernelGGL((k_attn_split<D, GM, KT>), dim3(c.nsplit, c.Hkv, c.B),
-                                       dim3(kThreads), 0, st, c, q);
-                    hipLaunchKernelGGL((k_attn_merge<D>), dim3(c.Hq, c.B), dim3(kThreads), 0, st, c,
-                                       out);
+                    hipLaunchKernelGGL((k_hamming_argmax<BITS, GM>), dim3(nsh, c.Hkv, c.B), dim3(kThreads), 0, st, c);
+                    hipLaunchKernelGGL((k_evict_write<D, BITS, KT>), dim3(c.Hkv, c.B), dim3(128), 0, st, c,
+                                       (const KT*)k, (const KT*)v, evicted);
+                    hipLaunchKernelGGL((k_attn_split<D, GM, KT>), dim3(c.nsplit, c.Hkv, c.B), dim3(kThreads), 0, st, c,
+                                       q);
+                    hipLaunchKernelGGL((k_attn_merge<D>), dim3(c.Hq, c.B), dim3(kMergeThreads), 0, st, c, out);
                     return hipGetLastError();
                 });
             });
@@ -721,25 +1399,26 @@ hipError_t launch_scores(const DevCache& c, const uint32_t* qcodes, int* scores,
     return with_bits(c, [&](auto bb) {
         return with_gm(c, [&](auto gg) {
             dim3 grid((c.Smax + 255) / 256, c.Hkv, c.B);
-            hipLaunchKernelGGL((k_scores<decltype(bb)::value, decltype(gg)::value>), grid, dim3(256), 0, st, c, qcodes, scores);
+            hipLaunchKernelGGL((k_scores<decltype(bb)::value, decltype(gg)::value>), grid, dim3(256), 0, st, c, qcodes,
+                               scores);
             return hipGetLastError();
         });
     });
 }
 
-hipError_t launch_encode_rows(const DevCache& c, const void* X, int x_bf16, int n, uint32_t* codes,
-                              hipStream_t st)
+hipError_t launch_encode_rows(const DevCache& c, const void* X, int x_bf16, int n, uint32_t* codes, hipStream_t st)
 {
     if (n <= 0) return hipSuccess;
     return with_d(c, [&](auto dd) {
         return with_bits(c, [&](auto bb) {
-            dim3 grid((n + 63) / 64);
+            constexpr int D = decltype(dd)::value, BITS = decltype(bb)::value;
+            dim3 grid((n + 15) / 16);
             if (x_bf16)
-                hipLaunchKernelGGL((k_encode_rows<decltype(dd)::value, decltype(bb)::value, bf16_t>), grid, dim3(kThreads), 0,
-                                   st, c, (const bf16_t*)X, n, codes);
+                hipLaunchKernelGGL((k_encode_rows<D, BITS, bf16_t>), grid, dim3(kThreads), 0, st, c, (const bf16_t*)X,
+                                   n, codes);
             else
-                hipLaunchKernelGGL((k_encode_rows<decltype(dd)::value, decltype(bb)::value, float>), grid, dim3(kThreads), 0, st,
-                                   c, (const float*)X, n, codes);
+                hipLaunchKernelGGL((k_encode_rows<D, BITS, float>), grid, dim3(kThreads), 0, st, c, (const float*)X, n,
+                                   codes);
             return hipGetLastError();
         });
     });

@@ -33,7 +33,9 @@ __global__ void k_prefill_init(DevCache c)
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         c.state[2 * head] = occ;
         c.state[2 * head + 1] = N;
-        c.count[head] = 0;
+        c.ekey[2 * head] = 0ull;
+        c.ekey[2 * head + 1] = 0ull;
+        c.count[head] = 0u;
     }
 }
 
@@ -46,7 +48,9 @@ __global__ void k_reset(DevCache c)
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         c.state[2 * head] = 0;
         c.state[2 * head + 1] = 0;
-        c.count[head] = 0;
+        c.ekey[2 * head] = 0ull;
+        c.ekey[2 * head + 1] = 0ull;
+        c.count[head] = 0u;
     }
 }
 
@@ -258,6 +262,22 @@ hipError_t with_d_kv(const DevCache& c, F&& f)
 }
 
 }  // namespace
+
+__global__ void k_clear_step_scratch(DevCache c)
+{
+    const int head = blockIdx.x * blockDim.x + threadIdx.x;
+    if (head < c.B * c.Hkv) {
+        c.ekey[2 * head] = 0ull;
+        c.ekey[2 * head + 1] = 0ull;
+        c.count[head] = 0u;
+    }
+}
+
+hipError_t launch_clear_step_scratch(const DevCache& c, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_clear_step_scratch, dim3((c.B * c.Hkv + 255) / 256), dim3(256), 0, st, c);
+    return hipGetLastError();
+}
 
 hipError_t launch_reset(const DevCache& c, hipStream_t st)
 {
