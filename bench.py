@@ -14,7 +14,6 @@ Prints one JSON line (rank 0).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -45,14 +44,6 @@ def step_bytes(shape, budgets) -> int:
     return slots * per_slot + writes + qo
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for f in ("k_decode.hip", "hkv_device.h"):
-        with open(os.path.join(ROOT, "lsh_eviction_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 def load_traffic(workload: str, schedule: str):
     """HBM traffic per launch from committed rocprofv3 counter runs, or None if the
     kernel source changed since they were taken."""
@@ -62,6 +53,7 @@ def load_traffic(workload: str, schedule: str):
     try:
         data = json.load(open(p))
         rec = data.get(f"{workload}/{schedule}")
+        from lsh_eviction_amd.profiling import kernel_source_hash
         if rec and rec.get("kernel_hash") == kernel_source_hash():
             return rec.get("bytes_per_launch")
     except Exception:
@@ -86,6 +78,27 @@ def make_layer_inputs(shape, P, layer: int, seed: int):
     return K, V
 
 
+def copy_bandwidth(mib: int = 1024, reps: int = 10) -> float:
+    """GB/s of torch's device copy (read + write bytes), the practical ceiling of
+    a streaming kernel on this part."""
+    import torch
+    src = torch.empty((mib << 20) // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    gbs = 2 * (mib << 20) * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbs
+
+
 def cpu_baseline(shape, budget_s: float = 15.0):
     """The oracle's decode step timed on one host core on a bounded sample: the
     first sequence of the workload with all its KV heads, its cache filled with
@@ -98,12 +111,12 @@ def cpu_baseline(shape, budget_s: float = 15.0):
     S1 = int(s[0])
     one = shape.scaled(batch=1, prompt_range=None, budget_frac=None, prompt=S1, budget=S1)
     P = datagen.prompt(one)
-    D = datagen.decode(one, steps=64, key_scale=P.key_scale if one.key_outliers else None)
+    D = datagen.decode(one, steps=256, key_scale=P.key_scale if one.key_outliers else None)
     orc = oracle.OracleCache(P.R, P.budgets, one.n_q_heads, one.n_kv_heads)
     orc.prefill(P.K, P.V, P.prompt_lens, oracle.TRUNCATE)
     t0 = time.perf_counter()
     steps = 0
-    while steps < 64:
+    while steps < 256:
         orc.decode_step(D.q[steps], D.k[steps], D.v[steps])
         steps += 1
         if time.perf_counter() - t0 > budget_s:
@@ -216,24 +229,37 @@ def main():
         total_ms = e_start.elapsed_time(e_end)
         kern_ms = total_ms / K_
     else:
-        # timed region 1: the steps back to back
+        # the steps back to back, bracketed by events on the stream they run on
         e_start.record(stream)
         for i in range(K_):
             one(i)
         e_end.record(stream)
         torch.cuda.synchronize()
         total_ms = e_start.elapsed_time(e_end)
-        # timed region 2: the same steps, each launch bracketed by events on its stream
-        K2 = min(K_, 1000)
-        a = [torch.cuda.Event(enable_timing=True) for _ in range(K2)]
-        b = [torch.cuda.Event(enable_timing=True) for _ in range(K2)]
-        for i in range(K2):
-            a[i].record(stream)
+        # the fused schedule is one kernel launch per step: its average launch
+        # duration is the region's time over the launches (gaps included)
+        kern_ms = total_ms / K_
+    # spread: the same steps in blocks of 50, each block bracketed by events
+    blocks = []
+    for j in range(0, min(K_, 1000) - 49, 50):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(j, j + 50):
             one(i)
-            b[i].record(stream)
-        torch.cuda.synchronize()
-        kern_ms = float(np.mean([a[i].elapsed_time(b[i]) for i in range(K2)]))
+        b.record(stream)
+        blocks.append((a, b))
+    # warm: one layer cache only, so the step's bytes may stay in the 256 MB MALL
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    KW = min(K_, 500)
+    w0.record(stream)
+    for i in range(KW):
+        caches[0].decode_step(qs[i % POOL], ks[i % POOL], vs[i % POOL], outs[0], evs[0], stream)
+    w1.record(stream)
+    torch.cuda.synchronize()
+    block_us = sorted(a.elapsed_time(b) * 1e3 / 50 for a, b in blocks)
+    warm_us = w0.elapsed_time(w1) * 1e3 / KW
     wall = time.perf_counter() - t_wall
+    copy_gbs = copy_bandwidth()
 
     ms_per_step = total_ms / K_
     value = 1000.0 / ms_per_step
@@ -256,12 +282,17 @@ def main():
                    "n_kv_heads": shape.n_kv_heads, "head_dim": shape.head_dim, "n_bits": shape.n_bits,
                    "kv_storage": shape.kv_dtype, "budget_slots": int(budgets.sum()),
                    "prompt_tokens": int(n.sum()), "layers_rotated": L, "schedule": args.schedule,
-                   "chunk": caches[0].cfg.chunk or 512, "graph": bool(args.graph)},
+                   "chunk": caches[0].chunk, "graph": bool(args.graph)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
         "bytes_per_step": per_step,
         "kernel_us": round(kern_ms * 1e3, 3),
+        "kernel": "k_decode_fused" if args.schedule == "fused" else "all kernels of the split step",
         "hbm_frac_of_step": round(per_step / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "us_per_step_median_of_50_step_blocks": round(float(np.median(block_us)), 3) if block_us else None,
+        "warm_us_per_step_one_cache": round(warm_us, 3),
+        "copy_gbs": round(copy_gbs, 1),
+        "frac_of_copy": round(achieved / copy_gbs, 4),
         "prefill_ms_per_layer": round(float(np.mean(prefill_ms)), 2),
         "wall_s": round(wall, 3),
     }

@@ -85,8 +85,9 @@ typedef struct {
     int32_t prefill_policy;  /* HKV_PREFILL_* */
     int32_t decode_schedule; /* HKV_DECODE_* */
     int32_t max_prompt;      /* largest n_max a prefill will be given (>= 0) */
-    int32_t chunk;           /* slots per attention split; 0 = library default;
-                                otherwise a multiple of 64 in [64, 65536] */
+    int32_t chunk;           /* slots per attention split (one workgroup each);
+                                0 selects 1024; otherwise a multiple of 64 in
+                                [64, 65536] */
     const int32_t* budgets;  /* host [batch]: cache slots S_b of each sequence */
 } hkv_config;
 

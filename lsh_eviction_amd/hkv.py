@@ -202,6 +202,9 @@ def to_numpy(t) -> np.ndarray:
     return t.numpy()
 
 
+DEFAULT_CHUNK = 1024   # what hkv_config.chunk = 0 selects
+
+
 class Cache:
     """A HashEvict cache on the current GPU, in a torch-allocated workspace."""
 
@@ -220,6 +223,7 @@ class Cache:
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         self.h = hkv_create(self.cfg, R, self.workspace, stream)
         self.n_max = 0
+        self.chunk = int(chunk) or DEFAULT_CHUNK
 
     def close(self):
         if getattr(self, "h", None):

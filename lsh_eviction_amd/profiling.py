@@ -1,0 +1,157 @@
+"""Turn rocprofv3 output into the short text summaries kept under profiles/.
+
+    # a plain copy of known size, to scale the HBM byte counters
+    python -m lsh_eviction_amd.profiling copy --mib 1024 --reps 4
+
+    # kernel-trace statistics -> markdown
+    python -m lsh_eviction_amd.profiling stats --csv <run_kernel_stats.csv> --cmd "<command>" --out <file.md>
+
+    # FETCH_SIZE / WRITE_SIZE counter runs (decode and copy) -> bytes per launch
+    python -m lsh_eviction_amd.profiling traffic --fetch <csv> --write <csv> --copy-fetch <csv> \
+        --copy-write <csv> --copy-mib 1024 --kernel k_decode_fused --key long_128k/fused --out <json>
+
+The counters are read from rocprofv3's `--output-format csv` files
+(`*_counter_collection.csv`: one row per dispatch and counter).  FETCH_SIZE and
+WRITE_SIZE count KiB moved between the L2 and memory; a copy of N bytes reads N
+and writes N, so the copy's readings give the factor by which each counter
+maps to bytes on this part.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def kernel_source_hash() -> str:
+    """Hash of the sources of the decode kernels; counter readings taken on other
+    sources are stale."""
+    h = hashlib.sha256()
+    for f in ("k_decode.hip", "hkv_device.h"):
+        with open(os.path.join(ROOT, "lsh_eviction_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _short(name: str) -> str:
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    base = name.split("(")[0]
+    if "<" in base:
+        head, _, args = base.partition("<")
+        base = head.split("::")[-1].split(" ")[-1] + "<" + args
+    else:
+        base = base.split("::")[-1].split(" ")[-1]
+    return base if len(base) <= 72 else base[:69] + "..."
+
+
+def per_dispatch(path: str, counter: str):
+    """{kernel name: [value per dispatch]} for one counter of a counter-collection csv."""
+    acc = collections.defaultdict(lambda: collections.defaultdict(float))
+    with open(path, newline="") as fh:
+        for row in csv.DictReader(fh):
+            if row.get("Counter_Name") != counter:
+                continue
+            acc[row["Kernel_Name"]][row.get("Dispatch_Id") or row.get("Correlation_Id")] += float(row["Counter_Value"])
+    return {k: list(v.values()) for k, v in acc.items()}
+
+
+def _pick(per: dict, needle: str):
+    hits = [(k, v) for k, v in per.items() if needle in k]
+    if not hits:
+        raise SystemExit(f"no dispatch of a kernel matching {needle!r}; kernels: {sorted(per)[:8]}")
+    k, v = max(hits, key=lambda kv: len(kv[1]))
+    return k, v
+
+
+def _mean(v):
+    return sum(v) / len(v)
+
+
+def cmd_copy(args):
+    import torch
+    n = args.mib << 20
+    src = torch.empty(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    torch.cuda.synchronize()
+    for _ in range(args.reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copied {args.mib} MiB {args.reps} times", flush=True)
+
+
+def cmd_stats(args):
+    rows = list(csv.DictReader(open(args.csv, newline="")))
+    lines = ["# rocprofv3 kernel statistics", "", f"Command: `{args.cmd}`", "",
+             "| kernel | calls | avg us | min us | max us | share % |", "|---|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        name = _short(r["Name"])
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    if args.note:
+        lines += ["", args.note]
+    text = "\n".join(lines) + "\n"
+    with open(args.out, "w") as fh:
+        fh.write(text)
+    print(text)
+
+
+def cmd_traffic(args):
+    copy_bytes = args.copy_mib << 20
+    cf = per_dispatch(args.copy_fetch, "FETCH_SIZE")
+    cw = per_dispatch(args.copy_write, "WRITE_SIZE")
+    ckf, cvf = _pick(cf, "copy")
+    ckw, cvw = _pick(cw, "copy")
+    f_fetch = _mean(cvf) * 1024.0 / copy_bytes     # counter bytes per byte read
+    f_write = _mean(cvw) * 1024.0 / copy_bytes
+    kf, vf = _pick(per_dispatch(args.fetch, "FETCH_SIZE"), args.kernel)
+    kw, vw = _pick(per_dispatch(args.write, "WRITE_SIZE"), args.kernel)
+    read_b = _mean(vf) * 1024.0 / f_fetch
+    write_b = _mean(vw) * 1024.0 / f_write
+    rec = {
+        "kernel": _short(kf), "kernel_hash": kernel_source_hash(),
+        "bytes_per_launch": round(read_b + write_b),
+        "read_bytes": round(read_b), "write_bytes": round(write_b),
+        "fetch_kib_raw": round(_mean(vf), 1), "write_kib_raw": round(_mean(vw), 1),
+        "dispatches": [len(vf), len(vw)],
+        "copy_kernel": _short(ckf), "copy_bytes": copy_bytes,
+        "copy_fetch_factor": round(f_fetch, 4), "copy_write_factor": round(f_write, 4),
+    }
+    data = {}
+    if os.path.exists(args.out):
+        data = json.load(open(args.out))
+    data[args.key] = rec
+    with open(args.out, "w") as fh:
+        json.dump(data, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps(rec, indent=1))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="mode", required=True)
+    a = sub.add_parser("copy")
+    a.add_argument("--mib", type=int, default=1024)
+    a.add_argument("--reps", type=int, default=4)
+    a = sub.add_parser("stats")
+    a.add_argument("--csv", required=True)
+    a.add_argument("--cmd", required=True)
+    a.add_argument("--out", required=True)
+    a.add_argument("--note", default="")
+    a = sub.add_parser("traffic")
+    for k in ("fetch", "write", "copy_fetch", "copy_write", "kernel", "key", "out"):
+        a.add_argument("--" + k.replace("_", "-"), required=True, dest=k)
+    a.add_argument("--copy-mib", type=int, default=1024)
+    args = ap.parse_args(argv)
+    {"copy": cmd_copy, "stats": cmd_stats, "traffic": cmd_traffic}[args.mode](args)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])
