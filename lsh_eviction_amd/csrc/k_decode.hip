@@ -148,6 +148,45 @@ __device__ __forceinline__ void encode_block16(const XT* __restrict__ X, int nve
     }
 }
 
+// Wave-level encoder over operands staged in LDS: rows 0 .. nq-1 of X are
+// the fp32 rows of Xq, row nq is the vector xk (stored as KT), rows above are
+// zero; Rs is R (d x b fp32, row-major).  Lane i returns the 16-bit chunk nt
+// of the code of row i (as encode16_mfma).
+template <int D, int BITS, typename KT>
+__device__ __forceinline__ uint32_t enc_lds(const float* Xq, int nq, const KT* xk, const float* Rs, int nt)
+{
+    constexpr int DQ = D / 4;
+    constexpr int EPL = Vec16<KT>::EPL;
+    const int lane = threadIdx.x & 63;
+    const int m = lane & 15, qd = lane >> 4;
+    const float* xr = Xq + (size_t)(m < nq ? m : 0) * D + qd * DQ;
+    const KT* kr = xk + qd * DQ;
+    const float* rc = Rs + (size_t)(qd * DQ) * BITS + nt * 16 + m;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int v = 0; v < DQ / EPL; ++v) {
+        float kf[EPL];
+        Vec16<KT>::cvt(*reinterpret_cast<const uint4*>(kr + v * EPL), kf);
+#pragma unroll
+        for (int e4 = 0; e4 < EPL / 4; ++e4) {
+            const float4 q4 = *reinterpret_cast<const float4*>(xr + v * EPL + 4 * e4);
+            const float qv[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int s = v * EPL + 4 * e4 + e;
+                const float x = m < nq ? qv[e] : (m == nq ? kf[4 * e4 + e] : 0.f);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x, rc[s * BITS], acc, 0, 0, 0);
+            }
+        }
+    }
+    unsigned long long mk[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mk[r] = __ballot(acc[r] > 0.f);
+    const int a = (lane & 15) >> 2, r = lane & 3;
+    const unsigned long long mm = r == 0 ? mk[0] : r == 1 ? mk[1] : r == 2 ? mk[2] : mk[3];
+    return (uint32_t)((mm >> (16 * a)) & 0xFFFFull);
+}
+
 template <int BITS>
 __device__ __forceinline__ unsigned long long join16(const uint32_t (*c16)[16], int row)
 {
@@ -864,8 +903,9 @@ struct MergeBlockSmem {
     float4 a[kWaves][GM][D / 4];
 };
 
-template <int D, int GM>
+template <int D, int BITS, int GM>
 union FusedSmem {
+    float R[D * BITS];          // encoder operand, dead once the codes are known
     AttnSmem<D, GM> at;
     MergeBlockSmem<D, GM> mg;
 };
@@ -880,22 +920,17 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     constexpr bool kMfma = std::is_same<KT, bf16_t>::value;
     constexpr int TR = tile_rows<GM>();
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int S = c.budget[b];
-    const int nsb = (S + c.chunk - 1) / c.chunk;
-    if (split >= nsb) return;
     const int G = c.G;
     const int head = b * c.Hkv + h;
-    const int n = c.state[2 * head];
-    const int t = c.state[2 * head + 1];
-    const bool full = n >= S;
     const int s0 = split * c.chunk;
-    const int len = max(min(s0 + c.chunk, n) - s0, 0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-    __shared__ FusedSmem<D, GM> u;
+    __shared__ FusedSmem<D, BITS, GM> u;
     __shared__ PSmem<GM, TR> ps;
+    __shared__ __align__(16) float s_q[GM][D];     // the group's queries (fp32)
+    __shared__ __align__(16) KT s_kn[D], s_vn[D];  // the new token's key and value
     __shared__ uint32_t s_q16[BITS / 16][16];
-    __shared__ uint32_t s_k16[BITS / 16][16];
+    __shared__ uint32_t s_k16[BITS / 16];
     __shared__ unsigned long long s_red[kWaves];
     __shared__ float s_nlg[GM];
     __shared__ int s_last;
@@ -911,26 +946,39 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     const KT* kh = knew + (size_t)head * D;
     const KT* vh = vnew + (size_t)head * D;
 
-    // Loads are issued in the order their data is needed (the vector memory
-    // counter completes in order): encoder operands, the new token's key and
-    // value, the chunk's codes, then the first tiles of every wave.
-    constexpr int NT = BITS / 16;
-    EncOps<D> eq, ek;
-    if (wave < NT) {
-        enc_load_x<D, BITS, float>(eq, qh, G);
-        if (split == 0) enc_load_x<D, BITS, KT>(ek, kh, 1);
-        enc_load_r<D, BITS>(eq, c.R, wave);
-    }
-    constexpr int NH = (GM + kWaves - 1) / kWaves;   // new-token logits per wave
-    float2 kn = make_float2(0.f, 0.f), qn[NH];
+    // The small operands (R, the group's queries, the new key and value) and
+    // the chunk's codes are fetched first and waited for before any K/V tile
+    // is requested: issued behind the tile prefetch of every block they would
+    // queue behind ~all of it in the memory system, and the loop cannot start
+    // before the codes are known.  They go through LDS.
+    constexpr int NR4 = D * BITS / 4;
+    constexpr int RPT = (NR4 + kThreads - 1) / kThreads;
+    constexpr int NK4 = D * (int)sizeof(KT) / 16;
+    static_assert(GM * D / 4 <= kThreads && NK4 <= 64, "staging shape");
+    float4 rst[RPT];
 #pragma unroll
-    for (int a = 0; a < NH; ++a) {
-        const int gn = min(wave + a * kWaves, G - 1);
-        qn[a] = 2 * lane < D ? make_float2(qh[gn * D + 2 * lane], qh[gn * D + 2 * lane + 1]) : make_float2(0.f, 0.f);
-    }
-    if (2 * lane < D) kn = make_float2(to_f32(kh[2 * lane]), to_f32(kh[2 * lane + 1]));
+    for (int j = 0; j < RPT; ++j) rst[j] = reinterpret_cast<const float4*>(c.R)[min(tid + j * kThreads, NR4 - 1)];
+    const int NQ4 = G * D / 4;
+    const float4 qst = reinterpret_cast<const float4*>(qh)[min(tid, NQ4 - 1)];
+    const uint4 kvst = reinterpret_cast<const uint4*>(wave == 0 ? kh : vh)[min(lane, NK4 - 1)];
     const int cvec = min(s0 + tid * VS, (int)c.code_slots - VS);
-    uint4 craw = *reinterpret_cast<const uint4*>(codeh + cvec);
+    const uint4 craw = *reinterpret_cast<const uint4*>(codeh + cvec);
+#pragma unroll
+    for (int j = 0; j < RPT; ++j)
+        if (tid + j * kThreads < NR4) reinterpret_cast<float4*>(u.R)[tid + j * kThreads] = rst[j];
+    if (tid < NQ4) reinterpret_cast<float4*>(&s_q[0][0])[tid] = qst;
+    if (lane < NK4 && wave < 2) reinterpret_cast<uint4*>(wave == 0 ? s_kn : s_vn)[lane] = kvst;
+    // the cache state (its loads overlap the ones above)
+    const int S = c.budget[b];
+    const int nsb = (S + c.chunk - 1) / c.chunk;
+    const int n = c.state[2 * head];
+    const int t = c.state[2 * head + 1];
+    const bool full = n >= S;
+    const int len = max(min(s0 + c.chunk, n) - s0, 0);
+    __syncthreads();
+    if (split >= nsb) return;   // ragged batch: this sequence has fewer chunks
+
+    // the first tiles of every wave, in flight while the codes are computed
     constexpr int NB = ring_depth<GM>();
     MTile<D, TR> ring[kMfma ? NB : 1];
     Tile<D, KT> first;
@@ -941,33 +989,37 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
         first.load(Kh, Vh, s0, len, wave * Tile<D, KT>::ROWS);
     }
 
-    // stages 1-2: codes of the group's queries (and of the new key, once)
+    // stages 1-2: codes of the group's queries (rows 0 .. G-1) and of the new
+    // key (row G, or a pass of its own when the group fills all 16 rows)
+    constexpr int NT = BITS / 16;
     if (wave < NT) {
-        const uint32_t c16 = enc_compute<D>(eq);
+        const uint32_t c16 = enc_lds<D, BITS, KT>(&s_q[0][0], G, s_kn, u.R, wave);
         if (lane < G) s_q16[wave][lane] = c16;
-        if (split == 0) {
-#pragma unroll
-            for (int s2 = 0; s2 < D / 4; ++s2) ek.rv[s2] = eq.rv[s2];
-            const uint32_t k16 = enc_compute<D>(ek);
-            if (lane == 0) s_k16[wave][0] = k16;
+        if (lane == G && G < 16) s_k16[wave] = c16;
+    } else if (G == 16 && wave < 2 * NT) {
+        const uint32_t c16 = enc_lds<D, BITS, KT>(&s_q[0][0], 0, s_kn, u.R, wave - NT);
+        if (lane == 0) s_k16[wave - NT] = c16;
+    }
+    // base-2 logit of the new token for each head (only the head's last block
+    // uses them)
+    {
+        const float qs = qscale2<D>();
+        const int i0 = 2 * lane;
+        for (int g = wave; g < G; g += kWaves) {
+            float dot = 0.f;
+            if (i0 < D) dot = fmaf(s_q[g][i0] * qs, to_f32(s_kn[i0]), s_q[g][i0 + 1] * qs * to_f32(s_kn[i0 + 1]));
+            dot = wave_sum_f(dot);
+            if (lane == 0) s_nlg[g] = dot;
         }
     }
-    // base-2 logit of the new token for head `wave` (only the head's last
-    // block uses it)
-#pragma unroll
-    for (int a = 0; a < NH; ++a) {
-        const int g = wave + a * kWaves;
-        float dot = qn[a].x * qscale2<D>() * kn.x + qn[a].y * qscale2<D>() * kn.y;
-        dot = wave_sum_f(dot);
-        if (lane == 0 && g < G) s_nlg[g] = dot;
-    }
-    __syncthreads();
+    __syncthreads();   // the codes are known; u.R is dead from here on
     if (split == 0) {
         if (tid < G) store_words(c.dbg_q + (size_t)(hq0 + tid) * c.W, c.W, join16<BITS>(s_q16, tid));
         if (tid == 0) {
-            const unsigned long long kc = join16<BITS>(s_k16, 0);
-            st_dev(c.dbg_k + (size_t)head * c.W, (uint32_t)kc);
-            if (c.W > 1) st_dev(c.dbg_k + (size_t)head * c.W + 1, (uint32_t)(kc >> 32));
+            unsigned long long kc = 0;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) kc |= (unsigned long long)s_k16[nt] << (16 * nt);
+            store_words(c.dbg_k + (size_t)head * c.W, c.W, kc);
         }
     }
 
@@ -993,9 +1045,9 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
 
     // attention over the chunk with the candidate held out
     if constexpr (kMfma)
-        attend_rows_mfma<D, GM, TR, NB>(Kh, Vh, qh, G, s0, len, cand, ring, sm, ps);
+        attend_rows_mfma<D, GM, TR, NB>(Kh, Vh, &s_q[0][0], G, s0, len, cand, ring, sm, ps);
     else
-        attend_rows<D, GM, KT>(Kh, Vh, qh, G, s0, len, cand, first, sm);
+        attend_rows<D, GM, KT>(Kh, Vh, &s_q[0][0], G, s0, len, cand, first, sm);
 
     // publish this chunk: partial softmax, candidate logits and value row
     publish_partial<D, GM>(sm, c.part, hq0, G, c.nsplit, split);
@@ -1004,7 +1056,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
         const int i0 = 2 * lane;
         for (int g = wave; g < G; g += kWaves) {
             float dot = 0.f;
-            if (i0 < D) dot = fmaf(qh[g * D + i0] * qs, kc2.x, qh[g * D + i0 + 1] * qs * kc2.y);
+            if (i0 < D) dot = fmaf(s_q[g][i0] * qs, kc2.x, s_q[g][i0 + 1] * qs * kc2.y);
             dot = wave_sum_f(dot);
             if (lane == 0) st_dev(c.cand_lg + crec * G + g, dot);
         }
@@ -1107,7 +1159,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     for (int idx = tid; idx < G * TPR; idx += kThreads) {
         const int g = idx / TPR, cc = idx % TPR;
         float M = s_nlg[g], L = 1.f;
-        float4 A = load4_f32(vh + 4 * cc);
+        float4 A = load4_f32(s_vn + 4 * cc);
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) lse_add4(M, L, A, mg.m[w][g], mg.l[w][g], mg.a[w][g][cc]);
         const float inv = 1.f / L;
@@ -1117,12 +1169,13 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
 
     // stage 5: the new token takes slot e
     for (int i = tid; i < D; i += kThreads) {
-        Kh[(size_t)e * D + i] = kh[i];
-        Vh[(size_t)e * D + i] = vh[i];
+        Kh[(size_t)e * D + i] = s_kn[i];
+        Vh[(size_t)e * D + i] = s_vn[i];
     }
     if (tid == 0) {
-        unsigned long long kc = ld_dev(c.dbg_k + (size_t)head * c.W);
-        if (c.W > 1) kc |= (unsigned long long)ld_dev(c.dbg_k + (size_t)head * c.W + 1) << 32;
+        unsigned long long kc = 0;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) kc |= (unsigned long long)s_k16[nt] << (16 * nt);
         reinterpret_cast<CT*>(c.code)[(size_t)head * c.code_slots + e] = (CT)kc;
         c.tok[rowbase + e] = t;
         c.state[2 * head] = full ? n : n + 1;
