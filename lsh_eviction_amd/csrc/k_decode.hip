@@ -896,6 +896,100 @@ __device__ __forceinline__ void publish_partial(const AttnSmem<D, GM>& sm, float
 
 // Shared memory of the last block's merge: one (max, sum, 4 outputs) per
 // wave, head and 4-element column.
+// Loads of records other blocks wrote through to memory, with the cache
+// policy of an agent-scope load (sc1: a line this XCD's L2 may hold stale is
+// fetched again), 16, 8 or 4 bytes at byte offset `off` of a buffer resource.
+// Out-of-range offsets read zero.
+constexpr int kCpolSC1 = 16;
+constexpr int kRsrcWord3 = 0x00020000;   // 32-bit data format, no swizzle
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const float* base, size_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, (int)bytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ float4 ld_sc1_16(__amdgpu_buffer_rsrc_t rs, int off)
+{
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kCpolSC1);
+    float4 f;
+    __builtin_memcpy(&f, &v, 16);
+    return f;
+}
+
+__device__ __forceinline__ float2 ld_sc1_8(__amdgpu_buffer_rsrc_t rs, int off)
+{
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kCpolSC1);
+    float2 f;
+    __builtin_memcpy(&f, &v, 8);
+    return f;
+}
+
+__device__ __forceinline__ float ld_sc1_4(__amdgpu_buffer_rsrc_t rs, int off)
+{
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, kCpolSC1));
+}
+
+// The published records of the other blocks of a head, as seen by its last
+// block: partials [Hq-slice][nsplit][D + 4] (acc, m, l), candidate logits
+// [cstride][G] and candidate value rows [cstride][D].
+struct MergeArgs {
+    __amdgpu_buffer_rsrc_t part, clg, cv;
+    int nsplit, G, nsb, r, c4;
+    bool full;
+    unsigned long long wkey;
+    int chunk;
+};
+
+// Folds the records of splits j = j0 + r + RS * jj (jj < JB, all j0) into the
+// thread's running (M, L, A) of its 4 output columns c4 for every head.  The
+// loads of a batch are all issued before any is used (one round trip to
+// memory per batch).  Every split's held-out candidate is added back except
+// the winner's (split js of the evicted slot).  Returns the evicted slot
+// (`e` when the cache is not full).
+template <int D, int GM, int JB>
+__device__ __forceinline__ int merge_splits(const MergeArgs& a, int e, float (&Mt)[GM], float (&Lt)[GM],
+                                            float4 (&At)[GM])
+{
+    constexpr int RS = kThreads / (D / 4);
+    int js = -1;
+    for (int j0 = 0; j0 < a.nsb; j0 += RS * JB) {
+        float4 av[JB][GM], cv[JB];
+        float mj[JB][GM], lj[JB][GM], cl[JB][GM];
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj) {
+            const int j = min(j0 + a.r + RS * jj, a.nsb - 1);
+            cv[jj] = ld_sc1_16(a.cv, (j * D + 4 * a.c4) * 4);
+#pragma unroll
+            for (int g = 0; g < GM; ++g) {
+                const int gg = min(g, a.G - 1);
+                const int rec = (gg * a.nsplit + j) * (D + 4);
+                av[jj][g] = ld_sc1_16(a.part, (rec + 4 * a.c4) * 4);
+                const float2 ml = ld_sc1_8(a.part, (rec + D) * 4);
+                mj[jj][g] = ml.x;
+                lj[jj][g] = ml.y;
+                cl[jj][g] = ld_sc1_4(a.clg, (j * a.G + gg) * 4);
+            }
+        }
+        if (a.full) {
+            e = cand_slot(a.wkey);
+            js = e / a.chunk;
+        }
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj) {
+            const int j = j0 + a.r + RS * jj;
+            if (j < a.nsb) {
+                const bool hold = a.full && j != js;
+#pragma unroll
+                for (int g = 0; g < GM; ++g) {
+                    if (lj[jj][g] > 0.f) lse_add4(Mt[g], Lt[g], At[g], mj[jj][g], lj[jj][g], av[jj][g]);
+                    if (hold) lse_add4(Mt[g], Lt[g], At[g], cl[jj][g], 1.f, cv[jj]);
+                }
+            }
+        }
+    }
+    return e;
+}
+
 template <int D, int GM>
 struct MergeBlockSmem {
     float m[kWaves][GM];
@@ -1077,12 +1171,9 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     // j = r + RS * jj.  All loads of a batch of splits are issued before any
     // of them is used, so the merge costs one round trip to memory per batch.
     if (tid == 0) c.count[head] = 0u;
-    // Acquire: drop this XCD's cached lines so that the plain loads below see
-    // what the other blocks wrote through to memory.
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     constexpr int TPR = D / 4;
     constexpr int RS = kThreads / TPR;
-    constexpr int JB = GM <= 4 ? 4 : (GM <= 8 ? 2 : 1);   // splits per thread and batch
+    constexpr int JBMAX = GM <= 4 ? 4 : (GM <= 8 ? 2 : 1);   // register budget
     const int c4 = tid % TPR, r = tid / TPR;
     const unsigned long long wkey = ld_dev(&c.ekey[2 * head + (t & 1)]);
     float Mt[GM], Lt[GM];
@@ -1093,45 +1184,18 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
         Lt[g] = 0.f;
         At[g] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    const float* partb = c.part + (size_t)hq0 * c.nsplit * (D + 4);
-    const float* clgb = c.cand_lg + (size_t)head * c.cstride * G;
-    const float* cvb = c.cand_v + (size_t)head * c.cstride * D;
-    int e = n, js = -1;
-    for (int j0 = 0; j0 < nsb; j0 += RS * JB) {
-        float4 av[JB][GM], cv[JB];
-        float mj[JB][GM], lj[JB][GM], cl[JB][GM];
-#pragma unroll
-        for (int jj = 0; jj < JB; ++jj) {
-            const int j = min(j0 + r + RS * jj, nsb - 1);
-            cv[jj] = reinterpret_cast<const float4*>(cvb + (size_t)j * D)[c4];
-#pragma unroll
-            for (int g = 0; g < GM; ++g) {
-                const int gg = min(g, G - 1);
-                const float* rec = partb + ((size_t)gg * c.nsplit + j) * (D + 4);
-                av[jj][g] = reinterpret_cast<const float4*>(rec)[c4];
-                const float2 ml = *reinterpret_cast<const float2*>(rec + D);
-                mj[jj][g] = ml.x;
-                lj[jj][g] = ml.y;
-                cl[jj][g] = clgb[(size_t)j * G + gg];
-            }
-        }
-        if (full) {
-            e = cand_slot(wkey);
-            js = e / c.chunk;
-        }
-#pragma unroll
-        for (int jj = 0; jj < JB; ++jj) {
-            const int j = j0 + r + RS * jj;
-            if (j < nsb) {
-                const bool hold = full && j != js;
-#pragma unroll
-                for (int g = 0; g < GM; ++g) {
-                    if (lj[jj][g] > 0.f) lse_add4(Mt[g], Lt[g], At[g], mj[jj][g], lj[jj][g], av[jj][g]);
-                    if (hold) lse_add4(Mt[g], Lt[g], At[g], cl[jj][g], 1.f, cv[jj]);
-                }
-            }
-        }
-    }
+    MergeArgs ma{dev_rsrc(c.part + (size_t)hq0 * c.nsplit * (D + 4), (size_t)G * c.nsplit * (D + 4) * 4),
+                 dev_rsrc(c.cand_lg + (size_t)head * c.cstride * G, (size_t)c.cstride * G * 4),
+                 dev_rsrc(c.cand_v + (size_t)head * c.cstride * D, (size_t)c.cstride * D * 4),
+                 c.nsplit, G, nsb, r, c4, full, wkey, c.chunk};
+    const int per = (nsb + RS - 1) / RS;   // splits per thread
+    int e = n;
+    if (per <= 1 || JBMAX == 1)
+        e = merge_splits<D, GM, 1>(ma, e, Mt, Lt, At);
+    else if (per <= 2 || JBMAX == 2)
+        e = merge_splits<D, GM, (JBMAX >= 2 ? 2 : 1)>(ma, e, Mt, Lt, At);
+    else
+        e = merge_splits<D, GM, JBMAX>(ma, e, Mt, Lt, At);
     MergeBlockSmem<D, GM>& mg = u.mg;
     // lanes of a wave that share c4 (lane % TPR) combine, then one entry per wave
 #pragma unroll
