@@ -102,15 +102,15 @@ extern "C" hkv_status hkv_create(const hkv_config* cfg, const float* R_host, voi
     d.dbg_q = (uint32_t*)(ws + L.off_dbg_q);
     d.dbg_k = (uint32_t*)(ws + L.off_dbg_k);
     d.part = (float*)(ws + L.off_part);
-    d.cand_key = (unsigned long long*)(ws + L.off_cand_key);
-    d.cand_lg = (float*)(ws + L.off_cand_lg);
+    d.frec = (float*)(ws + L.off_frec);
+    d.fscal = (float*)(ws + L.off_fscal);
     d.cand_v = (float*)(ws + L.off_cand_v);
     d.ekey = (unsigned long long*)(ws + L.off_ekey);
     d.info = (int*)(ws + L.off_info);
     d.count = (unsigned*)(ws + L.off_count);
     d.pcode = ws + L.off_pcode;
     d.B = L.B; d.Hq = L.Hq; d.Hkv = L.Hkv; d.G = L.G; d.d = L.d; d.bits = L.bits; d.W = L.W;
-    d.Smax = L.Smax; d.chunk = L.chunk; d.nsplit = L.nsplit; d.cstride = L.cstride;
+    d.Smax = L.Smax; d.chunk = L.chunk; d.nsplit = L.nsplit;
     d.kv_bf16 = L.kv_dtype == HKV_BF16;
     d.code_slots = (long long)L.code_slots;
     d.pcode_slots = (long long)L.pcode_slots;

@@ -21,15 +21,14 @@ struct DevCache {
     uint32_t* dbg_q;                // [B][Hq][W] query codes of the last step
     uint32_t* dbg_k;                // [B][Hkv][W] key codes of the last step
     float* part;                    // [B][Hq][nsplit][d + 4]: acc[d], m, l
-    unsigned long long* cand_key;   // [B][Hkv][cstride] (score << 32) | ~slot, 0 = none
-    float* cand_lg;                 // [B][Hkv][cstride][G] logits (base 2) of the candidate
-    float* cand_v;                  // [B][Hkv][cstride][d] value row of the candidate (fp32)
+    float* frec;                    // [B][Hkv][nsplit][G][d] fused-step partial acc of each split
+    float* fscal;                   // [B][Hkv][nsplit][G][4] (max, sum, candidate logit, 0), base 2
+    float* cand_v;                  // [B][Hkv][nsplit][d] value row of the split's candidate (fp32)
     unsigned long long* ekey;       // [B][Hkv][2] eviction key of the step, by parity of its position
     int* info;                      // [B][Hkv][2] occupancy and position at the start of the step
     unsigned* count;                // [B][Hkv] blocks of the current step that have published
     void* pcode;                    // [B][Hkv][pcode_slots] prompt key codes
     int B, Hq, Hkv, G, d, bits, W, Smax, chunk, nsplit;
-    int cstride;                    // candidates per head in cand_key / cand_lg
     int kv_bf16;
     long long code_slots, pcode_slots;
 };

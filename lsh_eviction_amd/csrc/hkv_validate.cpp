@@ -64,10 +64,6 @@ hkv_status compute_layout(const hkv_config* cfg, Layout* L, char* err, size_t er
     l.Smax = Smax;
     l.chunk = cfg->chunk ? cfg->chunk : kDefaultChunk;
     l.nsplit = (Smax + l.chunk - 1) / l.chunk;
-    {
-        const int nscore = (Smax + kScoreChunk - 1) / kScoreChunk;
-        l.cstride = l.nsplit > nscore ? l.nsplit : nscore;
-    }
     l.max_prompt = cfg->max_prompt;
     l.code_slots = align_up((size_t)Smax, 64);
     l.pcode_slots = align_up((size_t)(cfg->max_prompt > 0 ? cfg->max_prompt : 1), 64);
@@ -90,9 +86,9 @@ hkv_status compute_layout(const hkv_config* cfg, Layout* L, char* err, size_t er
     l.off_dbg_q = take((size_t)l.B * l.Hq * l.W * 4);
     l.off_dbg_k = take(heads * l.W * 4);
     l.off_part = take((size_t)l.B * l.Hq * l.nsplit * (l.d + 4) * 4);
-    l.off_cand_key = take(heads * l.cstride * 8);
-    l.off_cand_lg = take(heads * l.cstride * G * 4);
-    l.off_cand_v = take(heads * l.cstride * l.d * 4);
+    l.off_frec = take(heads * l.nsplit * G * l.d * 4);
+    l.off_fscal = take(heads * l.nsplit * G * 16);
+    l.off_cand_v = take(heads * l.nsplit * l.d * 4);
     l.off_ekey = take(heads * 2 * 8);
     l.off_info = take(heads * 2 * 4);
     l.off_count = take(heads * 4);

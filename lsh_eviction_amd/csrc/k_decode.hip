@@ -691,29 +691,6 @@ __device__ __forceinline__ void attend_rows_mfma(const bf16_t* __restrict__ Kh, 
     __syncthreads();
 }
 
-// The held-out candidate of a chunk: its base-2 logits for the G heads (VALU
-// dot products, one head per wave) into clg[0 .. G) and its value row (fp32)
-// into candv.  kc / vc: the lane's two elements of the candidate's K and V
-// rows (every wave holds them).
-template <int D>
-__device__ __forceinline__ void candidate_terms(const float* __restrict__ qh, int G, float2 kc, float2 vc,
-                                                float* __restrict__ clg, float* __restrict__ candv)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int i0 = 2 * lane;
-    const bool in = i0 < D;
-    const float qs = qscale2<D>();
-    for (int g = wave; g < G; g += kWaves) {
-        float dot = 0.f;
-        if (in) dot = fmaf(qh[g * D + i0] * qs, kc.x, qh[g * D + i0 + 1] * qs * kc.y);
-        dot = wave_sum_f(dot);
-        if (lane == 0) clg[g] = dot;
-    }
-    if (wave == 0 && in) {
-        candv[i0] = vc.x;
-        candv[i0 + 1] = vc.y;
-    }
-}
 
 // ---------------------------------------------------------------------------
 // LSE merge of the partials of one query head
@@ -827,33 +804,9 @@ constexpr int ring_depth()
 // other; agent-scope atomic loads and stores (the sc1 cache policy) write
 // through and re-fetch past them, so the data never sits stale in a writer's
 // or a reader's L2, and no L2-wide writeback fence is needed.
-__device__ __forceinline__ void st_dev(float* p, float v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_dev(unsigned long long* p, unsigned long long v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_dev(const float* p)
-{
-    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t ld_dev(const uint32_t* p)
-{
-    return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ unsigned long long ld_dev(const unsigned long long* p)
 {
     return __hip_atomic_load(const_cast<unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float4 ld_dev4(const float* p)
-{
-    return make_float4(ld_dev(p), ld_dev(p + 1), ld_dev(p + 2), ld_dev(p + 3));
 }
 
 // Every memory operation this thread issued has completed -- its write-through
@@ -866,36 +819,6 @@ __device__ __forceinline__ void own_stores_complete()
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// The block's partial for query heads g < G, device-coherent:
-// part[(hq, split)] = acc[D], m, l.
-template <int D, int GM>
-__device__ __forceinline__ void publish_partial(const AttnSmem<D, GM>& sm, float* __restrict__ part, int hq0, int G,
-                                                int nsplit, int split)
-{
-    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-        const int g = idx / D, i = idx % D;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm.m[w][g]);
-        const float ms = mx == -INFINITY ? 0.f : mx;
-        float a = 0.f, ls = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float sc = exp2_fast(sm.m[w][g] - ms);
-            a += sm.acc[w][g][i] * sc;
-            ls += sm.l[w][g] * sc;
-        }
-        float* rec = part + ((size_t)(hq0 + g) * nsplit + split) * (D + 4);
-        st_dev(rec + i, a);
-        if (i == 0) {
-            st_dev(rec + D, mx);
-            st_dev(rec + D + 1, ls);
-        }
-    }
-}
-
-// Shared memory of the last block's merge: one (max, sum, 4 outputs) per
-// wave, head and 4-element column.
 // Loads of records other blocks wrote through to memory, with the cache
 // policy of an agent-scope load (sc1: a line this XCD's L2 may hold stale is
 // fetched again), 16, 8 or 4 bytes at byte offset `off` of a buffer resource.
@@ -929,12 +852,61 @@ __device__ __forceinline__ float ld_sc1_4(__amdgpu_buffer_rsrc_t rs, int off)
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, kCpolSC1));
 }
 
-// The published records of the other blocks of a head, as seen by its last
-// block: partials [Hq-slice][nsplit][D + 4] (acc, m, l), candidate logits
-// [cstride][G] and candidate value rows [cstride][D].
+// Write-through stores with the same policy (the store side of the hand-off).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void st_sc1_16(__amdgpu_buffer_rsrc_t rs, int off, float4 v)
+{
+    u32x4 u;
+    __builtin_memcpy(&u, &v, 16);
+    __builtin_amdgcn_raw_buffer_store_b128(u, rs, off, 0, kCpolSC1);
+}
+
+__device__ __forceinline__ void st_sc1_8(__amdgpu_buffer_rsrc_t rs, int off, float2 v)
+{
+    u32x2 u;
+    __builtin_memcpy(&u, &v, 8);
+    __builtin_amdgcn_raw_buffer_store_b64(u, rs, off, 0, kCpolSC1);
+}
+
+// The block's partial of the fused step, write-through: acc [G][D] at `rec`
+// and one (max, sum, candidate logit, 0) per head at `scal` (base 2; the
+// candidate logit is 0 when the chunk has no candidate).
+template <int D, int GM>
+__device__ __forceinline__ void publish_fused(const AttnSmem<D, GM>& sm, __amdgpu_buffer_rsrc_t rec,
+                                              __amdgpu_buffer_rsrc_t scal, int G, const float* clg, bool has_cand)
+{
+    constexpr int D4 = D / 4;
+    for (int idx = threadIdx.x; idx < G * D4; idx += kThreads) {
+        const int g = idx / D4, i = (idx % D4) * 4;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm.m[w][g]);
+        const float ms = mx == -INFINITY ? 0.f : mx;
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+        float ls = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float sc = exp2_fast(sm.m[w][g] - ms);
+            const float4 x = *reinterpret_cast<const float4*>(&sm.acc[w][g][i]);
+            a.x += x.x * sc;
+            a.y += x.y * sc;
+            a.z += x.z * sc;
+            a.w += x.w * sc;
+            ls += sm.l[w][g] * sc;
+        }
+        st_sc1_16(rec, (g * D + i) * 4, a);
+        if (i == 0) st_sc1_16(scal, g * 16, make_float4(mx, ls, has_cand ? clg[g] : 0.f, 0.f));
+    }
+}
+
+// The published records of the blocks of a head, as read by its last block:
+// acc [nsplit][G][D], (max, sum, candidate logit, 0) [nsplit][G] and
+// candidate value rows [nsplit][D].
 struct MergeArgs {
-    __amdgpu_buffer_rsrc_t part, clg, cv;
-    int nsplit, G, nsb, r, c4;
+    __amdgpu_buffer_rsrc_t rec, scal, cv;
+    int G, nsb, r, c4;
     bool full;
     unsigned long long wkey;
     int chunk;
@@ -943,18 +915,22 @@ struct MergeArgs {
 // Folds the records of splits j = j0 + r + RS * jj (jj < JB, all j0) into the
 // thread's running (M, L, A) of its 4 output columns c4 for every head.  The
 // loads of a batch are all issued before any is used (one round trip to
-// memory per batch).  Every split's held-out candidate is added back except
-// the winner's (split js of the evicted slot).  Returns the evicted slot
-// (`e` when the cache is not full).
+// memory per batch); the (max, sum, logit) records of a batch are fetched
+// once, one per thread, and shared through s_sc.  Every split's held-out
+// candidate is added back except the winner's (split js of the evicted
+// slot).  Returns the evicted slot (`e` when the cache is not full).
 template <int D, int GM, int JB>
-__device__ __forceinline__ int merge_splits(const MergeArgs& a, int e, float (&Mt)[GM], float (&Lt)[GM],
-                                            float4 (&At)[GM])
+__device__ __forceinline__ int merge_splits(const MergeArgs& a, int e, float4* s_sc, float (&Mt)[GM],
+                                            float (&Lt)[GM], float4 (&At)[GM])
 {
     constexpr int RS = kThreads / (D / 4);
+    const int tid = threadIdx.x;
+    const int nsc = RS * JB * a.G;   // (split, head) records of a batch, <= kThreads
+    const int jl = tid / a.G, gl = tid - jl * a.G;
     int js = -1;
     for (int j0 = 0; j0 < a.nsb; j0 += RS * JB) {
+        const float4 scv = ld_sc1_16(a.scal, (min(j0 + jl, a.nsb - 1) * a.G + gl) * 16);
         float4 av[JB][GM], cv[JB];
-        float mj[JB][GM], lj[JB][GM], cl[JB][GM];
 #pragma unroll
         for (int jj = 0; jj < JB; ++jj) {
             const int j = min(j0 + a.r + RS * jj, a.nsb - 1);
@@ -962,18 +938,16 @@ __device__ __forceinline__ int merge_splits(const MergeArgs& a, int e, float (&M
 #pragma unroll
             for (int g = 0; g < GM; ++g) {
                 const int gg = min(g, a.G - 1);
-                const int rec = (gg * a.nsplit + j) * (D + 4);
-                av[jj][g] = ld_sc1_16(a.part, (rec + 4 * a.c4) * 4);
-                const float2 ml = ld_sc1_8(a.part, (rec + D) * 4);
-                mj[jj][g] = ml.x;
-                lj[jj][g] = ml.y;
-                cl[jj][g] = ld_sc1_4(a.clg, (j * a.G + gg) * 4);
+                av[jj][g] = ld_sc1_16(a.rec, ((j * a.G + gg) * D + 4 * a.c4) * 4);
             }
         }
         if (a.full) {
             e = cand_slot(a.wkey);
             js = e / a.chunk;
         }
+        __syncthreads();   // readers of the previous batch are done
+        if (tid < nsc) s_sc[tid] = scv;
+        __syncthreads();
 #pragma unroll
         for (int jj = 0; jj < JB; ++jj) {
             const int j = j0 + a.r + RS * jj;
@@ -981,8 +955,9 @@ __device__ __forceinline__ int merge_splits(const MergeArgs& a, int e, float (&M
                 const bool hold = a.full && j != js;
 #pragma unroll
                 for (int g = 0; g < GM; ++g) {
-                    if (lj[jj][g] > 0.f) lse_add4(Mt[g], Lt[g], At[g], mj[jj][g], lj[jj][g], av[jj][g]);
-                    if (hold) lse_add4(Mt[g], Lt[g], At[g], cl[jj][g], 1.f, cv[jj]);
+                    const float4 sc = s_sc[(a.r + RS * jj) * a.G + min(g, a.G - 1)];
+                    if (sc.y > 0.f) lse_add4(Mt[g], Lt[g], At[g], sc.x, sc.y, av[jj][g]);
+                    if (hold) lse_add4(Mt[g], Lt[g], At[g], sc.z, 1.f, cv[jj]);
                 }
             }
         }
@@ -990,11 +965,15 @@ __device__ __forceinline__ int merge_splits(const MergeArgs& a, int e, float (&M
     return e;
 }
 
+// Shared memory of the last block's merge: one (max, sum, 4 outputs) per
+// wave, head and 4-element column, and the (max, sum, logit) records of the
+// batch being folded.
 template <int D, int GM>
 struct MergeBlockSmem {
     float m[kWaves][GM];
     float l[kWaves][GM];
     float4 a[kWaves][GM][D / 4];
+    float4 sc[kThreads];
 };
 
 template <int D, int BITS, int GM>
@@ -1027,6 +1006,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     __shared__ uint32_t s_k16[BITS / 16];
     __shared__ unsigned long long s_red[kWaves];
     __shared__ float s_nlg[GM];
+    __shared__ float s_clg[GM];
     __shared__ int s_last;
     AttnSmem<D, GM>& sm = u.at;
 
@@ -1036,7 +1016,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     KT* Kh = reinterpret_cast<KT*>(c.K) + rowbase * D;
     KT* Vh = reinterpret_cast<KT*>(c.V) + rowbase * D;
     const CT* codeh = reinterpret_cast<const CT*>(c.code) + (size_t)head * c.code_slots;
-    const size_t crec = (size_t)head * c.cstride + split;
+    const size_t crec = (size_t)head * c.nsplit + split;
     const KT* kh = knew + (size_t)head * D;
     const KT* vh = vnew + (size_t)head * D;
 
@@ -1144,7 +1124,6 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
         attend_rows<D, GM, KT>(Kh, Vh, &s_q[0][0], G, s0, len, cand, first, sm);
 
     // publish this chunk: partial softmax, candidate logits and value row
-    publish_partial<D, GM>(sm, c.part, hq0, G, c.nsplit, split);
     if (cand >= 0) {
         const float qs = qscale2<D>();
         const int i0 = 2 * lane;
@@ -1152,14 +1131,13 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
             float dot = 0.f;
             if (i0 < D) dot = fmaf(s_q[g][i0] * qs, kc2.x, s_q[g][i0 + 1] * qs * kc2.y);
             dot = wave_sum_f(dot);
-            if (lane == 0) st_dev(c.cand_lg + crec * G + g, dot);
+            if (lane == 0) s_clg[g] = dot;
         }
-        if (wave == 0 && i0 < D) {
-            st_dev(c.cand_v + crec * D + i0, vc2.x);
-            st_dev(c.cand_v + crec * D + i0 + 1, vc2.y);
-        }
+        if (wave == 0 && i0 < D) st_sc1_8(dev_rsrc(c.cand_v + crec * D, (size_t)D * 4), i0 * 4, vc2);
     }
-    if (tid == 0) st_dev(c.cand_key + crec, ckey);
+    __syncthreads();
+    publish_fused<D, GM>(sm, dev_rsrc(c.frec + crec * G * D, (size_t)G * D * 4),
+                         dev_rsrc(c.fscal + crec * G * 4, (size_t)G * 16), G, s_clg, cand >= 0);
     own_stores_complete();
     __syncthreads();
     if (tid == 0) s_last = atomicAdd(&c.count[head], 1u) == (unsigned)(nsb - 1);
@@ -1184,18 +1162,18 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
         Lt[g] = 0.f;
         At[g] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    MergeArgs ma{dev_rsrc(c.part + (size_t)hq0 * c.nsplit * (D + 4), (size_t)G * c.nsplit * (D + 4) * 4),
-                 dev_rsrc(c.cand_lg + (size_t)head * c.cstride * G, (size_t)c.cstride * G * 4),
-                 dev_rsrc(c.cand_v + (size_t)head * c.cstride * D, (size_t)c.cstride * D * 4),
-                 c.nsplit, G, nsb, r, c4, full, wkey, c.chunk};
+    const size_t hrec = (size_t)head * c.nsplit;
+    MergeArgs ma{dev_rsrc(c.frec + hrec * G * D, (size_t)c.nsplit * G * D * 4),
+                 dev_rsrc(c.fscal + hrec * G * 4, (size_t)c.nsplit * G * 16),
+                 dev_rsrc(c.cand_v + hrec * D, (size_t)c.nsplit * D * 4), G, nsb, r, c4, full, wkey, c.chunk};
     const int per = (nsb + RS - 1) / RS;   // splits per thread
     int e = n;
     if (per <= 1 || JBMAX == 1)
-        e = merge_splits<D, GM, 1>(ma, e, Mt, Lt, At);
+        e = merge_splits<D, GM, 1>(ma, e, u.mg.sc, Mt, Lt, At);
     else if (per <= 2 || JBMAX == 2)
-        e = merge_splits<D, GM, (JBMAX >= 2 ? 2 : 1)>(ma, e, Mt, Lt, At);
+        e = merge_splits<D, GM, (JBMAX >= 2 ? 2 : 1)>(ma, e, u.mg.sc, Mt, Lt, At);
     else
-        e = merge_splits<D, GM, JBMAX>(ma, e, Mt, Lt, At);
+        e = merge_splits<D, GM, JBMAX>(ma, e, u.mg.sc, Mt, Lt, At);
     MergeBlockSmem<D, GM>& mg = u.mg;
     // lanes of a wave that share c4 (lane % TPR) combine, then one entry per wave
 #pragma unroll
