@@ -132,6 +132,38 @@ def cmd_traffic(args):
         json.dump(data, fh, indent=1, sort_keys=True)
         fh.write("\n")
     print(json.dumps(rec, indent=1))
+    if args.md:
+        write_traffic_md(args, rec)
+
+
+def write_traffic_md(args, rec):
+    """Markdown summary of one traffic record, with the commands that made it."""
+    d = os.path.dirname
+    runs = [("FETCH_SIZE", d(args.fetch), "bench"), ("WRITE_SIZE", d(args.write), "bench"),
+            ("FETCH_SIZE", d(args.copy_fetch), "copy"), ("WRITE_SIZE", d(args.copy_write), "copy")]
+    lines = [f"# HBM traffic of {args.kernel}, {args.key} (counter runs)", "", "Commands (each a run of its own):", ""]
+    for ctr, outdir, what in runs:
+        prog = (f"python -u bench.py {args.bench_args}" if what == "bench" else
+                f"python -u -m lsh_eviction_amd.profiling copy --mib {args.copy_mib} --reps 4")
+        lines.append(f"    rocprofv3 --pmc {ctr} --output-format csv -d {outdir} -o run -- {prog}")
+    lines.append(f"    python -m lsh_eviction_amd.profiling traffic --fetch {args.fetch} --write {args.write} \\")
+    lines.append(f"        --copy-fetch {args.copy_fetch} --copy-write {args.copy_write} --copy-mib {args.copy_mib} \\")
+    lines.append(f"        --kernel {args.kernel} --key {args.key} --out {args.out} --md {args.md}"
+                 + (f" --alg-bytes {args.alg_bytes}" if args.alg_bytes else ""))
+    lines += ["", f"Calibration: a {args.copy_mib} MiB device copy (`{rec['copy_kernel']}`) reads and writes "
+              f"{args.copy_mib} MiB per dispatch; its FETCH_SIZE reading gives {rec['copy_fetch_factor']} counter "
+              f"bytes per byte read and its WRITE_SIZE reading {rec['copy_write_factor']} per byte written.", "",
+              f"| per launch ({rec['dispatches'][0]} dispatches) | raw counter (KiB) | scaled bytes |", "|---|---:|---:|",
+              f"| read (FETCH_SIZE) | {rec['fetch_kib_raw']} | {rec['read_bytes']:,} |",
+              f"| write (WRITE_SIZE) | {rec['write_kib_raw']} | {rec['write_bytes']:,} |",
+              f"| **total** | | **{rec['bytes_per_launch']:,}** |"]
+    if args.alg_bytes:
+        lines += ["", f"Algorithmic bytes per launch: {args.alg_bytes:,}; measured traffic is "
+                  f"{rec['bytes_per_launch'] / args.alg_bytes:.3f}x that."]
+    lines += ["", f"Kernel source hash when measured: `{rec['kernel_hash']}` (bench.py reports this traffic only "
+              "while the source still has that hash)."]
+    with open(args.md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
 
 
 def main(argv=None):
@@ -149,6 +181,9 @@ def main(argv=None):
     for k in ("fetch", "write", "copy_fetch", "copy_write", "kernel", "key", "out"):
         a.add_argument("--" + k.replace("_", "-"), required=True, dest=k)
     a.add_argument("--copy-mib", type=int, default=1024)
+    a.add_argument("--md", default="")
+    a.add_argument("--alg-bytes", type=int, default=0)
+    a.add_argument("--bench-args", default="--steps 20 --warmup 2 --no-cpu")
     args = ap.parse_args(argv)
     {"copy": cmd_copy, "stats": cmd_stats, "traffic": cmd_traffic}[args.mode](args)
 
