@@ -24,6 +24,7 @@ SOURCES = [os.path.join(_HERE, "hkv_oracle.c")]
 
 STREAM = 0
 TRUNCATE = 1
+QUERY = 2
 
 
 def build(verbose: bool = False) -> str:
@@ -54,6 +55,8 @@ def lib():
         L.orc_encode_many.argtypes = [P, C.c_int, P, P, P]
         L.orc_prefill.restype = C.c_int
         L.orc_prefill.argtypes = [P, C.c_int, C.c_int, P, P, P]
+        L.orc_prefill_query.argtypes = [P, C.c_int, P, P, P, P, P]
+        L.orc_prefill_query.restype = C.c_int
         L.orc_decode_step.restype = C.c_int
         L.orc_decode_step.argtypes = [P] * 3 + [P] * 8 + [P]
         L.orc_scores.argtypes = [P, P, P]
@@ -131,6 +134,21 @@ class OracleHead:
         if rc != 0:
             raise RuntimeError("orc_prefill failed (cache not empty?)")
 
+    def prefill_query(self, K: np.ndarray, V: np.ndarray, Q: np.ndarray,
+                      inj_codes: Optional[np.ndarray] = None, inj_qcodes: Optional[np.ndarray] = None):
+        """QUERY rule: Q[n][group][d] are the query rows of each prompt token."""
+        K, V, Q = _f64(K), _f64(V), _f64(Q)
+        n = K.shape[0]
+        assert Q.shape == (n, self.group, self.d)
+        inj, injq = _u32(inj_codes), _u32(inj_qcodes)
+        if inj is not None:
+            assert inj.shape == (n, self.W)
+        if injq is not None:
+            assert injq.shape == (n, self.group, self.W)
+        rc = lib().orc_prefill_query(self._h, n, _p(K), _p(V), _p(Q), _p(inj), _p(injq))
+        if rc != 0:
+            raise RuntimeError("orc_prefill_query failed (cache not empty?)")
+
     def decode_step(self, q, k, v, inj_qcodes=None, inj_kcode=None):
         q, k, v = _f64(q).reshape(self.group, self.d), _f64(k), _f64(v)
         out = np.zeros((self.group, self.d), np.float64)
@@ -187,11 +205,20 @@ class OracleCache:
         self.sel = heads if heads is not None else [(b, h) for b in range(self.B) for h in range(self.Hkv)]
         self.heads = {(b, h): OracleHead(R, int(budgets[b]), self.G) for (b, h) in self.sel}
 
-    def prefill(self, K, V, prompt_lens, policy=STREAM, inj_codes=None):
+    def prefill(self, K, V, prompt_lens, policy=STREAM, inj_codes=None, Q=None, inj_qcodes=None):
+        """K, V [B][Hkv][n_max][d]; with policy QUERY also Q [B][Hq][n_max][d] (fp32) and
+        optionally inj_qcodes [B][Hq][n_max][W]."""
+        G = self.G
         for (b, h), o in self.heads.items():
             n = int(prompt_lens[b])
             inj = None if inj_codes is None else inj_codes[b, h, :n]
-            o.prefill(widen(K[b, h, :n]), widen(V[b, h, :n]), policy, inj)
+            if policy == QUERY:
+                q = widen(Q[b, h * G:(h + 1) * G, :n]).transpose(1, 0, 2)
+                iq = None if inj_qcodes is None else np.ascontiguousarray(
+                    inj_qcodes[b, h * G:(h + 1) * G, :n].transpose(1, 0, 2))
+                o.prefill_query(widen(K[b, h, :n]), widen(V[b, h, :n]), q, inj, iq)
+            else:
+                o.prefill(widen(K[b, h, :n]), widen(V[b, h, :n]), policy, inj)
 
     def decode_step(self, q, k, v, inj_qcodes=None, inj_kcodes=None):
         """q [B][Hq][d] fp32; k, v [B][Hkv][d]; returns per-head dicts keyed (b, h)."""

@@ -179,6 +179,56 @@ int orc_prefill(orc_head* h, int policy, int n, const double* K, const double* V
     return 0;
 }
 
+/* Query-driven prefill (READING: the pages do not describe prefill).  Every
+ * prompt token past the budget is placed by the decode rule itself: its
+ * group's query rows Q[t][g] are hashed (stages 1-2), the occupied slot with
+ * the largest summed Hamming distance to them is evicted (stages 3-4, ties to
+ * the lowest slot) and the token's key, value and key code take it (stage 5).
+ * Tokens before the budget fill slots 0, 1, ... in order.
+ * Q: [n][group][d]; inj_codes [n][W] replace E(K[t]); inj_qcodes
+ * [n][group][W] replace E(Q[t][g]).  Returns 0, or -1 if the cache is not
+ * empty or n < 0. */
+int orc_prefill_query(orc_head* h, int n, const double* K, const double* V, const double* Q,
+                      const uint32_t* inj_codes, const uint32_t* inj_qcodes)
+{
+    if (h->n != 0 || n < 0) return -1;
+    uint32_t* c = (uint32_t*)malloc(sizeof(uint32_t) * h->words);
+    uint32_t* f = (uint32_t*)malloc(sizeof(uint32_t) * h->words);
+    uint32_t* qc = (uint32_t*)malloc(sizeof(uint32_t) * h->words * h->group);
+    uint32_t* qf = (uint32_t*)malloc(sizeof(uint32_t) * h->words);
+    for (int t = 0; t < n; ++t) {
+        const double* kt = K + (size_t)t * h->d;
+        const uint32_t* ct;
+        if (inj_codes) {
+            ct = inj_codes + (size_t)t * h->words;
+        } else {
+            orc_encode(h, kt, c, f);
+            ct = c;
+        }
+        int e;
+        if (h->n < h->budget) {
+            e = h->n++;
+        } else {
+            const uint32_t* qcodes;
+            if (inj_qcodes) {
+                qcodes = inj_qcodes + (size_t)t * h->group * h->words;
+            } else {
+                for (int g = 0; g < h->group; ++g)
+                    orc_encode(h, Q + ((size_t)t * h->group + g) * h->d, qc + (size_t)g * h->words, qf);
+                qcodes = qc;
+            }
+            e = pick_victim(h, qcodes, h->group);
+        }
+        write_slot(h, e, kt, V + (size_t)t * h->d, ct, (int64_t)t);
+    }
+    free(c);
+    free(f);
+    free(qc);
+    free(qf);
+    h->t = n;
+    return 0;
+}
+
 /* Attention over the occupied slots: softmax(q . K^T / sqrt(d)) V, with the
  * maximum logit subtracted before exponentiation. */
 void orc_attend(const orc_head* h, const double* q, double* out)

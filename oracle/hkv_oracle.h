@@ -34,7 +34,7 @@ extern "C" {
 
 typedef struct orc_head orc_head;
 
-enum { ORC_PREFILL_STREAM = 0, ORC_PREFILL_TRUNCATE = 1 };
+enum { ORC_PREFILL_STREAM = 0, ORC_PREFILL_TRUNCATE = 1, ORC_PREFILL_QUERY = 2 };
 
 /* R: [d][n_bits] fp32 values widened to double; copied. NULL on bad args. */
 orc_head* orc_create(int d, int n_bits, int budget, int group, const double* R);
@@ -51,6 +51,13 @@ void orc_encode_many(const orc_head* h, int n, const double* X, uint32_t* codes,
  * Returns 0 on success, -1 if the cache is not empty or n < 0. */
 int orc_prefill(orc_head* h, int policy, int n, const double* K, const double* V,
                 const uint32_t* inj_codes);
+
+/* P with the QUERY rule: tokens past the budget evict by the decode rule,
+ * scored against their own group's query rows.  Q: [n][group][d];
+ * inj_codes [n][W] and inj_qcodes [n][group][W] (may be NULL) replace the
+ * key and query codes.  Returns 0, or -1 if the cache is not empty or n < 0. */
+int orc_prefill_query(orc_head* h, int n, const double* K, const double* V, const double* Q,
+                      const uint32_t* inj_codes, const uint32_t* inj_qcodes);
 
 /* D + A: one decode step.  q: [group][d], k, v: [d].
  * inj_qcodes [group][W] / inj_kcode [W] (may be NULL) replace E's output.

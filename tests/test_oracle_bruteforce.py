@@ -38,11 +38,13 @@ class Brute:
                          "bits": bits}
         return e
 
-    def prefill(self, K, V, truncate=False):
+    def prefill(self, K, V, truncate=False, Q=None):
         for t in range(len(K)):
             self.t = t
             b = self.bits(K[t])
-            if truncate:
+            if Q is not None:
+                self._place([self.bits(qg) for qg in Q[t]], K[t], V[t], b)
+            elif truncate:
                 if len(self.slots) < self.S:
                     self.slots.append({"tok": t, "k": K[t].copy(), "v": V[t].copy(), "bits": b})
             else:
@@ -113,3 +115,46 @@ def test_constructed_ties(oracle_mod):
     q = key[None, :]                       # code of key: slot 2 differs in every bit
     r = o.decode_step(q, key, np.zeros(d))
     assert r["evicted"] == 2
+
+
+@pytest.mark.parametrize("d,b,S,N,G,seed", [
+    (8, 16, 4, 12, 1, 21),
+    (8, 16, 5, 24, 2, 22),
+    (16, 32, 6, 30, 4, 23),
+    (8, 64, 5, 20, 3, 24),
+    (8, 16, 6, 4, 2, 25),       # prompt shorter than the budget
+])
+def test_bruteforce_query_prefill(oracle_mod, d, b, S, N, G, seed):
+    """The QUERY prefill rule against the brute-force model, then decode."""
+    rng = np.random.default_rng(seed)
+    R = rng.standard_normal((d, b)).astype(np.float32).astype(np.float64)
+    K = rng.standard_normal((N, d)); V = rng.standard_normal((N, d))
+    Q = rng.standard_normal((N, G, d))
+    o = oracle_mod.OracleHead(R, S, G)
+    bf = Brute(R, S, G)
+    o.prefill_query(K, V, Q)
+    bf.prefill(K, V, Q=Q)
+    assert list(o.state()["tok"]) == bf.toks()
+    for _ in range(6):
+        q = rng.standard_normal((G, d)); k = rng.standard_normal(d); v = rng.standard_normal(d)
+        r = o.decode_step(q, k, v)
+        e, out = bf.step(q, k, v)
+        assert r["evicted"] == e
+        np.testing.assert_allclose(r["out"], out, rtol=1e-12, atol=1e-12)
+
+
+def test_query_prefill_reduces_to_stream(oracle_mod):
+    """With one query head per KV head and each token's query equal to its
+    key, the QUERY rule scores exactly what STREAM scores: same cache."""
+    rng = np.random.default_rng(31)
+    d, b, S, N = 32, 32, 16, 80
+    R = rng.standard_normal((d, b))
+    K = rng.standard_normal((N, d)); V = rng.standard_normal((N, d))
+    a = oracle_mod.OracleHead(R, S, 1)
+    q = oracle_mod.OracleHead(R, S, 1)
+    a.prefill(K, V, oracle_mod.STREAM)
+    q.prefill_query(K, V, K[:, None, :])
+    sa, sq = a.state(), q.state()
+    assert list(sa["tok"]) == list(sq["tok"])
+    np.testing.assert_array_equal(sa["code"], sq["code"])
+    np.testing.assert_array_equal(sa["K"], sq["K"])

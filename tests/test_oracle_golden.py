@@ -25,6 +25,8 @@ def _cases():
                    "policy": kv["policy"], "decode": []}
         elif tok[0] == "prompt":
             cur["prompt"] = [int(x, 16) for x in tok[1:]]
+        elif tok[0] == "pquery":
+            cur["pquery"] = [[int(x, 16) for x in t.split(",")] for t in tok[1:]]
         elif tok[0] == "prefill_tok":
             cur["prefill_tok"] = [int(x) for x in tok[1:]]
         elif tok[0] == "decode":
@@ -44,8 +46,12 @@ def test_handworked(oracle_mod, case):
     o = oracle_mod.OracleHead(R, case["budget"], case["group"])
     K = np.stack([_vec(c) for c in case["prompt"]])
     V = np.arange(K.size, dtype=np.float64).reshape(K.shape)
-    pol = oracle_mod.STREAM if case["policy"] == "stream" else oracle_mod.TRUNCATE
-    o.prefill(K, V, pol)
+    if case["policy"] == "query":
+        Q = np.stack([np.stack([_vec(c) for c in row]) for row in case["pquery"]])
+        o.prefill_query(K, V, Q)
+    else:
+        pol = oracle_mod.STREAM if case["policy"] == "stream" else oracle_mod.TRUNCATE
+        o.prefill(K, V, pol)
     st = o.state()
     assert list(st["tok"]) == case["prefill_tok"]
     # codes of the prompt are the sign patterns (bit order pin on the way)
