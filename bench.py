@@ -138,6 +138,8 @@ def main():
     ap.add_argument("--config", default=DEFAULT_WORKLOAD)
     ap.add_argument("--schedule", default="fused", choices=["fused", "split"])
     ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--prefill", default="stream", choices=["stream", "truncate", "query"],
+                    help="prefill rule of the layer caches (timed per layer, not part of a step)")
     ap.add_argument("--layers", type=int, default=0, help="layer caches rotated (0 = enough to exceed the MALL twice)")
     ap.add_argument("--graph", action="store_true", help="replay the steps of one rotation as a HIP graph")
     ap.add_argument("--no-cpu", action="store_true")
@@ -166,17 +168,24 @@ def main():
 
     caches, prefill_ms = [], []
     for layer in range(L):
+        pol = {"stream": hkv.HKV_PREFILL_STREAM, "truncate": hkv.HKV_PREFILL_TRUNCATE,
+               "query": hkv.HKV_PREFILL_QUERY}[args.prefill]
         c = hkv.Cache(shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.n_bits, kvd,
-                      budgets, P.R, decode_schedule=sched, max_prompt=n_max, chunk=args.chunk)
+                      budgets, P.R, prefill_policy=pol, decode_schedule=sched, max_prompt=n_max, chunk=args.chunk)
         K, V = make_layer_inputs(shape, P, layer, shape.index)
+        Q = None
+        if args.prefill == "query":
+            gq = torch.Generator(device="cuda")
+            gq.manual_seed(shape.index * 1000 + 500 + layer)
+            Q = torch.randn((shape.batch, shape.n_q_heads, n_max, shape.head_dim), generator=gq, device="cuda")
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        c.prefill(K, V, n)
+        c.prefill(K, V, n, Q=Q)
         e1.record()
         torch.cuda.synchronize()
         prefill_ms.append(e0.elapsed_time(e1))
-        del K, V
+        del K, V, Q
         caches.append(c)
     torch.cuda.empty_cache()
 
@@ -294,6 +303,7 @@ def main():
         "copy_gbs": round(copy_gbs, 1),
         "frac_of_copy": round(achieved / copy_gbs, 4),
         "prefill_ms_per_layer": round(float(np.mean(prefill_ms)), 2),
+        "prefill_rule": args.prefill,
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu:

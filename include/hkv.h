@@ -29,7 +29,10 @@
  *     cache after the write, with logits q.k / sqrt(d), no mask, no rotary;
  *   - prefill (HKV_PREFILL_STREAM, default): the prompt tokens enter one at a
  *     time by the decode rule, each scored against its own key code (prefill
- *     has no query); HKV_PREFILL_TRUNCATE keeps the first `budget` tokens.
+ *     has no query); HKV_PREFILL_TRUNCATE keeps the first `budget` tokens;
+ *     HKV_PREFILL_QUERY applies the decode rule itself to every prompt token
+ *     past the budget, scored against the token's own group of query rows
+ *     (the caller passes the prompt's queries to hkv_prefill_queries).
  *
  * Conventions for every call:
  *   - all device pointers are HIP device memory of the current device; `stream`
@@ -47,8 +50,9 @@
  *   - supported: n_bits in {16, 32, 64}; head_dim in {64, 128};
  *     n_q_heads % n_kv_heads == 0 with G = n_q_heads / n_kv_heads <= 16;
  *     kv dtype fp32 or bf16; 1 <= budget <= 2^22 per sequence (a prefill
- *     with HKV_PREFILL_STREAM needs budget * ceil(b/8) <= 128 KiB, its code
- *     table lives in on-chip LDS); 1 <= batch <= 4096.
+ *     with HKV_PREFILL_STREAM or HKV_PREFILL_QUERY needs
+ *     budget * ceil(b/8) <= 128 KiB, its code table lives in on-chip LDS);
+ *     1 <= batch <= 4096.
  */
 #ifndef HKV_H
 #define HKV_H
@@ -69,7 +73,7 @@ typedef enum {
 } hkv_status;
 
 enum { HKV_F32 = 0, HKV_BF16 = 1 };                        /* kv_dtype */
-enum { HKV_PREFILL_STREAM = 0, HKV_PREFILL_TRUNCATE = 1 };  /* prefill_policy */
+enum { HKV_PREFILL_STREAM = 0, HKV_PREFILL_TRUNCATE = 1, HKV_PREFILL_QUERY = 2 };  /* prefill_policy */
 /* decode_schedule: FUSED = one launch per step (score, hold-out attention,
  * merge, write); SPLIT = the separate kernels lsh_encode, hamming_argmax,
  * evict_write, split-K attention and LSE merge (five launches). */
@@ -114,9 +118,21 @@ hkv_status hkv_create(const hkv_config* cfg, const float* R_host, void* workspac
  * 0 <= prompt_lens[b] <= n_max <= cfg.max_prompt.  Builds the b-bit code of
  * every prompt key (method stages 1-2; an MFMA projection), applies the
  * prefill policy, and leaves occupancy min(N_b, S_b) and next position N_b.
- * HKV_ERR_STATE if the cache is not empty. */
+ * HKV_ERR_STATE if the cache is not empty; HKV_ERR_INVALID_ARG under
+ * HKV_PREFILL_QUERY, which needs the queries (hkv_prefill_queries). */
 hkv_status hkv_prefill(hkv_cache* c, const void* K, const void* V, const int32_t* prompt_lens,
                        int32_t n_max, void* stream);
+
+/* Prefill under HKV_PREFILL_QUERY (a cache created with that policy; any
+ * other policy gives HKV_ERR_INVALID_ARG).  K, V, prompt_lens, n_max as in
+ * hkv_prefill; Q: device fp32 [B][Hq][n_max][d], the query rows of the prompt
+ * tokens (16-byte aligned).  Tokens t < S_b take slots 0, 1, ...; every later
+ * token t is placed by the decode rule (method stages 1-5): the codes of its
+ * G query rows Q[b][h*G + g][t] are projected and sign-packed, the occupied
+ * slot with the largest summed Hamming distance to them (ties to the lowest
+ * slot) is evicted and token t's key, value and key code take it. */
+hkv_status hkv_prefill_queries(hkv_cache* c, const void* K, const void* V, const float* Q,
+                               const int32_t* prompt_lens, int32_t n_max, void* stream);
 
 /* One decode step for every sequence (method stages 1-5, then attention).
  * q: device fp32 [B][Hq][d]; k, v: device kv dtype [B][Hkv][d], the new token;
@@ -155,6 +171,11 @@ hkv_status hkv_debug_last_codes(const hkv_cache* c, uint32_t* qcodes, uint32_t* 
  * codes [B][Hkv][n_max][W] (uint32 device buffer; rows t >= prompt_lens[b] are
  * unspecified). */
 hkv_status hkv_debug_prefill_codes(const hkv_cache* c, uint32_t* codes, void* stream);
+/* Codes the last QUERY prefill computed for every prompt query row:
+ * codes [B][Hq][n_max][W] (uint32 device buffer; rows t >= prompt_lens[b] are
+ * unspecified).  HKV_ERR_STATE unless the last prefill ran with
+ * HKV_PREFILL_QUERY. */
+hkv_status hkv_debug_prefill_query_codes(const hkv_cache* c, uint32_t* codes, void* stream);
 /* GQA Hamming score of every slot against the given query codes
  * qcodes [B][Hq][W] (device): scores [B][Hkv][Smax] int32 (device), -1 for
  * slots at or beyond the occupancy. */

@@ -20,6 +20,7 @@ struct hkv_cache {
     int device = 0;
     int last_n_max = 0;
     bool prefilled = false;
+    bool last_query_prefill = false;
     bool stepped = false;
     bool poisoned = false;
     bool debug_sync = false;
@@ -109,6 +110,7 @@ extern "C" hkv_status hkv_create(const hkv_config* cfg, const float* R_host, voi
     d.info = (int*)(ws + L.off_info);
     d.count = (unsigned*)(ws + L.off_count);
     d.pcode = ws + L.off_pcode;
+    d.qcode = ws + L.off_qcode;
     d.B = L.B; d.Hq = L.Hq; d.Hkv = L.Hkv; d.G = L.G; d.d = L.d; d.bits = L.bits; d.W = L.W;
     d.Smax = L.Smax; d.chunk = L.chunk; d.nsplit = L.nsplit;
     d.kv_bf16 = L.kv_dtype == HKV_BF16;
@@ -138,35 +140,60 @@ extern "C" hkv_status hkv_destroy(hkv_cache* c)
     return HKV_OK;
 }
 
-extern "C" hkv_status hkv_prefill(hkv_cache* c, const void* K, const void* V, const int32_t* prompt_lens,
-                                  int32_t n_max, void* stream)
+// Checks shared by the two prefill calls, then the prompt lengths go to the
+// device and the kernels are enqueued.
+static hkv_status prefill_impl(hkv_cache* c, const void* K, const void* V, const float* Q,
+                               const int32_t* prompt_lens, int32_t n_max, void* stream, const char* fn)
 {
-    hkv_status s = usable(c);
-    if (s != HKV_OK) return s;
-    if (c->prefilled) return fail(c, HKV_ERR_STATE, "hkv_prefill: cache is not empty");
-    if (!prompt_lens) return fail(c, HKV_ERR_INVALID_ARG, "hkv_prefill: prompt_lens is NULL");
+    const std::string f(fn);
+    if (c->prefilled) return fail(c, HKV_ERR_STATE, f + ": cache is not empty");
+    if (!prompt_lens) return fail(c, HKV_ERR_INVALID_ARG, f + ": prompt_lens is NULL");
     if (n_max < 0 || n_max > c->lay.max_prompt)
         return fail(c, HKV_ERR_INVALID_ARG,
-                    "hkv_prefill: n_max " + std::to_string(n_max) + " outside [0, max_prompt = " +
+                    f + ": n_max " + std::to_string(n_max) + " outside [0, max_prompt = " +
                         std::to_string(c->lay.max_prompt) + "]");
     for (int b = 0; b < c->lay.B; ++b)
         if (prompt_lens[b] < 0 || prompt_lens[b] > n_max)
             return fail(c, HKV_ERR_INVALID_ARG,
-                        "hkv_prefill: prompt_lens[" + std::to_string(b) + "] outside [0, n_max]");
-    if (n_max > 0 && (!K || !V)) return fail(c, HKV_ERR_INVALID_ARG, "hkv_prefill: K or V is NULL");
+                        f + ": prompt_lens[" + std::to_string(b) + "] outside [0, n_max]");
+    if (n_max > 0 && (!K || !V)) return fail(c, HKV_ERR_INVALID_ARG, f + ": K or V is NULL");
     if (n_max > 0 && (!aligned(K, 16) || !aligned(V, 16)))
-        return fail(c, HKV_ERR_INVALID_ARG, "hkv_prefill: K and V must be 16-byte aligned");
+        return fail(c, HKV_ERR_INVALID_ARG, f + ": K and V must be 16-byte aligned");
+    const bool query = c->lay.prefill_policy == HKV_PREFILL_QUERY;
+    if (query && n_max > 0 && (!Q || !aligned(Q, 16)))
+        return fail(c, HKV_ERR_INVALID_ARG, f + ": Q is NULL or not 16-byte aligned");
     hipStream_t st = (hipStream_t)stream;
     c->plens.assign(prompt_lens, prompt_lens + c->lay.B);
     hipError_t e = hipMemcpyAsync((void*)c->dev.plen, c->plens.data(), (size_t)c->lay.B * sizeof(int32_t),
                                   hipMemcpyHostToDevice, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);   // plens is host memory of the handle
-    if (e == hipSuccess) e = hkv::launch_prefill(c->dev, K, V, n_max, c->lay.prefill_policy, st);
-    s = check_launch(c, e, st, "hkv_prefill");
+    if (e == hipSuccess) e = hkv::launch_prefill(c->dev, K, V, Q, n_max, c->lay.prefill_policy, st);
+    hkv_status s = check_launch(c, e, st, fn);
     if (s != HKV_OK) return s;
     c->last_n_max = n_max;
+    c->last_query_prefill = query;
     c->prefilled = true;
     return HKV_OK;
+}
+
+extern "C" hkv_status hkv_prefill(hkv_cache* c, const void* K, const void* V, const int32_t* prompt_lens,
+                                  int32_t n_max, void* stream)
+{
+    hkv_status s = usable(c);
+    if (s != HKV_OK) return s;
+    if (c->lay.prefill_policy == HKV_PREFILL_QUERY)
+        return fail(c, HKV_ERR_INVALID_ARG, "hkv_prefill: this cache uses HKV_PREFILL_QUERY; call hkv_prefill_queries");
+    return prefill_impl(c, K, V, nullptr, prompt_lens, n_max, stream, "hkv_prefill");
+}
+
+extern "C" hkv_status hkv_prefill_queries(hkv_cache* c, const void* K, const void* V, const float* Q,
+                                          const int32_t* prompt_lens, int32_t n_max, void* stream)
+{
+    hkv_status s = usable(c);
+    if (s != HKV_OK) return s;
+    if (c->lay.prefill_policy != HKV_PREFILL_QUERY)
+        return fail(c, HKV_ERR_INVALID_ARG, "hkv_prefill_queries: this cache was not created with HKV_PREFILL_QUERY");
+    return prefill_impl(c, K, V, Q, prompt_lens, n_max, stream, "hkv_prefill_queries");
 }
 
 extern "C" hkv_status hkv_decode_step(hkv_cache* c, const float* q, const void* k, const void* v,
@@ -227,7 +254,10 @@ extern "C" hkv_status hkv_set_state(hkv_cache* c, const void* K, const void* V, 
     if (e == hipSuccess) e = hipMemcpyAsync(c->dev.state, head_state, heads * 8, hipMemcpyDeviceToDevice, st);
     if (e == hipSuccess) e = hkv::launch_clear_step_scratch(c->dev, st);
     s = check_launch(c, e, st, "hkv_set_state");
-    if (s == HKV_OK) c->prefilled = true;
+    if (s == HKV_OK) {
+        c->prefilled = true;
+        c->last_query_prefill = false;
+    }
     return s;
 }
 
@@ -254,8 +284,21 @@ extern "C" hkv_status hkv_debug_prefill_codes(const hkv_cache* cc, uint32_t* cod
     if (!c->prefilled) return fail(c, HKV_ERR_STATE, "hkv_debug_prefill_codes: no prefill yet");
     if (!codes) return fail(c, HKV_ERR_INVALID_ARG, "hkv_debug_prefill_codes: codes is NULL");
     hipStream_t st = (hipStream_t)stream;
-    return check_launch(c, hkv::launch_export_pcodes(c->dev, codes, c->last_n_max, st), st,
+    return check_launch(c, hkv::launch_export_pcodes(c->dev, codes, c->last_n_max, false, st), st,
                         "hkv_debug_prefill_codes");
+}
+
+extern "C" hkv_status hkv_debug_prefill_query_codes(const hkv_cache* cc, uint32_t* codes, void* stream)
+{
+    hkv_cache* c = const_cast<hkv_cache*>(cc);
+    hkv_status s = usable(c);
+    if (s != HKV_OK) return s;
+    if (!c->prefilled || !c->last_query_prefill)
+        return fail(c, HKV_ERR_STATE, "hkv_debug_prefill_query_codes: no QUERY prefill yet");
+    if (!codes) return fail(c, HKV_ERR_INVALID_ARG, "hkv_debug_prefill_query_codes: codes is NULL");
+    hipStream_t st = (hipStream_t)stream;
+    return check_launch(c, hkv::launch_export_pcodes(c->dev, codes, c->last_n_max, true, st), st,
+                        "hkv_debug_prefill_query_codes");
 }
 
 extern "C" hkv_status hkv_debug_scores(const hkv_cache* cc, const uint32_t* qcodes, int32_t* scores, void* stream)

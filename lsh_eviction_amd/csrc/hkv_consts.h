@@ -3,4 +3,5 @@
 
 namespace hkv {
 constexpr int kScoreChunk = 4096;   // slots per block of the stand-alone hamming_argmax
+constexpr int kMaxGroup = 16;       // query heads per KV head
 }  // namespace hkv

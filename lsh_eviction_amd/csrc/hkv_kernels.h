@@ -28,6 +28,7 @@ struct DevCache {
     int* info;                      // [B][Hkv][2] occupancy and position at the start of the step
     unsigned* count;                // [B][Hkv] blocks of the current step that have published
     void* pcode;                    // [B][Hkv][pcode_slots] prompt key codes
+    void* qcode;                    // [B][Hq][pcode_slots] prompt query codes (QUERY prefill)
     int B, Hq, Hkv, G, d, bits, W, Smax, chunk, nsplit;
     int kv_bf16;
     long long code_slots, pcode_slots;
@@ -45,12 +46,12 @@ hipError_t launch_encode_rows(const DevCache& c, const void* X, int x_bf16, int 
 
 // prefill
 hipError_t launch_reset(const DevCache& c, hipStream_t st);
-hipError_t launch_prefill(const DevCache& c, const void* K, const void* V, int n_max, int policy,
+hipError_t launch_prefill(const DevCache& c, const void* K, const void* V, const float* Q, int n_max, int policy,
                           hipStream_t st);
 // checkpoint
 hipError_t launch_export_codes(const DevCache& c, uint32_t* codes, hipStream_t st);
 hipError_t launch_import_codes(const DevCache& c, const uint32_t* codes, hipStream_t st);
-hipError_t launch_export_pcodes(const DevCache& c, uint32_t* codes, int n_max, hipStream_t st);
+hipError_t launch_export_pcodes(const DevCache& c, uint32_t* codes, int n_max, bool queries, hipStream_t st);
 // clears the per-step scratch (eviction keys) after a state import
 hipError_t launch_clear_step_scratch(const DevCache& c, hipStream_t st);
 

@@ -11,7 +11,6 @@
 
 namespace hkv {
 
-constexpr int kMaxGroup = 16;
 constexpr int kMaxBudget = 1 << 22;
 constexpr int kMaxBatch = 4096;
 constexpr size_t kLdsTableBytes = 128 * 1024;   // prefill code table in LDS
@@ -27,7 +26,7 @@ struct Layout {
     // byte offsets into the workspace
     size_t off_R, off_budget, off_plen, off_state, off_K, off_V, off_code, off_tok;
     size_t off_dbg_q, off_dbg_k, off_part, off_frec, off_fscal, off_cand_v, off_ekey;
-    size_t off_info, off_count, off_pcode;
+    size_t off_info, off_count, off_pcode, off_qcode;
     size_t total;
 };
 

@@ -32,7 +32,8 @@ hkv_status compute_layout(const hkv_config* cfg, Layout* L, char* err, size_t er
         FAIL(HKV_ERR_UNSUPPORTED, "n_bits %d not in {16, 32, 64}", cfg->n_bits);
     if (cfg->kv_dtype != HKV_F32 && cfg->kv_dtype != HKV_BF16)
         FAIL(HKV_ERR_UNSUPPORTED, "kv_dtype %d unknown", cfg->kv_dtype);
-    if (cfg->prefill_policy != HKV_PREFILL_STREAM && cfg->prefill_policy != HKV_PREFILL_TRUNCATE)
+    if (cfg->prefill_policy != HKV_PREFILL_STREAM && cfg->prefill_policy != HKV_PREFILL_TRUNCATE &&
+        cfg->prefill_policy != HKV_PREFILL_QUERY)
         FAIL(HKV_ERR_UNSUPPORTED, "prefill_policy %d unknown", cfg->prefill_policy);
     if (cfg->decode_schedule != HKV_DECODE_FUSED && cfg->decode_schedule != HKV_DECODE_SPLIT)
         FAIL(HKV_ERR_UNSUPPORTED, "decode_schedule %d unknown", cfg->decode_schedule);
@@ -47,10 +48,10 @@ hkv_status compute_layout(const hkv_config* cfg, Layout* L, char* err, size_t er
         const int s = cfg->budgets[b];
         if (s < 1 || s > kMaxBudget)
             FAIL(HKV_ERR_UNSUPPORTED, "budget[%d] = %d outside [1, %d]", b, s, kMaxBudget);
-        if (cfg->prefill_policy == HKV_PREFILL_STREAM && (size_t)s * cb > kLdsTableBytes)
+        if (cfg->prefill_policy != HKV_PREFILL_TRUNCATE && (size_t)s * cb > kLdsTableBytes)
             FAIL(HKV_ERR_UNSUPPORTED,
                  "budget[%d] = %d: its %d-byte code table exceeds the %zu-byte on-chip table of "
-                 "the STREAM prefill", b, s, s * cb, kLdsTableBytes);
+                 "the sequential prefill", b, s, s * cb, kLdsTableBytes);
         if (s > Smax) Smax = s;
     }
 
@@ -93,6 +94,7 @@ hkv_status compute_layout(const hkv_config* cfg, Layout* L, char* err, size_t er
     l.off_info = take(heads * 2 * 4);
     l.off_count = take(heads * 4);
     l.off_pcode = take(heads * l.pcode_slots * cb);
+    l.off_qcode = take(cfg->prefill_policy == HKV_PREFILL_QUERY ? (size_t)l.B * l.Hq * l.pcode_slots * cb : 0);
     l.total = off;
     return HKV_OK;
 #undef FAIL

@@ -14,6 +14,7 @@
 #include <type_traits>
 
 #include "hkv.h"
+#include "hkv_consts.h"
 #include "hkv_device.h"
 
 namespace hkv {
@@ -54,19 +55,22 @@ __global__ void k_reset(DevCache c)
     }
 }
 
-// Codes of prompt keys [64 * blockIdx.x, +64) of one head on the matrix
-// cores.  Wave w takes 16 keys; lane l feeds key row (l % 16) and the quarter
-// (l / 16) of the head dimension, so MFMA step s contracts dimension
-// (l / 16) * D/4 + s.  The 16 x 16 result tile of bit columns nt*16 .. +15 is
-// sign-packed by a wave ballot per accumulator register.
+// Codes of prompt rows [64 * blockIdx.x, +64) of one head on the matrix
+// cores: X is [B][nh][n_max][D] (prompt keys with nh = Hkv, prompt queries
+// with nh = Hq), codes go to dst[(b * nh + h) * pcode_slots + t].  Wave w
+// takes 16 rows; lane l feeds row (l % 16) and the quarter (l / 16) of the
+// head dimension, so MFMA step s contracts dimension (l / 16) * D/4 + s.  The
+// 16 x 16 result tile of bit columns nt*16 .. +15 is sign-packed by a wave
+// ballot per accumulator register.
 template <int D, int BITS, typename KT>
-__global__ __launch_bounds__(256) void k_project_mfma(DevCache c, const KT* __restrict__ Kp, int n_max)
+__global__ __launch_bounds__(256) void k_project_mfma(DevCache c, const KT* __restrict__ Kp, int n_max, int nh,
+                                                      void* __restrict__ dst)
 {
     using CT = typename CodeT<BITS>::T;
     constexpr int DQ = D / 4;          // dimensions fed by one lane
     constexpr int NT = BITS / 16;      // bit tiles
     __shared__ float sR[D * BITS];
-    const int h = blockIdx.y, b = blockIdx.z, head = b * c.Hkv + h;
+    const int h = blockIdx.y, b = blockIdx.z, head = b * nh + h;
     const int N = c.plen[b];
     const int t0 = blockIdx.x * 64;
     if (t0 >= N) return;
@@ -114,69 +118,124 @@ __global__ __launch_bounds__(256) void k_project_mfma(DevCache c, const KT* __re
             cde |= ((m >> (16 * a)) & 0xFFFFull) << (16 * nt);
         }
         const int t = t0 + wave * 16 + lane;
-        if (t < N) reinterpret_cast<CT*>(c.pcode)[(size_t)head * c.pcode_slots + t] = (CT)cde;
+        if (t < N) reinterpret_cast<CT*>(dst)[(size_t)head * c.pcode_slots + t] = (CT)cde;
     }
 }
 
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp_u(unsigned x)
+{
+    return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+
+// Maximum over the wave (all 64 lanes active), returned wave-uniform: DPP
+// steps within each 16-lane row, then the four row maxima by readlane (no
+// LDS traffic).
 __device__ __forceinline__ unsigned wave_max_u32(unsigned v)
 {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        const unsigned o = __shfl_xor(v, m);
-        v = o > v ? o : v;
-    }
-    return v;
+    v = max(v, dpp_u<kDppXor1>(v));
+    v = max(v, dpp_u<kDppXor2>(v));
+    v = max(v, dpp_u<kDppHalfMirror>(v));
+    v = max(v, dpp_u<kDppMirror>(v));
+    const unsigned a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const unsigned c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    return max(max(a, b), max(c, d));
 }
 
-// STREAM selection for one (sequence, KV head): prompt tokens t >= S evict,
-// one after the other, the slot whose code is farthest from their own code
-// (ties to the lowest slot).  The code table stays in LDS; tok[] records the
-// token of every slot.
+// Sequential prefill selection for one (sequence, KV head): prompt tokens
+// t >= S, one after the other, evict the occupied slot farthest in summed
+// Hamming distance from their query codes -- their own key code under
+// STREAM, the codes of their G query rows under QUERY -- ties to the lowest
+// slot, and take it.  The code table and a window of the coming tokens' codes
+// stay in LDS.  One barrier per token: the waves' (score, slot) maxima are
+// double-buffered, every wave reduces them to the same winner, and the thread
+// whose scan covers the winning slot updates that table entry itself (it is
+// the entry's only reader).
+constexpr int kSelTokens = 128;   // tokens whose codes are staged at a time
+
 template <int BITS>
+constexpr size_t select_lds_bytes(int Smax, int nq)
+{
+    return ((size_t)((Smax + 63) & ~63) + (size_t)kSelTokens * (1 + nq)) * (BITS / 8);
+}
+
+// GQ = 0: STREAM (the token's key code); GQ > 0: QUERY with G <= GQ query
+// codes per token (GQ a power of two, so a group of G costs G popcounts).
+template <int BITS, int GQ>
 __global__ __launch_bounds__(1024) void k_prefill_select(DevCache c)
 {
     using CT = typename CodeT<BITS>::T;
     constexpr int VS = 16 / sizeof(CT);
+    constexpr int SLOT_BITS = 17;   // slot field of the 32-bit (score, slot) key
+    constexpr unsigned SLOT_MASK = (1u << SLOT_BITS) - 1u;
     extern __shared__ uint4 dyn_lds[];
-    CT* table = reinterpret_cast<CT*>(dyn_lds);
-    __shared__ unsigned s_red[16];
+    __shared__ unsigned s_red[2][16];
     const int h = blockIdx.x, b = blockIdx.y, head = b * c.Hkv + h;
     const int N = c.plen[b], S = c.budget[b];
     if (N <= S) return;
+    const int G = c.G;
+    const int Sp = (S + 63) & ~63;
+    CT* table = reinterpret_cast<CT*>(dyn_lds);
+    CT* skey = table + Sp;                 // [kSelTokens] key codes of the window
+    CT* sq = skey + kSelTokens;            // [kSelTokens][G] query codes of the window (QUERY)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const CT* pc = reinterpret_cast<const CT*>(c.pcode) + (size_t)head * c.pcode_slots;
+    constexpr bool QRY = GQ > 0;
+    const CT* qc = QRY ? reinterpret_cast<const CT*>(c.qcode) + (size_t)(b * c.Hq + h * G) * c.pcode_slots : nullptr;
     int* tok = c.tok + (size_t)head * c.Smax;
-    const int Sp = (S + 63) & ~63;
     for (int s = tid; s < Sp; s += blockDim.x) table[s] = s < S ? pc[s] : (CT)0;
-    __syncthreads();
-    for (int t = S; t < N; ++t) {
-        const CT cq = pc[t];
-        unsigned best = 0;
-        for (int s = tid * VS; s < S; s += 1024 * VS) {
-            const uint4 raw = *reinterpret_cast<const uint4*>(table + s);
-            CT cs[VS];
-            __builtin_memcpy(cs, &raw, 16);
+    int par = 0;
+    for (int t0 = S; t0 < N; t0 += kSelTokens) {
+        const int cnt = min(kSelTokens, N - t0);
+        __syncthreads();   // the previous window has been consumed
+        for (int i = tid; i < cnt; i += blockDim.x) skey[i] = pc[t0 + i];
+        if constexpr (QRY) {
+            for (int i = tid; i < cnt * G; i += blockDim.x) {
+                const int j = i / G, g = i - j * G;
+                sq[i] = qc[(size_t)g * c.pcode_slots + t0 + j];
+            }
+        }
+        __syncthreads();
+        for (int j = 0; j < cnt; ++j) {
+            CT qv[QRY ? GQ : 1];
+            if constexpr (QRY) {
 #pragma unroll
-            for (int u = 0; u < VS; ++u) {
-                const unsigned k = (s + u < S)
-                                       ? (((unsigned)popc((CT)(cq ^ cs[u])) << 24) | (0xFFFFFFu - (unsigned)(s + u)))
-                                       : 0u;
-                best = k > best ? k : best;
+                for (int g = 0; g < GQ; ++g) qv[g] = g < G ? sq[j * G + g] : (CT)0;
+            } else {
+                qv[0] = skey[j];
             }
-        }
-        best = wave_max_u32(best);
-        if (lane == 0) s_red[wave] = best;
-        __syncthreads();
-        if (wave == 0) {
-            unsigned v = lane < 16 ? s_red[lane] : 0u;
+            unsigned best = 0;
+            for (int s = tid * VS; s < S; s += 1024 * VS) {
+                const uint4 raw = *reinterpret_cast<const uint4*>(table + s);
+                CT cs[VS];
+                __builtin_memcpy(cs, &raw, 16);
+#pragma unroll
+                for (int u = 0; u < VS; ++u) {
+                    int sc = 0;
+                    if constexpr (QRY) {
+#pragma unroll
+                        for (int g = 0; g < GQ; ++g)
+                            if (g < G) sc += popc((CT)(qv[g] ^ cs[u]));
+                    } else {
+                        sc = popc((CT)(qv[0] ^ cs[u]));
+                    }
+                    const unsigned k = (s + u < S) ? (((unsigned)sc << SLOT_BITS) | (SLOT_MASK - (unsigned)(s + u)))
+                                                   : 0u;
+                    best = k > best ? k : best;
+                }
+            }
+            best = wave_max_u32(best);
+            if (lane == 0) s_red[par][wave] = best;
+            __syncthreads();
+            unsigned v = lane < 16 ? s_red[par][lane] : 0u;
             v = wave_max_u32(v);
-            if (lane == 0) {
-                const int e = (int)(0xFFFFFFu - (v & 0xFFFFFFu));
-                table[e] = cq;
-                tok[e] = t;
+            const int e = (int)(SLOT_MASK - (v & SLOT_MASK));
+            if (tid == (e / VS) % 1024) {
+                table[e] = skey[j];
+                tok[e] = t0 + j;
             }
+            par ^= 1;
         }
-        __syncthreads();
     }
 }
 
@@ -232,13 +291,14 @@ __global__ void k_import_codes(DevCache c, const uint32_t* __restrict__ in)
 }
 
 template <int BITS>
-__global__ void k_export_pcodes(DevCache c, uint32_t* __restrict__ out, int n_max)
+__global__ void k_export_pcodes(DevCache c, const void* __restrict__ src, int nh, uint32_t* __restrict__ out,
+                                int n_max)
 {
     using CT = typename CodeT<BITS>::T;
-    const int h = blockIdx.y, b = blockIdx.z, head = b * c.Hkv + h;
+    const int h = blockIdx.y, b = blockIdx.z, head = b * nh + h;
     const int t = blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= n_max) return;
-    const unsigned long long v = reinterpret_cast<const CT*>(c.pcode)[(size_t)head * c.pcode_slots + t];
+    const unsigned long long v = reinterpret_cast<const CT*>(src)[(size_t)head * c.pcode_slots + t];
     store_words(out + ((size_t)head * n_max + t) * c.W, c.W, v);
 }
 
@@ -285,7 +345,28 @@ hipError_t launch_reset(const DevCache& c, hipStream_t st)
     return hipGetLastError();
 }
 
-hipError_t launch_prefill(const DevCache& c, const void* K, const void* V, int n_max, int policy,
+template <int BITS, int GQ>
+hipError_t launch_select(const DevCache& c, hipStream_t st)
+{
+    const size_t lds = select_lds_bytes<BITS>(c.Smax, GQ > 0 ? c.G : 0);
+    hipError_t e = hipFuncSetAttribute((const void*)k_prefill_select<BITS, GQ>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_prefill_select<BITS, GQ>), dim3(c.Hkv, c.B), dim3(1024), lds, st, c);
+    return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_select_query(const DevCache& c, hipStream_t st)
+{
+    if (c.G <= 1) return launch_select<BITS, 1>(c, st);
+    if (c.G <= 2) return launch_select<BITS, 2>(c, st);
+    if (c.G <= 4) return launch_select<BITS, 4>(c, st);
+    if (c.G <= 8) return launch_select<BITS, 8>(c, st);
+    return launch_select<BITS, 16>(c, st);
+}
+
+hipError_t launch_prefill(const DevCache& c, const void* K, const void* V, const float* Q, int n_max, int policy,
                           hipStream_t st)
 {
     hipLaunchKernelGGL(k_prefill_init, dim3((c.Smax + 255) / 256, c.Hkv, c.B), dim3(256), 0, st, c);
@@ -298,15 +379,18 @@ hipError_t launch_prefill(const DevCache& c, const void* K, const void* V, int n
             constexpr int D = decltype(dd)::value;
             using KT = decltype(kt);
             hipLaunchKernelGGL((k_project_mfma<D, BITS, KT>), dim3((n_max + 63) / 64, c.Hkv, c.B),
-                               dim3(256), 0, st, c, (const KT*)K, n_max);
+                               dim3(256), 0, st, c, (const KT*)K, n_max, c.Hkv, c.pcode);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
             if (policy == HKV_PREFILL_STREAM) {
-                using CT = typename CodeT<BITS>::T;
-                const size_t lds = (size_t)((c.Smax + 63) & ~63) * sizeof(CT);
-                hipError_t e2 = hipFuncSetAttribute((const void*)k_prefill_select<BITS>,
-                                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-                if (e2 != hipSuccess) return e2;
-                hipLaunchKernelGGL((k_prefill_select<BITS>), dim3(c.Hkv, c.B), dim3(1024), lds, st, c);
+                e = launch_select<BITS, 0>(c, st);
+            } else if (policy == HKV_PREFILL_QUERY) {
+                hipLaunchKernelGGL((k_project_mfma<D, BITS, float>), dim3((n_max + 63) / 64, c.Hq, c.B),
+                                   dim3(256), 0, st, c, Q, n_max, c.Hq, c.qcode);
+                e = hipGetLastError();
+                if (e == hipSuccess) e = launch_select_query<BITS>(c, st);
             }
+            if (e != hipSuccess) return e;
             hipLaunchKernelGGL((k_prefill_gather<D, BITS, KT>), dim3((c.Smax + 15) / 16, c.Hkv, c.B),
                                dim3(256), 0, st, c, (const KT*)K, (const KT*)V, n_max);
             return hipGetLastError();
@@ -332,12 +416,14 @@ hipError_t launch_import_codes(const DevCache& c, const uint32_t* codes, hipStre
     });
 }
 
-hipError_t launch_export_pcodes(const DevCache& c, uint32_t* codes, int n_max, hipStream_t st)
+hipError_t launch_export_pcodes(const DevCache& c, uint32_t* codes, int n_max, bool queries, hipStream_t st)
 {
     if (n_max <= 0) return hipSuccess;
+    const int nh = queries ? c.Hq : c.Hkv;
+    const void* src = queries ? c.qcode : c.pcode;
     return with_bits(c, [&](auto bb) {
-        hipLaunchKernelGGL((k_export_pcodes<decltype(bb)::value>), dim3((n_max + 255) / 256, c.Hkv, c.B),
-                           dim3(256), 0, st, c, codes, n_max);
+        hipLaunchKernelGGL((k_export_pcodes<decltype(bb)::value>), dim3((n_max + 255) / 256, nh, c.B),
+                           dim3(256), 0, st, c, src, nh, codes, n_max);
         return hipGetLastError();
     });
 }

@@ -30,7 +30,7 @@ import numpy as np
 from .configs import SEED_BASE, Shape
 
 # stream ids inside one workload's SeedSequence
-_S_R, _S_SCALE, _S_PK, _S_PV, _S_LEN, _S_DQ, _S_DK, _S_DV = range(8)
+_S_R, _S_SCALE, _S_PK, _S_PV, _S_LEN, _S_DQ, _S_DK, _S_DV, _S_PQ = range(9)
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -43,7 +43,7 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 
 def _streams(shape: Shape, seed: Optional[int]):
     s = SEED_BASE + shape.index if seed is None else seed
-    return np.random.SeedSequence(s).spawn(8)
+    return np.random.SeedSequence(s).spawn(9)   # child i does not depend on the count
 
 
 def _rng(ss) -> np.random.Generator:
@@ -108,6 +108,15 @@ def prompt(shape: Shape, seed: Optional[int] = None) -> Prompt:
     V = _rng(ss[_S_PV]).standard_normal((B, H, n_max, d), dtype=np.float32)
     return Prompt(R=R, K=_store(K, shape.kv_dtype), V=_store(V, shape.kv_dtype),
                   prompt_lens=n, budgets=s, key_scale=scale)
+
+
+def prompt_queries(shape: Shape, seed: Optional[int] = None) -> np.ndarray:
+    """Query rows of the prompt tokens, fp32 [B][Hq][n_max][d] ~ N(0, 1) (the
+    decode queries' distribution), for the query-driven prefill."""
+    ss = _streams(shape, seed)
+    n, _ = lengths(shape, seed)
+    return _rng(ss[_S_PQ]).standard_normal((shape.batch, shape.n_q_heads, int(n.max()), shape.head_dim),
+                                           dtype=np.float32)
 
 
 def decode(shape: Shape, steps: Optional[int] = None, seed: Optional[int] = None,

@@ -18,14 +18,14 @@ LIB_PATH = os.path.join(HERE, "libhkv.so")
 
 HKV_OK, HKV_ERR_INVALID_ARG, HKV_ERR_UNSUPPORTED, HKV_ERR_STATE, HKV_ERR_DEVICE = range(5)
 HKV_F32, HKV_BF16 = 0, 1
-HKV_PREFILL_STREAM, HKV_PREFILL_TRUNCATE = 0, 1
+HKV_PREFILL_STREAM, HKV_PREFILL_TRUNCATE, HKV_PREFILL_QUERY = 0, 1, 2
 HKV_DECODE_FUSED, HKV_DECODE_SPLIT = 0, 1
 
 # every symbol include/hkv.h declares
 EXPORTS = ("hkv_validate_config", "hkv_workspace_bytes", "hkv_create", "hkv_prefill",
-           "hkv_decode_step", "hkv_destroy", "hkv_status_str", "hkv_last_error", "hkv_get_state",
-           "hkv_set_state", "hkv_debug_last_codes", "hkv_debug_prefill_codes", "hkv_debug_scores",
-           "hkv_encode")
+           "hkv_prefill_queries", "hkv_decode_step", "hkv_destroy", "hkv_status_str", "hkv_last_error",
+           "hkv_get_state", "hkv_set_state", "hkv_debug_last_codes", "hkv_debug_prefill_codes",
+           "hkv_debug_prefill_query_codes", "hkv_debug_scores", "hkv_encode")
 
 
 class hkv_config(C.Structure):
@@ -61,6 +61,7 @@ def load():
         "hkv_workspace_bytes": (I, [cfgp, C.POINTER(Z)]),
         "hkv_create": (I, [cfgp, P, P, Z, P, C.POINTER(P)]),
         "hkv_prefill": (I, [P, P, P, P, I, P]),
+        "hkv_prefill_queries": (I, [P, P, P, P, P, I, P]),
         "hkv_decode_step": (I, [P, P, P, P, P, P, P]),
         "hkv_destroy": (I, [P]),
         "hkv_status_str": (C.c_char_p, [I]),
@@ -69,6 +70,7 @@ def load():
         "hkv_set_state": (I, [P, P, P, P, P, P, P]),
         "hkv_debug_last_codes": (I, [P, P, P, P]),
         "hkv_debug_prefill_codes": (I, [P, P, P]),
+        "hkv_debug_prefill_query_codes": (I, [P, P, P]),
         "hkv_debug_scores": (I, [P, P, P, P]),
         "hkv_encode": (I, [P, P, I, I, P, P]),
     }
@@ -169,6 +171,16 @@ def hkv_debug_prefill_codes(h, codes, stream=None):
     _check(load().hkv_debug_prefill_codes(h, _ptr(codes), _stream(stream)), h)
 
 
+def hkv_prefill_queries(h, K, V, Q, prompt_lens, n_max: int, stream=None):
+    pl = np.ascontiguousarray(prompt_lens, dtype=np.int32)
+    _check(load().hkv_prefill_queries(h, _ptr(K), _ptr(V), _ptr(Q), pl.ctypes.data_as(C.c_void_p), int(n_max),
+                                      _stream(stream)), h)
+
+
+def hkv_debug_prefill_query_codes(h, codes, stream=None):
+    _check(load().hkv_debug_prefill_query_codes(h, _ptr(codes), _stream(stream)), h)
+
+
 def hkv_debug_scores(h, qcodes, scores, stream=None):
     _check(load().hkv_debug_scores(h, _ptr(qcodes), _ptr(scores), _stream(stream)), h)
 
@@ -236,9 +248,13 @@ class Cache:
         except Exception:
             pass
 
-    def prefill(self, K, V, prompt_lens, stream=None):
+    def prefill(self, K, V, prompt_lens, stream=None, Q=None):
+        """K, V [B][Hkv][n_max][d]; Q [B][Hq][n_max][d] fp32 for a cache made with HKV_PREFILL_QUERY."""
         self.n_max = int(K.shape[2])
-        hkv_prefill(self.h, K, V, prompt_lens, self.n_max, stream)
+        if Q is None:
+            hkv_prefill(self.h, K, V, prompt_lens, self.n_max, stream)
+        else:
+            hkv_prefill_queries(self.h, K, V, Q, prompt_lens, self.n_max, stream)
 
     def decode_step(self, q, k, v, out=None, evicted=None, stream=None):
         import torch
@@ -274,6 +290,12 @@ class Cache:
         import torch
         pc = torch.empty((self.B, self.Hkv, max(self.n_max, 1), self.W), dtype=torch.int32, device="cuda")
         hkv_debug_prefill_codes(self.h, pc, stream)
+        return pc
+
+    def prefill_query_codes(self, stream=None):
+        import torch
+        pc = torch.empty((self.B, self.Hq, max(self.n_max, 1), self.W), dtype=torch.int32, device="cuda")
+        hkv_debug_prefill_query_codes(self.h, pc, stream)
         return pc
 
     def scores(self, qcodes, stream=None):

@@ -79,10 +79,14 @@ def run_case(shape: Shape, steps: int, schedule: int = 0, policy: int = 0, chunk
     cache = hkv.Cache(B, Hq, Hkv, d, bits, kvd, P.budgets, P.R, prefill_policy=policy,
                       decode_schedule=schedule, max_prompt=n_max, chunk=chunk)
     Kt, Vt = hkv.to_device(P.K), hkv.to_device(P.V)
-    cache.prefill(Kt, Vt, P.prompt_lens)
+    query = policy == oracle.QUERY
+    Qp = datagen.prompt_queries(shape, seed) if query else None
+    Qt = hkv.to_device(Qp) if query else None
+    cache.prefill(Kt, Vt, P.prompt_lens, Q=Qt)
     pcodes = words_u32(cache.prefill_codes())
+    qpcodes = words_u32(cache.prefill_query_codes()) if query else None
     torch.cuda.synchronize()
-    del Kt, Vt
+    del Kt, Vt, Qt
 
     sel = list(heads) if heads is not None else [(b, h) for b in range(B) for h in range(Hkv)]
     orc = oracle.OracleCache(P.R, P.budgets, Hq, Hkv, heads=sel)
@@ -93,8 +97,12 @@ def run_case(shape: Shape, steps: int, schedule: int = 0, policy: int = 0, chunk
             continue
         codes_o, flags_o = orc.heads[(b, h)].encode(oracle.widen(P.K[b, h, :n]))
         flagged += check_codes(pcodes[b, h, :n], codes_o, flags_o, f"prefill codes b={b} h={h}")
+        if query:
+            for g in range(G):
+                qo, qf = orc.heads[(b, h)].encode(oracle.widen(Qp[b, h * G + g, :n]))
+                flagged += check_codes(qpcodes[b, h * G + g, :n], qo, qf, f"prefill query codes b={b} hq={h * G + g}")
     # replay the oracle's prefill with the GPU codes
-    orc.prefill(P.K, P.V, P.prompt_lens, policy, inj_codes=pcodes)
+    orc.prefill(P.K, P.V, P.prompt_lens, policy, inj_codes=pcodes, Q=Qp, inj_qcodes=qpcodes)
     log(f"  prefill codes ok ({flagged} flagged bits differ), {time.time()-t0:.1f}s")
     compare_state(cache, orc, sel, shape, "after prefill")
     log(f"  prefill state ok, {time.time()-t0:.1f}s")

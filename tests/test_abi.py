@@ -63,6 +63,8 @@ def test_named_shapes_validate(hkv):
     (dict(budgets=[1 << 23], prefill_policy=1), "UNSUPPORTED"),
     (dict(budgets=[40000]), "UNSUPPORTED"),               # 160 KB code table > on-chip table
     (dict(kv_dtype=7), "UNSUPPORTED"),
+    (dict(prefill_policy=3), "UNSUPPORTED"),
+    (dict(budgets=[40000], prefill_policy=2), "UNSUPPORTED"),   # QUERY keeps its table on chip too
     (dict(chunk=100), "UNSUPPORTED"),
     (dict(chunk=32), "UNSUPPORTED"),
     (dict(max_prompt=-1), "UNSUPPORTED"),
@@ -72,6 +74,14 @@ def test_named_shapes_validate(hkv):
 def test_bad_configs(hkv, kw, status):
     cfg = _cfg(hkv, **kw)
     assert hkv.hkv_validate_config(cfg) == getattr(hkv, "HKV_ERR_" + status)
+
+
+def test_query_policy_validates_and_sizes_its_code_buffer(hkv):
+    a = _cfg(hkv, prefill_policy=hkv.HKV_PREFILL_QUERY)
+    assert hkv.hkv_validate_config(a) == hkv.HKV_OK
+    # the prompt query codes ([B][Hq][max_prompt] of 4 bytes) come on top of the STREAM workspace
+    extra = hkv.hkv_workspace_bytes(a) - hkv.hkv_workspace_bytes(_cfg(hkv))
+    assert extra >= 32 * 8192 * 4
 
 
 def test_truncate_allows_large_budget(hkv):
@@ -86,9 +96,9 @@ def test_null_pointers(hkv):
     cfg.budgets = C.POINTER(C.c_int32)()
     assert L.hkv_validate_config(C.byref(cfg)) == hkv.HKV_ERR_INVALID_ARG
     assert L.hkv_workspace_bytes(C.byref(_cfg(hkv)), None) == hkv.HKV_ERR_INVALID_ARG
-    for f, n in (("hkv_prefill", 6), ("hkv_decode_step", 7), ("hkv_destroy", 1), ("hkv_get_state", 7),
-                 ("hkv_set_state", 7), ("hkv_debug_last_codes", 4), ("hkv_debug_prefill_codes", 3),
-                 ("hkv_debug_scores", 4)):
+    for f, n in (("hkv_prefill", 6), ("hkv_prefill_queries", 7), ("hkv_decode_step", 7), ("hkv_destroy", 1),
+                 ("hkv_get_state", 7), ("hkv_set_state", 7), ("hkv_debug_last_codes", 4),
+                 ("hkv_debug_prefill_codes", 3), ("hkv_debug_prefill_query_codes", 3), ("hkv_debug_scores", 4)):
         fn = getattr(L, f)
         args = [0 if t is C.c_int32 else None for t in fn.argtypes]
         assert len(args) == n

@@ -13,7 +13,7 @@ from lsh_eviction_amd.configs import Shape
 pytestmark = pytest.mark.gpu
 
 FUSED, SPLIT = 0, 1
-STREAM, TRUNCATE = 0, 1
+STREAM, TRUNCATE, QUERY = 0, 1, 2
 
 SMALL = {
     "tiny": (C.TINY, 64, 0),
@@ -45,6 +45,35 @@ def test_small(name, schedule):
 def test_truncate_policy(schedule):
     from hkv_harness import run_case
     run_case(C.LLAMA8B.scaled(prompt=2100, budget=1000), 8, schedule=schedule, policy=TRUNCATE)
+
+
+QUERY_SMALL = {
+    "tiny": (C.TINY, 8, 0),
+    "llama8b_small": (C.LLAMA8B.scaled(prompt=3000, budget=1500), 6, 0),
+    "ragged_small": (C.RAGGED.scaled(batch=4, prompt_range=(600, 1800)), 4, 0),
+    "llama70b_small": (C.LLAMA70B.scaled(batch=2, prompt=2500, budget=1200), 4, 0),
+    "g16_b16": (SMALL["g16_b16"][0], 4, 0),
+    "d128_f32_g1": (SMALL["d128_f32_g1"][0], 4, 64),
+    "d64_bf16_g2": (SMALL["d64_bf16_g2"][0], 4, 128),
+    "not_full": (C.LLAMA8B.scaled(prompt=700, budget=1000), 4, 0),
+    "empty_prompt": (C.TINY.scaled(prompt=0, budget=8), 4, 64),
+}
+
+
+@pytest.mark.parametrize("name", list(QUERY_SMALL))
+def test_query_prefill_small(name):
+    """Query-driven prefill: codes of every prompt query row, the sequential
+    selection and the cache it leaves, then decode steps."""
+    from hkv_harness import run_case
+    shape, steps, chunk = QUERY_SMALL[name]
+    run_case(shape, steps, schedule=FUSED, policy=QUERY, chunk=chunk)
+
+
+def test_query_prefill_full_llama3_8b_layer():
+    """The 8B layer shape (8192-token prompt, 4096 slots, 4096 sequential
+    evictions per head) under the query-driven prefill, sampled heads."""
+    from hkv_harness import run_case
+    run_case(C.LLAMA8B, 2, schedule=FUSED, policy=QUERY, heads=[(0, 0), (0, 3), (0, 7)], check_every=0)
 
 
 def test_scores_and_encoder():
