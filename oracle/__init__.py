@@ -56,6 +56,11 @@ def lib():
         L.orc_prefill.restype = C.c_int
         L.orc_prefill.argtypes = [P, C.c_int, C.c_int, P, P, P]
         L.orc_prefill_query.argtypes = [P, C.c_int, P, P, P, P, P]
+        L.orc_set_value_bits.argtypes = [P, C.c_int]
+        L.orc_set_value_bits.restype = C.c_int
+        L.orc_quantize_row.argtypes = [P, C.c_int, P, P]
+        L.orc_get_value_codes.argtypes = [P, P, P]
+        L.orc_set_value_codes.argtypes = [P, P, P]
         L.orc_prefill_query.restype = C.c_int
         L.orc_decode_step.restype = C.c_int
         L.orc_decode_step.argtypes = [P] * 3 + [P] * 8 + [P]
@@ -97,7 +102,7 @@ def _u32(a) -> Optional[np.ndarray]:
 class OracleHead:
     """One eviction domain: the cache of one (sequence, KV head) pair."""
 
-    def __init__(self, R: np.ndarray, budget: int, group: int):
+    def __init__(self, R: np.ndarray, budget: int, group: int, value_bits: int = 0):
         R = _f64(widen(R) if R.dtype != np.float64 else R)
         self.d, self.nbits = R.shape
         self.budget, self.group = int(budget), int(group)
@@ -106,6 +111,9 @@ class OracleHead:
         self._h = lib().orc_create(self.d, self.nbits, self.budget, self.group, _p(R))
         if not self._h:
             raise ValueError("orc_create rejected its arguments")
+        self.value_bits = int(value_bits)
+        if lib().orc_set_value_bits(self._h, self.value_bits) != 0:
+            raise ValueError("value_bits must be 0 or 8")
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -177,6 +185,14 @@ class OracleHead:
         lib().orc_attend(self._h, _p(q), _p(out))
         return out
 
+    def value_codes(self):
+        """int8 codes [budget][d] and fp32 scales [budget] of an int8-value cache."""
+        S = max(self.budget, 0)
+        q = np.zeros((S, self.d), np.int8)
+        sc = np.zeros(S, np.float32)
+        lib().orc_get_value_codes(self._h, _p(q), _p(sc))
+        return q, sc
+
     def state(self) -> dict:
         S = max(self.budget, 0)
         K = np.zeros((S, self.d)); V = np.zeros((S, self.d))
@@ -193,17 +209,29 @@ class OracleHead:
         lib().orc_set_state(self._h, _p(K), _p(V), _p(code), _p(tok), int(st["n"]), int(st["t"]))
 
 
+def quantize_rows(V: np.ndarray):
+    """The value-compression rule applied to rows V[..][d]: int8 codes, fp32 scales."""
+    V = _f64(V)
+    d = V.shape[-1]
+    flat = V.reshape(-1, d)
+    q = np.zeros(flat.shape, np.int8)
+    sc = np.zeros(flat.shape[0], np.float32)
+    for i in range(flat.shape[0]):
+        lib().orc_quantize_row(_p(flat[i]), d, _p(q[i]), _p(sc[i:i + 1]))
+    return q.reshape(V.shape), sc.reshape(V.shape[:-1])
+
+
 class OracleCache:
     """All eviction domains of a batch: heads[b][h] for b < B, h < Hkv.
 
     Query head hq belongs to KV head hq // G (contiguous groups)."""
 
-    def __init__(self, R, budgets, n_q_heads: int, n_kv_heads: int, heads=None):
+    def __init__(self, R, budgets, n_q_heads: int, n_kv_heads: int, heads=None, value_bits: int = 0):
         self.B = len(budgets)
         self.Hq, self.Hkv = int(n_q_heads), int(n_kv_heads)
         self.G = self.Hq // self.Hkv
         self.sel = heads if heads is not None else [(b, h) for b in range(self.B) for h in range(self.Hkv)]
-        self.heads = {(b, h): OracleHead(R, int(budgets[b]), self.G) for (b, h) in self.sel}
+        self.heads = {(b, h): OracleHead(R, int(budgets[b]), self.G, value_bits) for (b, h) in self.sel}
 
     def prefill(self, K, V, prompt_lens, policy=STREAM, inj_codes=None, Q=None, inj_qcodes=None):
         """K, V [B][Hkv][n_max][d]; with policy QUERY also Q [B][Hq][n_max][d] (fp32) and

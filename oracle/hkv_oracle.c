@@ -28,6 +28,9 @@ struct orc_head {
     int64_t* tok;     /* [budget]  token position held by the slot, -1 if empty */
     int n;            /* occupancy: slots 0 .. n-1 hold tokens */
     int64_t t;        /* position of the next token */
+    int vbits;        /* 0: values kept as given; 8: int8 codes with a per-row scale */
+    int8_t* vq;       /* [budget][d] value codes (vbits == 8) */
+    float* vs;        /* [budget]    value scales (vbits == 8) */
 };
 
 int orc_words(const orc_head* h) { return h->words; }
@@ -64,6 +67,7 @@ void orc_destroy(orc_head* h)
 {
     if (!h) return;
     free(h->R); free(h->rnorm); free(h->K); free(h->V); free(h->code); free(h->tok);
+    free(h->vq); free(h->vs);
     free(h);
 }
 
@@ -126,12 +130,46 @@ static int pick_victim(const orc_head* h, const uint32_t* qcodes, int ngroup)
     return e;
 }
 
+/* READING of the value compression (the DASH-KV summary page, "Value
+ * compression strategy": values tolerate a coarser quantization than keys
+ * because the output is their weighted average; it gives no rule).  One row
+ * of d values (exact fp32 / bf16 numbers) becomes d int8 codes and one fp32
+ * scale, all in fp32 arithmetic: scale = max_i |v_i| / 127; code_i = v_i /
+ * scale rounded to nearest, ties to even, clamped to [-127, 127]; a zero row
+ * has scale 0 and codes 0.  The value the cache holds is code_i * scale. */
+void orc_quantize_row(const double* v, int d, int8_t* q, float* scale)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < d; ++i) {
+        const float a = fabsf((float)v[i]);
+        if (a > amax) amax = a;
+    }
+    const float sc = amax / 127.0f;
+    for (int i = 0; i < d; ++i) {
+        float c = 0.0f;
+        if (sc > 0.0f) {
+            const float x = (float)v[i] / sc;
+            c = rintf(x);
+            if (c > 127.0f) c = 127.0f;
+            if (c < -127.0f) c = -127.0f;
+        }
+        q[i] = (int8_t)c;
+    }
+    *scale = sc;
+}
+
 /* Stage 5: the token's key, value and key code take the slot. */
 static void write_slot(orc_head* h, int e, const double* k, const double* v, const uint32_t* kc,
                        int64_t pos)
 {
     memcpy(h->K + (size_t)e * h->d, k, sizeof(double) * h->d);
-    memcpy(h->V + (size_t)e * h->d, v, sizeof(double) * h->d);
+    if (h->vbits == 8) {
+        int8_t* q = h->vq + (size_t)e * h->d;
+        orc_quantize_row(v, h->d, q, &h->vs[e]);
+        for (int i = 0; i < h->d; ++i) h->V[(size_t)e * h->d + i] = (double)q[i] * (double)h->vs[e];
+    } else {
+        memcpy(h->V + (size_t)e * h->d, v, sizeof(double) * h->d);
+    }
     memcpy(h->code + (size_t)e * h->words, kc, sizeof(uint32_t) * h->words);
     h->tok[e] = pos;
 }
@@ -293,6 +331,40 @@ void orc_scores(const orc_head* h, const uint32_t* qcodes, int32_t* scores)
 {
     for (int s = 0; s < h->budget; ++s)
         scores[s] = s < h->n ? gqa_score(h, qcodes, h->group, s) : -1;
+}
+
+/* Store values as int8 codes with a per-row scale (bits = 8) or as given
+ * (bits = 0).  Only on an empty cache; returns 0, or -1. */
+int orc_set_value_bits(orc_head* h, int bits)
+{
+    if (h->n != 0 || (bits != 0 && bits != 8)) return -1;
+    h->vbits = bits;
+    if (bits == 8 && !h->vq) {
+        size_t slots = h->budget > 0 ? (size_t)h->budget : 1;
+        h->vq = (int8_t*)calloc(slots * h->d, 1);
+        h->vs = (float*)calloc(slots, sizeof(float));
+    }
+    return 0;
+}
+
+/* Value codes [budget][d] and scales [budget] of an int8-value cache. */
+void orc_get_value_codes(const orc_head* h, int8_t* q, float* scale)
+{
+    if (h->vbits != 8) return;
+    size_t S = (size_t)h->budget;
+    if (q) memcpy(q, h->vq, S * h->d);
+    if (scale) memcpy(scale, h->vs, S * sizeof(float));
+}
+
+/* Restore value codes and scales (the held values become code * scale). */
+void orc_set_value_codes(orc_head* h, const int8_t* q, const float* scale)
+{
+    if (h->vbits != 8) return;
+    size_t S = (size_t)h->budget;
+    memcpy(h->vq, q, S * h->d);
+    memcpy(h->vs, scale, S * sizeof(float));
+    for (size_t e = 0; e < S; ++e)
+        for (int i = 0; i < h->d; ++i) h->V[e * h->d + i] = (double)h->vq[e * h->d + i] * (double)h->vs[e];
 }
 
 void orc_get_state(const orc_head* h, double* K, double* V, uint32_t* code, int64_t* tok,

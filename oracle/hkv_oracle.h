@@ -59,6 +59,19 @@ int orc_prefill(orc_head* h, int policy, int n, const double* K, const double* V
 int orc_prefill_query(orc_head* h, int n, const double* K, const double* V, const double* Q,
                       const uint32_t* inj_codes, const uint32_t* inj_qcodes);
 
+/* Value compression (a reading; see the .c file): bits = 8 stores every
+ * value row as int8 codes with one fp32 scale (fp32 arithmetic: scale =
+ * max|v| / 127, code = round-half-even(v / scale) clamped to +-127) and the
+ * cache then holds code * scale; bits = 0 stores values as given.  Only on an
+ * empty cache; returns 0, or -1. */
+int orc_set_value_bits(orc_head* h, int bits);
+/* The rule on one row: q [d] codes, *scale. */
+void orc_quantize_row(const double* v, int d, int8_t* q, float* scale);
+/* Codes [budget][d] and scales [budget] of an int8-value cache (export,
+ * import; import sets the held values to code * scale). */
+void orc_get_value_codes(const orc_head* h, int8_t* q, float* scale);
+void orc_set_value_codes(orc_head* h, const int8_t* q, const float* scale);
+
 /* D + A: one decode step.  q: [group][d], k, v: [d].
  * inj_qcodes [group][W] / inj_kcode [W] (may be NULL) replace E's output.
  * Outputs (may be NULL): out [group][d], evicted slot, the codes and flags used. */
