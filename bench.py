@@ -29,17 +29,18 @@ MALL_BYTES = 256 << 20
 DEFAULT_WORKLOAD = "long_128k"
 
 
-def step_bytes(shape, budgets) -> int:
+def step_bytes(shape, budgets, value_bits: int = 0) -> int:
     """Algorithmic HBM bytes of one decode step: per cached slot and KV head the
-    code (b/8 bytes) and the K and V rows (2 * d * kv bytes) are read; per KV
-    head the new k, v, code and position are written; q is read and out written
-    (fp32)."""
+    code (b/8 bytes), the K row (d * kv bytes) and the V row (d * kv bytes, or
+    d int8 codes and a 4-byte scale) are read; per KV head the new k, v, code
+    and position are written; q is read and out written (fp32)."""
     es = 2 if shape.kv_dtype == "bf16" else 4
     cb = shape.n_bits // 8
     H, d = shape.n_kv_heads, shape.head_dim
     slots = int(sum(int(s) for s in budgets)) * H
-    per_slot = cb + 2 * d * es
-    writes = shape.batch * H * (2 * d * es + cb + 4)
+    vrow = d + 4 if value_bits == 8 else d * es
+    per_slot = cb + d * es + vrow
+    writes = shape.batch * H * (d * es + vrow + cb + 4)
     qo = shape.batch * shape.n_q_heads * d * 4 * 2
     return slots * per_slot + writes + qo
 
@@ -138,6 +139,8 @@ def main():
     ap.add_argument("--config", default=DEFAULT_WORKLOAD)
     ap.add_argument("--schedule", default="fused", choices=["fused", "split"])
     ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--value-bits", type=int, default=0, choices=[0, 8],
+                    help="8: values kept as int8 codes with a per-row scale (a different workload)")
     ap.add_argument("--prefill", default="stream", choices=["stream", "truncate", "query"],
                     help="prefill rule of the layer caches (timed per layer, not part of a step)")
     ap.add_argument("--layers", type=int, default=0, help="layer caches rotated (0 = enough to exceed the MALL twice)")
@@ -158,7 +161,7 @@ def main():
     shape = configs.BY_NAME[args.config]
     torch.cuda.set_device(0)
     n, budgets = datagen.lengths(shape)
-    per_step = step_bytes(shape, budgets)
+    per_step = step_bytes(shape, budgets, args.value_bits)
     L = args.layers or max(1, math.ceil(2 * MALL_BYTES / per_step))
     kvd = hkv.HKV_BF16 if shape.kv_dtype == "bf16" else hkv.HKV_F32
     sched = hkv.HKV_DECODE_FUSED if args.schedule == "fused" else hkv.HKV_DECODE_SPLIT
@@ -171,7 +174,8 @@ def main():
         pol = {"stream": hkv.HKV_PREFILL_STREAM, "truncate": hkv.HKV_PREFILL_TRUNCATE,
                "query": hkv.HKV_PREFILL_QUERY}[args.prefill]
         c = hkv.Cache(shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.n_bits, kvd,
-                      budgets, P.R, prefill_policy=pol, decode_schedule=sched, max_prompt=n_max, chunk=args.chunk)
+                      budgets, P.R, prefill_policy=pol, decode_schedule=sched, max_prompt=n_max, chunk=args.chunk,
+                      value_bits=args.value_bits)
         K, V = make_layer_inputs(shape, P, layer, shape.index)
         Q = None
         if args.prefill == "query":
@@ -273,7 +277,7 @@ def main():
     ms_per_step = total_ms / K_
     value = 1000.0 / ms_per_step
     achieved = per_step / (kern_ms * 1e-3) / 1e9
-    traffic = load_traffic(args.config, args.schedule)
+    traffic = load_traffic(args.config, args.schedule + ("/v8" if args.value_bits == 8 else ""))
     rec = {
         "metric": "decode steps/s (LSH score+evict+attend) & % HBM peak, 8B-shape 128K ctx",
         "value": round(value, 1),
@@ -291,7 +295,7 @@ def main():
                    "n_kv_heads": shape.n_kv_heads, "head_dim": shape.head_dim, "n_bits": shape.n_bits,
                    "kv_storage": shape.kv_dtype, "budget_slots": int(budgets.sum()),
                    "prompt_tokens": int(n.sum()), "layers_rotated": L, "schedule": args.schedule,
-                   "chunk": caches[0].chunk, "graph": bool(args.graph)},
+                   "chunk": caches[0].chunk, "graph": bool(args.graph), "value_bits": args.value_bits},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
         "bytes_per_step": per_step,

@@ -47,6 +47,10 @@
  *     anything is enqueued, so a call that fails validation has no effect.  A
  *     launch failure poisons the handle: every later call returns
  *     HKV_ERR_STATE.  hkv_last_error() gives a one-line reason.
+ *   - values (value_bits = 8, a reading of the DASH-KV page's value
+ *     compression): V rows are kept as int8 codes with a per-row fp32 scale;
+ *     keys, codes and eviction are unchanged.  Inputs stay kv dtype; the
+ *     library quantizes when it stores a row.
  *   - supported: n_bits in {16, 32, 64}; head_dim in {64, 128};
  *     n_q_heads % n_kv_heads == 0 with G = n_q_heads / n_kv_heads <= 16;
  *     kv dtype fp32 or bf16; 1 <= budget <= 2^22 per sequence (a prefill
@@ -92,6 +96,12 @@ typedef struct {
     int32_t chunk;           /* slots per attention split (one workgroup each);
                                 0 selects 1024; otherwise a multiple of 64 in
                                 [64, 65536] */
+    int32_t value_bits;      /* 0: values stored in kv_dtype; 8: each value row
+                                stored as d int8 codes and one fp32 scale
+                                (scale = max|v| / 127, code = v / scale rounded
+                                half to even, clamped to +-127, in fp32; the
+                                cache holds code * scale).  8 needs kv_dtype
+                                HKV_BF16 and HKV_DECODE_FUSED */
     const int32_t* budgets;  /* host [batch]: cache slots S_b of each sequence */
 } hkv_config;
 
@@ -155,7 +165,9 @@ const char* hkv_last_error(const hkv_cache* c);
 /* Checkpoint export (device -> caller device buffers; any may be NULL):
  * K, V [B][Hkv][Smax][d] kv dtype; codes [B][Hkv][Smax][W] uint32 with
  * W = ceil(b/32) (unused high bits zero); slot_token [B][Hkv][Smax] int32
- * (-1 = empty slot); head_state [B][Hkv][2] int32 = (occupancy, next position). */
+ * (-1 = empty slot); head_state [B][Hkv][2] int32 = (occupancy, next position).
+ * With value_bits = 8, V is [B][Hkv][Smax][d] int8 codes followed by
+ * [B][Hkv][Smax] fp32 scales (B*Hkv*Smax*(d + 4) bytes). */
 hkv_status hkv_get_state(const hkv_cache* c, void* K, void* V, uint32_t* codes,
                          int32_t* slot_token, int32_t* head_state, void* stream);
 /* Checkpoint import, same layouts; all five buffers required.  Marks the

@@ -111,6 +111,8 @@ extern "C" hkv_status hkv_create(const hkv_config* cfg, const float* R_host, voi
     d.count = (unsigned*)(ws + L.off_count);
     d.pcode = ws + L.off_pcode;
     d.qcode = ws + L.off_qcode;
+    d.vs = (float*)(ws + L.off_vs);
+    d.vq = L.value_bits == 8;
     d.B = L.B; d.Hq = L.Hq; d.Hkv = L.Hkv; d.G = L.G; d.d = L.d; d.bits = L.bits; d.W = L.W;
     d.Smax = L.Smax; d.chunk = L.chunk; d.nsplit = L.nsplit;
     d.kv_bf16 = L.kv_dtype == HKV_BF16;
@@ -123,6 +125,9 @@ extern "C" hkv_status hkv_create(const hkv_config* cfg, const float* R_host, voi
         e = hipMemcpyAsync((void*)d.budget, cfg->budgets, (size_t)L.B * sizeof(int32_t),
                            hipMemcpyHostToDevice, st);
     if (e == hipSuccess) e = hkv::launch_reset(d, st);
+    // value scales start at zero (the attention tile reads the scales of 16 rows at once)
+    if (e == hipSuccess && L.value_bits == 8)
+        e = hipMemsetAsync(d.vs, 0, ((size_t)L.B * L.Hkv * L.Smax + 16) * 4, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     if (e != hipSuccess) {
         std::string m = std::string("hkv_create: ") + hipGetErrorString(e);
@@ -227,7 +232,9 @@ extern "C" hkv_status hkv_get_state(const hkv_cache* cc, void* K, void* V, uint3
     const size_t kv = heads * L.Smax * L.d * L.es;
     hipError_t e = hipSuccess;
     if (K) e = hipMemcpyAsync(K, c->dev.K, kv, hipMemcpyDeviceToDevice, st);
-    if (e == hipSuccess && V) e = hipMemcpyAsync(V, c->dev.V, kv, hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess && V) e = hipMemcpyAsync(V, c->dev.V, L.v_bytes, hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess && V && L.value_bits == 8)
+        e = hipMemcpyAsync((char*)V + L.v_bytes, c->dev.vs, heads * L.Smax * 4, hipMemcpyDeviceToDevice, st);
     if (e == hipSuccess && codes) e = hkv::launch_export_codes(c->dev, codes, st);
     if (e == hipSuccess && slot_token)
         e = hipMemcpyAsync(slot_token, c->dev.tok, heads * L.Smax * 4, hipMemcpyDeviceToDevice, st);
@@ -248,7 +255,9 @@ extern "C" hkv_status hkv_set_state(hkv_cache* c, const void* K, const void* V, 
     const size_t heads = (size_t)L.B * L.Hkv;
     const size_t kv = heads * L.Smax * L.d * L.es;
     hipError_t e = hipMemcpyAsync(c->dev.K, K, kv, hipMemcpyDeviceToDevice, st);
-    if (e == hipSuccess) e = hipMemcpyAsync(c->dev.V, V, kv, hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(c->dev.V, V, L.v_bytes, hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess && L.value_bits == 8)
+        e = hipMemcpyAsync(c->dev.vs, (const char*)V + L.v_bytes, heads * L.Smax * 4, hipMemcpyDeviceToDevice, st);
     if (e == hipSuccess) e = hkv::launch_import_codes(c->dev, codes, st);
     if (e == hipSuccess) e = hipMemcpyAsync(c->dev.tok, slot_token, heads * L.Smax * 4, hipMemcpyDeviceToDevice, st);
     if (e == hipSuccess) e = hipMemcpyAsync(c->dev.state, head_state, heads * 8, hipMemcpyDeviceToDevice, st);

@@ -92,6 +92,19 @@ __device__ __forceinline__ float group_sum(float x)
     return x;
 }
 
+// Eight values -> eight int8 codes v / scale, rounded half to even (the
+// default rounding of rintf), clamped to +-127; all zero when scale is 0.
+__device__ __forceinline__ uint2 quantize8(const float (&f)[8], float scale)
+{
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float cq = scale > 0.f ? fminf(fmaxf(rintf(f[e] / scale), -127.f), 127.f) : 0.f;
+        w[e >> 2] |= ((uint32_t)(int32_t)cq & 0xFFu) << (8 * (e & 3));
+    }
+    return make_uint2(w[0], w[1]);
+}
+
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
 {
 #pragma unroll

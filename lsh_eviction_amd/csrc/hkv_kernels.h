@@ -29,7 +29,9 @@ struct DevCache {
     unsigned* count;                // [B][Hkv] blocks of the current step that have published
     void* pcode;                    // [B][Hkv][pcode_slots] prompt key codes
     void* qcode;                    // [B][Hq][pcode_slots] prompt query codes (QUERY prefill)
+    float* vs;                      // [B][Hkv][Smax] (+16) value scales when values are int8
     int B, Hq, Hkv, G, d, bits, W, Smax, chunk, nsplit;
+    bool vq;                        // values stored as int8 codes + scales
     int kv_bf16;
     long long code_slots, pcode_slots;
 };

@@ -19,14 +19,15 @@ constexpr size_t kAlign = 256;
 
 struct Layout {
     int B, Hq, Hkv, G, d, bits, W, cb, es;   // cb: code bytes, es: kv element bytes
-    int kv_dtype, prefill_policy, schedule;
+    int kv_dtype, prefill_policy, schedule, value_bits;
     int Smax, chunk, nsplit, max_prompt;
     size_t code_slots;     // slots per head in the code table (padded)
     size_t pcode_slots;    // prompt positions per head in the prefill code buffer (padded)
     // byte offsets into the workspace
     size_t off_R, off_budget, off_plen, off_state, off_K, off_V, off_code, off_tok;
     size_t off_dbg_q, off_dbg_k, off_part, off_frec, off_fscal, off_cand_v, off_ekey;
-    size_t off_info, off_count, off_pcode, off_qcode;
+    size_t off_info, off_count, off_pcode, off_qcode, off_vs;
+    size_t v_bytes;        // bytes of the V region (kv dtype, or int8 codes)
     size_t total;
 };
 

@@ -35,6 +35,10 @@ hkv_status compute_layout(const hkv_config* cfg, Layout* L, char* err, size_t er
     if (cfg->prefill_policy != HKV_PREFILL_STREAM && cfg->prefill_policy != HKV_PREFILL_TRUNCATE &&
         cfg->prefill_policy != HKV_PREFILL_QUERY)
         FAIL(HKV_ERR_UNSUPPORTED, "prefill_policy %d unknown", cfg->prefill_policy);
+    if (cfg->value_bits != 0 && cfg->value_bits != 8)
+        FAIL(HKV_ERR_UNSUPPORTED, "value_bits %d not in {0, 8}", cfg->value_bits);
+    if (cfg->value_bits == 8 && (cfg->kv_dtype != HKV_BF16 || cfg->decode_schedule != HKV_DECODE_FUSED))
+        FAIL(HKV_ERR_UNSUPPORTED, "value_bits 8 needs kv_dtype HKV_BF16 and HKV_DECODE_FUSED");
     if (cfg->decode_schedule != HKV_DECODE_FUSED && cfg->decode_schedule != HKV_DECODE_SPLIT)
         FAIL(HKV_ERR_UNSUPPORTED, "decode_schedule %d unknown", cfg->decode_schedule);
     if (cfg->max_prompt < 0 || cfg->max_prompt > (1 << 24))
@@ -62,6 +66,7 @@ hkv_status compute_layout(const hkv_config* cfg, Layout* L, char* err, size_t er
     l.es = cfg->kv_dtype == HKV_BF16 ? 2 : 4;
     l.kv_dtype = cfg->kv_dtype; l.prefill_policy = cfg->prefill_policy;
     l.schedule = cfg->decode_schedule;
+    l.value_bits = cfg->value_bits;
     l.Smax = Smax;
     l.chunk = cfg->chunk ? cfg->chunk : kDefaultChunk;
     l.nsplit = (Smax + l.chunk - 1) / l.chunk;
@@ -81,7 +86,10 @@ hkv_status compute_layout(const hkv_config* cfg, Layout* L, char* err, size_t er
     l.off_plen = take((size_t)l.B * 4);
     l.off_state = take(heads * 2 * 4);
     l.off_K = take(heads * Smax * l.d * l.es);
-    l.off_V = take(heads * Smax * l.d * l.es);
+    l.v_bytes = heads * Smax * l.d * (l.value_bits == 8 ? 1 : l.es);
+    l.off_V = take(l.v_bytes);
+    // value scales, padded by 16 entries: the attention tile reads 16 rows' scales at once
+    l.off_vs = take(l.value_bits == 8 ? (heads * Smax + 16) * 4 : 0);
     l.off_code = take(heads * l.code_slots * cb);
     l.off_tok = take(heads * Smax * 4);
     l.off_dbg_q = take((size_t)l.B * l.Hq * l.W * 4);

@@ -449,22 +449,25 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // (l / 16) of the head dimension, 16 bytes per k-step), V in coalesced
 // 16-byte row segments (lane l: row group l / (D/8), segment l % (D/8)).
 // Rows at or beyond `len` are not loaded and read as zero.
-template <int D, int TR>
+template <int D, int TR, bool VQ = false>
 struct MTile {
     static constexpr int H = TR / 16;          // 16-row halves
     static constexpr int KS = D / 32;          // k-steps of 32 per half
-    static constexpr int LPR = D / 8;          // V lanes per row
+    static constexpr int LPR = D / 8;          // V lanes per row (8 values each)
     static constexpr int RPW = 64 / LPR;       // V rows per wave load
     static constexpr int VU = TR / RPW;        // V loads per lane
+    using VW = typename std::conditional<VQ, uint2, uint4>::type;   // 8 bf16 values or 8 int8 codes
     uint4 k[H][KS];
-    uint4 v[VU];
+    VW v[VU];
+    float vs[VQ ? H : 1][4];   // int8 values: scales of rows 16h + 4(l/16) + r (MFMA layout)
 
     // Rows beyond the range are clamped to its last row (loaded, then masked by
     // the caller); len == 0 clamps to row 0 of the range, which is in bounds.
     // No load sits in a branch, so the wait counters stay exact and the tile
     // in flight is never waited for early.
-    __device__ __forceinline__ void load(const bf16_t* __restrict__ Kh, const bf16_t* __restrict__ Vh, int r0,
-                                         int len, int base)
+    // Vh: bf16 rows, or int8 code rows with their scales at Vsh (VQ).
+    __device__ __forceinline__ void load(const bf16_t* __restrict__ Kh, const void* __restrict__ Vh,
+                                         const float* __restrict__ Vsh, int r0, int len, int base)
     {
         const int lane = threadIdx.x & 63;
         const int i = lane & 15, qd = lane >> 4;
@@ -480,7 +483,16 @@ struct MTile {
 #pragma unroll
         for (int u = 0; u < VU; ++u) {
             const int row = min(base + u * RPW + rg, last);
-            v[u] = *reinterpret_cast<const uint4*>(Vh + (size_t)(r0 + row) * D + cc * 8);
+            if constexpr (VQ)
+                v[u] = *reinterpret_cast<const uint2*>(reinterpret_cast<const int8_t*>(Vh) + (size_t)(r0 + row) * D + cc * 8);
+            else
+                v[u] = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(Vh) + (size_t)(r0 + row) * D + cc * 8);
+        }
+        if constexpr (VQ) {
+#pragma unroll
+            for (int h = 0; h < H; ++h)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) vs[h][r] = Vsh[r0 + min(base + 16 * h + 4 * qd + r, last)];
         }
     }
 };
@@ -507,12 +519,12 @@ struct MState {
     float acc[GM][8];       // value view: 8 elements of the lane's row segment
 };
 
-template <int D, int GM, int TR>
-__device__ __forceinline__ void mfma_tile(const MTile<D, TR>& tl, int base, int r0, int len, int skip,
+template <int D, int GM, int TR, bool VQ>
+__device__ __forceinline__ void mfma_tile(const MTile<D, TR, VQ>& tl, int base, int r0, int len, int skip,
                                           const bf16x8 (&qhi)[D / 32], const bf16x8 (&qlo)[D / 32],
                                           PSmem<GM, TR>& ps, MState<GM>& st)
 {
-    using T = MTile<D, TR>;
+    using T = MTile<D, TR, VQ>;
     constexpr int H = T::H, KS = T::KS, LPR = T::LPR, RPW = T::RPW, VU = T::VU;
     constexpr int GP = pad_g<GM>();
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -555,7 +567,9 @@ __device__ __forceinline__ void mfma_tile(const MTile<D, TR>& tl, int base, int 
         for (int r = 0; r < 4; ++r) {
             const float p = exp2_fast(lg[h][r] - ms);
             psum += p;
-            if (n < GM) ps.p[wave][16 * h + 4 * qd + r][n] = p;
+            // int8 values: the row's scale rides on its probability
+            const float pv = VQ ? p * tl.vs[VQ ? h : 0][r] : p;
+            if (n < GM) ps.p[wave][16 * h + 4 * qd + r][n] = pv;
         }
     st.lsum = st.lsum * alpha + psum;
     if (qd == 0 && n < GM) ps.alpha[wave][n] = alpha;
@@ -590,7 +604,13 @@ __device__ __forceinline__ void mfma_tile(const MTile<D, TR>& tl, int base, int 
             pg[4 * g4 + 3] = p4.w;
         }
         float vf[8];
-        Vec16<bf16_t>::cvt(tl.v[u], vf);
+        if constexpr (VQ) {
+            const uint32_t w[2] = {tl.v[u].x, tl.v[u].y};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vf[e] = (float)(int8_t)((w[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+        } else {
+            Vec16<bf16_t>::cvt(tl.v[u], vf);
+        }
 #pragma unroll
         for (int g = 0; g < GM; ++g)
 #pragma unroll
@@ -607,10 +627,11 @@ __device__ __forceinline__ void mfma_tile(const MTile<D, TR>& tl, int base, int 
 // keep fp32 accuracy while K stays exact.  Probabilities go through LDS to the
 // lanes that hold the value rows; P.V is accumulated in fp32 on the VALU.
 // Two tiles alternate: one is computed while the other is in flight.
-template <int D, int GM, int TR, int NB>
-__device__ __forceinline__ void attend_rows_mfma(const bf16_t* __restrict__ Kh, const bf16_t* __restrict__ Vh,
-                                                 const float* __restrict__ qh, int G, int r0, int len, int skip,
-                                                 MTile<D, TR> (&ring)[NB], AttnSmem<D, GM>& sm, PSmem<GM, TR>& ps)
+template <int D, int GM, int TR, int NB, bool VQ = false>
+__device__ __forceinline__ void attend_rows_mfma(const bf16_t* __restrict__ Kh, const void* __restrict__ Vh,
+                                                 const float* __restrict__ Vsh, const float* __restrict__ qh, int G,
+                                                 int r0, int len, int skip, MTile<D, TR, VQ> (&ring)[NB],
+                                                 AttnSmem<D, GM>& sm, PSmem<GM, TR>& ps)
 {
     constexpr int KS = D / 32, LPR = D / 8;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -654,14 +675,14 @@ __device__ __forceinline__ void attend_rows_mfma(const bf16_t* __restrict__ Kh, 
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             mfma_tile<D, GM, TR>(ring[i], b0 + (k + i) * step, r0, len, skip, qhi, qlo, ps, st);
-            ring[i].load(Kh, Vh, r0, len, b0 + (k + i + NB) * step);
+            ring[i].load(Kh, Vh, Vsh, r0, len, b0 + (k + i + NB) * step);
         }
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
         if (k + i < ntile) {
             mfma_tile<D, GM, TR>(ring[i], b0 + (k + i) * step, r0, len, skip, qhi, qlo, ps, st);
-            if (k + i + NB < ntile) ring[i].load(Kh, Vh, r0, len, b0 + (k + i + NB) * step);
+            if (k + i + NB < ntile) ring[i].load(Kh, Vh, Vsh, r0, len, b0 + (k + i + NB) * step);
         }
     }
 #pragma unroll
@@ -983,7 +1004,8 @@ union FusedSmem {
     MergeBlockSmem<D, GM> mg;
 };
 
-template <int D, int BITS, int GM, typename KT>
+// VQ: values are int8 codes with a per-row scale (bf16 keys only).
+template <int D, int BITS, int GM, typename KT, bool VQ = false>
 __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const float* __restrict__ q,
                                                            const KT* __restrict__ knew, const KT* __restrict__ vnew,
                                                            float* __restrict__ out, int* __restrict__ evicted)
@@ -1002,6 +1024,9 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     __shared__ PSmem<GM, TR> ps;
     __shared__ __align__(16) float s_q[GM][D];     // the group's queries (fp32)
     __shared__ __align__(16) KT s_kn[D], s_vn[D];  // the new token's key and value
+    __shared__ __align__(16) float s_vdq[VQ ? D : 1];   // int8 values: the new value as the cache holds it
+    __shared__ uint16_t s_vq2[VQ ? D / 2 : 1];          // ... its codes, two per entry
+    __shared__ float s_vsc;                              // ... and its scale
     __shared__ uint32_t s_q16[BITS / 16][16];
     __shared__ uint32_t s_k16[BITS / 16];
     __shared__ unsigned long long s_red[kWaves];
@@ -1015,6 +1040,9 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     const size_t rowbase = (size_t)head * c.Smax;
     KT* Kh = reinterpret_cast<KT*>(c.K) + rowbase * D;
     KT* Vh = reinterpret_cast<KT*>(c.V) + rowbase * D;
+    int8_t* Vq8 = reinterpret_cast<int8_t*>(c.V) + rowbase * D;   // int8 values (VQ)
+    float* Vsh = VQ ? c.vs + rowbase : nullptr;
+    const void* Vbase = VQ ? (const void*)Vq8 : (const void*)Vh;
     const CT* codeh = reinterpret_cast<const CT*>(c.code) + (size_t)head * c.code_slots;
     const size_t crec = (size_t)head * c.nsplit + split;
     const KT* kh = knew + (size_t)head * D;
@@ -1054,11 +1082,11 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
 
     // the first tiles of every wave, in flight while the codes are computed
     constexpr int NB = ring_depth<GM>();
-    MTile<D, TR> ring[kMfma ? NB : 1];
+    MTile<D, TR, VQ> ring[kMfma ? NB : 1];
     Tile<D, KT> first;
     if constexpr (kMfma) {
 #pragma unroll
-        for (int i = 0; i < NB; ++i) ring[i].load(Kh, Vh, s0, len, (wave + i * kWaves) * TR);
+        for (int i = 0; i < NB; ++i) ring[i].load(Kh, Vbase, Vsh, s0, len, (wave + i * kWaves) * TR);
     } else {
         first.load(Kh, Vh, s0, len, wave * Tile<D, KT>::ROWS);
     }
@@ -1114,12 +1142,18 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     float2 kc2 = make_float2(0.f, 0.f), vc2 = make_float2(0.f, 0.f);
     if (cand >= 0 && 2 * lane < D) {
         kc2 = make_float2(to_f32(Kh[(size_t)cand * D + 2 * lane]), to_f32(Kh[(size_t)cand * D + 2 * lane + 1]));
-        vc2 = make_float2(to_f32(Vh[(size_t)cand * D + 2 * lane]), to_f32(Vh[(size_t)cand * D + 2 * lane + 1]));
+        if constexpr (VQ) {
+            const uint16_t w = *reinterpret_cast<const uint16_t*>(Vq8 + (size_t)cand * D + 2 * lane);
+            const float sc = Vsh[cand];
+            vc2 = make_float2((float)(int8_t)(w & 0xFFu) * sc, (float)(int8_t)(w >> 8) * sc);
+        } else {
+            vc2 = make_float2(to_f32(Vh[(size_t)cand * D + 2 * lane]), to_f32(Vh[(size_t)cand * D + 2 * lane + 1]));
+        }
     }
 
     // attention over the chunk with the candidate held out
     if constexpr (kMfma)
-        attend_rows_mfma<D, GM, TR, NB>(Kh, Vh, &s_q[0][0], G, s0, len, cand, ring, sm, ps);
+        attend_rows_mfma<D, GM, TR, NB, VQ>(Kh, Vbase, Vsh, &s_q[0][0], G, s0, len, cand, ring, sm, ps);
     else
         attend_rows<D, GM, KT>(Kh, Vh, &s_q[0][0], G, s0, len, cand, first, sm);
 
@@ -1149,6 +1183,25 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     // j = r + RS * jj.  All loads of a batch of splits are issued before any
     // of them is used, so the merge costs one round trip to memory per batch.
     if (tid == 0) c.count[head] = 0u;
+    if constexpr (VQ) {
+        // the new token's value row as the cache will hold it: int8 codes
+        // (v / scale rounded half to even, clamped to +-127) with scale =
+        // max|v| / 127, all in fp32; every later use of the value is
+        // code * scale
+        if (wave == 0) {
+            const int i0 = 2 * lane;
+            const float f0 = i0 < D ? to_f32(s_vn[i0]) : 0.f, f1 = i0 < D ? to_f32(s_vn[i0 + 1]) : 0.f;
+            const float sc = wave_max_f(fmaxf(fabsf(f0), fabsf(f1))) / 127.0f;
+            const float c0 = sc > 0.f ? fminf(fmaxf(rintf(f0 / sc), -127.f), 127.f) : 0.f;
+            const float c1 = sc > 0.f ? fminf(fmaxf(rintf(f1 / sc), -127.f), 127.f) : 0.f;
+            if (i0 < D) {
+                s_vq2[lane] = (uint16_t)(((uint32_t)(int32_t)c0 & 0xFFu) | (((uint32_t)(int32_t)c1 & 0xFFu) << 8));
+                s_vdq[i0] = c0 * sc;
+                s_vdq[i0 + 1] = c1 * sc;
+            }
+            if (lane == 0) s_vsc = sc;
+        }
+    }
     constexpr int TPR = D / 4;
     constexpr int RS = kThreads / TPR;
     constexpr int JBMAX = GM <= 4 ? 4 : (GM <= 8 ? 2 : 1);   // register budget
@@ -1201,7 +1254,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     for (int idx = tid; idx < G * TPR; idx += kThreads) {
         const int g = idx / TPR, cc = idx % TPR;
         float M = s_nlg[g], L = 1.f;
-        float4 A = load4_f32(s_vn + 4 * cc);
+        float4 A = VQ ? *reinterpret_cast<const float4*>(&s_vdq[VQ ? 4 * cc : 0]) : load4_f32(s_vn + 4 * cc);
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) lse_add4(M, L, A, mg.m[w][g], mg.l[w][g], mg.a[w][g][cc]);
         const float inv = 1.f / L;
@@ -1212,8 +1265,13 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     // stage 5: the new token takes slot e
     for (int i = tid; i < D; i += kThreads) {
         Kh[(size_t)e * D + i] = s_kn[i];
-        Vh[(size_t)e * D + i] = s_vn[i];
+        if constexpr (VQ) {
+            if (i < D / 2) reinterpret_cast<uint16_t*>(Vq8 + (size_t)e * D)[i] = s_vq2[i];
+        } else {
+            Vh[(size_t)e * D + i] = s_vn[i];
+        }
     }
+    if (VQ && tid == 0) Vsh[e] = s_vsc;
     if (tid == 0) {
         unsigned long long kc = 0;
 #pragma unroll
@@ -1345,8 +1403,8 @@ __global__ __launch_bounds__(kThreads) void k_attn_split(DevCache c, const float
         const int ntile = len > wave * TR ? (len - wave * TR + kWaves * TR - 1) / (kWaves * TR) : 0;
 #pragma unroll
         for (int i = 0; i < NB; ++i)
-            if (i < ntile) ring[i].load(Kh, Vh, s0, len, (wave + i * kWaves) * TR);
-        attend_rows_mfma<D, GM, TR, NB>(Kh, Vh, q + (size_t)hq0 * D, c.G, s0, len, -1, ring, sm, ps);
+            if (i < ntile) ring[i].load(Kh, Vh, nullptr, s0, len, (wave + i * kWaves) * TR);
+        attend_rows_mfma<D, GM, TR, NB>(Kh, Vh, nullptr, q + (size_t)hq0 * D, c.G, s0, len, -1, ring, sm, ps);
     } else {
         Tile<D, KT> first;
         first.load(Kh, Vh, s0, len, wave * Tile<D, KT>::ROWS);
@@ -1454,6 +1512,13 @@ hipError_t launch_decode_fused(const DevCache& c, const float* q, const void* k,
             return with_bits(c, [&](auto bb) {
                 return with_gm(c, [&](auto gg) {
                     constexpr int D = decltype(dd)::value, BITS = decltype(bb)::value, GM = decltype(gg)::value;
+                    if constexpr (std::is_same<KT, bf16_t>::value) {
+                        if (c.vq) {
+                            hipLaunchKernelGGL((k_decode_fused<D, BITS, GM, KT, true>), dim3(c.nsplit, c.Hkv, c.B),
+                                               dim3(kThreads), 0, st, c, q, (const KT*)k, (const KT*)v, out, evicted);
+                            return hipGetLastError();
+                        }
+                    }
                     hipLaunchKernelGGL((k_decode_fused<D, BITS, GM, KT>), dim3(c.nsplit, c.Hkv, c.B), dim3(kThreads),
                                        0, st, c, q, (const KT*)k, (const KT*)v, out, evicted);
                     return hipGetLastError();

@@ -257,10 +257,33 @@ __global__ __launch_bounds__(256) void k_prefill_gather(DevCache c, const KT* __
     const uint4* vs = reinterpret_cast<const uint4*>(Vp + ((size_t)head * n_max + t) * D);
     uint4* kd = reinterpret_cast<uint4*>(reinterpret_cast<KT*>(c.K) + (rowbase + s) * D);
     uint4* vd = reinterpret_cast<uint4*>(reinterpret_cast<KT*>(c.V) + (rowbase + s) * D);
-    for (int q = j; q < CH; q += 16) {
-        kd[q] = ks[q];
-        vd[q] = vs[q];
+    for (int q = j; q < CH; q += 16) kd[q] = ks[q];
+    bool quantized = false;
+    if constexpr (std::is_same<KT, bf16_t>::value) {
+        if (c.vq) {
+            // value row -> int8 codes and one scale (scale = max|v| / 127,
+            // code = v / scale rounded half to even, clamped to +-127, fp32);
+            // the 16 lanes of the row each take 8 values (D / 8 <= 16)
+            float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            const int nchunk = D / 8;
+            if (j < nchunk) Vec16<bf16_t>::cvt(vs[j], f);
+            float amax = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(f[e]));
+            amax = fmaxf(amax, dpp_f<kDppXor1>(amax));
+            amax = fmaxf(amax, dpp_f<kDppXor2>(amax));
+            amax = fmaxf(amax, dpp_f<kDppHalfMirror>(amax));
+            amax = fmaxf(amax, dpp_f<kDppMirror>(amax));
+            const float sc = amax / 127.0f;
+            if (j < nchunk) {
+                reinterpret_cast<uint2*>(reinterpret_cast<int8_t*>(c.V) + (rowbase + s) * D)[j] = quantize8(f, sc);
+            }
+            if (j == 0) c.vs[rowbase + s] = sc;
+            quantized = true;
+        }
     }
+    if (!quantized)
+        for (int q = j; q < CH; q += 16) vd[q] = vs[q];
     if (j == 0)
         reinterpret_cast<CT*>(c.code)[(size_t)head * c.code_slots + s] =
             reinterpret_cast<const CT*>(c.pcode)[(size_t)head * c.pcode_slots + t];

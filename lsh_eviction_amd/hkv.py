@@ -32,7 +32,7 @@ class hkv_config(C.Structure):
     _fields_ = [("batch", C.c_int32), ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32),
                 ("head_dim", C.c_int32), ("n_bits", C.c_int32), ("kv_dtype", C.c_int32),
                 ("prefill_policy", C.c_int32), ("decode_schedule", C.c_int32),
-                ("max_prompt", C.c_int32), ("chunk", C.c_int32),
+                ("max_prompt", C.c_int32), ("chunk", C.c_int32), ("value_bits", C.c_int32),
                 ("budgets", C.POINTER(C.c_int32))]
 
 
@@ -87,11 +87,11 @@ def status_str(s: int) -> str:
 
 def make_config(batch, n_q_heads, n_kv_heads, head_dim, n_bits, kv_dtype, budgets,
                 prefill_policy=HKV_PREFILL_STREAM, decode_schedule=HKV_DECODE_FUSED,
-                max_prompt=0, chunk=0):
+                max_prompt=0, chunk=0, value_bits=0):
     b = np.ascontiguousarray(budgets, dtype=np.int32)
     cfg = hkv_config(int(batch), int(n_q_heads), int(n_kv_heads), int(head_dim), int(n_bits),
                      int(kv_dtype), int(prefill_policy), int(decode_schedule), int(max_prompt),
-                     int(chunk), b.ctypes.data_as(C.POINTER(C.c_int32)))
+                     int(chunk), int(value_bits), b.ctypes.data_as(C.POINTER(C.c_int32)))
     cfg._keep = b          # keep the budgets array alive with the struct
     return cfg
 
@@ -222,10 +222,11 @@ class Cache:
 
     def __init__(self, batch, n_q_heads, n_kv_heads, head_dim, n_bits, kv_dtype, budgets, R,
                  prefill_policy=HKV_PREFILL_STREAM, decode_schedule=HKV_DECODE_FUSED, max_prompt=0,
-                 chunk=0, stream=None):
+                 chunk=0, stream=None, value_bits=0):
         import torch
         self.cfg = make_config(batch, n_q_heads, n_kv_heads, head_dim, n_bits, kv_dtype, budgets,
-                               prefill_policy, decode_schedule, max_prompt, chunk)
+                               prefill_policy, decode_schedule, max_prompt, chunk, value_bits)
+        self.value_bits = int(value_bits)
         self.B, self.Hq, self.Hkv, self.d, self.bits = batch, n_q_heads, n_kv_heads, head_dim, n_bits
         self.W = (n_bits + 31) // 32
         self.kv_dtype = kv_dtype
@@ -269,12 +270,21 @@ class Cache:
         import torch
         dt = kv_torch_dtype(self.kv_dtype)
         K = torch.empty((self.B, self.Hkv, self.Smax, self.d), dtype=dt, device="cuda")
-        V = torch.empty_like(K)
+        rows = self.B * self.Hkv * self.Smax
+        if self.value_bits == 8:
+            V = torch.empty(rows * (self.d + 4), dtype=torch.uint8, device="cuda")
+        else:
+            V = torch.empty_like(K)
         codes = torch.empty((self.B, self.Hkv, self.Smax, self.W), dtype=torch.int32, device="cuda")
         tok = torch.empty((self.B, self.Hkv, self.Smax), dtype=torch.int32, device="cuda")
         st = torch.empty((self.B, self.Hkv, 2), dtype=torch.int32, device="cuda")
         hkv_get_state(self.h, K, V, codes, tok, st, stream)
-        return {"K": K, "V": V, "codes": codes, "tok": tok, "state": st}
+        out = {"K": K, "V": V, "codes": codes, "tok": tok, "state": st}
+        if self.value_bits == 8:
+            # int8 codes [B][Hkv][Smax][d], then fp32 scales [B][Hkv][Smax]
+            out["Vq"] = V[:rows * self.d].view(torch.int8).view(self.B, self.Hkv, self.Smax, self.d)
+            out["Vs"] = V[rows * self.d:].view(torch.float32).view(self.B, self.Hkv, self.Smax)
+        return out
 
     def set_state(self, s, stream=None):
         hkv_set_state(self.h, s["K"], s["V"], s["codes"], s["tok"], s["state"], stream)

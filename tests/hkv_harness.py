@@ -60,7 +60,7 @@ def kv_bytes_equal(gpu_rows: np.ndarray, ref_rows_f64: np.ndarray, kv_dtype: str
 
 def run_case(shape: Shape, steps: int, schedule: int = 0, policy: int = 0, chunk: int = 0,
              heads: Optional[Sequence[Tuple[int, int]]] = None, seed: Optional[int] = None,
-             check_every: int = 1, stats: Optional[dict] = None):
+             check_every: int = 1, stats: Optional[dict] = None, value_bits: int = 0):
     """Prefill + `steps` decode steps on the GPU, replayed on the oracle for `heads`
     (all heads if None).  Raises AssertionError on any parity failure."""
     import torch
@@ -74,10 +74,11 @@ def run_case(shape: Shape, steps: int, schedule: int = 0, policy: int = 0, chunk
     kvd = hkv.HKV_BF16 if shape.kv_dtype == "bf16" else hkv.HKV_F32
     n_max = P.n_max
     log(f"[{shape.name}] B={B} Hq={Hq} Hkv={Hkv} d={d} b={bits} N<={n_max} S<={P.budgets.max()} "
-        f"steps={steps} schedule={schedule} policy={policy} chunk={chunk} (data {time.time()-t0:.1f}s)")
+        f"steps={steps} schedule={schedule} policy={policy} chunk={chunk} value_bits={value_bits} "
+        f"(data {time.time()-t0:.1f}s)")
 
     cache = hkv.Cache(B, Hq, Hkv, d, bits, kvd, P.budgets, P.R, prefill_policy=policy,
-                      decode_schedule=schedule, max_prompt=n_max, chunk=chunk)
+                      decode_schedule=schedule, max_prompt=n_max, chunk=chunk, value_bits=value_bits)
     Kt, Vt = hkv.to_device(P.K), hkv.to_device(P.V)
     query = policy == oracle.QUERY
     Qp = datagen.prompt_queries(shape, seed) if query else None
@@ -89,7 +90,7 @@ def run_case(shape: Shape, steps: int, schedule: int = 0, policy: int = 0, chunk
     del Kt, Vt, Qt
 
     sel = list(heads) if heads is not None else [(b, h) for b in range(B) for h in range(Hkv)]
-    orc = oracle.OracleCache(P.R, P.budgets, Hq, Hkv, heads=sel)
+    orc = oracle.OracleCache(P.R, P.budgets, Hq, Hkv, heads=sel, value_bits=value_bits)
     flagged = 0
     for (b, h) in sel:
         n = int(P.prompt_lens[b])
@@ -139,7 +140,12 @@ def compare_state(cache, orc, sel, shape: Shape, when: str):
     tok = hkv.to_numpy(st["tok"])
     codes = words_u32(st["codes"])
     hs = hkv.to_numpy(st["state"])
-    K = hkv.to_numpy(st["K"]); V = hkv.to_numpy(st["V"])
+    K = hkv.to_numpy(st["K"])
+    vq = getattr(cache, "value_bits", 0) == 8
+    if vq:
+        Vq = st["Vq"].cpu().numpy(); Vs = st["Vs"].cpu().numpy()
+    else:
+        V = hkv.to_numpy(st["V"])
     for (b, h) in sel:
         o = orc.heads[(b, h)].state()
         S = orc.heads[(b, h)].budget
@@ -151,4 +157,10 @@ def compare_state(cache, orc, sel, shape: Shape, when: str):
         np.testing.assert_array_equal(codes[b, h, :n], o["code"][:n],
                                       err_msg=f"{when} b={b} h={h}: code table")
         assert kv_bytes_equal(K[b, h, :n], o["K"][:n], shape.kv_dtype), f"{when} b={b} h={h}: K rows"
-        assert kv_bytes_equal(V[b, h, :n], o["V"][:n], shape.kv_dtype), f"{when} b={b} h={h}: V rows"
+        if vq:
+            oq, osc = orc.heads[(b, h)].value_codes()
+            np.testing.assert_array_equal(Vq[b, h, :n], oq[:n], err_msg=f"{when} b={b} h={h}: value codes")
+            np.testing.assert_array_equal(Vs[b, h, :n].view(np.uint32), osc[:n].view(np.uint32),
+                                          err_msg=f"{when} b={b} h={h}: value scales")
+        else:
+            assert kv_bytes_equal(V[b, h, :n], o["V"][:n], shape.kv_dtype), f"{when} b={b} h={h}: V rows"

@@ -64,6 +64,9 @@ def test_named_shapes_validate(hkv):
     (dict(budgets=[40000]), "UNSUPPORTED"),               # 160 KB code table > on-chip table
     (dict(kv_dtype=7), "UNSUPPORTED"),
     (dict(prefill_policy=3), "UNSUPPORTED"),
+    (dict(value_bits=4), "UNSUPPORTED"),
+    (dict(value_bits=8, kv_dtype=0), "UNSUPPORTED"),        # int8 values need bf16 keys
+    (dict(value_bits=8, decode_schedule=1), "UNSUPPORTED"), # and the fused schedule
     (dict(budgets=[40000], prefill_policy=2), "UNSUPPORTED"),   # QUERY keeps its table on chip too
     (dict(chunk=100), "UNSUPPORTED"),
     (dict(chunk=32), "UNSUPPORTED"),
@@ -140,3 +143,10 @@ def test_status_strings(hkv):
     assert hkv.status_str(0) == "HKV_OK"
     assert hkv.status_str(3) == "HKV_ERR_STATE"
     assert hkv.status_str(99) == "HKV_UNKNOWN_STATUS"
+
+
+def test_int8_values_shrink_the_workspace(hkv):
+    full = hkv.hkv_workspace_bytes(_cfg(hkv))
+    v8 = hkv.hkv_workspace_bytes(_cfg(hkv, value_bits=8))
+    # V: 8 heads x 4096 slots x 128 values go from 2 bytes to 1 byte (+ a 4-byte scale per slot)
+    assert full - v8 >= 8 * 4096 * (128 - 4) - 4096

@@ -76,6 +76,37 @@ def test_query_prefill_full_llama3_8b_layer():
     run_case(C.LLAMA8B, 2, schedule=FUSED, policy=QUERY, heads=[(0, 0), (0, 3), (0, 7)], check_every=0)
 
 
+INT8_VALUES = {
+    "llama8b_small": (C.LLAMA8B.scaled(prompt=3000, budget=1500), 12, 0),
+    "ragged_small": (C.RAGGED.scaled(batch=4, prompt_range=(600, 1800)), 6, 0),
+    "llama70b_small": (C.LLAMA70B.scaled(batch=2, prompt=2500, budget=1200), 6, 0),
+    "d64_bf16_g2": (SMALL["d64_bf16_g2"][0], 8, 128),
+    "g16_b16": (SMALL["g16_b16"][0], 6, 0),
+    "not_full": (C.LLAMA8B.scaled(prompt=700, budget=1000), 8, 0),
+    "fill_then_evict": (C.LLAMA8B.scaled(prompt=990, budget=1000), 16, 0),
+    "empty_prompt": (C.TINY.scaled(prompt=0, budget=8, kv_dtype="bf16"), 10, 64),
+}
+
+
+@pytest.mark.parametrize("name", list(INT8_VALUES))
+def test_int8_values_small(name):
+    """Values kept as int8 codes with per-row scales: codes and scales bit-exact,
+    evictions exact, attention within tolerance of the oracle over code * scale."""
+    from hkv_harness import run_case
+    shape, steps, chunk = INT8_VALUES[name]
+    run_case(shape, steps, schedule=FUSED, policy=STREAM, chunk=chunk, value_bits=8)
+
+
+def test_int8_values_query_prefill():
+    from hkv_harness import run_case
+    run_case(C.LLAMA8B.scaled(prompt=2500, budget=1200), 4, schedule=FUSED, policy=QUERY, value_bits=8)
+
+
+def test_int8_values_full_long_128k():
+    from hkv_harness import run_case
+    run_case(C.LONG128K, 3, schedule=FUSED, policy=STREAM, heads=[(0, 2)], check_every=0, value_bits=8)
+
+
 def test_scores_and_encoder():
     """hkv_debug_scores and hkv_encode against the oracle."""
     import torch
