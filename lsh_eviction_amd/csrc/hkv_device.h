@@ -44,14 +44,6 @@ struct Vec16<float> {
     }
 };
 
-// Streaming 16-byte load: the non-temporal hint keeps rows that are read once
-// per step from displacing reusable lines in the caches.
-__device__ __forceinline__ uint4 ld_stream(const void* p)
-{
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    return make_uint4(w.x, w.y, w.z, w.w);
-}
 
 // code of `BITS` bits held in the smallest unsigned type
 template <int BITS>
@@ -139,39 +131,6 @@ __device__ __forceinline__ int cand_slot(unsigned long long key)
     return (int)(0xFFFFFFFFu - (unsigned)(key & 0xFFFFFFFFull));
 }
 
-// Stages 1-2 of the method for `nvec` rows of X (row stride D): lane j of a
-// row's bit-lanes projects the row onto column j of R in fp32 (ascending
-// fused multiply-adds), the wave ballot of (y > 0) packs the signs, and the
-// first bit-lane of every row hands its code to store(row, code).  Called by
-// whole blocks; each wave handles 64 / BITS rows per pass.
-template <int D, int BITS, typename XT, typename Store>
-__device__ __forceinline__ void encode_rows(const XT* __restrict__ X, int nvec,
-                                            const float* __restrict__ R, Store&& store)
-{
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int nwaves = blockDim.x >> 6;
-    constexpr int VPW = 64 / BITS;
-    const int j = lane % BITS;
-    for (int v0 = wave * VPW; v0 < nvec; v0 += nwaves * VPW) {
-        const int v = v0 + lane / BITS;
-        float y = 0.f;
-        if (v < nvec) {
-            const XT* x = X + (size_t)v * D;
-#pragma unroll 16
-            for (int i = 0; i < D; ++i) y = fmaf(to_f32(x[i]), R[i * BITS + j], y);
-        }
-        const unsigned long long m = __ballot(y > 0.f);
-        if (j == 0 && v < nvec) {
-            unsigned long long cde;
-            if constexpr (BITS == 64)
-                cde = m;
-            else
-                cde = (m >> ((lane / BITS) * BITS)) & ((1ull << BITS) - 1ull);
-            store(v, cde);
-        }
-    }
-}
 
 // A code as W little-endian uint32 words.
 __device__ __forceinline__ void store_words(uint32_t* dst, int W, unsigned long long code)

@@ -8,26 +8,25 @@
 //
 // Two schedules of the same step:
 //
-//   FUSED (two launches).  k_fused_attend: every block owns a chunk of slots
-//   of one (sequence, KV head).  It encodes the group's queries (matrix
-//   cores), finds its chunk's candidate (highest GQA score, lowest slot on
-//   ties), folds the candidate into the head's eviction key with a 64-bit
-//   atomic max, and accumulates softmax partials over its chunk with that
-//   candidate held out.  k_fused_merge: one block per query head takes the
-//   winner from the eviction key (the global argmax with lowest-index ties is
-//   always its own chunk's candidate), adds back the held-out candidates of
-//   the other chunks and the new token, merges by log-sum-exp, and the first
-//   query head of the group writes the new token into the winner's slot.  The
-//   result equals "evict, write, then attend" with every K/V byte read once
-//   and no grid-wide fence inside a kernel.
+//   FUSED (one launch).  Every block owns a chunk of slots of one (sequence,
+//   KV head).  It encodes the group's queries and the new key on the matrix
+//   cores, finds its chunk's candidate (highest GQA score, lowest slot on
+//   ties), folds it into the head's eviction key with a 64-bit atomic max,
+//   and accumulates softmax partials over its chunk with that candidate held
+//   out.  It then publishes its partial with write-through stores and takes a
+//   ticket; the head's last block reads the winner from the eviction key
+//   (the global argmax with lowest-index ties is always its own chunk's
+//   candidate), adds back the held-out candidates of the other chunks and the
+//   new token, merges by log-sum-exp and writes the new token into the
+//   winner's slot.  The result equals "evict, write, then attend" with every
+//   K/V byte read once and no grid-wide barrier or L2-wide fence.
 //
 //   SPLIT (five launches): lsh_encode, hamming_argmax, evict_write, split-K
 //   attention, LSE merge.
 //
-// Eviction keys are double-buffered by the parity of the step's token
-// position: the step at position t folds into ekey[t & 1] and its merge
-// clears ekey[(t + 1) & 1] for the next step, so no block ever clears a key
-// another block of the same step may still read.
+// The step at token position t folds its candidates into ekey[t & 1]; the
+// reader of that key (the head's last block, or evict_write) clears it, so
+// the next step starts from a cleared key without a launch of its own.
 #include <type_traits>
 
 #include "hkv_consts.h"
@@ -50,14 +49,6 @@ __device__ __forceinline__ float qscale2()
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// (m, l) <- log-sum-exp union of (m, l) and (mo, lo), base 2.
-__device__ __forceinline__ void lse_add(float& m, float& l, float mo, float lo)
-{
-    const float mx = fmaxf(m, mo);
-    if (mx == -INFINITY) return;
-    l = l * exp2_fast(m - mx) + lo * exp2_fast(mo - mx);
-    m = mx;
-}
 
 // ---------------------------------------------------------------------------
 // stages 1-2 on the matrix cores
@@ -842,7 +833,7 @@ __device__ __forceinline__ void own_stores_complete()
 
 // Loads of records other blocks wrote through to memory, with the cache
 // policy of an agent-scope load (sc1: a line this XCD's L2 may hold stale is
-// fetched again), 16, 8 or 4 bytes at byte offset `off` of a buffer resource.
+// fetched again), 16 bytes at byte offset `off` of a buffer resource.
 // Out-of-range offsets read zero.
 constexpr int kCpolSC1 = 16;
 constexpr int kRsrcWord3 = 0x00020000;   // 32-bit data format, no swizzle
@@ -858,19 +849,6 @@ __device__ __forceinline__ float4 ld_sc1_16(__amdgpu_buffer_rsrc_t rs, int off)
     float4 f;
     __builtin_memcpy(&f, &v, 16);
     return f;
-}
-
-__device__ __forceinline__ float2 ld_sc1_8(__amdgpu_buffer_rsrc_t rs, int off)
-{
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kCpolSC1);
-    float2 f;
-    __builtin_memcpy(&f, &v, 8);
-    return f;
-}
-
-__device__ __forceinline__ float ld_sc1_4(__amdgpu_buffer_rsrc_t rs, int off)
-{
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, kCpolSC1));
 }
 
 // Write-through stores with the same policy (the store side of the hand-off).

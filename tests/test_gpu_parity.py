@@ -137,19 +137,20 @@ def test_scores_and_encoder():
     cache.close()
 
 
-def test_snapshot_restore_continues_identically():
+@pytest.mark.parametrize("value_bits", [0, 8])
+def test_snapshot_restore_continues_identically(value_bits):
     import torch
     from lsh_eviction_amd import datagen, hkv
     shape = C.LLAMA8B.scaled(prompt=2000, budget=900)
     wl = datagen.workload(shape, steps=12)
     P, D = wl["prompt"], wl["decode"]
-    a = hkv.Cache(1, 32, 8, 128, 32, hkv.HKV_BF16, P.budgets, P.R, max_prompt=P.n_max)
+    a = hkv.Cache(1, 32, 8, 128, 32, hkv.HKV_BF16, P.budgets, P.R, max_prompt=P.n_max, value_bits=value_bits)
     a.prefill(hkv.to_device(P.K), hkv.to_device(P.V), P.prompt_lens)
     for s in range(5):
         a.decode_step(hkv.to_device(D.q[s]), hkv.to_device(D.k[s]), hkv.to_device(D.v[s]))
     snap = a.get_state()
     snap = {k: v.clone() for k, v in snap.items()}
-    b = hkv.Cache(1, 32, 8, 128, 32, hkv.HKV_BF16, P.budgets, P.R, max_prompt=P.n_max)
+    b = hkv.Cache(1, 32, 8, 128, 32, hkv.HKV_BF16, P.budgets, P.R, max_prompt=P.n_max, value_bits=value_bits)
     b.set_state(snap)
     for s in range(5, 12):
         args = (hkv.to_device(D.q[s]), hkv.to_device(D.k[s]), hkv.to_device(D.v[s]))
@@ -180,7 +181,8 @@ def test_fused_equals_split_bitwise_evictions():
         assert torch.allclose(o1, o2, rtol=1e-4, atol=1e-5)
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("value_bits", [0, 8])
+def test_graph_replay_matches_eager(value_bits):
     """A captured decode step replayed several times equals the same steps run eagerly."""
     import torch
     from lsh_eviction_amd import datagen, hkv
@@ -188,7 +190,7 @@ def test_graph_replay_matches_eager():
     wl = datagen.workload(shape, steps=6)
     P, D = wl["prompt"], wl["decode"]
     q, k, v = (hkv.to_device(D.q[0]), hkv.to_device(D.k[0]), hkv.to_device(D.v[0]))
-    caches = [hkv.Cache(1, 32, 8, 128, 32, hkv.HKV_BF16, P.budgets, P.R, max_prompt=P.n_max)
+    caches = [hkv.Cache(1, 32, 8, 128, 32, hkv.HKV_BF16, P.budgets, P.R, max_prompt=P.n_max, value_bits=value_bits)
               for _ in range(2)]
     for c in caches:
         c.prefill(hkv.to_device(P.K), hkv.to_device(P.V), P.prompt_lens)
