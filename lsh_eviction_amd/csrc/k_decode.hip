@@ -722,6 +722,44 @@ __device__ __forceinline__ void lse_add4(float& m, float& l, float4& a, float mo
     m = mx;
 }
 
+// The lane's (m, l, a) joined with those of lane ^ X (X = 16 or 32), by the
+// lane-swap instructions of gfx950 (VALU, no LDS).  A swap of a register with
+// itself hands each lane its own value and its partner's, in an order that
+// depends on the lane; the join is symmetric, so it takes the two as given.
+template <int X>
+__device__ __forceinline__ float2 swap_pair(float v)
+{
+    const unsigned u = __float_as_uint(v);
+    if constexpr (X == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    } else {
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+}
+
+template <int X>
+__device__ __forceinline__ void lse_join_swap(float& m, float& l, float4& a)
+{
+    const float2 m2 = swap_pair<X>(m), l2 = swap_pair<X>(l);
+    const float2 x2 = swap_pair<X>(a.x), y2 = swap_pair<X>(a.y), z2 = swap_pair<X>(a.z), w2 = swap_pair<X>(a.w);
+    m = m2.x;
+    l = l2.x;
+    a = make_float4(x2.x, y2.x, z2.x, w2.x);
+    lse_add4(m, l, a, m2.y, l2.y, make_float4(x2.y, y2.y, z2.y, w2.y));
+}
+
+// Sum over aligned groups of n adjacent lanes, n in {1, 2, 4, 8} and uniform
+// over the block; every lane of a group ends with the group's sum.
+__device__ __forceinline__ float lane_group_sum(float x, int n)
+{
+    if (n >= 2) x += dpp_f<kDppXor1>(x);
+    if (n >= 4) x += dpp_f<kDppXor2>(x);
+    if (n >= 8) x += dpp_f<kDppHalfMirror>(x);
+    return x;
+}
+
 constexpr int kMergeThreads = 1024;
 
 template <int D>
@@ -964,13 +1002,13 @@ __device__ __forceinline__ int merge_splits(const MergeArgs& a, int e, float4* s
     return e;
 }
 
-// Shared memory of the last block's merge: one (max, sum, 4 outputs) per
-// wave, head and 4-element column, and the (max, sum, logit) records of the
+// Shared memory of the last block's merge: one (max, sum) per head and wave
+// and 4 outputs per wave, head and 4-element column, and the (max, sum, logit) records of the
 // batch being folded.
 template <int D, int GM>
 struct MergeBlockSmem {
-    float m[kWaves][GM];
-    float l[kWaves][GM];
+    float m[GM][kWaves];
+    float l[GM][kWaves];
     float4 a[kWaves][GM][D / 4];
     float4 sc[kThreads];
 };
@@ -1206,38 +1244,62 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     else
         e = merge_splits<D, GM, JBMAX>(ma, e, u.mg.sc, Mt, Lt, At);
     MergeBlockSmem<D, GM>& mg = u.mg;
-    // lanes of a wave that share c4 (lane % TPR) combine, then one entry per wave
+    // the rows of a wave (its lanes that share c4) join, then one entry per wave
+    static_assert(TPR == 16 || TPR == 32, "rows per wave");
 #pragma unroll
-    for (int off = TPR; off < 64; off <<= 1) {
-#pragma unroll
-        for (int g = 0; g < GM; ++g) {
-            const float mo = __shfl_xor(Mt[g], off), lo = __shfl_xor(Lt[g], off);
-            const float4 ao = make_float4(__shfl_xor(At[g].x, off), __shfl_xor(At[g].y, off),
-                                          __shfl_xor(At[g].z, off), __shfl_xor(At[g].w, off));
-            lse_add4(Mt[g], Lt[g], At[g], mo, lo, ao);
+    for (int g = 0; g < GM; ++g) {
+        if (g < G) {
+            if constexpr (TPR == 16) lse_join_swap<16>(Mt[g], Lt[g], At[g]);
+            lse_join_swap<32>(Mt[g], Lt[g], At[g]);
         }
     }
-    __syncthreads();   // the attention's shared memory is free from here on
+    // merge_splits' barriers already ordered the attention's last use of this
+    // memory before these writes, and its s_sc is a separate member
     if (lane < TPR) {
 #pragma unroll
         for (int g = 0; g < GM; ++g) {
-            mg.a[wave][g][c4] = At[g];
-            if (c4 == 0) {
-                mg.m[wave][g] = Mt[g];
-                mg.l[wave][g] = Lt[g];
+            if (g < G) {
+                mg.a[wave][g][c4] = At[g];
+                if (c4 == 0) {
+                    mg.m[g][wave] = Mt[g];
+                    mg.l[g][wave] = Lt[g];
+                }
             }
         }
     }
     __syncthreads();
-    for (int idx = tid; idx < G * TPR; idx += kThreads) {
-        const int g = idx / TPR, cc = idx % TPR;
-        float M = s_nlg[g], L = 1.f;
-        float4 A = VQ ? *reinterpret_cast<const float4*>(&s_vdq[VQ ? 4 * cc : 0]) : load4_f32(s_vn + 4 * cc);
+    // Output float4 (head g, columns 4 cc .. 4 cc + 3) is summed by Q adjacent
+    // lanes, lane k taking waves k, k + Q, ..., every entry scaled to the
+    // head's largest max M (the new token's logit included), so each entry
+    // costs one exp2 and the lanes' sums add plainly.
+    const int nout = G * TPR;
+    int qsh = 0;
+    while ((2 << qsh) <= kWaves && (nout << (qsh + 1)) <= kThreads) ++qsh;
+    const int Q = 1 << qsh, k = tid & (Q - 1);
+    const int oi = min(tid >> qsh, nout - 1);
+    const int og = oi / TPR, cc = oi % TPR;
+    float M = s_nlg[og];
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) lse_add4(M, L, A, mg.m[w][g], mg.l[w][g], mg.a[w][g][cc]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mg.m[og][w]);
+    float L = 0.f;
+    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int w = k; w < kWaves; w += Q) {
+        const float s = exp2_fast(mg.m[og][w] - M);   // 0 for a wave that holds no split
+        const float4 a = mg.a[w][og][cc];
+        L = fmaf(mg.l[og][w], s, L);
+        A = make_float4(fmaf(a.x, s, A.x), fmaf(a.y, s, A.y), fmaf(a.z, s, A.z), fmaf(a.w, s, A.w));
+    }
+    L = lane_group_sum(L, Q);
+    A = make_float4(lane_group_sum(A.x, Q), lane_group_sum(A.y, Q), lane_group_sum(A.z, Q),
+                    lane_group_sum(A.w, Q));
+    if (k == 0 && (tid >> qsh) < nout) {
+        const float sn = exp2_fast(s_nlg[og] - M);
+        const float4 vn = VQ ? *reinterpret_cast<const float4*>(&s_vdq[VQ ? 4 * cc : 0]) : load4_f32(s_vn + 4 * cc);
+        L += sn;
         const float inv = 1.f / L;
-        reinterpret_cast<float4*>(out + (size_t)(hq0 + g) * D)[cc] = make_float4(A.x * inv, A.y * inv, A.z * inv,
-                                                                               A.w * inv);
+        reinterpret_cast<float4*>(out + (size_t)(hq0 + og) * D)[cc] =
+            make_float4(fmaf(vn.x, sn, A.x) * inv, fmaf(vn.y, sn, A.y) * inv, fmaf(vn.z, sn, A.z) * inv,
+                        fmaf(vn.w, sn, A.w) * inv);
     }
 
     // stage 5: the new token takes slot e
