@@ -25,6 +25,8 @@ SOURCES = [os.path.join(_HERE, "hkv_oracle.c")]
 STREAM = 0
 TRUNCATE = 1
 QUERY = 2
+CHUNK = 3
+DEFAULT_CHUNK_TOKENS = 10
 
 
 def build(verbose: bool = False) -> str:
@@ -62,6 +64,8 @@ def lib():
         L.orc_get_value_codes.argtypes = [P, P, P]
         L.orc_set_value_codes.argtypes = [P, P, P]
         L.orc_prefill_query.restype = C.c_int
+        L.orc_prefill_chunks.restype = C.c_int
+        L.orc_prefill_chunks.argtypes = [P, C.c_int, C.c_int] + [P] * 7
         L.orc_decode_step.restype = C.c_int
         L.orc_decode_step.argtypes = [P] * 3 + [P] * 8 + [P]
         L.orc_scores.argtypes = [P, P, P]
@@ -157,6 +161,30 @@ class OracleHead:
         if rc != 0:
             raise RuntimeError("orc_prefill_query failed (cache not empty?)")
 
+    def prefill_chunks(self, K: np.ndarray, V: np.ndarray, qobs: Optional[np.ndarray], chunk: int,
+                       inj_codes: Optional[np.ndarray] = None, inj_qcodes: Optional[np.ndarray] = None,
+                       reuse: Optional[np.ndarray] = None) -> np.ndarray:
+        """CHUNK rule: whole chunks of `chunk` prompt tokens kept or evicted, scored
+        against the observation queries qobs[group][d].  Returns the kept chunk
+        indices, [ceil(budget / chunk)] int32, -1 after the last."""
+        K, V = _f64(K), _f64(V)
+        n = K.shape[0]
+        q = None if qobs is None else _f64(qobs)
+        if q is not None:
+            assert q.shape == (self.group, self.d)
+        inj, injq = _u32(inj_codes), _u32(inj_qcodes)
+        if inj is not None:
+            assert inj.shape == (n, self.W)
+        if injq is not None:
+            assert injq.shape == (self.group, self.W)
+        ru = None if reuse is None else np.ascontiguousarray(reuse, np.int32)
+        kept = np.empty((self.budget + chunk - 1) // chunk, np.int32)
+        rc = lib().orc_prefill_chunks(self._h, n, int(chunk), _p(K), _p(V), _p(q), _p(inj), _p(injq), _p(ru),
+                                      _p(kept))
+        if rc < 0:
+            raise RuntimeError("orc_prefill_chunks failed (cache not empty?)")
+        return kept
+
     def decode_step(self, q, k, v, inj_qcodes=None, inj_kcode=None):
         q, k, v = _f64(q).reshape(self.group, self.d), _f64(k), _f64(v)
         out = np.zeros((self.group, self.d), np.float64)
@@ -233,20 +261,30 @@ class OracleCache:
         self.sel = heads if heads is not None else [(b, h) for b in range(self.B) for h in range(self.Hkv)]
         self.heads = {(b, h): OracleHead(R, int(budgets[b]), self.G, value_bits) for (b, h) in self.sel}
 
-    def prefill(self, K, V, prompt_lens, policy=STREAM, inj_codes=None, Q=None, inj_qcodes=None):
+    def prefill(self, K, V, prompt_lens, policy=STREAM, inj_codes=None, Q=None, inj_qcodes=None,
+                chunk=DEFAULT_CHUNK_TOKENS, reuse=None):
         """K, V [B][Hkv][n_max][d]; with policy QUERY also Q [B][Hq][n_max][d] (fp32) and
-        optionally inj_qcodes [B][Hq][n_max][W]."""
+        optionally inj_qcodes [B][Hq][n_max][W]; with policy CHUNK, Q [B][Hq][d] are the
+        observation queries, inj_qcodes [B][Hq][W] and reuse [B][Hkv][k] kept lists.
+        Under CHUNK returns the kept lists {(b, h): [ceil(S_b / chunk)] int32}."""
         G = self.G
+        kept = {}
         for (b, h), o in self.heads.items():
             n = int(prompt_lens[b])
             inj = None if inj_codes is None else inj_codes[b, h, :n]
-            if policy == QUERY:
+            if policy == CHUNK:
+                q = None if Q is None else widen(Q[b, h * G:(h + 1) * G])
+                iq = None if inj_qcodes is None else inj_qcodes[b, h * G:(h + 1) * G]
+                ru = None if reuse is None else reuse[b, h]
+                kept[(b, h)] = o.prefill_chunks(widen(K[b, h, :n]), widen(V[b, h, :n]), q, chunk, inj, iq, ru)
+            elif policy == QUERY:
                 q = widen(Q[b, h * G:(h + 1) * G, :n]).transpose(1, 0, 2)
                 iq = None if inj_qcodes is None else np.ascontiguousarray(
                     inj_qcodes[b, h * G:(h + 1) * G, :n].transpose(1, 0, 2))
                 o.prefill_query(widen(K[b, h, :n]), widen(V[b, h, :n]), q, inj, iq)
             else:
                 o.prefill(widen(K[b, h, :n]), widen(V[b, h, :n]), policy, inj)
+        return kept if policy == CHUNK else None
 
     def decode_step(self, q, k, v, inj_qcodes=None, inj_kcodes=None):
         """q [B][Hq][d] fp32; k, v [B][Hkv][d]; returns per-head dicts keyed (b, h)."""

@@ -267,6 +267,92 @@ int orc_prefill_query(orc_head* h, int n, const double* K, const double* V, cons
     return 0;
 }
 
+/* READING of chunk-granular eviction (the ChunkKV summary page: tokens are
+ * kept or dropped in groups of consecutive tokens rather than one by one, a
+ * chunk of about 10 tokens works best, and the indices kept at one layer can
+ * be reused at other layers; the page scores chunks by attention, which the
+ * method replaces by its Hamming proxy).  The prompt is cut into chunks of
+ * `chunk` consecutive tokens, the last one possibly shorter.  With n <= budget
+ * every chunk is kept.  Otherwise floor(budget / chunk) chunks are kept: the
+ * decode rule is applied to chunks, evicting one at a time the remaining
+ * chunk whose key codes are farthest in summed Hamming distance (over its
+ * tokens and the group's observation query codes) from the observation
+ * queries, ties to the lowest chunk, until that many remain.  The kept chunks
+ * then fill slots 0, 1, ... in token order.
+ *
+ * qobs [group][d]: the observation queries (those of the token decoding
+ * starts from).  inj_codes [n][W] and inj_qcodes [group][W] (may be NULL)
+ * replace E's output.  reuse (may be NULL): the first k entries are the chunk
+ * indices to keep instead of scoring (k = the count above); entries outside
+ * [0, number of chunks) are ignored and repeats count once.  kept (may be
+ * NULL): out, [ceil(budget / chunk)] kept chunk indices in ascending order,
+ * -1 after the last.  Returns the number of kept chunks, or -1 if the cache
+ * is not empty, n < 0 or chunk < 1. */
+int orc_prefill_chunks(orc_head* h, int n, int chunk, const double* K, const double* V, const double* qobs,
+                       const uint32_t* inj_codes, const uint32_t* inj_qcodes, const int32_t* reuse,
+                       int32_t* kept)
+{
+    if (h->n != 0 || n < 0 || chunk < 1) return -1;
+    const int W = h->words;
+    const int nch = (n + chunk - 1) / chunk;
+    const int k = n <= h->budget ? nch : h->budget / chunk;
+    uint32_t* codes = (uint32_t*)malloc(sizeof(uint32_t) * W * (n > 0 ? n : 1));
+    uint32_t* f = (uint32_t*)malloc(sizeof(uint32_t) * W);
+    char* keep = (char*)calloc(nch > 0 ? nch : 1, 1);
+    for (int t = 0; t < n; ++t) {
+        if (inj_codes)
+            memcpy(codes + (size_t)t * W, inj_codes + (size_t)t * W, sizeof(uint32_t) * W);
+        else
+            orc_encode(h, K + (size_t)t * h->d, codes + (size_t)t * W, f);
+    }
+    if (reuse) {
+        for (int j = 0; j < k; ++j)
+            if (reuse[j] >= 0 && reuse[j] < nch) keep[reuse[j]] = 1;
+    } else if (n <= h->budget) {
+        for (int i = 0; i < nch; ++i) keep[i] = 1;
+    } else {
+        uint32_t* qc = (uint32_t*)malloc(sizeof(uint32_t) * W * h->group);
+        if (inj_qcodes)
+            memcpy(qc, inj_qcodes, sizeof(uint32_t) * W * h->group);
+        else
+            for (int g = 0; g < h->group; ++g) orc_encode(h, qobs + (size_t)g * h->d, qc + (size_t)g * W, f);
+        int* score = (int*)malloc(sizeof(int) * nch);
+        for (int i = 0; i < nch; ++i) {
+            score[i] = 0;
+            for (int t = i * chunk; t < n && t < (i + 1) * chunk; ++t)
+                for (int g = 0; g < h->group; ++g)
+                    score[i] += hamming(qc + (size_t)g * W, codes + (size_t)t * W, W);
+            keep[i] = 1;
+        }
+        /* stage 4 on chunks, repeated: the farthest remaining chunk goes,
+         * the lowest of equals first */
+        for (int left = nch; left > k; --left) {
+            int best = -1, e = -1;
+            for (int i = 0; i < nch; ++i)
+                if (keep[i] && score[i] > best) { best = score[i]; e = i; }
+            keep[e] = 0;
+        }
+        free(score);
+        free(qc);
+    }
+    int slot = 0, j = 0;
+    for (int i = 0; i < nch; ++i) {
+        if (!keep[i]) continue;
+        if (kept) kept[j] = i;
+        ++j;
+        for (int t = i * chunk; t < n && t < (i + 1) * chunk; ++t, ++slot)
+            write_slot(h, slot, K + (size_t)t * h->d, V + (size_t)t * h->d, codes + (size_t)t * W, (int64_t)t);
+    }
+    if (kept)
+        for (int r = j; r < (h->budget + chunk - 1) / chunk; ++r) kept[r] = -1;
+    h->n = slot;
+    h->t = n;
+    free(codes);
+    free(f);
+    free(keep);
+    return j;
+}
+
 /* Attention over the occupied slots: softmax(q . K^T / sqrt(d)) V, with the
  * maximum logit subtracted before exponentiation. */
 void orc_attend(const orc_head* h, const double* q, double* out)

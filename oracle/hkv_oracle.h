@@ -34,7 +34,7 @@ extern "C" {
 
 typedef struct orc_head orc_head;
 
-enum { ORC_PREFILL_STREAM = 0, ORC_PREFILL_TRUNCATE = 1, ORC_PREFILL_QUERY = 2 };
+enum { ORC_PREFILL_STREAM = 0, ORC_PREFILL_TRUNCATE = 1, ORC_PREFILL_QUERY = 2, ORC_PREFILL_CHUNK = 3 };
 
 /* R: [d][n_bits] fp32 values widened to double; copied. NULL on bad args. */
 orc_head* orc_create(int d, int n_bits, int budget, int group, const double* R);
@@ -58,6 +58,21 @@ int orc_prefill(orc_head* h, int policy, int n, const double* K, const double* V
  * key and query codes.  Returns 0, or -1 if the cache is not empty or n < 0. */
 int orc_prefill_query(orc_head* h, int n, const double* K, const double* V, const double* Q,
                       const uint32_t* inj_codes, const uint32_t* inj_qcodes);
+
+/* P with chunk-granular eviction (a reading; see the .c file): the prompt
+ * is cut into chunks of `chunk` consecutive tokens; with n > budget only
+ * floor(budget / chunk) whole chunks stay, the others evicted one at a time
+ * by the decode rule applied to chunks (summed Hamming distance of a chunk's
+ * key codes to the observation query codes, ties to the lowest chunk); kept
+ * chunks fill slots 0, 1, ... in token order.  qobs [group][d];
+ * inj_codes [n][W], inj_qcodes [group][W], reuse [k] (kept chunks given
+ * instead of scored) may be NULL; kept (may be NULL) receives
+ * [ceil(budget / chunk)] kept chunk indices, ascending, -1 after the last.
+ * Returns the number of kept chunks, or -1 (cache not empty, n < 0,
+ * chunk < 1). */
+int orc_prefill_chunks(orc_head* h, int n, int chunk, const double* K, const double* V, const double* qobs,
+                       const uint32_t* inj_codes, const uint32_t* inj_qcodes, const int32_t* reuse,
+                       int32_t* kept);
 
 /* Value compression (a reading; see the .c file): bits = 8 stores every
  * value row as int8 codes with one fp32 scale (fp32 arithmetic: scale =

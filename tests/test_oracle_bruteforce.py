@@ -51,6 +51,25 @@ class Brute:
                 self._place([b], K[t], V[t], b)
         self.t = len(K)
 
+    def prefill_chunks(self, K, V, qobs, C):
+        """Chunk rule by sorting: the chunks come in order of (summed distance,
+        higher index first) and the first floor(S / C) of them stay."""
+        N = len(K)
+        nch = -(-N // C)
+        if N <= self.S:
+            keep = set(range(nch))
+        else:
+            qb = [self.bits(qg) for qg in qobs]
+            score = [sum(int(np.count_nonzero(q != self.bits(K[t]))) for t in range(i * C, min(N, (i + 1) * C))
+                         for q in qb) for i in range(nch)]
+            keep = set(sorted(range(nch), key=lambda i: (score[i], -i))[:self.S // C])
+        for i in sorted(keep):
+            for t in range(i * C, min(N, (i + 1) * C)):
+                self.slots.append({"tok": t, "k": K[t].copy(), "v": V[t].copy(), "bits": self.bits(K[t])})
+        self.t = N
+        kmax = -(-self.S // C)
+        return sorted(keep) + [-1] * (kmax - len(keep))
+
     def step(self, q, k, v):
         qb = [self.bits(qg) for qg in q]
         e = self._place(qb, k, v, self.bits(k))
@@ -158,3 +177,84 @@ def test_query_prefill_reduces_to_stream(oracle_mod):
     assert list(sa["tok"]) == list(sq["tok"])
     np.testing.assert_array_equal(sa["code"], sq["code"])
     np.testing.assert_array_equal(sa["K"], sq["K"])
+
+
+@pytest.mark.parametrize("d,b,S,N,G,C,seed", [
+    (8, 16, 10, 47, 1, 3, 41),      # ragged last chunk
+    (8, 16, 12, 60, 2, 4, 42),
+    (16, 32, 20, 99, 4, 10, 43),
+    (8, 16, 8, 30, 2, 1, 44),       # one token per chunk
+    (8, 64, 9, 40, 3, 5, 45),
+    (8, 16, 12, 9, 2, 4, 46),       # prompt shorter than the budget
+    (8, 16, 3, 20, 1, 4, 47),       # budget below one chunk: nothing stays
+    (4, 16, 16, 70, 2, 3, 48),      # d = 4 on 16 bits: many equal scores
+])
+def test_bruteforce_chunk_prefill(oracle_mod, d, b, S, N, G, C, seed):
+    """The CHUNK prefill rule against sorting in the brute-force model, then decode."""
+    rng = np.random.default_rng(seed)
+    R = rng.standard_normal((d, b)).astype(np.float32).astype(np.float64)
+    K = rng.standard_normal((N, d)); V = rng.standard_normal((N, d))
+    qobs = rng.standard_normal((G, d))
+    o = oracle_mod.OracleHead(R, S, G)
+    bf = Brute(R, S, G)
+    kept = o.prefill_chunks(K, V, qobs, C)
+    assert list(kept) == bf.prefill_chunks(K, V, qobs, C)
+    assert list(o.state()["tok"]) == bf.toks()
+    for _ in range(S // 2 + 4):      # fills the free slots, then evicts
+        q = rng.standard_normal((G, d)); k = rng.standard_normal(d); v = rng.standard_normal(d)
+        r = o.decode_step(q, k, v)
+        e, out = bf.step(q, k, v)
+        assert r["evicted"] == e
+        np.testing.assert_allclose(r["out"], out, rtol=1e-12, atol=1e-12)
+
+
+def test_chunk_prefill_invariants(oracle_mod):
+    """Whole chunks, token order, occupancy, and the eviction order by score."""
+    rng = np.random.default_rng(51)
+    d, b, S, N, G, C = 16, 16, 300, 1203, 4, 10
+    R = rng.standard_normal((d, b))
+    K = rng.standard_normal((N, d)); V = rng.standard_normal((N, d))
+    qobs = rng.standard_normal((G, d))
+    o = oracle_mod.OracleHead(R, S, G)
+    kept = [int(i) for i in o.prefill_chunks(K, V, qobs, C) if i >= 0]
+    nch = -(-N // C)
+    assert len(kept) == S // C and kept == sorted(set(kept))
+    st = o.state()
+    toks = [int(t) for t in st["tok"] if t >= 0]
+    assert toks == [t for i in kept for t in range(i * C, min(N, (i + 1) * C))]
+    assert st["n"] == len(toks) <= S
+    # scores recomputed from the oracle's own codes
+    codes, _ = o.encode(K)
+    qc, _ = o.encode(qobs)
+    pc = np.array([bin(int(x)).count("1") for x in range(1 << 16)])
+    dist = sum(pc[codes[:, 0] ^ qc[g, 0]] for g in range(G))
+    score = np.array([dist[i * C:(i + 1) * C].sum() for i in range(nch)])
+    ev = sorted(set(range(nch)) - set(kept))
+    assert score[kept].max() <= score[ev].min()
+    T = score[kept].max()
+    if score[ev].min() == T:       # at the threshold the lower indices went first
+        assert max(i for i in ev if score[i] == T) < min(i for i in kept if score[i] == T)
+
+
+def test_chunk_prefill_reuse(oracle_mod):
+    """The kept list of one layer, reused by another layer's cache, places the
+    same tokens there; repeats and out-of-range entries are ignored."""
+    rng = np.random.default_rng(61)
+    d, b, S, N, G, C = 16, 32, 40, 133, 2, 10
+    R = rng.standard_normal((d, b))
+    K1, V1 = rng.standard_normal((N, d)), rng.standard_normal((N, d))
+    K2, V2 = rng.standard_normal((N, d)), rng.standard_normal((N, d))
+    a = oracle_mod.OracleHead(R, S, G)
+    kept = a.prefill_chunks(K1, V1, rng.standard_normal((G, d)), C)
+    bb = oracle_mod.OracleHead(R, S, G)
+    kept2 = bb.prefill_chunks(K2, V2, None, C, reuse=kept)
+    assert list(kept2) == list(kept)
+    sa, sb = a.state(), bb.state()
+    assert list(sa["tok"]) == list(sb["tok"])
+    n = sb["n"]
+    np.testing.assert_array_equal(sb["K"][:n], K2[sa["tok"][:n]])
+    np.testing.assert_array_equal(sb["V"][:n], V2[sa["tok"][:n]])
+    odd = np.array([kept[1], kept[1], 999, -5], np.int32)
+    c = oracle_mod.OracleHead(R, S, G)
+    kept3 = c.prefill_chunks(K2, V2, None, C, reuse=odd)
+    assert list(kept3) == [kept[1]] + [-1] * (len(kept) - 1)

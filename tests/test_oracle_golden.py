@@ -22,11 +22,15 @@ def _cases():
         if tok[0] == "case":
             kv = dict(zip(tok[2::2], tok[3::2]))
             cur = {"name": tok[1], "budget": int(kv["budget"]), "group": int(kv["group"]),
-                   "policy": kv["policy"], "decode": []}
+                   "policy": kv["policy"], "chunk": int(kv.get("chunk", 0)), "decode": []}
         elif tok[0] == "prompt":
             cur["prompt"] = [int(x, 16) for x in tok[1:]]
         elif tok[0] == "pquery":
             cur["pquery"] = [[int(x, 16) for x in t.split(",")] for t in tok[1:]]
+        elif tok[0] == "qobs":
+            cur["qobs"] = [int(x, 16) for x in tok[1].split(",")]
+        elif tok[0] == "kept":
+            cur["kept"] = [int(x) for x in tok[1:]]
         elif tok[0] == "prefill_tok":
             cur["prefill_tok"] = [int(x) for x in tok[1:]]
         elif tok[0] == "decode":
@@ -49,6 +53,15 @@ def test_handworked(oracle_mod, case):
     if case["policy"] == "query":
         Q = np.stack([np.stack([_vec(c) for c in row]) for row in case["pquery"]])
         o.prefill_query(K, V, Q)
+    elif case["policy"] == "chunk":
+        qobs = np.stack([_vec(c) for c in case["qobs"]])
+        kept = o.prefill_chunks(K, V, qobs, case["chunk"])
+        assert list(kept) == case["kept"]
+        # the kept list, reused on a prompt with other keys, reproduces the placement
+        o2 = oracle_mod.OracleHead(R, case["budget"], case["group"])
+        kept2 = o2.prefill_chunks(-K, V, None, case["chunk"], reuse=kept)
+        assert list(kept2) == case["kept"]
+        assert list(o2.state()["tok"]) == case["prefill_tok"]
     else:
         pol = oracle_mod.STREAM if case["policy"] == "stream" else oracle_mod.TRUNCATE
         o.prefill(K, V, pol)
