@@ -282,9 +282,10 @@ int orc_prefill_query(orc_head* h, int n, const double* K, const double* V, cons
  *
  * qobs [group][d]: the observation queries (those of the token decoding
  * starts from).  inj_codes [n][W] and inj_qcodes [group][W] (may be NULL)
- * replace E's output.  reuse (may be NULL): the first k entries are the chunk
- * indices to keep instead of scoring (k = the count above); entries outside
- * [0, number of chunks) are ignored and repeats count once.  kept (may be
+ * replace E's output.  reuse (may be NULL): when n > budget, its first k
+ * entries are the chunk indices to keep instead of scoring (k = the count
+ * above); entries outside [0, number of chunks) are ignored and repeats count
+ * once.  A prompt that fits keeps every token whatever reuse says.  kept (may be
  * NULL): out, [ceil(budget / chunk)] kept chunk indices in ascending order,
  * -1 after the last.  Returns the number of kept chunks, or -1 if the cache
  * is not empty, n < 0 or chunk < 1. */
@@ -305,11 +306,11 @@ int orc_prefill_chunks(orc_head* h, int n, int chunk, const double* K, const dou
         else
             orc_encode(h, K + (size_t)t * h->d, codes + (size_t)t * W, f);
     }
-    if (reuse) {
+    if (n <= h->budget) {
+        for (int i = 0; i < nch; ++i) keep[i] = 1;
+    } else if (reuse) {
         for (int j = 0; j < k; ++j)
             if (reuse[j] >= 0 && reuse[j] < nch) keep[reuse[j]] = 1;
-    } else if (n <= h->budget) {
-        for (int i = 0; i < nch; ++i) keep[i] = 1;
     } else {
         uint32_t* qc = (uint32_t*)malloc(sizeof(uint32_t) * W * h->group);
         if (inj_qcodes)

@@ -66,7 +66,7 @@ int orc_prefill_query(orc_head* h, int n, const double* K, const double* V, cons
  * key codes to the observation query codes, ties to the lowest chunk); kept
  * chunks fill slots 0, 1, ... in token order.  qobs [group][d];
  * inj_codes [n][W], inj_qcodes [group][W], reuse [k] (kept chunks given
- * instead of scored) may be NULL; kept (may be NULL) receives
+ * instead of scored when n > budget) may be NULL; kept (may be NULL) receives
  * [ceil(budget / chunk)] kept chunk indices, ascending, -1 after the last.
  * Returns the number of kept chunks, or -1 (cache not empty, n < 0,
  * chunk < 1). */

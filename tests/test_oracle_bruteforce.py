@@ -258,3 +258,7 @@ def test_chunk_prefill_reuse(oracle_mod):
     c = oracle_mod.OracleHead(R, S, G)
     kept3 = c.prefill_chunks(K2, V2, None, C, reuse=odd)
     assert list(kept3) == [kept[1]] + [-1] * (len(kept) - 1)
+    # a prompt within the budget keeps every token whatever the list says
+    f = oracle_mod.OracleHead(R, N, G)
+    kf = f.prefill_chunks(K2, V2, None, C, reuse=np.array([3] + [-1] * 20, np.int32))
+    assert list(f.state()["tok"]) == list(range(N)) and list(kf) == list(range(-(-N // C)))
