@@ -141,7 +141,7 @@ def main():
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--value-bits", type=int, default=0, choices=[0, 8],
                     help="8: values kept as int8 codes with a per-row scale (a different workload)")
-    ap.add_argument("--prefill", default="stream", choices=["stream", "truncate", "query"],
+    ap.add_argument("--prefill", default="stream", choices=["stream", "truncate", "query", "chunk"],
                     help="prefill rule of the layer caches (timed per layer, not part of a step)")
     ap.add_argument("--layers", type=int, default=0, help="layer caches rotated (0 = enough to exceed the MALL twice)")
     ap.add_argument("--graph", action="store_true", help="replay the steps of one rotation as a HIP graph")
@@ -170,9 +170,10 @@ def main():
     n_max = int(n.max())
 
     caches, prefill_ms = [], []
+    kept = None      # chunk rule: layer 0 scores its chunks, later layers reuse its kept lists
     for layer in range(L):
         pol = {"stream": hkv.HKV_PREFILL_STREAM, "truncate": hkv.HKV_PREFILL_TRUNCATE,
-               "query": hkv.HKV_PREFILL_QUERY}[args.prefill]
+               "query": hkv.HKV_PREFILL_QUERY, "chunk": hkv.HKV_PREFILL_CHUNK}[args.prefill]
         c = hkv.Cache(shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.n_bits, kvd,
                       budgets, P.R, prefill_policy=pol, decode_schedule=sched, max_prompt=n_max, chunk=args.chunk,
                       value_bits=args.value_bits)
@@ -182,10 +183,16 @@ def main():
             gq = torch.Generator(device="cuda")
             gq.manual_seed(shape.index * 1000 + 500 + layer)
             Q = torch.randn((shape.batch, shape.n_q_heads, n_max, shape.head_dim), generator=gq, device="cuda")
+        elif args.prefill == "chunk" and kept is None:
+            gq = torch.Generator(device="cuda")
+            gq.manual_seed(shape.index * 1000 + 600)
+            Q = torch.randn((shape.batch, shape.n_q_heads, shape.head_dim), generator=gq, device="cuda")
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        c.prefill(K, V, n, Q=Q)
+        r = c.prefill(K, V, n, Q=Q, reuse=kept)
+        if args.prefill == "chunk" and kept is None:
+            kept = r
         e1.record()
         torch.cuda.synchronize()
         prefill_ms.append(e0.elapsed_time(e1))
@@ -308,6 +315,8 @@ def main():
         "frac_of_copy": round(achieved / copy_gbs, 4),
         "prefill_ms_per_layer": round(float(np.mean(prefill_ms)), 2),
         "prefill_rule": args.prefill,
+        **({"prefill_ms_scored_then_reused": [round(float(x), 2) for x in prefill_ms]}
+           if args.prefill == "chunk" else {}),
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu:

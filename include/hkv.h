@@ -32,7 +32,10 @@
  *     has no query); HKV_PREFILL_TRUNCATE keeps the first `budget` tokens;
  *     HKV_PREFILL_QUERY applies the decode rule itself to every prompt token
  *     past the budget, scored against the token's own group of query rows
- *     (the caller passes the prompt's queries to hkv_prefill_queries).
+ *     (the caller passes the prompt's queries to hkv_prefill_queries);
+ *     HKV_PREFILL_CHUNK keeps or evicts whole chunks of consecutive prompt
+ *     tokens (a reading of the ChunkKV summary page, with the method's
+ *     Hamming score in place of attention; hkv_prefill_chunks).
  *
  * Conventions for every call:
  *   - all device pointers are HIP device memory of the current device; `stream`
@@ -56,7 +59,7 @@
  *     kv dtype fp32 or bf16; 1 <= budget <= 2^22 per sequence (a prefill
  *     with HKV_PREFILL_STREAM or HKV_PREFILL_QUERY needs
  *     budget * ceil(b/8) <= 128 KiB, its code table lives in on-chip LDS);
- *     1 <= batch <= 4096.
+ *     1 <= batch <= 4096; 1 <= prefill chunk <= 32 tokens.
  */
 #ifndef HKV_H
 #define HKV_H
@@ -77,7 +80,8 @@ typedef enum {
 } hkv_status;
 
 enum { HKV_F32 = 0, HKV_BF16 = 1 };                        /* kv_dtype */
-enum { HKV_PREFILL_STREAM = 0, HKV_PREFILL_TRUNCATE = 1, HKV_PREFILL_QUERY = 2 };  /* prefill_policy */
+enum { HKV_PREFILL_STREAM = 0, HKV_PREFILL_TRUNCATE = 1, HKV_PREFILL_QUERY = 2, HKV_PREFILL_CHUNK = 3 };
+/* (prefill_policy) */
 /* decode_schedule: FUSED = one launch per step (score, hold-out attention,
  * merge, write); SPLIT = the separate kernels lsh_encode, hamming_argmax,
  * evict_write, split-K attention and LSE merge (five launches). */
@@ -102,6 +106,9 @@ typedef struct {
                                 half to even, clamped to +-127, in fp32; the
                                 cache holds code * scale).  8 needs kv_dtype
                                 HKV_BF16 and HKV_DECODE_FUSED */
+    int32_t prefill_chunk;   /* tokens per chunk under HKV_PREFILL_CHUNK: 0
+                                selects 10, else 1 .. 32; must be 0 under the
+                                other policies */
     const int32_t* budgets;  /* host [batch]: cache slots S_b of each sequence */
 } hkv_config;
 
@@ -129,7 +136,8 @@ hkv_status hkv_create(const hkv_config* cfg, const float* R_host, void* workspac
  * every prompt key (method stages 1-2; an MFMA projection), applies the
  * prefill policy, and leaves occupancy min(N_b, S_b) and next position N_b.
  * HKV_ERR_STATE if the cache is not empty; HKV_ERR_INVALID_ARG under
- * HKV_PREFILL_QUERY, which needs the queries (hkv_prefill_queries). */
+ * HKV_PREFILL_QUERY or HKV_PREFILL_CHUNK, which take their own entry points
+ * (hkv_prefill_queries, hkv_prefill_chunks). */
 hkv_status hkv_prefill(hkv_cache* c, const void* K, const void* V, const int32_t* prompt_lens,
                        int32_t n_max, void* stream);
 
@@ -143,6 +151,40 @@ hkv_status hkv_prefill(hkv_cache* c, const void* K, const void* V, const int32_t
  * slot) is evicted and token t's key, value and key code take it. */
 hkv_status hkv_prefill_queries(hkv_cache* c, const void* K, const void* V, const float* Q,
                                const int32_t* prompt_lens, int32_t n_max, void* stream);
+
+/* Prefill under HKV_PREFILL_CHUNK (a cache created with that policy; any other
+ * policy gives HKV_ERR_INVALID_ARG).  Reading of the ChunkKV summary page:
+ * prompt tokens are kept or dropped in chunks of C = prefill_chunk
+ * consecutive tokens (the last chunk of a prompt may be shorter), and the
+ * indices kept for one layer can be reused for other layers.  K, V,
+ * prompt_lens, n_max as in hkv_prefill.  With N_b <= S_b every token is kept.
+ * Otherwise k = floor(S_b / C) chunks stay.  Chunks are evicted one at a
+ * time by the decode rule applied to chunks (method stages 3-4): the chunk
+ * whose key codes have the largest summed Hamming distance to the G
+ * observation query codes goes first, ties to the lowest chunk.  The kept
+ * chunks then fill slots 0, 1, ... in token order.  Occupancy becomes the
+ * number of kept tokens (possibly below S_b: decode fills the rest first);
+ * next position N_b.
+ *   q_obs: device fp32 [B][Hq][d], 16-byte aligned, the observation queries
+ *          (normally those of each sequence's last prompt token).  They are
+ *          hashed with R (stages 1-2).  Not read when `reuse` is given; may
+ *          then be NULL.
+ *   reuse: device int32 [B][Hkv][kmax] or NULL.  For a sequence with
+ *          N_b > S_b, entries 0 .. floor(S_b / C) - 1 of a head are the chunks
+ *          to keep instead of scoring; entries outside [0, ceil(N_b / C)) are
+ *          ignored and repeats count once.  Not read for a sequence whose
+ *          prompt fits its budget (every token is kept).  Normally
+ *          the `kept` output of the same call on another layer's cache with
+ *          the same budgets, chunk size and prompt lengths.
+ *   kept:  device int32 [B][Hkv][kmax] or NULL; receives the kept chunk
+ *          indices of each head in ascending order, then -1.
+ * kmax = ceil(Smax / C), Smax the largest budget.  When q_obs is given,
+ * hkv_debug_last_codes then returns its codes as qcodes (until the first
+ * decode step; kcodes unspecified).  HKV_ERR_INVALID_ARG if both q_obs and
+ * reuse are NULL while some prompt exceeds its budget. */
+hkv_status hkv_prefill_chunks(hkv_cache* c, const void* K, const void* V, const float* q_obs,
+                              const int32_t* reuse, int32_t* kept, const int32_t* prompt_lens,
+                              int32_t n_max, void* stream);
 
 /* One decode step for every sequence (method stages 1-5, then attention).
  * q: device fp32 [B][Hq][d]; k, v: device kv dtype [B][Hkv][d], the new token;
@@ -176,7 +218,9 @@ hkv_status hkv_set_state(hkv_cache* c, const void* K, const void* V, const uint3
                          const int32_t* slot_token, const int32_t* head_state, void* stream);
 
 /* Codes the last decode step computed: qcodes [B][Hq][W], kcodes [B][Hkv][W]
- * (uint32 device buffers). */
+ * (uint32 device buffers).  After hkv_prefill_chunks with q_obs and before
+ * any decode step: the observation query codes, kcodes unspecified.
+ * HKV_ERR_STATE before either. */
 hkv_status hkv_debug_last_codes(const hkv_cache* c, uint32_t* qcodes, uint32_t* kcodes,
                                 void* stream);
 /* Codes the last prefill computed for every prompt key:

@@ -22,6 +22,7 @@ struct hkv_cache {
     bool prefilled = false;
     bool last_query_prefill = false;
     bool stepped = false;
+    bool obs_codes = false;    // dbg_q holds a CHUNK prefill's observation codes
     bool poisoned = false;
     bool debug_sync = false;
     std::string err;
@@ -118,6 +119,9 @@ extern "C" hkv_status hkv_create(const hkv_config* cfg, const float* R_host, voi
     d.kv_bf16 = L.kv_dtype == HKV_BF16;
     d.code_slots = (long long)L.code_slots;
     d.pcode_slots = (long long)L.pcode_slots;
+    d.csum = (int*)(ws + L.off_csum);
+    d.pchunk = L.pchunk;
+    d.nchunk_max = (long long)L.nchunk_max;
 
     hipError_t e = hipMemcpyAsync((void*)d.R, R_host, (size_t)L.d * L.bits * sizeof(float),
                                   hipMemcpyHostToDevice, st);
@@ -145,10 +149,14 @@ extern "C" hkv_status hkv_destroy(hkv_cache* c)
     return HKV_OK;
 }
 
-// Checks shared by the two prefill calls, then the prompt lengths go to the
+// Entries per head of a kept-chunk list: ceil(Smax / C).
+static int chunk_list_len(const hkv::Layout& L) { return L.pchunk ? (L.Smax + L.pchunk - 1) / L.pchunk : 0; }
+
+// Checks shared by the prefill calls, then the prompt lengths go to the
 // device and the kernels are enqueued.
 static hkv_status prefill_impl(hkv_cache* c, const void* K, const void* V, const float* Q,
-                               const int32_t* prompt_lens, int32_t n_max, void* stream, const char* fn)
+                               const int32_t* prompt_lens, int32_t n_max, void* stream, const char* fn,
+                               const int32_t* reuse = nullptr, int32_t* kept = nullptr)
 {
     const std::string f(fn);
     if (c->prefilled) return fail(c, HKV_ERR_STATE, f + ": cache is not empty");
@@ -165,18 +173,31 @@ static hkv_status prefill_impl(hkv_cache* c, const void* K, const void* V, const
     if (n_max > 0 && (!aligned(K, 16) || !aligned(V, 16)))
         return fail(c, HKV_ERR_INVALID_ARG, f + ": K and V must be 16-byte aligned");
     const bool query = c->lay.prefill_policy == HKV_PREFILL_QUERY;
+    const bool chunked = c->lay.prefill_policy == HKV_PREFILL_CHUNK;
     if (query && n_max > 0 && (!Q || !aligned(Q, 16)))
         return fail(c, HKV_ERR_INVALID_ARG, f + ": Q is NULL or not 16-byte aligned");
+    if (chunked) {
+        bool over = false;
+        for (int b = 0; b < c->lay.B; ++b) over = over || prompt_lens[b] > c->budgets[b];
+        if (over && !Q && !reuse)
+            return fail(c, HKV_ERR_INVALID_ARG,
+                        f + ": q_obs and reuse are both NULL while a prompt exceeds its budget");
+        if ((Q && !aligned(Q, 4)) || (reuse && !aligned(reuse, 4)) || (kept && !aligned(kept, 4)))
+            return fail(c, HKV_ERR_INVALID_ARG, f + ": q_obs, reuse and kept must be 4-byte aligned");
+    }
     hipStream_t st = (hipStream_t)stream;
     c->plens.assign(prompt_lens, prompt_lens + c->lay.B);
     hipError_t e = hipMemcpyAsync((void*)c->dev.plen, c->plens.data(), (size_t)c->lay.B * sizeof(int32_t),
                                   hipMemcpyHostToDevice, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);   // plens is host memory of the handle
-    if (e == hipSuccess) e = hkv::launch_prefill(c->dev, K, V, Q, n_max, c->lay.prefill_policy, st);
+    if (e == hipSuccess)
+        e = chunked ? hkv::launch_prefill_chunks(c->dev, K, V, Q, reuse, kept, chunk_list_len(c->lay), n_max, st)
+                    : hkv::launch_prefill(c->dev, K, V, Q, n_max, c->lay.prefill_policy, st);
     hkv_status s = check_launch(c, e, st, fn);
     if (s != HKV_OK) return s;
     c->last_n_max = n_max;
     c->last_query_prefill = query;
+    c->obs_codes = chunked && Q;
     c->prefilled = true;
     return HKV_OK;
 }
@@ -188,6 +209,8 @@ extern "C" hkv_status hkv_prefill(hkv_cache* c, const void* K, const void* V, co
     if (s != HKV_OK) return s;
     if (c->lay.prefill_policy == HKV_PREFILL_QUERY)
         return fail(c, HKV_ERR_INVALID_ARG, "hkv_prefill: this cache uses HKV_PREFILL_QUERY; call hkv_prefill_queries");
+    if (c->lay.prefill_policy == HKV_PREFILL_CHUNK)
+        return fail(c, HKV_ERR_INVALID_ARG, "hkv_prefill: this cache uses HKV_PREFILL_CHUNK; call hkv_prefill_chunks");
     return prefill_impl(c, K, V, nullptr, prompt_lens, n_max, stream, "hkv_prefill");
 }
 
@@ -199,6 +222,17 @@ extern "C" hkv_status hkv_prefill_queries(hkv_cache* c, const void* K, const voi
     if (c->lay.prefill_policy != HKV_PREFILL_QUERY)
         return fail(c, HKV_ERR_INVALID_ARG, "hkv_prefill_queries: this cache was not created with HKV_PREFILL_QUERY");
     return prefill_impl(c, K, V, Q, prompt_lens, n_max, stream, "hkv_prefill_queries");
+}
+
+extern "C" hkv_status hkv_prefill_chunks(hkv_cache* c, const void* K, const void* V, const float* q_obs,
+                                         const int32_t* reuse, int32_t* kept, const int32_t* prompt_lens,
+                                         int32_t n_max, void* stream)
+{
+    hkv_status s = usable(c);
+    if (s != HKV_OK) return s;
+    if (c->lay.prefill_policy != HKV_PREFILL_CHUNK)
+        return fail(c, HKV_ERR_INVALID_ARG, "hkv_prefill_chunks: this cache was not created with HKV_PREFILL_CHUNK");
+    return prefill_impl(c, K, V, q_obs, prompt_lens, n_max, stream, "hkv_prefill_chunks", reuse, kept);
 }
 
 extern "C" hkv_status hkv_decode_step(hkv_cache* c, const float* q, const void* k, const void* v,
@@ -216,7 +250,10 @@ extern "C" hkv_status hkv_decode_step(hkv_cache* c, const float* q, const void* 
                        ? hkv::launch_decode_fused(c->dev, q, k, v, out, evicted_slot, st)
                        : hkv::launch_decode_split(c->dev, q, k, v, out, evicted_slot, st);
     s = check_launch(c, e, st, "hkv_decode_step");
-    if (s == HKV_OK) c->stepped = true;
+    if (s == HKV_OK) {
+        c->stepped = true;
+        c->obs_codes = false;
+    }
     return s;
 }
 
@@ -266,6 +303,7 @@ extern "C" hkv_status hkv_set_state(hkv_cache* c, const void* K, const void* V, 
     if (s == HKV_OK) {
         c->prefilled = true;
         c->last_query_prefill = false;
+        c->obs_codes = false;
     }
     return s;
 }
@@ -275,7 +313,8 @@ extern "C" hkv_status hkv_debug_last_codes(const hkv_cache* cc, uint32_t* qcodes
     hkv_cache* c = const_cast<hkv_cache*>(cc);
     hkv_status s = usable(c);
     if (s != HKV_OK) return s;
-    if (!c->stepped) return fail(c, HKV_ERR_STATE, "hkv_debug_last_codes: no decode step yet");
+    if (!c->stepped && !c->obs_codes)
+        return fail(c, HKV_ERR_STATE, "hkv_debug_last_codes: no decode step (or observed chunk prefill) yet");
     const hkv::Layout& L = c->lay;
     hipStream_t st = (hipStream_t)stream;
     hipError_t e = hipSuccess;

@@ -34,6 +34,9 @@ struct DevCache {
     bool vq;                        // values stored as int8 codes + scales
     int kv_bf16;
     long long code_slots, pcode_slots;
+    int* csum;                      // [B][Hkv][nchunk_max] per-chunk scores or flags (CHUNK prefill)
+    int pchunk;                     // tokens per prefill chunk (CHUNK prefill)
+    long long nchunk_max;
 };
 
 // decode, fused schedule: one launch
@@ -50,6 +53,9 @@ hipError_t launch_encode_rows(const DevCache& c, const void* X, int x_bf16, int 
 hipError_t launch_reset(const DevCache& c, hipStream_t st);
 hipError_t launch_prefill(const DevCache& c, const void* K, const void* V, const float* Q, int n_max, int policy,
                           hipStream_t st);
+// CHUNK prefill: q_obs [B][Hq][d] fp32 (may be null with reuse), reuse / kept [B][Hkv][kmax] (may be null)
+hipError_t launch_prefill_chunks(const DevCache& c, const void* K, const void* V, const float* q_obs,
+                                 const int* reuse, int* kept, int kmax, int n_max, hipStream_t st);
 // checkpoint
 hipError_t launch_export_codes(const DevCache& c, uint32_t* codes, hipStream_t st);
 hipError_t launch_import_codes(const DevCache& c, const uint32_t* codes, hipStream_t st);

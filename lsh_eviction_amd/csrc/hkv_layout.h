@@ -15,18 +15,22 @@ constexpr int kMaxBudget = 1 << 22;
 constexpr int kMaxBatch = 4096;
 constexpr size_t kLdsTableBytes = 128 * 1024;   // prefill code table in LDS
 constexpr int kDefaultChunk = 1024;
+constexpr int kDefaultPrefillChunk = 10;   // tokens per prefill chunk (HKV_PREFILL_CHUNK)
+constexpr int kMaxPrefillChunk = 32;
 constexpr size_t kAlign = 256;
 
 struct Layout {
     int B, Hq, Hkv, G, d, bits, W, cb, es;   // cb: code bytes, es: kv element bytes
     int kv_dtype, prefill_policy, schedule, value_bits;
     int Smax, chunk, nsplit, max_prompt;
+    int pchunk;            // tokens per prefill chunk (HKV_PREFILL_CHUNK), else 0
+    size_t nchunk_max;     // prompt chunks per head, padded (HKV_PREFILL_CHUNK)
     size_t code_slots;     // slots per head in the code table (padded)
     size_t pcode_slots;    // prompt positions per head in the prefill code buffer (padded)
     // byte offsets into the workspace
     size_t off_R, off_budget, off_plen, off_state, off_K, off_V, off_code, off_tok;
     size_t off_dbg_q, off_dbg_k, off_part, off_frec, off_fscal, off_cand_v, off_ekey;
-    size_t off_info, off_count, off_pcode, off_qcode, off_vs;
+    size_t off_info, off_count, off_pcode, off_qcode, off_vs, off_csum;
     size_t v_bytes;        // bytes of the V region (kv dtype, or int8 codes)
     size_t total;
 };

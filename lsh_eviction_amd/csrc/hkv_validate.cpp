@@ -33,8 +33,13 @@ hkv_status compute_layout(const hkv_config* cfg, Layout* L, char* err, size_t er
     if (cfg->kv_dtype != HKV_F32 && cfg->kv_dtype != HKV_BF16)
         FAIL(HKV_ERR_UNSUPPORTED, "kv_dtype %d unknown", cfg->kv_dtype);
     if (cfg->prefill_policy != HKV_PREFILL_STREAM && cfg->prefill_policy != HKV_PREFILL_TRUNCATE &&
-        cfg->prefill_policy != HKV_PREFILL_QUERY)
+        cfg->prefill_policy != HKV_PREFILL_QUERY && cfg->prefill_policy != HKV_PREFILL_CHUNK)
         FAIL(HKV_ERR_UNSUPPORTED, "prefill_policy %d unknown", cfg->prefill_policy);
+    const bool chunked = cfg->prefill_policy == HKV_PREFILL_CHUNK;
+    if (!chunked && cfg->prefill_chunk != 0)
+        FAIL(HKV_ERR_UNSUPPORTED, "prefill_chunk %d set without HKV_PREFILL_CHUNK", cfg->prefill_chunk);
+    if (chunked && (cfg->prefill_chunk < 0 || cfg->prefill_chunk > kMaxPrefillChunk))
+        FAIL(HKV_ERR_UNSUPPORTED, "prefill_chunk %d outside [0, %d]", cfg->prefill_chunk, kMaxPrefillChunk);
     if (cfg->value_bits != 0 && cfg->value_bits != 8)
         FAIL(HKV_ERR_UNSUPPORTED, "value_bits %d not in {0, 8}", cfg->value_bits);
     if (cfg->value_bits == 8 && (cfg->kv_dtype != HKV_BF16 || cfg->decode_schedule != HKV_DECODE_FUSED))
@@ -52,7 +57,8 @@ hkv_status compute_layout(const hkv_config* cfg, Layout* L, char* err, size_t er
         const int s = cfg->budgets[b];
         if (s < 1 || s > kMaxBudget)
             FAIL(HKV_ERR_UNSUPPORTED, "budget[%d] = %d outside [1, %d]", b, s, kMaxBudget);
-        if (cfg->prefill_policy != HKV_PREFILL_TRUNCATE && (size_t)s * cb > kLdsTableBytes)
+        if ((cfg->prefill_policy == HKV_PREFILL_STREAM || cfg->prefill_policy == HKV_PREFILL_QUERY) &&
+            (size_t)s * cb > kLdsTableBytes)
             FAIL(HKV_ERR_UNSUPPORTED,
                  "budget[%d] = %d: its %d-byte code table exceeds the %zu-byte on-chip table of "
                  "the sequential prefill", b, s, s * cb, kLdsTableBytes);
@@ -73,6 +79,8 @@ hkv_status compute_layout(const hkv_config* cfg, Layout* L, char* err, size_t er
     l.max_prompt = cfg->max_prompt;
     l.code_slots = align_up((size_t)Smax, 64);
     l.pcode_slots = align_up((size_t)(cfg->max_prompt > 0 ? cfg->max_prompt : 1), 64);
+    l.pchunk = chunked ? (cfg->prefill_chunk ? cfg->prefill_chunk : kDefaultPrefillChunk) : 0;
+    l.nchunk_max = chunked ? align_up((size_t)((cfg->max_prompt + l.pchunk - 1) / l.pchunk) + 1, 64) : 0;
 
     const size_t heads = (size_t)l.B * l.Hkv;
     size_t off = 0;
@@ -103,6 +111,8 @@ hkv_status compute_layout(const hkv_config* cfg, Layout* L, char* err, size_t er
     l.off_count = take(heads * 4);
     l.off_pcode = take(heads * l.pcode_slots * cb);
     l.off_qcode = take(cfg->prefill_policy == HKV_PREFILL_QUERY ? (size_t)l.B * l.Hq * l.pcode_slots * cb : 0);
+    // per-chunk scores of the prompt (HKV_PREFILL_CHUNK)
+    l.off_csum = take(heads * l.nchunk_max * 4);
     l.total = off;
     return HKV_OK;
 #undef FAIL

@@ -11,6 +11,14 @@
 // decode rule, each token scored against its own key code; TRUNCATE keeps
 // the first `budget` tokens.  The sequential selection keeps the whole code
 // table of one (sequence, KV head) in LDS.
+//
+// Chunk-granular prefill (a reading of the ChunkKV summary page: tokens kept
+// or dropped in groups of consecutive tokens, kept indices reusable across
+// layers): the prompt is cut into chunks of C tokens, every chunk is scored
+// by its summed Hamming distance to the observation query codes, and the
+// chunks are evicted in order of (score descending, index ascending) until
+// floor(S / C) remain.  That order is found by a two-level radix histogram
+// over the scores, so the selection is one block per (sequence, KV head).
 #include <type_traits>
 
 #include "hkv.h"
@@ -247,7 +255,7 @@ __global__ __launch_bounds__(256) void k_prefill_gather(DevCache c, const KT* __
     using CT = typename CodeT<BITS>::T;
     constexpr int CH = D * (int)sizeof(KT) / 16;   // 16-byte chunks per row
     const int h = blockIdx.y, b = blockIdx.z, head = b * c.Hkv + h;
-    const int occ = min(c.plen[b], c.budget[b]);
+    const int occ = c.state[2 * head];   // min(N, S), or the kept tokens of a CHUNK prefill
     const int s = blockIdx.x * 16 + threadIdx.x / 16;
     const int j = threadIdx.x % 16;
     if (s >= occ) return;
@@ -287,6 +295,183 @@ __global__ __launch_bounds__(256) void k_prefill_gather(DevCache c, const KT* __
     if (j == 0)
         reinterpret_cast<CT*>(c.code)[(size_t)head * c.code_slots + s] =
             reinterpret_cast<const CT*>(c.pcode)[(size_t)head * c.pcode_slots + t];
+}
+
+// Exclusive prefix count of `flag` over the block's threads in thread order,
+// and the block's total.  All threads of the block must call it; it holds
+// two barriers and uses s_w[kSelWaves].
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+
+__device__ __forceinline__ int block_prefix(bool flag, int* s_w, int& total)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const unsigned long long m = __ballot(flag);
+    const int below = __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+    if (lane == 0) s_w[wave] = __popcll(m);
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) {
+        const int x = s_w[w];
+        before += w < wave ? x : 0;
+        all += x;
+    }
+    __syncthreads();   // s_w is reused by the next call
+    total = all;
+    return before + below;
+}
+
+// Chunk-granular selection for one (sequence, KV head); 1024 threads.
+//   1. the G observation queries are hashed (fp32 dot products against R, any
+//      summation order is exact outside the flagged band) and sign-packed;
+//   2. score[i] = sum over the chunk's tokens and the G query codes of the
+//      Hamming distances (integer);
+//   3. E = nch - k evictions: a histogram of score >> 8, then of the low 8
+//      bits inside the bin that holds the E-th largest, gives the threshold T
+//      and how many chunks score above it; of the chunks scoring exactly T
+//      the lowest-indexed ones are evicted;
+//   4. a prefix count in chunk order places the kept chunks in slots
+//      0, 1, ... and writes the kept list.
+// With a reuse list step 3 is replaced by flags set from the list; with
+// N <= S every chunk is kept.  The per-chunk scores live in c.csum (global;
+// a score is read back only by the thread that wrote it, the reuse flags by
+// any thread of the block, through L2).
+template <int BITS>
+__global__ __launch_bounds__(kSelThreads) void k_chunk_select(DevCache c, const float* __restrict__ qobs,
+                                                             const int* __restrict__ reuse, int* __restrict__ kept,
+                                                             int kmax)
+{
+    using CT = typename CodeT<BITS>::T;
+    const int h = blockIdx.x, b = blockIdx.y, head = b * c.Hkv + h;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int G = c.G, C = c.pchunk;
+    const int N = c.plen[b], S = c.budget[b];
+    const int nch = (N + C - 1) / C;
+    const bool all = N <= S;
+    const int k = all ? nch : S / C;
+    int* score = c.csum + (size_t)head * c.nchunk_max;
+    const CT* pc = reinterpret_cast<const CT*>(c.pcode) + (size_t)head * c.pcode_slots;
+    const size_t rowbase = (size_t)head * c.Smax;
+
+    __shared__ CT s_qc[kMaxGroup];
+    __shared__ unsigned s_hist[256];
+    __shared__ int s_w[kSelWaves];
+    __shared__ int s_hb, s_T, s_evict_eq, s_ntok;
+
+    // 1. observation query codes (also exported for inspection)
+    if (qobs) {
+        const int g = tid / BITS, j = tid % BITS;
+        float y = 0.f;
+        if (g < G) {
+            const float* x = qobs + ((size_t)b * c.Hq + (size_t)h * G + g) * c.d;
+            for (int i = 0; i < c.d; ++i) y = fmaf(x[i], c.R[i * BITS + j], y);
+        }
+        const unsigned long long m = __ballot(y > 0.f);
+        if (g < G && j == 0) {
+            const CT code = (CT)(m >> (lane & ~(BITS - 1) & 63));
+            s_qc[g] = code;
+            store_words(c.dbg_q + ((size_t)b * c.Hq + (size_t)h * G + g) * c.W, c.W, (unsigned long long)code);
+        }
+    }
+    if (tid == 0) s_ntok = 0;
+    for (int i = tid; i < 256; i += kSelThreads) s_hist[i] = 0u;
+    __syncthreads();
+
+    const bool scored = !all && !reuse;
+    if (scored) {
+        // 2. chunk scores, histogram of their high bits (scores < 2^15)
+        for (int i = tid; i < nch; i += kSelThreads) {
+            int sum = 0;
+            const int t1 = min(N, (i + 1) * C);
+            for (int t = i * C; t < t1; ++t) {
+                const CT kc = pc[t];
+                for (int g = 0; g < G; ++g) sum += popc((CT)(kc ^ s_qc[g]));
+            }
+            score[i] = sum;
+            atomicAdd(&s_hist[sum >> 8], 1u);
+        }
+        __syncthreads();
+        // 3. threshold: the E-th largest score, E = nch - k >= 1
+        const int E = nch - k;
+        if (tid == 0) {
+            int cum = 0, hb = 255;
+            for (; hb > 0; --hb) {
+                if (cum + (int)s_hist[hb] >= E) break;
+                cum += (int)s_hist[hb];
+            }
+            s_hb = hb;
+            s_evict_eq = cum;   // chunks above bin hb, for now
+        }
+        __syncthreads();
+        const int hb = s_hb;
+        for (int i = tid; i < 256; i += kSelThreads) s_hist[i] = 0u;
+        __syncthreads();
+        for (int i = tid; i < nch; i += kSelThreads) {
+            const int sc = score[i];
+            if ((sc >> 8) == hb) atomicAdd(&s_hist[sc & 255], 1u);
+        }
+        __syncthreads();
+        if (tid == 0) {
+            int cum = s_evict_eq, lo = 255;
+            for (; lo > 0; --lo) {
+                if (cum + (int)s_hist[lo] >= E) break;
+                cum += (int)s_hist[lo];
+            }
+            s_T = (hb << 8) | lo;
+            s_evict_eq = E - cum;   // chunks scoring exactly T that go, lowest first
+        }
+    } else if (!all) {
+        // reuse: flags from the list.  Other threads read these flags: the
+        // stores are waited for (agent-scope fence) before each barrier and
+        // read back with agent-scope loads from L2, so the hand-off does not
+        // depend on how the CU's L1 treats stores of other waves.
+        for (int i = tid; i < nch; i += kSelThreads) score[i] = 0;
+        __threadfence();
+        __syncthreads();
+        for (int j = tid; j < k; j += kSelThreads) {
+            const int i = reuse[(size_t)head * kmax + j];
+            if (i >= 0 && i < nch) __hip_atomic_store(score + i, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __threadfence();
+    }
+    __syncthreads();
+    const int T = scored ? s_T : 0, evict_eq = scored ? s_evict_eq : 0;
+
+    // 4. kept chunks in chunk order -> slots
+    int base = 0, base_eq = 0;
+    for (int i0 = 0; i0 < nch; i0 += kSelThreads) {
+        const int i = i0 + tid;
+        const bool valid = i < nch;
+        int sc = 0;
+        if (valid && scored) sc = score[i];   // written by this thread
+        else if (valid && !all) sc = __hip_atomic_load(score + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        bool keep = valid;
+        if (scored) {
+            int neq;
+            const bool eq = valid && sc == T;
+            const int rank = base_eq + block_prefix(eq, s_w, neq);
+            keep = valid && (sc < T || (eq && rank >= evict_eq));
+            base_eq += neq;
+        } else if (!all) {
+            keep = valid && sc != 0;
+        }
+        int nkeep;
+        const int pos = base + block_prefix(keep, s_w, nkeep);
+        if (keep) {
+            if (kept) kept[(size_t)head * kmax + pos] = i;
+            const int len = min(C, N - i * C);
+            for (int r = 0; r < len; ++r) c.tok[rowbase + (size_t)pos * C + r] = i * C + r;
+            atomicAdd(&s_ntok, len);
+        }
+        base += nkeep;
+    }
+    __syncthreads();
+    const int n = s_ntok;
+    for (int s = n + tid; s < min(N, S); s += kSelThreads) c.tok[rowbase + s] = -1;
+    if (kept)
+        for (int j = base + tid; j < kmax; j += kSelThreads) kept[(size_t)head * kmax + j] = -1;
+    if (tid == 0) c.state[2 * head] = n;
 }
 
 template <int BITS>
@@ -414,6 +599,34 @@ hipError_t launch_prefill(const DevCache& c, const void* K, const void* V, const
                 if (e == hipSuccess) e = launch_select_query<BITS>(c, st);
             }
             if (e != hipSuccess) return e;
+            hipLaunchKernelGGL((k_prefill_gather<D, BITS, KT>), dim3((c.Smax + 15) / 16, c.Hkv, c.B),
+                               dim3(256), 0, st, c, (const KT*)K, (const KT*)V, n_max);
+            return hipGetLastError();
+        });
+    });
+}
+
+hipError_t launch_prefill_chunks(const DevCache& c, const void* K, const void* V, const float* q_obs,
+                                 const int* reuse, int* kept, int kmax, int n_max, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_prefill_init, dim3((c.Smax + 255) / 256, c.Hkv, c.B), dim3(256), 0, st, c);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    return with_bits(c, [&](auto bb) {
+        constexpr int BITS = decltype(bb)::value;
+        return with_d_kv(c, [&](auto dd, auto kt) {
+            constexpr int D = decltype(dd)::value;
+            using KT = decltype(kt);
+            if (n_max > 0) {
+                hipLaunchKernelGGL((k_project_mfma<D, BITS, KT>), dim3((n_max + 63) / 64, c.Hkv, c.B),
+                                   dim3(256), 0, st, c, (const KT*)K, n_max, c.Hkv, c.pcode);
+                hipError_t e = hipGetLastError();
+                if (e != hipSuccess) return e;
+            }
+            hipLaunchKernelGGL((k_chunk_select<BITS>), dim3(c.Hkv, c.B), dim3(kSelThreads), 0, st, c, q_obs,
+                               reuse, kept, kmax);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess || n_max <= 0) return e;
             hipLaunchKernelGGL((k_prefill_gather<D, BITS, KT>), dim3((c.Smax + 15) / 16, c.Hkv, c.B),
                                dim3(256), 0, st, c, (const KT*)K, (const KT*)V, n_max);
             return hipGetLastError();

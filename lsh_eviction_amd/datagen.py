@@ -30,7 +30,7 @@ import numpy as np
 from .configs import SEED_BASE, Shape
 
 # stream ids inside one workload's SeedSequence
-_S_R, _S_SCALE, _S_PK, _S_PV, _S_LEN, _S_DQ, _S_DK, _S_DV, _S_PQ = range(9)
+_S_R, _S_SCALE, _S_PK, _S_PV, _S_LEN, _S_DQ, _S_DK, _S_DV, _S_PQ, _S_OQ = range(10)
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -43,7 +43,7 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 
 def _streams(shape: Shape, seed: Optional[int]):
     s = SEED_BASE + shape.index if seed is None else seed
-    return np.random.SeedSequence(s).spawn(9)   # child i does not depend on the count
+    return np.random.SeedSequence(s).spawn(10)   # child i does not depend on the count
 
 
 def _rng(ss) -> np.random.Generator:
@@ -117,6 +117,13 @@ def prompt_queries(shape: Shape, seed: Optional[int] = None) -> np.ndarray:
     n, _ = lengths(shape, seed)
     return _rng(ss[_S_PQ]).standard_normal((shape.batch, shape.n_q_heads, int(n.max()), shape.head_dim),
                                            dtype=np.float32)
+
+
+def observation_queries(shape: Shape, seed: Optional[int] = None) -> np.ndarray:
+    """Observation queries of the chunk prefill (those of the token decoding
+    starts from), fp32 [B][Hq][d] ~ N(0, 1) like the decode queries."""
+    ss = _streams(shape, seed)
+    return _rng(ss[_S_OQ]).standard_normal((shape.batch, shape.n_q_heads, shape.head_dim), dtype=np.float32)
 
 
 def decode(shape: Shape, steps: Optional[int] = None, seed: Optional[int] = None,

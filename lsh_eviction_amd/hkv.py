@@ -18,12 +18,13 @@ LIB_PATH = os.path.join(HERE, "libhkv.so")
 
 HKV_OK, HKV_ERR_INVALID_ARG, HKV_ERR_UNSUPPORTED, HKV_ERR_STATE, HKV_ERR_DEVICE = range(5)
 HKV_F32, HKV_BF16 = 0, 1
-HKV_PREFILL_STREAM, HKV_PREFILL_TRUNCATE, HKV_PREFILL_QUERY = 0, 1, 2
+HKV_PREFILL_STREAM, HKV_PREFILL_TRUNCATE, HKV_PREFILL_QUERY, HKV_PREFILL_CHUNK = 0, 1, 2, 3
+DEFAULT_PREFILL_CHUNK = 10   # tokens per chunk when prefill_chunk is 0
 HKV_DECODE_FUSED, HKV_DECODE_SPLIT = 0, 1
 
 # every symbol include/hkv.h declares
 EXPORTS = ("hkv_validate_config", "hkv_workspace_bytes", "hkv_create", "hkv_prefill",
-           "hkv_prefill_queries", "hkv_decode_step", "hkv_destroy", "hkv_status_str", "hkv_last_error",
+           "hkv_prefill_queries", "hkv_prefill_chunks", "hkv_decode_step", "hkv_destroy", "hkv_status_str", "hkv_last_error",
            "hkv_get_state", "hkv_set_state", "hkv_debug_last_codes", "hkv_debug_prefill_codes",
            "hkv_debug_prefill_query_codes", "hkv_debug_scores", "hkv_encode")
 
@@ -33,7 +34,7 @@ class hkv_config(C.Structure):
                 ("head_dim", C.c_int32), ("n_bits", C.c_int32), ("kv_dtype", C.c_int32),
                 ("prefill_policy", C.c_int32), ("decode_schedule", C.c_int32),
                 ("max_prompt", C.c_int32), ("chunk", C.c_int32), ("value_bits", C.c_int32),
-                ("budgets", C.POINTER(C.c_int32))]
+                ("prefill_chunk", C.c_int32), ("budgets", C.POINTER(C.c_int32))]
 
 
 class HkvError(RuntimeError):
@@ -62,6 +63,7 @@ def load():
         "hkv_create": (I, [cfgp, P, P, Z, P, C.POINTER(P)]),
         "hkv_prefill": (I, [P, P, P, P, I, P]),
         "hkv_prefill_queries": (I, [P, P, P, P, P, I, P]),
+        "hkv_prefill_chunks": (I, [P, P, P, P, P, P, P, I, P]),
         "hkv_decode_step": (I, [P, P, P, P, P, P, P]),
         "hkv_destroy": (I, [P]),
         "hkv_status_str": (C.c_char_p, [I]),
@@ -87,11 +89,11 @@ def status_str(s: int) -> str:
 
 def make_config(batch, n_q_heads, n_kv_heads, head_dim, n_bits, kv_dtype, budgets,
                 prefill_policy=HKV_PREFILL_STREAM, decode_schedule=HKV_DECODE_FUSED,
-                max_prompt=0, chunk=0, value_bits=0):
+                max_prompt=0, chunk=0, value_bits=0, prefill_chunk=0):
     b = np.ascontiguousarray(budgets, dtype=np.int32)
     cfg = hkv_config(int(batch), int(n_q_heads), int(n_kv_heads), int(head_dim), int(n_bits),
                      int(kv_dtype), int(prefill_policy), int(decode_schedule), int(max_prompt),
-                     int(chunk), int(value_bits), b.ctypes.data_as(C.POINTER(C.c_int32)))
+                     int(chunk), int(value_bits), int(prefill_chunk), b.ctypes.data_as(C.POINTER(C.c_int32)))
     cfg._keep = b          # keep the budgets array alive with the struct
     return cfg
 
@@ -177,6 +179,12 @@ def hkv_prefill_queries(h, K, V, Q, prompt_lens, n_max: int, stream=None):
                                       _stream(stream)), h)
 
 
+def hkv_prefill_chunks(h, K, V, q_obs, reuse, kept, prompt_lens, n_max: int, stream=None):
+    pl = np.ascontiguousarray(prompt_lens, dtype=np.int32)
+    _check(load().hkv_prefill_chunks(h, _ptr(K), _ptr(V), _ptr(q_obs), _ptr(reuse), _ptr(kept),
+                                     pl.ctypes.data_as(C.c_void_p), int(n_max), _stream(stream)), h)
+
+
 def hkv_debug_prefill_query_codes(h, codes, stream=None):
     _check(load().hkv_debug_prefill_query_codes(h, _ptr(codes), _stream(stream)), h)
 
@@ -222,10 +230,13 @@ class Cache:
 
     def __init__(self, batch, n_q_heads, n_kv_heads, head_dim, n_bits, kv_dtype, budgets, R,
                  prefill_policy=HKV_PREFILL_STREAM, decode_schedule=HKV_DECODE_FUSED, max_prompt=0,
-                 chunk=0, stream=None, value_bits=0):
+                 chunk=0, stream=None, value_bits=0, prefill_chunk=0):
         import torch
         self.cfg = make_config(batch, n_q_heads, n_kv_heads, head_dim, n_bits, kv_dtype, budgets,
-                               prefill_policy, decode_schedule, max_prompt, chunk, value_bits)
+                               prefill_policy, decode_schedule, max_prompt, chunk, value_bits,
+                               prefill_chunk)
+        self.prefill_policy = int(prefill_policy)
+        self.prefill_chunk = (int(prefill_chunk) or DEFAULT_PREFILL_CHUNK) if prefill_policy == HKV_PREFILL_CHUNK else 0
         self.value_bits = int(value_bits)
         self.B, self.Hq, self.Hkv, self.d, self.bits = batch, n_q_heads, n_kv_heads, head_dim, n_bits
         self.W = (n_bits + 31) // 32
@@ -249,13 +260,27 @@ class Cache:
         except Exception:
             pass
 
-    def prefill(self, K, V, prompt_lens, stream=None, Q=None):
-        """K, V [B][Hkv][n_max][d]; Q [B][Hq][n_max][d] fp32 for a cache made with HKV_PREFILL_QUERY."""
+    @property
+    def kept_len(self) -> int:
+        """Entries per head of a kept-chunk list (HKV_PREFILL_CHUNK): ceil(Smax / C)."""
+        return -(-self.Smax // self.prefill_chunk) if self.prefill_chunk else 0
+
+    def prefill(self, K, V, prompt_lens, stream=None, Q=None, reuse=None):
+        """K, V [B][Hkv][n_max][d].  HKV_PREFILL_QUERY: Q [B][Hq][n_max][d] fp32.
+        HKV_PREFILL_CHUNK: Q [B][Hq][d] fp32 observation queries (may be None with
+        reuse), reuse [B][Hkv][kept_len] int32 or None; returns the kept chunk
+        lists [B][Hkv][kept_len] int32 (device)."""
         self.n_max = int(K.shape[2])
+        if self.prefill_policy == HKV_PREFILL_CHUNK:
+            import torch
+            kept = torch.empty((self.B, self.Hkv, max(self.kept_len, 1)), dtype=torch.int32, device="cuda")
+            hkv_prefill_chunks(self.h, K, V, Q, reuse, kept, prompt_lens, self.n_max, stream)
+            return kept
         if Q is None:
             hkv_prefill(self.h, K, V, prompt_lens, self.n_max, stream)
         else:
             hkv_prefill_queries(self.h, K, V, Q, prompt_lens, self.n_max, stream)
+        return None
 
     def decode_step(self, q, k, v, out=None, evicted=None, stream=None):
         import torch

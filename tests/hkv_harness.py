@@ -60,9 +60,15 @@ def kv_bytes_equal(gpu_rows: np.ndarray, ref_rows_f64: np.ndarray, kv_dtype: str
 
 def run_case(shape: Shape, steps: int, schedule: int = 0, policy: int = 0, chunk: int = 0,
              heads: Optional[Sequence[Tuple[int, int]]] = None, seed: Optional[int] = None,
-             check_every: int = 1, stats: Optional[dict] = None, value_bits: int = 0):
+             check_every: int = 1, stats: Optional[dict] = None, value_bits: int = 0,
+             prefill_chunk: int = 0, reuse: Optional[np.ndarray] = None, observe: bool = True):
     """Prefill + `steps` decode steps on the GPU, replayed on the oracle for `heads`
-    (all heads if None).  Raises AssertionError on any parity failure."""
+    (all heads if None).  Raises AssertionError on any parity failure.
+
+    Under the CHUNK policy the observation queries are passed when `observe`
+    (their codes are checked and injected), `reuse` [B][Hkv][k] is passed as
+    the kept list, and the GPU's kept lists are compared with the oracle's and
+    returned in stats["kept"]."""
     import torch
     from lsh_eviction_amd import hkv
 
@@ -75,17 +81,29 @@ def run_case(shape: Shape, steps: int, schedule: int = 0, policy: int = 0, chunk
     n_max = P.n_max
     log(f"[{shape.name}] B={B} Hq={Hq} Hkv={Hkv} d={d} b={bits} N<={n_max} S<={P.budgets.max()} "
         f"steps={steps} schedule={schedule} policy={policy} chunk={chunk} value_bits={value_bits} "
+        f"prefill_chunk={prefill_chunk} reuse={reuse is not None} "
         f"(data {time.time()-t0:.1f}s)")
 
     cache = hkv.Cache(B, Hq, Hkv, d, bits, kvd, P.budgets, P.R, prefill_policy=policy,
-                      decode_schedule=schedule, max_prompt=n_max, chunk=chunk, value_bits=value_bits)
+                      decode_schedule=schedule, max_prompt=n_max, chunk=chunk, value_bits=value_bits,
+                      prefill_chunk=prefill_chunk)
     Kt, Vt = hkv.to_device(P.K), hkv.to_device(P.V)
     query = policy == oracle.QUERY
-    Qp = datagen.prompt_queries(shape, seed) if query else None
-    Qt = hkv.to_device(Qp) if query else None
-    cache.prefill(Kt, Vt, P.prompt_lens, Q=Qt)
+    chunked = policy == oracle.CHUNK
+    if query:
+        Qp = datagen.prompt_queries(shape, seed)
+    elif chunked and observe:
+        Qp = datagen.observation_queries(shape, seed)
+    else:
+        Qp = None
+    Qt = hkv.to_device(Qp) if Qp is not None else None
+    reuse_t = torch.from_numpy(np.ascontiguousarray(reuse, np.int32)).to("cuda") if reuse is not None else None
+    kept_t = cache.prefill(Kt, Vt, P.prompt_lens, Q=Qt, reuse=reuse_t)
     pcodes = words_u32(cache.prefill_codes())
     qpcodes = words_u32(cache.prefill_query_codes()) if query else None
+    if chunked and Qp is not None:
+        qpcodes = words_u32(cache.last_codes()[0])      # observation query codes [B][Hq][W]
+    kept = hkv.to_numpy(kept_t) if chunked else None
     torch.cuda.synchronize()
     del Kt, Vt, Qt
 
@@ -102,8 +120,19 @@ def run_case(shape: Shape, steps: int, schedule: int = 0, policy: int = 0, chunk
             for g in range(G):
                 qo, qf = orc.heads[(b, h)].encode(oracle.widen(Qp[b, h * G + g, :n]))
                 flagged += check_codes(qpcodes[b, h * G + g, :n], qo, qf, f"prefill query codes b={b} hq={h * G + g}")
+        if chunked and Qp is not None:
+            qo, qf = orc.heads[(b, h)].encode(oracle.widen(Qp[b, h * G:(h + 1) * G]))
+            flagged += check_codes(qpcodes[b, h * G:(h + 1) * G], qo, qf, f"observation codes b={b} h={h}")
     # replay the oracle's prefill with the GPU codes
-    orc.prefill(P.K, P.V, P.prompt_lens, policy, inj_codes=pcodes, Q=Qp, inj_qcodes=qpcodes)
+    kept_o = orc.prefill(P.K, P.V, P.prompt_lens, policy, inj_codes=pcodes, Q=Qp, inj_qcodes=qpcodes,
+                         chunk=cache.prefill_chunk or oracle.DEFAULT_CHUNK_TOKENS, reuse=reuse)
+    if chunked:
+        for (b, h) in sel:
+            ko = kept_o[(b, h)]
+            np.testing.assert_array_equal(kept[b, h, :len(ko)], ko, err_msg=f"kept chunks b={b} h={h}")
+            assert (kept[b, h, len(ko):] == -1).all(), f"kept list tail b={b} h={h}"
+        if stats is not None:
+            stats["kept"] = kept
     log(f"  prefill codes ok ({flagged} flagged bits differ), {time.time()-t0:.1f}s")
     compare_state(cache, orc, sel, shape, "after prefill")
     log(f"  prefill state ok, {time.time()-t0:.1f}s")

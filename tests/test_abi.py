@@ -63,7 +63,10 @@ def test_named_shapes_validate(hkv):
     (dict(budgets=[1 << 23], prefill_policy=1), "UNSUPPORTED"),
     (dict(budgets=[40000]), "UNSUPPORTED"),               # 160 KB code table > on-chip table
     (dict(kv_dtype=7), "UNSUPPORTED"),
-    (dict(prefill_policy=3), "UNSUPPORTED"),
+    (dict(prefill_policy=4), "UNSUPPORTED"),
+    (dict(prefill_chunk=5), "UNSUPPORTED"),                 # chunk size without the CHUNK policy
+    (dict(prefill_policy=3, prefill_chunk=33), "UNSUPPORTED"),
+    (dict(prefill_policy=3, prefill_chunk=-1), "UNSUPPORTED"),
     (dict(value_bits=4), "UNSUPPORTED"),
     (dict(value_bits=8, kv_dtype=0), "UNSUPPORTED"),        # int8 values need bf16 keys
     (dict(value_bits=8, decode_schedule=1), "UNSUPPORTED"), # and the fused schedule
@@ -87,6 +90,19 @@ def test_query_policy_validates_and_sizes_its_code_buffer(hkv):
     assert extra >= 32 * 8192 * 4
 
 
+def test_chunk_policy_validates_and_sizes_its_score_buffer(hkv):
+    a = _cfg(hkv, prefill_policy=hkv.HKV_PREFILL_CHUNK)
+    assert hkv.hkv_validate_config(a) == hkv.HKV_OK
+    # one int32 score per chunk of 10 prompt tokens and KV head
+    extra = hkv.hkv_workspace_bytes(a) - hkv.hkv_workspace_bytes(_cfg(hkv))
+    assert extra >= 8 * (8192 // 10) * 4
+    one = _cfg(hkv, prefill_policy=hkv.HKV_PREFILL_CHUNK, prefill_chunk=1)
+    assert hkv.hkv_workspace_bytes(one) - hkv.hkv_workspace_bytes(_cfg(hkv)) >= 8 * 8192 * 4
+    # no on-chip code table: a large budget is fine
+    big = _cfg(hkv, budgets=[40000], prefill_policy=hkv.HKV_PREFILL_CHUNK, prefill_chunk=32)
+    assert hkv.hkv_validate_config(big) == hkv.HKV_OK
+
+
 def test_truncate_allows_large_budget(hkv):
     cfg = _cfg(hkv, budgets=[40000], prefill_policy=hkv.HKV_PREFILL_TRUNCATE)
     assert hkv.hkv_validate_config(cfg) == hkv.HKV_OK
@@ -99,7 +115,8 @@ def test_null_pointers(hkv):
     cfg.budgets = C.POINTER(C.c_int32)()
     assert L.hkv_validate_config(C.byref(cfg)) == hkv.HKV_ERR_INVALID_ARG
     assert L.hkv_workspace_bytes(C.byref(_cfg(hkv)), None) == hkv.HKV_ERR_INVALID_ARG
-    for f, n in (("hkv_prefill", 6), ("hkv_prefill_queries", 7), ("hkv_decode_step", 7), ("hkv_destroy", 1),
+    for f, n in (("hkv_prefill", 6), ("hkv_prefill_queries", 7), ("hkv_prefill_chunks", 9),
+                 ("hkv_decode_step", 7), ("hkv_destroy", 1),
                  ("hkv_get_state", 7), ("hkv_set_state", 7), ("hkv_debug_last_codes", 4),
                  ("hkv_debug_prefill_codes", 3), ("hkv_debug_prefill_query_codes", 3), ("hkv_debug_scores", 4)):
         fn = getattr(L, f)

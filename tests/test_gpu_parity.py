@@ -13,7 +13,7 @@ from lsh_eviction_amd.configs import Shape
 pytestmark = pytest.mark.gpu
 
 FUSED, SPLIT = 0, 1
-STREAM, TRUNCATE, QUERY = 0, 1, 2
+STREAM, TRUNCATE, QUERY, CHUNK = 0, 1, 2, 3
 
 SMALL = {
     "tiny": (C.TINY, 64, 0),
@@ -74,6 +74,60 @@ def test_query_prefill_full_llama3_8b_layer():
     evictions per head) under the query-driven prefill, sampled heads."""
     from hkv_harness import run_case
     run_case(C.LLAMA8B, 2, schedule=FUSED, policy=QUERY, heads=[(0, 0), (0, 3), (0, 7)], check_every=0)
+
+
+# (shape, decode steps, attention split, tokens per prefill chunk)
+CHUNK_SMALL = {
+    "tiny": (C.TINY, 8, 0, 10),
+    "llama8b_small": (C.LLAMA8B.scaled(prompt=3000, budget=1500), 6, 0, 10),
+    "ragged_small": (C.RAGGED.scaled(batch=4, prompt_range=(600, 1800)), 4, 0, 10),
+    "llama70b_small": (C.LLAMA70B.scaled(batch=2, prompt=2500, budget=1200), 4, 0, 16),
+    "g16_b16_c32": (SMALL["g16_b16"][0], 4, 0, 32),
+    "g16_b64_c32": (Shape("g16_b64", 14, batch=1, n_q_heads=16, n_kv_heads=1, head_dim=64, n_bits=64,
+                          kv_dtype="bf16", prompt=2000, budget=700, steps=4, key_outliers=True), 4, 128, 32),
+    "d64_bf16_g2_c3": (SMALL["d64_bf16_g2"][0], 4, 128, 3),
+    "d128_f32_g1_c1": (SMALL["d128_f32_g1"][0], 4, 64, 1),
+    "not_full": (C.LLAMA8B.scaled(prompt=700, budget=1000), 4, 0, 10),
+    "budget_below_chunk": (C.TINY.scaled(prompt=100, budget=7), 9, 64, 10),
+    "empty_prompt": (C.TINY.scaled(prompt=0, budget=8), 4, 64, 10),
+    "many_chunks": (C.TINY.scaled(prompt=40000, budget=9000), 3, 1024, 3),   # > 1024 chunks per block pass
+}
+
+
+@pytest.mark.parametrize("name", list(CHUNK_SMALL))
+def test_chunk_prefill_small(name):
+    """Chunk-granular prefill: observation codes, kept chunk lists, the cache
+    they leave (bit-exact given the GPU's codes), then decode steps, which
+    first fill any slots the whole chunks left free."""
+    from hkv_harness import run_case
+    shape, steps, chunk, pchunk = CHUNK_SMALL[name]
+    run_case(shape, steps, schedule=FUSED, policy=CHUNK, chunk=chunk, prefill_chunk=pchunk)
+
+
+def test_chunk_prefill_reuse_across_layers():
+    """The kept lists of one layer's cache, given to the next layer's cache
+    (other keys and values, no observation queries), place the same tokens."""
+    from hkv_harness import run_case
+    shape = C.LLAMA8B.scaled(batch=2, prompt=2105, budget=1000)   # same lengths and budgets for any seed
+    st, st2 = {}, {}
+    run_case(shape, 2, schedule=FUSED, policy=CHUNK, prefill_chunk=10, stats=st)
+    run_case(shape, 2, schedule=FUSED, policy=CHUNK, prefill_chunk=10, seed=777, reuse=st["kept"],
+             observe=False, stats=st2)
+    np.testing.assert_array_equal(st2["kept"], st["kept"])
+
+
+def test_chunk_prefill_int8_values():
+    from hkv_harness import run_case
+    run_case(C.LLAMA8B.scaled(prompt=2500, budget=1200), 4, schedule=FUSED, policy=CHUNK, prefill_chunk=10,
+             value_bits=8)
+
+
+def test_chunk_prefill_full_long_128k():
+    """The 128K workload (131072-token prompt, 32768 slots per head): 13108
+    chunks per head scored, 3276 kept; sampled heads."""
+    from hkv_harness import run_case
+    run_case(C.LONG128K, 2, schedule=FUSED, policy=CHUNK, prefill_chunk=10, heads=[(0, 1), (0, 6)],
+             check_every=0)
 
 
 INT8_VALUES = {
