@@ -65,6 +65,11 @@ def lib():
         L.orc_set_value_codes.argtypes = [P, P, P]
         L.orc_prefill_query.restype = C.c_int
         L.orc_prefill_chunks.restype = C.c_int
+        L.orc_set_tier.restype = C.c_int
+        L.orc_set_tier.argtypes = [P, C.c_int]
+        L.orc_get_tier.restype = C.c_int64
+        L.orc_get_tier.argtypes = [P, P, P, P]
+        L.orc_attend_tiered.argtypes = [P, P, P]
         L.orc_prefill_chunks.argtypes = [P, C.c_int, C.c_int] + [P] * 7
         L.orc_decode_step.restype = C.c_int
         L.orc_decode_step.argtypes = [P] * 3 + [P] * 8 + [P]
@@ -106,7 +111,7 @@ def _u32(a) -> Optional[np.ndarray]:
 class OracleHead:
     """One eviction domain: the cache of one (sequence, KV head) pair."""
 
-    def __init__(self, R: np.ndarray, budget: int, group: int, value_bits: int = 0):
+    def __init__(self, R: np.ndarray, budget: int, group: int, value_bits: int = 0, tier: int = -1):
         R = _f64(widen(R) if R.dtype != np.float64 else R)
         self.d, self.nbits = R.shape
         self.budget, self.group = int(budget), int(group)
@@ -118,6 +123,9 @@ class OracleHead:
         self.value_bits = int(value_bits)
         if lib().orc_set_value_bits(self._h, self.value_bits) != 0:
             raise ValueError("value_bits must be 0 or 8")
+        self.tier_cap = int(tier)
+        if self.tier_cap >= 0 and lib().orc_set_tier(self._h, self.tier_cap) != 0:
+            raise ValueError("a host tier needs values stored as given")
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -213,6 +221,21 @@ class OracleHead:
         lib().orc_attend(self._h, _p(q), _p(out))
         return out
 
+    def attend_tiered(self, q) -> np.ndarray:
+        """Attention over the cache and the host tier."""
+        q = _f64(q).reshape(self.group, self.d)
+        out = np.zeros((self.group, self.d), np.float64)
+        lib().orc_attend_tiered(self._h, _p(q), _p(out))
+        return out
+
+    def tier(self) -> dict:
+        """Host tier contents: K, V [kept][d], tok [kept], count (tokens sent, kept or not)."""
+        m = max(self.tier_cap, 0)
+        K = np.zeros((m, self.d)); V = np.zeros((m, self.d)); tok = np.zeros(m, np.int64)
+        count = int(lib().orc_get_tier(self._h, _p(K), _p(V), _p(tok)))
+        k = min(count, m)
+        return {"K": K[:k], "V": V[:k], "tok": tok[:k], "count": count}
+
     def value_codes(self):
         """int8 codes [budget][d] and fp32 scales [budget] of an int8-value cache."""
         S = max(self.budget, 0)
@@ -254,12 +277,13 @@ class OracleCache:
 
     Query head hq belongs to KV head hq // G (contiguous groups)."""
 
-    def __init__(self, R, budgets, n_q_heads: int, n_kv_heads: int, heads=None, value_bits: int = 0):
+    def __init__(self, R, budgets, n_q_heads: int, n_kv_heads: int, heads=None, value_bits: int = 0,
+                 tier: int = -1):
         self.B = len(budgets)
         self.Hq, self.Hkv = int(n_q_heads), int(n_kv_heads)
         self.G = self.Hq // self.Hkv
         self.sel = heads if heads is not None else [(b, h) for b in range(self.B) for h in range(self.Hkv)]
-        self.heads = {(b, h): OracleHead(R, int(budgets[b]), self.G, value_bits) for (b, h) in self.sel}
+        self.heads = {(b, h): OracleHead(R, int(budgets[b]), self.G, value_bits, tier) for (b, h) in self.sel}
 
     def prefill(self, K, V, prompt_lens, policy=STREAM, inj_codes=None, Q=None, inj_qcodes=None,
                 chunk=DEFAULT_CHUNK_TOKENS, reuse=None):
@@ -285,6 +309,11 @@ class OracleCache:
             else:
                 o.prefill(widen(K[b, h, :n]), widen(V[b, h, :n]), policy, inj)
         return kept if policy == CHUNK else None
+
+    def attend_tiered(self, q):
+        """q [B][Hq][d]; attention over cache and host tier per head, keyed (b, h)."""
+        G = self.G
+        return {(b, h): o.attend_tiered(widen(q[b, h * G:(h + 1) * G])) for (b, h), o in self.heads.items()}
 
     def decode_step(self, q, k, v, inj_qcodes=None, inj_kcodes=None):
         """q [B][Hq][d] fp32; k, v [B][Hkv][d]; returns per-head dicts keyed (b, h)."""

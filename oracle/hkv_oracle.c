@@ -31,6 +31,11 @@ struct orc_head {
     int vbits;        /* 0: values kept as given; 8: int8 codes with a per-row scale */
     int8_t* vq;       /* [budget][d] value codes (vbits == 8) */
     float* vs;        /* [budget]    value scales (vbits == 8) */
+    int tcap;         /* host tier: capacity in tokens, -1 when there is no tier */
+    int64_t tcount;   /* tokens sent to the tier (may exceed tcap; the excess is not kept) */
+    double* tK;       /* [tcap][d] */
+    double* tV;       /* [tcap][d] */
+    int64_t* ttok;    /* [tcap] */
 };
 
 int orc_words(const orc_head* h) { return h->words; }
@@ -60,6 +65,7 @@ orc_head* orc_create(int d, int n_bits, int budget, int group, const double* R)
     for (size_t s = 0; s < slots; ++s) h->tok[s] = -1;
     h->n = 0;
     h->t = 0;
+    h->tcap = -1;
     return h;
 }
 
@@ -68,6 +74,7 @@ void orc_destroy(orc_head* h)
     if (!h) return;
     free(h->R); free(h->rnorm); free(h->K); free(h->V); free(h->code); free(h->tok);
     free(h->vq); free(h->vs);
+    free(h->tK); free(h->tV); free(h->ttok);
     free(h);
 }
 
@@ -182,6 +189,96 @@ static int place(orc_head* h, const uint32_t* qcodes, int ngroup)
     return pick_victim(h, qcodes, ngroup);
 }
 
+/* READING of the tiered cache (the TTKV summary page: a fast tier in HBM and
+ * a slow tier in host DRAM; recent and important tokens stay fast, older ones
+ * go to the slow tier, and attention over the slow tier is streamed in small
+ * pieces overlapped with compute).  Here the HBM cache is the fast tier, and
+ * every token that leaves it goes to the slow tier instead of being dropped:
+ * the prompt tokens a prefill rule does not keep (in ascending position, once
+ * the prefill is done) and the token each full decode step evicts (in step
+ * order).  An entry is the token's key row, value row and position.  Tokens
+ * past the tier's capacity are counted but not kept. */
+int orc_set_tier(orc_head* h, int capacity)
+{
+    if (h->n != 0 || h->t != 0 || capacity < 0 || h->vbits != 0 || h->tcap >= 0) return -1;
+    size_t c = capacity > 0 ? (size_t)capacity : 1;
+    h->tcap = capacity;
+    h->tcount = 0;
+    h->tK = (double*)calloc(c * h->d, sizeof(double));
+    h->tV = (double*)calloc(c * h->d, sizeof(double));
+    h->ttok = (int64_t*)malloc(c * sizeof(int64_t));
+    for (size_t j = 0; j < c; ++j) h->ttok[j] = -1;
+    return 0;
+}
+
+static void tier_push(orc_head* h, const double* k, const double* v, int64_t pos)
+{
+    if (h->tcap < 0) return;
+    if (h->tcount < h->tcap) {
+        memcpy(h->tK + (size_t)h->tcount * h->d, k, sizeof(double) * h->d);
+        memcpy(h->tV + (size_t)h->tcount * h->d, v, sizeof(double) * h->d);
+        h->ttok[h->tcount] = pos;
+    }
+    h->tcount += 1;
+}
+
+/* After a prefill of n prompt tokens: the ones the cache does not hold go to
+ * the tier in ascending position. */
+static void tier_spill_prompt(orc_head* h, int n, const double* K, const double* V)
+{
+    if (h->tcap < 0 || n <= 0) return;
+    char* held = (char*)calloc((size_t)n, 1);
+    for (int s = 0; s < h->n; ++s)
+        if (h->tok[s] >= 0 && h->tok[s] < n) held[h->tok[s]] = 1;
+    for (int t = 0; t < n; ++t)
+        if (!held[t]) tier_push(h, K + (size_t)t * h->d, V + (size_t)t * h->d, (int64_t)t);
+    free(held);
+}
+
+/* Tier contents: K, V [min(count, capacity)][d], tok [...]; returns the
+ * number of tokens sent to the tier, or -1 without a tier. */
+int64_t orc_get_tier(const orc_head* h, double* K, double* V, int64_t* tok)
+{
+    if (h->tcap < 0) return -1;
+    const int64_t m = h->tcount < h->tcap ? h->tcount : h->tcap;
+    if (K) memcpy(K, h->tK, sizeof(double) * (size_t)m * h->d);
+    if (V) memcpy(V, h->tV, sizeof(double) * (size_t)m * h->d);
+    if (tok) memcpy(tok, h->ttok, sizeof(int64_t) * (size_t)m);
+    return h->tcount;
+}
+
+/* Attention over both tiers: softmax(q . k / sqrt(d)) v over the occupied
+ * cache slots and the tier's kept entries, max logit subtracted first. */
+void orc_attend_tiered(const orc_head* h, const double* q, double* out)
+{
+    const int64_t m = h->tcap < 0 ? 0 : (h->tcount < h->tcap ? h->tcount : h->tcap);
+    const int64_t rows = h->n + m;
+    double* lg = (double*)malloc(sizeof(double) * (rows > 0 ? (size_t)rows : 1));
+    const double scale = 1.0 / sqrt((double)h->d);
+    for (int g = 0; g < h->group; ++g) {
+        const double* qg = q + (size_t)g * h->d;
+        double* og = out + (size_t)g * h->d;
+        double mx = -INFINITY;
+        for (int64_t r = 0; r < rows; ++r) {
+            const double* kr = r < h->n ? h->K + (size_t)r * h->d : h->tK + (size_t)(r - h->n) * h->d;
+            double dot = 0.0;
+            for (int i = 0; i < h->d; ++i) dot += qg[i] * kr[i];
+            lg[r] = dot * scale;
+            if (lg[r] > mx) mx = lg[r];
+        }
+        double den = 0.0;
+        for (int i = 0; i < h->d; ++i) og[i] = 0.0;
+        for (int64_t r = 0; r < rows; ++r) {
+            const double* vr = r < h->n ? h->V + (size_t)r * h->d : h->tV + (size_t)(r - h->n) * h->d;
+            const double p = exp(lg[r] - mx);
+            den += p;
+            for (int i = 0; i < h->d; ++i) og[i] += p * vr[i];
+        }
+        for (int i = 0; i < h->d; ++i) og[i] = rows > 0 ? og[i] / den : 0.0;
+    }
+    free(lg);
+}
+
 /* READING of the prefill rule (the page does not describe prefill): STREAM
  * feeds the prompt through the decode rule one token at a time, scoring the
  * cache against the token's own key code because no query accompanies a
@@ -214,6 +311,7 @@ int orc_prefill(orc_head* h, int policy, int n, const double* K, const double* V
     free(c);
     free(f);
     h->t = n;
+    tier_spill_prompt(h, n, K, V);
     return 0;
 }
 
@@ -264,6 +362,7 @@ int orc_prefill_query(orc_head* h, int n, const double* K, const double* V, cons
     free(qc);
     free(qf);
     h->t = n;
+    tier_spill_prompt(h, n, K, V);
     return 0;
 }
 
@@ -348,6 +447,7 @@ int orc_prefill_chunks(orc_head* h, int n, int chunk, const double* K, const dou
         for (int r = j; r < (h->budget + chunk - 1) / chunk; ++r) kept[r] = -1;
     h->n = slot;
     h->t = n;
+    tier_spill_prompt(h, n, K, V);
     free(codes);
     free(f);
     free(keep);
@@ -401,7 +501,10 @@ int orc_decode_step(orc_head* h, const double* q, const double* k, const double*
     if (inj_qcodes) memcpy(qc, inj_qcodes, sizeof(uint32_t) * (size_t)G * W);
     if (inj_kcode) memcpy(kc, inj_kcode, sizeof(uint32_t) * (size_t)W);
 
+    const int was_full = h->n >= h->budget;
     int e = place(h, qc, G);
+    /* the evicted token leaves the cache for the tier, if there is one */
+    if (e >= 0 && was_full) tier_push(h, h->K + (size_t)e * h->d, h->V + (size_t)e * h->d, h->tok[e]);
     if (e >= 0) write_slot(h, e, k, v, kc, h->t);
     h->t += 1;
     if (out) orc_attend(h, q, out);
@@ -424,7 +527,7 @@ void orc_scores(const orc_head* h, const uint32_t* qcodes, int32_t* scores)
  * (bits = 0).  Only on an empty cache; returns 0, or -1. */
 int orc_set_value_bits(orc_head* h, int bits)
 {
-    if (h->n != 0 || (bits != 0 && bits != 8)) return -1;
+    if (h->n != 0 || (bits != 0 && bits != 8) || (bits == 8 && h->tcap >= 0)) return -1;
     h->vbits = bits;
     if (bits == 8 && !h->vq) {
         size_t slots = h->budget > 0 ? (size_t)h->budget : 1;

@@ -74,6 +74,18 @@ int orc_prefill_chunks(orc_head* h, int n, int chunk, const double* K, const dou
                        const uint32_t* inj_codes, const uint32_t* inj_qcodes, const int32_t* reuse,
                        int32_t* kept);
 
+/* Host tier (a reading; see the .c file): tokens leaving the cache -- the
+ * prompt tokens a prefill does not keep, in ascending position, then each
+ * token a full decode step evicts -- are kept in a tier of `capacity` tokens
+ * instead of being dropped.  Only on an empty cache with values as given;
+ * returns 0, or -1. */
+int orc_set_tier(orc_head* h, int capacity);
+/* Tier contents K, V [min(count, capacity)][d], tok [...] (any may be NULL);
+ * returns the number of tokens sent to the tier, -1 without a tier. */
+int64_t orc_get_tier(const orc_head* h, double* K, double* V, int64_t* tok);
+/* Attention over the cache and the tier's kept tokens: out [group][d]. */
+void orc_attend_tiered(const orc_head* h, const double* q, double* out);
+
 /* Value compression (a reading; see the .c file): bits = 8 stores every
  * value row as int8 codes with one fp32 scale (fp32 arithmetic: scale =
  * max|v| / 127, code = round-half-even(v / scale) clamped to +-127) and the

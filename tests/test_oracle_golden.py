@@ -39,15 +39,20 @@ def _cases():
                                   int(kv["evicted"])))
         elif tok[0] == "final_tok":
             cur["final_tok"] = [int(x) for x in tok[1:]]
+        elif tok[0] == "tier_tok":
+            cur["tier_tok"] = [int(x) for x in tok[1:]]
         elif tok[0] == "end":
             cases.append(cur)
     return cases
 
 
+@pytest.mark.parametrize("tier", [False, True], ids=["no_tier", "tier"])
 @pytest.mark.parametrize("case", _cases(), ids=lambda c: c["name"])
-def test_handworked(oracle_mod, case):
+def test_handworked(oracle_mod, case, tier):
     R = np.eye(D, B)
-    o = oracle_mod.OracleHead(R, case["budget"], case["group"])
+    if tier and "tier_tok" not in case:
+        pytest.skip("no tier_tok line")
+    o = oracle_mod.OracleHead(R, case["budget"], case["group"], tier=64 if tier else -1)
     K = np.stack([_vec(c) for c in case["prompt"]])
     V = np.arange(K.size, dtype=np.float64).reshape(K.shape)
     if case["policy"] == "query":
@@ -78,3 +83,11 @@ def test_handworked(oracle_mod, case):
         assert int(r["kcode"][0]) == kc
         assert r["evicted"] == ev
     assert list(o.state()["tok"]) == case["final_tok"]
+    if tier:
+        t = o.tier()
+        assert list(t["tok"]) == case["tier_tok"] and t["count"] == len(case["tier_tok"])
+        # the tier holds the rows the tokens had: prompt rows for prompt tokens
+        for j, tk in enumerate(t["tok"]):
+            if tk < len(case["prompt"]):
+                np.testing.assert_array_equal(t["K"][j], K[tk])
+                np.testing.assert_array_equal(t["V"][j], V[tk])
