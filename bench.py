@@ -131,6 +131,102 @@ def cpu_baseline(shape, budget_s: float = 15.0):
                       f"sequence(s) per workload step"}
 
 
+def host_link_bandwidth(mib: int = 512, reps: int = 5) -> float:
+    """GB/s of a host-to-device copy from pinned host memory: the ceiling of a
+    kernel that streams pinned host memory over the host link."""
+    import torch
+    src = torch.empty((mib << 20) // 4, dtype=torch.float32, pin_memory=True)
+    dst = torch.empty(src.shape, dtype=torch.float32, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src, non_blocking=True)
+    b.record()
+    torch.cuda.synchronize()
+    return (mib << 20) * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+
+
+def run_tier(args, shape, n, budgets, P, kvd, sched, make_layer_inputs):
+    """Tiered decode: one cache whose evicted and dropped tokens go to a host
+    tier in pinned memory; a step is hkv_decode_step followed by
+    hkv_attend_tiered (attention over cache and tier, the tier streamed over the
+    host link).  Prints one JSON line of its own."""
+    import numpy as np
+    import torch
+    from lsh_eviction_amd import hkv
+    n_max = int(n.max())
+    cap = n_max + args.steps + args.warmup + 8
+    pol = {"stream": hkv.HKV_PREFILL_STREAM, "truncate": hkv.HKV_PREFILL_TRUNCATE}[args.prefill]
+    c = hkv.Cache(shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.n_bits, kvd,
+                  budgets, P.R, prefill_policy=pol, decode_schedule=sched, max_prompt=n_max, chunk=args.chunk,
+                  tier_capacity=cap)
+    c.attach_tier()
+    K, V = make_layer_inputs(shape, P, 0, shape.index)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    c.prefill(K, V, n)
+    e1.record()
+    torch.cuda.synchronize()
+    prefill_ms = e0.elapsed_time(e1)
+    del K, V
+    g = torch.Generator(device="cuda")
+    g.manual_seed(shape.index + 7)
+    dt = torch.bfloat16 if shape.kv_dtype == "bf16" else torch.float32
+    POOL = 8
+    qs = torch.randn((POOL, shape.batch, shape.n_q_heads, shape.head_dim), generator=g, device="cuda")
+    ks = torch.randn((POOL, shape.batch, shape.n_kv_heads, shape.head_dim), generator=g, device="cuda").to(dt)
+    vs = torch.randn((POOL, shape.batch, shape.n_kv_heads, shape.head_dim), generator=g, device="cuda").to(dt)
+    out = torch.empty((shape.batch, shape.n_q_heads, shape.head_dim), device="cuda")
+    tout = torch.empty_like(out)
+    ev = torch.empty((shape.batch, shape.n_kv_heads), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        c.decode_step(qs[i % POOL], ks[i % POOL], vs[i % POOL], out, ev, stream)
+        c.attend_tiered(qs[i % POOL], tout, stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms_step = a.elapsed_time(b) / args.steps
+    # the tiered attention alone (the tier no longer changes)
+    a2, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a2.record(stream)
+    for i in range(args.steps):
+        c.attend_tiered(qs[i % POOL], tout, stream)
+    b2.record(stream)
+    torch.cuda.synchronize()
+    ms_att = a2.elapsed_time(b2) / args.steps
+    cnt = hkv.to_numpy(c.tier_counts()).astype(np.int64)
+    rows = int(np.minimum(cnt, cap).sum())
+    es = 2 if shape.kv_dtype == "bf16" else 4
+    tier_bytes = rows * 2 * shape.head_dim * es
+    link = host_link_bandwidth()
+    achieved = tier_bytes / (ms_att * 1e-3) / 1e9
+    rec = {
+        "metric": "tiered decode steps/s (decode step + attention over HBM cache and host tier)",
+        "value": round(1000.0 / ms_step, 2), "unit": "tiered decode steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "data": "synthetic",
+        "config": {"workload": args.config, "prefill_rule": args.prefill, "tier_capacity": cap,
+                   "tier_rows_per_head_mean": round(rows / (shape.batch * shape.n_kv_heads), 1)},
+        "roofline": {"bound": "host link", "achieved": round(achieved, 1), "peak": round(link, 1), "unit": "GB/s",
+                     "frac": round(achieved / link, 4), "traffic": None},
+        "attend_tiered_ms": round(ms_att, 4), "tier_bytes_per_attend": tier_bytes,
+        "host_link_h2d_gbs": round(link, 1), "prefill_ms_with_tier_spill": round(prefill_ms, 2),
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,6 +242,8 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="layer caches rotated (0 = enough to exceed the MALL twice)")
     ap.add_argument("--graph", action="store_true", help="replay the steps of one rotation as a HIP graph")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--tier", action="store_true",
+                    help="tiered decode: evictions kept in a pinned host tier, attention over both tiers")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
 
@@ -168,6 +266,12 @@ def main():
     P = datagen.prompt(shape.scaled(prompt=1, prompt_range=None, budget_frac=None, budget=1, batch=1))
     P.prompt_lens, P.budgets = n, budgets
     n_max = int(n.max())
+    if args.tier:
+        if args.prefill not in ("stream", "truncate"):
+            print(json.dumps({"error": "--tier takes --prefill stream or truncate"}))
+            sys.exit(2)
+        run_tier(args, shape, n, budgets, P, kvd, sched, make_layer_inputs)
+        return
 
     caches, prefill_ms = [], []
     kept = None      # chunk rule: layer 0 scores its chunks, later layers reuse its kept lists

@@ -50,6 +50,12 @@
  *     anything is enqueued, so a call that fails validation has no effect.  A
  *     launch failure poisons the handle: every later call returns
  *     HKV_ERR_STATE.  hkv_last_error() gives a one-line reason.
+ *   - host tier (tier_capacity > 0, a reading of the TTKV page's slow DRAM
+ *     tier): every token that leaves the cache -- the prompt tokens a prefill
+ *     rule does not keep, in position order, then the token each full decode
+ *     step evicts, in step order -- is appended to caller-owned tier buffers
+ *     (normally pinned host memory) instead of being dropped, and
+ *     hkv_attend_tiered attends over the cache and the tier together.
  *   - values (value_bits = 8, a reading of the DASH-KV page's value
  *     compression): V rows are kept as int8 codes with a per-row fp32 scale;
  *     keys, codes and eviction are unchanged.  Inputs stay kv dtype; the
@@ -109,6 +115,10 @@ typedef struct {
     int32_t prefill_chunk;   /* tokens per chunk under HKV_PREFILL_CHUNK: 0
                                 selects 10, else 1 .. 32; must be 0 under the
                                 other policies */
+    int32_t tier_capacity;   /* 0: no host tier; else the tokens per (sequence,
+                                KV head) a host tier attached with
+                                hkv_attach_tier keeps (at most 2^28; needs
+                                value_bits 0) */
     const int32_t* budgets;  /* host [batch]: cache slots S_b of each sequence */
 } hkv_config;
 
@@ -195,6 +205,31 @@ hkv_status hkv_prefill_chunks(hkv_cache* c, const void* K, const void* V, const 
  * in a HIP graph and replayed.  HKV_ERR_STATE before a prefill. */
 hkv_status hkv_decode_step(hkv_cache* c, const float* q, const void* k, const void* v,
                            float* out, int32_t* evicted_slot, void* stream);
+
+/* Attach the host tier (a cache created with tier_capacity > 0, before its
+ * prefill; HKV_ERR_STATE after it, HKV_ERR_INVALID_ARG without a capacity).
+ * K, V: [B][Hkv][tier_capacity][d] kv dtype; tok: [B][Hkv][tier_capacity]
+ * int32.  All three must be memory the GPU can address: pinned host memory
+ * (hipHostMalloc; the GPU reads and writes it over the host link) or device
+ * memory; owned by the caller and alive while the handle is used.  Entry j
+ * of a (sequence, KV head) holds the j-th token that left its cache (its key
+ * row, value row and position); entries past tier_capacity are not stored,
+ * but counted.  Tier counts start at 0.  Stream-ordered. */
+hkv_status hkv_attach_tier(hkv_cache* c, void* K, void* V, int32_t* tok, void* stream);
+
+/* Tokens sent to the tier so far, per (sequence, KV head): counts [B][Hkv]
+ * int32 (device or pinned host memory); may exceed tier_capacity (entries
+ * past it were not stored).  HKV_ERR_STATE without an attached tier. */
+hkv_status hkv_tier_counts(const hkv_cache* c, int32_t* counts, void* stream);
+
+/* Attention over the cache and its host tier together: out [B][Hq][d] fp32 =
+ * softmax(q K^T / sqrt(d)) V over the occupied slots and the stored tier
+ * entries of the query head's KV head; q: device fp32 [B][Hq][d] (16-byte
+ * aligned).  While no tier has overflowed this is attention over every token
+ * seen.  Split-K over both tiers and one LSE merge; the tier is read in place
+ * over the host link, every block streaming its rows while it computes.
+ * HKV_ERR_STATE before a prefill or without an attached tier. */
+hkv_status hkv_attend_tiered(hkv_cache* c, const float* q, float* out, void* stream);
 
 /* Free the handle (host metadata only; the workspace stays the caller's). */
 hkv_status hkv_destroy(hkv_cache* c);

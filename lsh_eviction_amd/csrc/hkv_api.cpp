@@ -122,6 +122,14 @@ extern "C" hkv_status hkv_create(const hkv_config* cfg, const float* R_host, voi
     d.csum = (int*)(ws + L.off_csum);
     d.pchunk = L.pchunk;
     d.nchunk_max = (long long)L.nchunk_max;
+    d.tK = d.tV = nullptr;
+    d.ttok = nullptr;
+    d.tcount = L.tcap > 0 ? (int*)(ws + L.off_tcount) : nullptr;
+    d.tpart = L.tcap > 0 ? (float*)(ws + L.off_tpart) : nullptr;
+    d.tflag = L.tcap > 0 ? (unsigned*)(ws + L.off_tflag) : nullptr;
+    d.tcap = L.tcap;
+    d.tsplit = L.tsplit;
+    d.tflag_words = (long long)L.tflag_words;
 
     hipError_t e = hipMemcpyAsync((void*)d.R, R_host, (size_t)L.d * L.bits * sizeof(float),
                                   hipMemcpyHostToDevice, st);
@@ -233,6 +241,78 @@ extern "C" hkv_status hkv_prefill_chunks(hkv_cache* c, const void* K, const void
     if (c->lay.prefill_policy != HKV_PREFILL_CHUNK)
         return fail(c, HKV_ERR_INVALID_ARG, "hkv_prefill_chunks: this cache was not created with HKV_PREFILL_CHUNK");
     return prefill_impl(c, K, V, q_obs, prompt_lens, n_max, stream, "hkv_prefill_chunks", reuse, kept);
+}
+
+// Device address of a buffer the GPU can reach: device memory as is, pinned
+// host memory through hipHostGetDevicePointer; null for anything else.
+static void* gpu_address(void* p)
+{
+    hipPointerAttribute_t a;
+    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    if (a.type == hipMemoryTypeDevice) return p;
+    if (a.type == hipMemoryTypeHost) {
+        void* d = nullptr;
+        if (hipHostGetDevicePointer(&d, p, 0) != hipSuccess) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        return d;
+    }
+    return nullptr;
+}
+
+extern "C" hkv_status hkv_attach_tier(hkv_cache* c, void* K, void* V, int32_t* tok, void* stream)
+{
+    hkv_status s = usable(c);
+    if (s != HKV_OK) return s;
+    if (c->lay.tcap <= 0)
+        return fail(c, HKV_ERR_INVALID_ARG, "hkv_attach_tier: the cache was created with tier_capacity 0");
+    if (c->prefilled) return fail(c, HKV_ERR_STATE, "hkv_attach_tier: attach the tier before the prefill");
+    if (!K || !V || !tok) return fail(c, HKV_ERR_INVALID_ARG, "hkv_attach_tier: NULL buffer");
+    if (!aligned(K, 16) || !aligned(V, 16) || !aligned(tok, 4))
+        return fail(c, HKV_ERR_INVALID_ARG, "hkv_attach_tier: K and V must be 16-byte aligned, tok 4-byte aligned");
+    void* dk = gpu_address(K);
+    void* dv = gpu_address(V);
+    void* dt = gpu_address(tok);
+    if (!dk || !dv || !dt)
+        return fail(c, HKV_ERR_INVALID_ARG,
+                    "hkv_attach_tier: tier buffers must be pinned host memory (hipHostMalloc) or device memory");
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = hipMemsetAsync(c->dev.tcount, 0, (size_t)c->lay.B * c->lay.Hkv * 4, st);
+    s = check_launch(c, e, st, "hkv_attach_tier");
+    if (s != HKV_OK) return s;
+    c->dev.tK = dk;
+    c->dev.tV = dv;
+    c->dev.ttok = (int*)dt;
+    return HKV_OK;
+}
+
+extern "C" hkv_status hkv_tier_counts(const hkv_cache* cc, int32_t* counts, void* stream)
+{
+    hkv_cache* c = const_cast<hkv_cache*>(cc);
+    hkv_status s = usable(c);
+    if (s != HKV_OK) return s;
+    if (!c->dev.tK) return fail(c, HKV_ERR_STATE, "hkv_tier_counts: no tier attached");
+    if (!counts) return fail(c, HKV_ERR_INVALID_ARG, "hkv_tier_counts: counts is NULL");
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = hipMemcpyAsync(counts, c->dev.tcount, (size_t)c->lay.B * c->lay.Hkv * 4, hipMemcpyDefault, st);
+    return check_launch(c, e, st, "hkv_tier_counts");
+}
+
+extern "C" hkv_status hkv_attend_tiered(hkv_cache* c, const float* q, float* out, void* stream)
+{
+    hkv_status s = usable(c);
+    if (s != HKV_OK) return s;
+    if (!c->dev.tK) return fail(c, HKV_ERR_STATE, "hkv_attend_tiered: no tier attached");
+    if (!c->prefilled) return fail(c, HKV_ERR_STATE, "hkv_attend_tiered: call hkv_prefill* or hkv_set_state first");
+    if (!q || !out) return fail(c, HKV_ERR_INVALID_ARG, "hkv_attend_tiered: NULL buffer");
+    if (!aligned(q, 16) || !aligned(out, 16))
+        return fail(c, HKV_ERR_INVALID_ARG, "hkv_attend_tiered: q and out must be 16-byte aligned");
+    hipStream_t st = (hipStream_t)stream;
+    return check_launch(c, hkv::launch_attend_tiered(c->dev, q, out, st), st, "hkv_attend_tiered");
 }
 
 extern "C" hkv_status hkv_decode_step(hkv_cache* c, const float* q, const void* k, const void* v,

@@ -37,6 +37,15 @@ struct DevCache {
     int* csum;                      // [B][Hkv][nchunk_max] per-chunk scores or flags (CHUNK prefill)
     int pchunk;                     // tokens per prefill chunk (CHUNK prefill)
     long long nchunk_max;
+    // host tier (null tK when none is attached)
+    void* tK;                       // [B][Hkv][tcap][d] kv dtype, GPU-addressable (pinned host or device)
+    void* tV;
+    int* ttok;                      // [B][Hkv][tcap] token positions
+    int* tcount;                    // [B][Hkv] tokens sent to the tier (device)
+    float* tpart;                   // [B][Hq][tsplit][d + 4] partials of the tiered attention
+    unsigned* tflag;                // [B][Hkv][tflag_words] prompt tokens the cache holds (prefill spill)
+    int tcap, tsplit;
+    long long tflag_words;
 };
 
 // decode, fused schedule: one launch
@@ -56,6 +65,9 @@ hipError_t launch_prefill(const DevCache& c, const void* K, const void* V, const
 // CHUNK prefill: q_obs [B][Hq][d] fp32 (may be null with reuse), reuse / kept [B][Hkv][kmax] (may be null)
 hipError_t launch_prefill_chunks(const DevCache& c, const void* K, const void* V, const float* q_obs,
                                  const int* reuse, int* kept, int kmax, int n_max, hipStream_t st);
+// host tier: prefill spill (after the gather) and attention over cache + tier
+hipError_t launch_tier_spill_prompt(const DevCache& c, const void* K, const void* V, int n_max, hipStream_t st);
+hipError_t launch_attend_tiered(const DevCache& c, const float* q, float* out, hipStream_t st);
 // checkpoint
 hipError_t launch_export_codes(const DevCache& c, uint32_t* codes, hipStream_t st);
 hipError_t launch_import_codes(const DevCache& c, const uint32_t* codes, hipStream_t st);

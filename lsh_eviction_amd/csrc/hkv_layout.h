@@ -17,6 +17,8 @@ constexpr size_t kLdsTableBytes = 128 * 1024;   // prefill code table in LDS
 constexpr int kDefaultChunk = 1024;
 constexpr int kDefaultPrefillChunk = 10;   // tokens per prefill chunk (HKV_PREFILL_CHUNK)
 constexpr int kMaxPrefillChunk = 32;
+constexpr int kMaxTierCapacity = 1 << 28;
+constexpr int kTierBlocks = 2048;   // tier attention: splits per head = this / heads, in [1, 256]
 constexpr size_t kAlign = 256;
 
 struct Layout {
@@ -25,12 +27,16 @@ struct Layout {
     int Smax, chunk, nsplit, max_prompt;
     int pchunk;            // tokens per prefill chunk (HKV_PREFILL_CHUNK), else 0
     size_t nchunk_max;     // prompt chunks per head, padded (HKV_PREFILL_CHUNK)
+    int tcap;              // host tier capacity per head (0: none)
+    int tsplit;            // splits per head of the tiered attention over the host tier
+    size_t tflag_words;    // words per head of the prompt's held-token bitset
     size_t code_slots;     // slots per head in the code table (padded)
     size_t pcode_slots;    // prompt positions per head in the prefill code buffer (padded)
     // byte offsets into the workspace
     size_t off_R, off_budget, off_plen, off_state, off_K, off_V, off_code, off_tok;
     size_t off_dbg_q, off_dbg_k, off_part, off_frec, off_fscal, off_cand_v, off_ekey;
     size_t off_info, off_count, off_pcode, off_qcode, off_vs, off_csum;
+    size_t off_tcount, off_tpart, off_tflag;
     size_t v_bytes;        // bytes of the V region (kv dtype, or int8 codes)
     size_t total;
 };

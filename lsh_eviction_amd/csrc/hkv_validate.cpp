@@ -44,6 +44,10 @@ hkv_status compute_layout(const hkv_config* cfg, Layout* L, char* err, size_t er
         FAIL(HKV_ERR_UNSUPPORTED, "value_bits %d not in {0, 8}", cfg->value_bits);
     if (cfg->value_bits == 8 && (cfg->kv_dtype != HKV_BF16 || cfg->decode_schedule != HKV_DECODE_FUSED))
         FAIL(HKV_ERR_UNSUPPORTED, "value_bits 8 needs kv_dtype HKV_BF16 and HKV_DECODE_FUSED");
+    if (cfg->tier_capacity < 0 || cfg->tier_capacity > kMaxTierCapacity)
+        FAIL(HKV_ERR_UNSUPPORTED, "tier_capacity %d outside [0, %d]", cfg->tier_capacity, kMaxTierCapacity);
+    if (cfg->tier_capacity > 0 && cfg->value_bits != 0)
+        FAIL(HKV_ERR_UNSUPPORTED, "a host tier needs value_bits 0");
     if (cfg->decode_schedule != HKV_DECODE_FUSED && cfg->decode_schedule != HKV_DECODE_SPLIT)
         FAIL(HKV_ERR_UNSUPPORTED, "decode_schedule %d unknown", cfg->decode_schedule);
     if (cfg->max_prompt < 0 || cfg->max_prompt > (1 << 24))
@@ -81,6 +85,14 @@ hkv_status compute_layout(const hkv_config* cfg, Layout* L, char* err, size_t er
     l.pcode_slots = align_up((size_t)(cfg->max_prompt > 0 ? cfg->max_prompt : 1), 64);
     l.pchunk = chunked ? (cfg->prefill_chunk ? cfg->prefill_chunk : kDefaultPrefillChunk) : 0;
     l.nchunk_max = chunked ? align_up((size_t)((cfg->max_prompt + l.pchunk - 1) / l.pchunk) + 1, 64) : 0;
+    l.tcap = cfg->tier_capacity;
+    if (l.tcap > 0) {
+        int ts = kTierBlocks / (l.B * l.Hkv);
+        ts = ts < 1 ? 1 : (ts > 256 ? 256 : ts);
+        const int rows16 = (l.tcap + 15) / 16;   // no split smaller than 16 rows
+        l.tsplit = ts < rows16 ? ts : rows16;
+        l.tflag_words = (size_t)(cfg->max_prompt + 31) / 32 + 1;
+    }
 
     const size_t heads = (size_t)l.B * l.Hkv;
     size_t off = 0;
@@ -113,6 +125,10 @@ hkv_status compute_layout(const hkv_config* cfg, Layout* L, char* err, size_t er
     l.off_qcode = take(cfg->prefill_policy == HKV_PREFILL_QUERY ? (size_t)l.B * l.Hq * l.pcode_slots * cb : 0);
     // per-chunk scores of the prompt (HKV_PREFILL_CHUNK)
     l.off_csum = take(heads * l.nchunk_max * 4);
+    // host tier: counts, partials of the tiered attention, held-token bitset of the prompt
+    l.off_tcount = take(l.tcap > 0 ? heads * 4 : 0);
+    l.off_tpart = take(l.tcap > 0 ? (size_t)l.B * l.Hq * l.tsplit * (l.d + 4) * 4 : 0);
+    l.off_tflag = take(l.tcap > 0 ? heads * l.tflag_words * 4 : 0);
     l.total = off;
     return HKV_OK;
 #undef FAIL

@@ -1302,6 +1302,24 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
                         fmaf(vn.w, sn, A.w) * inv);
     }
 
+    // a host tier keeps the token that leaves: its rows and position are
+    // copied out before the overwrite below (the same thread reads and then
+    // writes each element, so the rows need no barrier; the count does)
+    if constexpr (!VQ) {
+        if (c.tK != nullptr && full) {
+            const int cnt = c.tcount[head];
+            if (cnt < c.tcap) {
+                const size_t dst = ((size_t)head * c.tcap + cnt) * D;
+                for (int i = tid; i < D; i += kThreads) {
+                    reinterpret_cast<KT*>(c.tK)[dst + i] = Kh[(size_t)e * D + i];
+                    reinterpret_cast<KT*>(c.tV)[dst + i] = Vh[(size_t)e * D + i];
+                }
+                if (tid == 0) c.ttok[(size_t)head * c.tcap + cnt] = c.tok[rowbase + e];
+            }
+            __syncthreads();   // every thread has read the count before it moves
+            if (tid == 0) c.tcount[head] = cnt + 1;
+        }
+    }
     // stage 5: the new token takes slot e
     for (int i = tid; i < D; i += kThreads) {
         Kh[(size_t)e * D + i] = s_kn[i];
@@ -1402,6 +1420,20 @@ __global__ void k_evict_write(DevCache c, const KT* __restrict__ knew, const KT*
     const size_t rowbase = (size_t)head * c.Smax;
     KT* Kh = reinterpret_cast<KT*>(c.K) + rowbase * D;
     KT* Vh = reinterpret_cast<KT*>(c.V) + rowbase * D;
+    // the leaving token goes to the host tier first (same thread per element)
+    if (c.tK != nullptr && full) {
+        const int cnt = c.tcount[head];
+        if (cnt < c.tcap) {
+            const size_t dst = ((size_t)head * c.tcap + cnt) * D;
+            for (int i = threadIdx.x; i < D; i += blockDim.x) {
+                reinterpret_cast<KT*>(c.tK)[dst + i] = Kh[(size_t)e * D + i];
+                reinterpret_cast<KT*>(c.tV)[dst + i] = Vh[(size_t)e * D + i];
+            }
+            if (threadIdx.x == 0) c.ttok[(size_t)head * c.tcap + cnt] = c.tok[rowbase + e];
+        }
+        __syncthreads();   // every thread has read the count before it moves
+        if (threadIdx.x == 0) c.tcount[head] = cnt + 1;
+    }
     for (int i = threadIdx.x; i < D; i += blockDim.x) {
         Kh[(size_t)e * D + i] = knew[(size_t)head * D + i];
         Vh[(size_t)e * D + i] = vnew[(size_t)head * D + i];
@@ -1471,6 +1503,78 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(DevCache c, float*
     };
     float4 o;
     if (merge_head<D>(sm, c.nsplit, nsb, rec, false, -1, cand, false, nullptr, make_float4(0.f, 0.f, 0.f, 0.f), o))
+        reinterpret_cast<float4*>(out + row * D)[threadIdx.x] = o;
+}
+
+// Rows of one split of a head's host tier (at least 16, a multiple of 16).
+__device__ __forceinline__ int tier_rows_per_split(int m, int tsplit)
+{
+    return (((m + tsplit - 1) / tsplit) + 15) & ~15;
+}
+
+// Split-K attention over the host tier: the stored entries of a head's tier
+// are cut into c.tsplit splits and each block folds one into a partial
+// (acc, m, l), like k_attn_split does over the cache.  The rows are read in
+// place (pinned host memory over the host link, or device memory); every wave
+// keeps its next tiles in flight while it computes on the current ones.
+template <int D, int GM, typename KT>
+__global__ __launch_bounds__(kThreads) void k_attn_tier(DevCache c, const float* __restrict__ q)
+{
+    constexpr bool kMfma = std::is_same<KT, bf16_t>::value;
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int head = b * c.Hkv + h;
+    const int m = min(c.tcount[head], c.tcap);
+    const int rps = tier_rows_per_split(m, c.tsplit);
+    const int s0 = split * rps;
+    if (s0 >= m) return;
+    __shared__ AttnSmem<D, GM> sm;
+    __shared__ PSmem<GM, tile_rows<GM>()> ps;
+    const int hq0 = b * c.Hq + h * c.G;
+    const size_t rowbase = (size_t)head * c.tcap;
+    const KT* Kh = reinterpret_cast<const KT*>(c.tK) + rowbase * D;
+    const KT* Vh = reinterpret_cast<const KT*>(c.tV) + rowbase * D;
+    const int len = min(s0 + rps, m) - s0;
+    const int wave = threadIdx.x >> 6;
+    if constexpr (kMfma) {
+        constexpr int TR = tile_rows<GM>(), NB = ring_depth<GM>();
+        MTile<D, TR> ring[NB];
+        const int ntile = len > wave * TR ? (len - wave * TR + kWaves * TR - 1) / (kWaves * TR) : 0;
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+            if (i < ntile) ring[i].load(Kh, Vh, nullptr, s0, len, (wave + i * kWaves) * TR);
+        attend_rows_mfma<D, GM, TR, NB>(Kh, Vh, nullptr, q + (size_t)hq0 * D, c.G, s0, len, -1, ring, sm, ps);
+    } else {
+        Tile<D, KT> first;
+        first.load(Kh, Vh, s0, len, wave * Tile<D, KT>::ROWS);
+        attend_rows<D, GM, KT>(Kh, Vh, q + (size_t)hq0 * D, c.G, s0, len, -1, first, sm);
+    }
+    store_partial<D, GM>(sm, c.tpart, hq0, c.G, c.tsplit, split);
+}
+
+// LSE merge of the cache's split partials and the tier's split partials of
+// one query head into the output.
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void k_attn_merge_tiered(DevCache c, float* __restrict__ out)
+{
+    const int hq = blockIdx.x, b = blockIdx.y;
+    const int head = b * c.Hkv + hq / c.G;
+    const int n = c.state[2 * head];
+    const int nsb = max((n + c.chunk - 1) / c.chunk, 1);
+    const int m = min(c.tcount[head], c.tcap);
+    const int rps = tier_rows_per_split(m, c.tsplit);
+    const int nst = m > 0 ? (m + rps - 1) / rps : 0;
+    const size_t row = (size_t)b * c.Hq + hq;
+    const float* part = c.part + row * c.nsplit * (D + 4);
+    const float* tpart = c.tpart + row * c.tsplit * (D + 4);
+    __shared__ MergeSmem<D> sm;
+    auto rec = [&](int j) { return j < nsb ? part + (size_t)j * (D + 4) : tpart + (size_t)(j - nsb) * (D + 4); };
+    auto cand = [&](int, float& cl, const float*& cv) {
+        cl = -INFINITY;
+        cv = nullptr;
+    };
+    float4 o;
+    if (merge_head<D>(sm, nsb + nst, nsb + nst, rec, false, -1, cand, false, nullptr,
+                      make_float4(0.f, 0.f, 0.f, 0.f), o))
         reinterpret_cast<float4*>(out + row * D)[threadIdx.x] = o;
 }
 
@@ -1563,6 +1667,23 @@ hipError_t launch_decode_fused(const DevCache& c, const float* q, const void* k,
                                        0, st, c, q, (const KT*)k, (const KT*)v, out, evicted);
                     return hipGetLastError();
                 });
+            });
+        });
+    });
+}
+
+hipError_t launch_attend_tiered(const DevCache& c, const float* q, float* out, hipStream_t st)
+{
+    return with_kv(c, [&](auto kt) {
+        using KT = decltype(kt);
+        return with_d(c, [&](auto dd) {
+            constexpr int D = decltype(dd)::value;
+            return with_gm(c, [&](auto gg) {
+                constexpr int GM = decltype(gg)::value;
+                hipLaunchKernelGGL((k_attn_split<D, GM, KT>), dim3(c.nsplit, c.Hkv, c.B), dim3(kThreads), 0, st, c, q);
+                hipLaunchKernelGGL((k_attn_tier<D, GM, KT>), dim3(c.tsplit, c.Hkv, c.B), dim3(kThreads), 0, st, c, q);
+                hipLaunchKernelGGL((k_attn_merge_tiered<D>), dim3(c.Hq, c.B), dim3(kMergeThreads), 0, st, c, out);
+                return hipGetLastError();
             });
         });
     });

@@ -474,6 +474,68 @@ __global__ __launch_bounds__(kSelThreads) void k_chunk_select(DevCache c, const 
     if (tid == 0) c.state[2 * head] = n;
 }
 
+// Host tier at prefill: the prompt tokens the cache does not hold become the
+// tier's entries, in position order.  One block per head marks the held
+// tokens in a bitset (device atomics, read back through L2 after a fence) and
+// writes the positions of the others to the tier's token array with block
+// prefix counts; k_tier_copy_prompt then copies their rows.
+__global__ __launch_bounds__(kSelThreads) void k_tier_list_dropped(DevCache c)
+{
+    const int h = blockIdx.x, b = blockIdx.y, head = b * c.Hkv + h;
+    const int tid = threadIdx.x;
+    const int N = c.plen[b], n = c.state[2 * head];
+    const int words = (N + 31) / 32;
+    unsigned* flags = c.tflag + (size_t)head * c.tflag_words;
+    const size_t rowbase = (size_t)head * c.Smax;
+    __shared__ int s_w[kSelWaves];
+    for (int w = tid; w < words; w += kSelThreads) flags[w] = 0u;
+    __threadfence();
+    __syncthreads();
+    for (int s = tid; s < n; s += kSelThreads) {
+        const int t = c.tok[rowbase + s];
+        if (t >= 0 && t < N) atomicOr(flags + (t >> 5), 1u << (t & 31));
+    }
+    __threadfence();
+    __syncthreads();
+    const int cnt0 = c.tcount[head];
+    int base = 0;
+    for (int t0 = 0; t0 < N; t0 += kSelThreads) {
+        const int t = t0 + tid;
+        bool drop = false;
+        if (t < N) {
+            const unsigned w = __hip_atomic_load(flags + (t >> 5), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            drop = !((w >> (t & 31)) & 1u);
+        }
+        int total;
+        const int pos = cnt0 + base + block_prefix(drop, s_w, total);
+        if (drop && pos < c.tcap) c.ttok[(size_t)head * c.tcap + pos] = t;
+        base += total;
+    }
+    if (tid == 0) c.tcount[head] = cnt0 + base;   // every thread read cnt0 before the loop's barriers
+}
+
+// Rows of the listed prompt tokens into the tier: 16 rows per block, 16 lanes
+// per row.
+template <int D, typename KT>
+__global__ __launch_bounds__(256) void k_tier_copy_prompt(DevCache c, const KT* __restrict__ Kp,
+                                                          const KT* __restrict__ Vp, int n_max)
+{
+    constexpr int CH = D * (int)sizeof(KT) / 16;   // 16-byte pieces per row
+    const int h = blockIdx.y, b = blockIdx.z, head = b * c.Hkv + h;
+    const int m = min(c.tcount[head], c.tcap);
+    const int j = blockIdx.x * 16 + threadIdx.x / 16, l = threadIdx.x % 16;
+    if (j >= m) return;
+    const int t = c.ttok[(size_t)head * c.tcap + j];
+    const uint4* ks = reinterpret_cast<const uint4*>(Kp + ((size_t)head * n_max + t) * D);
+    const uint4* vs = reinterpret_cast<const uint4*>(Vp + ((size_t)head * n_max + t) * D);
+    uint4* kd = reinterpret_cast<uint4*>(reinterpret_cast<KT*>(c.tK) + ((size_t)head * c.tcap + j) * D);
+    uint4* vd = reinterpret_cast<uint4*>(reinterpret_cast<KT*>(c.tV) + ((size_t)head * c.tcap + j) * D);
+    for (int q = l; q < CH; q += 16) {
+        kd[q] = ks[q];
+        vd[q] = vs[q];
+    }
+}
+
 template <int BITS>
 __global__ void k_export_codes(DevCache c, uint32_t* __restrict__ out)
 {
@@ -581,7 +643,7 @@ hipError_t launch_prefill(const DevCache& c, const void* K, const void* V, const
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (n_max <= 0) return hipSuccess;
-    return with_bits(c, [&](auto bb) {
+    err = with_bits(c, [&](auto bb) {
         constexpr int BITS = decltype(bb)::value;
         return with_d_kv(c, [&](auto dd, auto kt) {
             constexpr int D = decltype(dd)::value;
@@ -604,6 +666,8 @@ hipError_t launch_prefill(const DevCache& c, const void* K, const void* V, const
             return hipGetLastError();
         });
     });
+    if (err == hipSuccess && c.tK) err = launch_tier_spill_prompt(c, K, V, n_max, st);
+    return err;
 }
 
 hipError_t launch_prefill_chunks(const DevCache& c, const void* K, const void* V, const float* q_obs,
@@ -612,7 +676,7 @@ hipError_t launch_prefill_chunks(const DevCache& c, const void* K, const void* V
     hipLaunchKernelGGL(k_prefill_init, dim3((c.Smax + 255) / 256, c.Hkv, c.B), dim3(256), 0, st, c);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    return with_bits(c, [&](auto bb) {
+    err = with_bits(c, [&](auto bb) {
         constexpr int BITS = decltype(bb)::value;
         return with_d_kv(c, [&](auto dd, auto kt) {
             constexpr int D = decltype(dd)::value;
@@ -631,6 +695,22 @@ hipError_t launch_prefill_chunks(const DevCache& c, const void* K, const void* V
                                dim3(256), 0, st, c, (const KT*)K, (const KT*)V, n_max);
             return hipGetLastError();
         });
+    });
+    if (err == hipSuccess && c.tK) err = launch_tier_spill_prompt(c, K, V, n_max, st);
+    return err;
+}
+
+hipError_t launch_tier_spill_prompt(const DevCache& c, const void* K, const void* V, int n_max, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_tier_list_dropped, dim3(c.Hkv, c.B), dim3(kSelThreads), 0, st, c);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || n_max <= 0) return e;
+    return with_d_kv(c, [&](auto dd, auto kt) {
+        constexpr int D = decltype(dd)::value;
+        using KT = decltype(kt);
+        hipLaunchKernelGGL((k_tier_copy_prompt<D, KT>), dim3((n_max + 15) / 16, c.Hkv, c.B), dim3(256), 0, st, c,
+                           (const KT*)K, (const KT*)V, n_max);
+        return hipGetLastError();
     });
 }
 

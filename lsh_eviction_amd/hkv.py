@@ -26,7 +26,8 @@ HKV_DECODE_FUSED, HKV_DECODE_SPLIT = 0, 1
 EXPORTS = ("hkv_validate_config", "hkv_workspace_bytes", "hkv_create", "hkv_prefill",
            "hkv_prefill_queries", "hkv_prefill_chunks", "hkv_decode_step", "hkv_destroy", "hkv_status_str", "hkv_last_error",
            "hkv_get_state", "hkv_set_state", "hkv_debug_last_codes", "hkv_debug_prefill_codes",
-           "hkv_debug_prefill_query_codes", "hkv_debug_scores", "hkv_encode")
+           "hkv_debug_prefill_query_codes", "hkv_debug_scores", "hkv_encode", "hkv_attach_tier",
+           "hkv_tier_counts", "hkv_attend_tiered")
 
 
 class hkv_config(C.Structure):
@@ -34,7 +35,7 @@ class hkv_config(C.Structure):
                 ("head_dim", C.c_int32), ("n_bits", C.c_int32), ("kv_dtype", C.c_int32),
                 ("prefill_policy", C.c_int32), ("decode_schedule", C.c_int32),
                 ("max_prompt", C.c_int32), ("chunk", C.c_int32), ("value_bits", C.c_int32),
-                ("prefill_chunk", C.c_int32), ("budgets", C.POINTER(C.c_int32))]
+                ("prefill_chunk", C.c_int32), ("tier_capacity", C.c_int32), ("budgets", C.POINTER(C.c_int32))]
 
 
 class HkvError(RuntimeError):
@@ -64,6 +65,9 @@ def load():
         "hkv_prefill": (I, [P, P, P, P, I, P]),
         "hkv_prefill_queries": (I, [P, P, P, P, P, I, P]),
         "hkv_prefill_chunks": (I, [P, P, P, P, P, P, P, I, P]),
+        "hkv_attach_tier": (I, [P, P, P, P, P]),
+        "hkv_tier_counts": (I, [P, P, P]),
+        "hkv_attend_tiered": (I, [P, P, P, P]),
         "hkv_decode_step": (I, [P, P, P, P, P, P, P]),
         "hkv_destroy": (I, [P]),
         "hkv_status_str": (C.c_char_p, [I]),
@@ -89,11 +93,12 @@ def status_str(s: int) -> str:
 
 def make_config(batch, n_q_heads, n_kv_heads, head_dim, n_bits, kv_dtype, budgets,
                 prefill_policy=HKV_PREFILL_STREAM, decode_schedule=HKV_DECODE_FUSED,
-                max_prompt=0, chunk=0, value_bits=0, prefill_chunk=0):
+                max_prompt=0, chunk=0, value_bits=0, prefill_chunk=0, tier_capacity=0):
     b = np.ascontiguousarray(budgets, dtype=np.int32)
     cfg = hkv_config(int(batch), int(n_q_heads), int(n_kv_heads), int(head_dim), int(n_bits),
                      int(kv_dtype), int(prefill_policy), int(decode_schedule), int(max_prompt),
-                     int(chunk), int(value_bits), int(prefill_chunk), b.ctypes.data_as(C.POINTER(C.c_int32)))
+                     int(chunk), int(value_bits), int(prefill_chunk), int(tier_capacity),
+                     b.ctypes.data_as(C.POINTER(C.c_int32)))
     cfg._keep = b          # keep the budgets array alive with the struct
     return cfg
 
@@ -185,6 +190,18 @@ def hkv_prefill_chunks(h, K, V, q_obs, reuse, kept, prompt_lens, n_max: int, str
                                      pl.ctypes.data_as(C.c_void_p), int(n_max), _stream(stream)), h)
 
 
+def hkv_attach_tier(h, K, V, tok, stream=None):
+    _check(load().hkv_attach_tier(h, _ptr(K), _ptr(V), _ptr(tok), _stream(stream)), h)
+
+
+def hkv_tier_counts(h, counts, stream=None):
+    _check(load().hkv_tier_counts(h, _ptr(counts), _stream(stream)), h)
+
+
+def hkv_attend_tiered(h, q, out, stream=None):
+    _check(load().hkv_attend_tiered(h, _ptr(q), _ptr(out), _stream(stream)), h)
+
+
 def hkv_debug_prefill_query_codes(h, codes, stream=None):
     _check(load().hkv_debug_prefill_query_codes(h, _ptr(codes), _stream(stream)), h)
 
@@ -230,11 +247,13 @@ class Cache:
 
     def __init__(self, batch, n_q_heads, n_kv_heads, head_dim, n_bits, kv_dtype, budgets, R,
                  prefill_policy=HKV_PREFILL_STREAM, decode_schedule=HKV_DECODE_FUSED, max_prompt=0,
-                 chunk=0, stream=None, value_bits=0, prefill_chunk=0):
+                 chunk=0, stream=None, value_bits=0, prefill_chunk=0, tier_capacity=0):
         import torch
         self.cfg = make_config(batch, n_q_heads, n_kv_heads, head_dim, n_bits, kv_dtype, budgets,
                                prefill_policy, decode_schedule, max_prompt, chunk, value_bits,
-                               prefill_chunk)
+                               prefill_chunk, tier_capacity)
+        self.tier_capacity = int(tier_capacity)
+        self.tier = None
         self.prefill_policy = int(prefill_policy)
         self.prefill_chunk = (int(prefill_chunk) or DEFAULT_PREFILL_CHUNK) if prefill_policy == HKV_PREFILL_CHUNK else 0
         self.value_bits = int(value_bits)
@@ -281,6 +300,32 @@ class Cache:
         else:
             hkv_prefill_queries(self.h, K, V, Q, prompt_lens, self.n_max, stream)
         return None
+
+    def attach_tier(self, stream=None):
+        """Allocate the host tier in pinned host memory ([B][Hkv][tier_capacity][d]
+        K and V in the kv dtype, int32 token positions) and attach it; returns
+        the dict of tensors (the handle keeps them alive)."""
+        import torch
+        dt = kv_torch_dtype(self.kv_dtype)
+        shape = (self.B, self.Hkv, self.tier_capacity)
+        self.tier = {"K": torch.zeros(shape + (self.d,), dtype=dt, pin_memory=True),
+                     "V": torch.zeros(shape + (self.d,), dtype=dt, pin_memory=True),
+                     "tok": torch.full(shape, -1, dtype=torch.int32, pin_memory=True)}
+        hkv_attach_tier(self.h, self.tier["K"], self.tier["V"], self.tier["tok"], stream)
+        return self.tier
+
+    def tier_counts(self, stream=None):
+        import torch
+        cnt = torch.empty((self.B, self.Hkv), dtype=torch.int32, device="cuda")
+        hkv_tier_counts(self.h, cnt, stream)
+        return cnt
+
+    def attend_tiered(self, q, out=None, stream=None):
+        import torch
+        if out is None:
+            out = torch.empty((self.B, self.Hq, self.d), dtype=torch.float32, device="cuda")
+        hkv_attend_tiered(self.h, q, out, stream)
+        return out
 
     def decode_step(self, q, k, v, out=None, evicted=None, stream=None):
         import torch

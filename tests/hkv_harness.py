@@ -61,14 +61,20 @@ def kv_bytes_equal(gpu_rows: np.ndarray, ref_rows_f64: np.ndarray, kv_dtype: str
 def run_case(shape: Shape, steps: int, schedule: int = 0, policy: int = 0, chunk: int = 0,
              heads: Optional[Sequence[Tuple[int, int]]] = None, seed: Optional[int] = None,
              check_every: int = 1, stats: Optional[dict] = None, value_bits: int = 0,
-             prefill_chunk: int = 0, reuse: Optional[np.ndarray] = None, observe: bool = True):
+             prefill_chunk: int = 0, reuse: Optional[np.ndarray] = None, observe: bool = True,
+             tier: int = 0):
     """Prefill + `steps` decode steps on the GPU, replayed on the oracle for `heads`
     (all heads if None).  Raises AssertionError on any parity failure.
 
     Under the CHUNK policy the observation queries are passed when `observe`
     (their codes are checked and injected), `reuse` [B][Hkv][k] is passed as
     the kept list, and the GPU's kept lists are compared with the oracle's and
-    returned in stats["kept"]."""
+    returned in stats["kept"].
+
+    With tier > 0 a host tier of that capacity (pinned host memory) is attached
+    before the prefill; its counts, token positions and rows are compared with
+    the oracle's tier, and attention over cache and tier with the oracle's, after
+    the prefill and after every step."""
     import torch
     from lsh_eviction_amd import hkv
 
@@ -86,7 +92,9 @@ def run_case(shape: Shape, steps: int, schedule: int = 0, policy: int = 0, chunk
 
     cache = hkv.Cache(B, Hq, Hkv, d, bits, kvd, P.budgets, P.R, prefill_policy=policy,
                       decode_schedule=schedule, max_prompt=n_max, chunk=chunk, value_bits=value_bits,
-                      prefill_chunk=prefill_chunk)
+                      prefill_chunk=prefill_chunk, tier_capacity=tier)
+    if tier:
+        cache.attach_tier()
     Kt, Vt = hkv.to_device(P.K), hkv.to_device(P.V)
     query = policy == oracle.QUERY
     chunked = policy == oracle.CHUNK
@@ -108,7 +116,7 @@ def run_case(shape: Shape, steps: int, schedule: int = 0, policy: int = 0, chunk
     del Kt, Vt, Qt
 
     sel = list(heads) if heads is not None else [(b, h) for b in range(B) for h in range(Hkv)]
-    orc = oracle.OracleCache(P.R, P.budgets, Hq, Hkv, heads=sel, value_bits=value_bits)
+    orc = oracle.OracleCache(P.R, P.budgets, Hq, Hkv, heads=sel, value_bits=value_bits, tier=tier if tier else -1)
     flagged = 0
     for (b, h) in sel:
         n = int(P.prompt_lens[b])
@@ -136,6 +144,11 @@ def run_case(shape: Shape, steps: int, schedule: int = 0, policy: int = 0, chunk
     log(f"  prefill codes ok ({flagged} flagged bits differ), {time.time()-t0:.1f}s")
     compare_state(cache, orc, sel, shape, "after prefill")
     log(f"  prefill state ok, {time.time()-t0:.1f}s")
+    tworst = 0.0
+    if tier:
+        compare_tier(cache, orc, sel, shape, "after prefill")
+        tworst = check_tiered(cache, orc, Dd.q[0], G, "after prefill")
+        log(f"  prefill tier ok, tiered attention rel err {tworst:.2e}, {time.time()-t0:.1f}s")
 
     worst = 0.0
     for s in range(steps):
@@ -156,11 +169,45 @@ def run_case(shape: Shape, steps: int, schedule: int = 0, policy: int = 0, chunk
             assert err <= ATTN_TOL, f"step {s} b={b} h={h}: attention rel err {err:.3e} > {ATTN_TOL}"
         if check_every and (s + 1) % check_every == 0 or s == steps - 1:
             compare_state(cache, orc, sel, shape, f"after step {s}")
-    log(f"  {steps} decode steps ok, worst attention rel err {worst:.2e}, {time.time()-t0:.1f}s")
+            if tier:
+                compare_tier(cache, orc, sel, shape, f"after step {s}")
+        if tier:
+            tworst = max(tworst, check_tiered(cache, orc, Dd.q[s], G, f"step {s}"))
+    log(f"  {steps} decode steps ok, worst attention rel err {worst:.2e}"
+        + (f", tiered {tworst:.2e}" if tier else "") + f", {time.time()-t0:.1f}s")
     if stats is not None:
-        stats.update(worst=worst, flagged=flagged)
+        stats.update(worst=worst, flagged=flagged, tiered_worst=tworst)
     cache.close()
     return worst
+
+
+def check_tiered(cache, orc, q, G: int, when: str) -> float:
+    """Attention over cache and host tier against the oracle's; returns the worst row error."""
+    from lsh_eviction_amd import hkv
+    out = hkv.to_numpy(cache.attend_tiered(hkv.to_device(q)))
+    worst = 0.0
+    for (b, h), ref in orc.attend_tiered(q).items():
+        err = rel_err_rows(out[b, h * G:(h + 1) * G].astype(np.float64), ref)
+        worst = max(worst, err)
+        assert err <= ATTN_TOL, f"{when} b={b} h={h}: tiered attention rel err {err:.3e} > {ATTN_TOL}"
+    return worst
+
+
+def compare_tier(cache, orc, sel, shape: Shape, when: str):
+    """Tier counts, token positions and rows, bit for bit."""
+    import torch
+    from lsh_eviction_amd import hkv
+    cnt = hkv.to_numpy(cache.tier_counts())
+    torch.cuda.synchronize()
+    tk, tv, tt = cache.tier["K"], cache.tier["V"], cache.tier["tok"].numpy()
+    for (b, h) in sel:
+        o = orc.heads[(b, h)].tier()
+        assert cnt[b, h] == o["count"], f"{when} b={b} h={h}: tier count {cnt[b, h]} != {o['count']}"
+        m = len(o["tok"])
+        np.testing.assert_array_equal(tt[b, h, :m], o["tok"].astype(np.int32),
+                                      err_msg=f"{when} b={b} h={h}: tier token positions")
+        assert kv_bytes_equal(hkv.to_numpy(tk[b, h, :m]), o["K"], shape.kv_dtype), f"{when} b={b} h={h}: tier K"
+        assert kv_bytes_equal(hkv.to_numpy(tv[b, h, :m]), o["V"], shape.kv_dtype), f"{when} b={b} h={h}: tier V"
 
 
 def compare_state(cache, orc, sel, shape: Shape, when: str):

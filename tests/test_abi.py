@@ -64,6 +64,9 @@ def test_named_shapes_validate(hkv):
     (dict(budgets=[40000]), "UNSUPPORTED"),               # 160 KB code table > on-chip table
     (dict(kv_dtype=7), "UNSUPPORTED"),
     (dict(prefill_policy=4), "UNSUPPORTED"),
+    (dict(tier_capacity=-1), "UNSUPPORTED"),
+    (dict(tier_capacity=(1 << 28) + 1), "UNSUPPORTED"),
+    (dict(tier_capacity=1000, value_bits=8), "UNSUPPORTED"),   # the tier keeps values as given
     (dict(prefill_chunk=5), "UNSUPPORTED"),                 # chunk size without the CHUNK policy
     (dict(prefill_policy=3, prefill_chunk=33), "UNSUPPORTED"),
     (dict(prefill_policy=3, prefill_chunk=-1), "UNSUPPORTED"),
@@ -103,6 +106,14 @@ def test_chunk_policy_validates_and_sizes_its_score_buffer(hkv):
     assert hkv.hkv_validate_config(big) == hkv.HKV_OK
 
 
+def test_tier_sizes_its_device_state(hkv):
+    a = _cfg(hkv, tier_capacity=100000)
+    assert hkv.hkv_validate_config(a) == hkv.HKV_OK
+    # counts, the partials of the tiered attention and the prompt bitset; the tier itself is the caller's
+    extra = hkv.hkv_workspace_bytes(a) - hkv.hkv_workspace_bytes(_cfg(hkv))
+    assert 32 * (128 + 4) * 4 <= extra < 64 << 20
+
+
 def test_truncate_allows_large_budget(hkv):
     cfg = _cfg(hkv, budgets=[40000], prefill_policy=hkv.HKV_PREFILL_TRUNCATE)
     assert hkv.hkv_validate_config(cfg) == hkv.HKV_OK
@@ -116,6 +127,7 @@ def test_null_pointers(hkv):
     assert L.hkv_validate_config(C.byref(cfg)) == hkv.HKV_ERR_INVALID_ARG
     assert L.hkv_workspace_bytes(C.byref(_cfg(hkv)), None) == hkv.HKV_ERR_INVALID_ARG
     for f, n in (("hkv_prefill", 6), ("hkv_prefill_queries", 7), ("hkv_prefill_chunks", 9),
+                 ("hkv_attach_tier", 5), ("hkv_tier_counts", 3), ("hkv_attend_tiered", 4),
                  ("hkv_decode_step", 7), ("hkv_destroy", 1),
                  ("hkv_get_state", 7), ("hkv_set_state", 7), ("hkv_debug_last_codes", 4),
                  ("hkv_debug_prefill_codes", 3), ("hkv_debug_prefill_query_codes", 3), ("hkv_debug_scores", 4)):

@@ -130,6 +130,44 @@ def test_chunk_prefill_full_long_128k():
              check_every=0)
 
 
+# (shape, decode steps, schedule, prefill policy, tier capacity)
+TIER = {
+    "tiny_stream": (C.TINY, 24, FUSED, STREAM, 4096),
+    "tiny_split": (C.TINY, 24, SPLIT, STREAM, 4096),
+    "llama8b_small_stream": (C.LLAMA8B.scaled(prompt=3000, budget=1500), 8, FUSED, STREAM, 8192),
+    "llama8b_small_truncate": (C.LLAMA8B.scaled(prompt=2100, budget=1000), 6, FUSED, TRUNCATE, 4096),
+    "ragged_small_query": (C.RAGGED.scaled(batch=4, prompt_range=(600, 1800)), 4, FUSED, QUERY, 4096),
+    "d128_f32_g1_split": (SMALL["d128_f32_g1"][0], 6, SPLIT, STREAM, 2048),
+    "g16_b16": (SMALL["g16_b16"][0], 4, FUSED, STREAM, 2048),
+    "overflow": (C.LLAMA8B.scaled(prompt=3000, budget=1500), 6, FUSED, STREAM, 1000),   # capacity < spills
+    "fill_then_evict": (C.LLAMA8B.scaled(prompt=990, budget=1000), 20, FUSED, STREAM, 64),
+}
+
+
+@pytest.mark.parametrize("name", list(TIER))
+def test_host_tier_small(name):
+    """Host tier in pinned host memory: the tokens leaving the cache (prefill
+    drops in position order, then every eviction) with their rows, bit-exact,
+    and attention over cache and tier within tolerance of the oracle's (equal
+    to attention over every token while the tier has room)."""
+    from hkv_harness import run_case
+    shape, steps, schedule, policy, cap = TIER[name]
+    run_case(shape, steps, schedule=schedule, policy=policy, tier=cap)
+
+
+def test_host_tier_chunk_prefill():
+    from hkv_harness import run_case
+    run_case(C.LLAMA8B.scaled(prompt=2500, budget=1200), 4, schedule=FUSED, policy=CHUNK, prefill_chunk=10,
+             tier=4096)
+
+
+def test_host_tier_full_long_128k():
+    """The 128K workload with every dropped prompt token (98 304 per head) and
+    every eviction kept in a pinned host tier; sampled heads."""
+    from hkv_harness import run_case
+    run_case(C.LONG128K, 2, schedule=FUSED, policy=STREAM, heads=[(0, 4)], check_every=0, tier=131072)
+
+
 INT8_VALUES = {
     "llama8b_small": (C.LLAMA8B.scaled(prompt=3000, budget=1500), 12, 0),
     "ragged_small": (C.RAGGED.scaled(batch=4, prompt_range=(600, 1800)), 6, 0),
