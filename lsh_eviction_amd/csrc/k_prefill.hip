@@ -63,71 +63,128 @@ __global__ void k_reset(DevCache c)
     }
 }
 
-// Codes of prompt rows [64 * blockIdx.x, +64) of one head on the matrix
-// cores: X is [B][nh][n_max][D] (prompt keys with nh = Hkv, prompt queries
-// with nh = Hq), codes go to dst[(b * nh + h) * pcode_slots + t].  Wave w
-// takes 16 rows; lane l feeds row (l % 16) and the quarter (l / 16) of the
-// head dimension, so MFMA step s contracts dimension (l / 16) * D/4 + s.  The
+// Codes of prompt rows of one head on the matrix cores: X is
+// [B][nh][n_max][D] (prompt keys with nh = Hkv, prompt queries with nh = Hq),
+// codes go to dst[(b * nh + h) * pcode_slots + t].  A block stages R in LDS
+// once and then takes the 64-row tiles blockIdx.x, blockIdx.x + gridDim.x,
+// ... of its head.  Wave w takes 16 rows of a tile; lane l feeds row (l % 16)
+// and the quarter (l / 16) of the head dimension: MFMA step s of the two
+// accumulators contracts dimensions (l / 16) * D/4 + s and + s + D/8.  The
 // 16 x 16 result tile of bit columns nt*16 .. +15 is sign-packed by a wave
 // ballot per accumulator register.
+constexpr int kProjMaxBlocks = 256;   // blocks per head of the projection grid
+
+// Element s of a lane's row quarter held as raw 16-byte words.
+template <typename KT, int NV>
+__device__ __forceinline__ float raw_elem(const uint4 (&r)[NV], int s)
+{
+    constexpr int EPL = Vec16<KT>::EPL;
+    const uint4 q = r[s / EPL];
+    const int e = s % EPL;
+    if constexpr (std::is_same<KT, bf16_t>::value) {
+        const uint32_t w = (e >> 1) == 0 ? q.x : (e >> 1) == 1 ? q.y : (e >> 1) == 2 ? q.z : q.w;
+        return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+    } else {
+        return __uint_as_float(e == 0 ? q.x : e == 1 ? q.y : e == 2 ? q.z : q.w);
+    }
+}
+
 template <int D, int BITS, typename KT>
 __global__ __launch_bounds__(256) void k_project_mfma(DevCache c, const KT* __restrict__ Kp, int n_max, int nh,
                                                       void* __restrict__ dst)
 {
     using CT = typename CodeT<BITS>::T;
-    constexpr int DQ = D / 4;          // dimensions fed by one lane
-    constexpr int NT = BITS / 16;      // bit tiles
-    __shared__ float sR[D * BITS];
+    constexpr int DQ = D / 4;                    // dimensions fed by one lane
+    constexpr int NT = BITS / 16;                // bit tiles
+    constexpr int NV = DQ / Vec16<KT>::EPL;      // 16-byte words per lane and row
+    // R in LDS with the rows of quarter q of the head dimension shifted by
+    // 16 q floats: the four lane groups of an operand read then fall on
+    // different banks
+    __shared__ __align__(16) float sR[D * BITS + 64];
     const int h = blockIdx.y, b = blockIdx.z, head = b * nh + h;
     const int N = c.plen[b];
-    const int t0 = blockIdx.x * 64;
-    if (t0 >= N) return;
-    for (int i = threadIdx.x; i < D * BITS; i += blockDim.x) sR[i] = c.R[i];
+    if (blockIdx.x * 64 >= N) return;
+    {
+        // every load of R is issued before any is waited for
+        constexpr int NR4 = D * BITS / 4, RPT = (NR4 + 255) / 256;
+        float4 rr[RPT];
+#pragma unroll
+        for (int j = 0; j < RPT; ++j)
+            rr[j] = reinterpret_cast<const float4*>(c.R)[min((int)threadIdx.x + j * 256, NR4 - 1)];
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) {
+            const int i = 4 * ((int)threadIdx.x + j * 256);
+            if (i < D * BITS) *reinterpret_cast<float4*>(sR + i + (i / (DQ * BITS)) * 16) = rr[j];
+        }
+    }
     __syncthreads();
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int row = t0 + wave * 16 + (lane & 15);
     const int qd = lane >> 4;
+    const int stride = gridDim.x * 64;
 
-    float x[DQ];
-    if (row < N) {
-        const KT* src = Kp + ((size_t)head * n_max + row) * D + qd * DQ;
-        constexpr int EPL = Vec16<KT>::EPL;
+    // the raw words of a tile's rows; the next tile's are in flight while
+    // the current one is computed
+    auto load_tile = [&](int t0, uint4 (&r)[NV]) {
+        const int row = t0 + wave * 16 + (lane & 15);
+        if (row < N) {
+            const uint4* src = reinterpret_cast<const uint4*>(Kp + ((size_t)head * n_max + row) * D + qd * DQ);
 #pragma unroll
-        for (int v = 0; v < DQ / EPL; ++v) {
-            const uint4 raw = *reinterpret_cast<const uint4*>(src + v * EPL);
-            float f[EPL];
-            Vec16<KT>::cvt(raw, f);
+            for (int v = 0; v < NV; ++v) r[v] = src[v];
+        } else {
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) x[v * EPL + e] = f[e];
+            for (int v = 0; v < NV; ++v) r[v] = make_uint4(0u, 0u, 0u, 0u);
         }
-    } else {
-#pragma unroll
-        for (int s = 0; s < DQ; ++s) x[s] = 0.f;
-    }
+    };
+    uint4 cur[NV], nxt[NV];
+    load_tile(blockIdx.x * 64, cur);
+    for (int t0 = blockIdx.x * 64; t0 < N; t0 += stride) {
+        if (t0 + stride < N) load_tile(t0 + stride, nxt);
 
-    unsigned long long mk[NT][4];
+        // two accumulators per bit tile (the two halves of the lane's
+        // dimensions), so twice as many independent MFMA chains are in
+        // flight; any fp32 summation order gives the same unflagged bits
+        unsigned long long mk[NT][4];
+        f32x4 acc[NT][2];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const float* rcol = sR + (size_t)(qd * DQ) * BITS + nt * 16 + (lane & 15);
+        for (int nt = 0; nt < NT; ++nt) acc[nt][0] = acc[nt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < DQ; ++s)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[s], rcol[s * BITS], acc, 0, 0, 0);
+        for (int s = 0; s < DQ / 2; ++s) {
+            const float x0 = raw_elem<KT>(cur, s), x1 = raw_elem<KT>(cur, s + DQ / 2);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mk[nt][r] = __ballot(acc[r] > 0.f);
-    }
-    // result row i = 4 * (lane / 16) + r sits in register r of lanes 16 * (i / 4) + col
-    if (lane < 16) {
-        const int a = lane >> 2, r = lane & 3;
-        unsigned long long cde = 0;
+            for (int nt = 0; nt < NT; ++nt) {
+                const float* rcol = sR + (size_t)(qd * DQ) * BITS + qd * 16 + nt * 16 + (lane & 15);
+                acc[nt][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(x0, rcol[s * BITS], acc[nt][0], 0, 0, 0);
+                acc[nt][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(x1, rcol[(s + DQ / 2) * BITS], acc[nt][1], 0, 0, 0);
+            }
+        }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            const unsigned long long m = r == 0 ? mk[nt][0] : r == 1 ? mk[nt][1] : r == 2 ? mk[nt][2] : mk[nt][3];
-            cde |= ((m >> (16 * a)) & 0xFFFFull) << (16 * nt);
+            const f32x4 y = acc[nt][0] + acc[nt][1];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mk[nt][r] = __ballot(y[r] > 0.f);
         }
-        const int t = t0 + wave * 16 + lane;
-        if (t < N) reinterpret_cast<CT*>(dst)[(size_t)head * c.pcode_slots + t] = (CT)cde;
+        // result row i = 4 * (lane / 16) + r sits in register r of lanes 16 * (i / 4) + col
+        if (lane < 16) {
+            const int a = lane >> 2, r = lane & 3;
+            unsigned long long cde = 0;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const unsigned long long m = r == 0 ? mk[nt][0] : r == 1 ? mk[nt][1] : r == 2 ? mk[nt][2] : mk[nt][3];
+                cde |= ((m >> (16 * a)) & 0xFFFFull) << (16 * nt);
+            }
+            const int t = t0 + wave * 16 + lane;
+            if (t < N) reinterpret_cast<CT*>(dst)[(size_t)head * c.pcode_slots + t] = (CT)cde;
+        }
+#pragma unroll
+        for (int v = 0; v < NV; ++v) cur[v] = nxt[v];
     }
+}
+
+// Blocks per head of the projection of n_max rows.
+static int proj_blocks(int n_max)
+{
+    const int tiles = (n_max + 63) / 64;
+    return tiles < kProjMaxBlocks ? tiles : kProjMaxBlocks;
 }
 
 template <int CTRL>
@@ -648,14 +705,14 @@ hipError_t launch_prefill(const DevCache& c, const void* K, const void* V, const
         return with_d_kv(c, [&](auto dd, auto kt) {
             constexpr int D = decltype(dd)::value;
             using KT = decltype(kt);
-            hipLaunchKernelGGL((k_project_mfma<D, BITS, KT>), dim3((n_max + 63) / 64, c.Hkv, c.B),
+            hipLaunchKernelGGL((k_project_mfma<D, BITS, KT>), dim3(proj_blocks(n_max), c.Hkv, c.B),
                                dim3(256), 0, st, c, (const KT*)K, n_max, c.Hkv, c.pcode);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
             if (policy == HKV_PREFILL_STREAM) {
                 e = launch_select<BITS, 0>(c, st);
             } else if (policy == HKV_PREFILL_QUERY) {
-                hipLaunchKernelGGL((k_project_mfma<D, BITS, float>), dim3((n_max + 63) / 64, c.Hq, c.B),
+                hipLaunchKernelGGL((k_project_mfma<D, BITS, float>), dim3(proj_blocks(n_max), c.Hq, c.B),
                                    dim3(256), 0, st, c, Q, n_max, c.Hq, c.qcode);
                 e = hipGetLastError();
                 if (e == hipSuccess) e = launch_select_query<BITS>(c, st);
@@ -682,7 +739,7 @@ hipError_t launch_prefill_chunks(const DevCache& c, const void* K, const void* V
             constexpr int D = decltype(dd)::value;
             using KT = decltype(kt);
             if (n_max > 0) {
-                hipLaunchKernelGGL((k_project_mfma<D, BITS, KT>), dim3((n_max + 63) / 64, c.Hkv, c.B),
+                hipLaunchKernelGGL((k_project_mfma<D, BITS, KT>), dim3(proj_blocks(n_max), c.Hkv, c.B),
                                    dim3(256), 0, st, c, (const KT*)K, n_max, c.Hkv, c.pcode);
                 hipError_t e = hipGetLastError();
                 if (e != hipSuccess) return e;
