@@ -122,6 +122,8 @@ extern "C" hkv_status hkv_create(const hkv_config* cfg, const float* R_host, voi
     d.csum = (int*)(ws + L.off_csum);
     d.pchunk = L.pchunk;
     d.nchunk_max = (long long)L.nchunk_max;
+    d.chist = (int*)(ws + L.off_chist);
+    d.chist_bins = L.chist_bins;
     d.tK = d.tV = nullptr;
     d.ttok = nullptr;
     d.tcount = L.tcap > 0 ? (int*)(ws + L.off_tcount) : nullptr;

@@ -37,6 +37,8 @@ struct DevCache {
     int* csum;                      // [B][Hkv][nchunk_max] per-chunk scores or flags (CHUNK prefill)
     int pchunk;                     // tokens per prefill chunk (CHUNK prefill)
     long long nchunk_max;
+    int* chist;                     // [B][Hkv][chist_bins] histogram of chunk scores (CHUNK prefill)
+    int chist_bins;                 // C * G * b + 1: every possible chunk score
     // host tier (null tK when none is attached)
     void* tK;                       // [B][Hkv][tcap][d] kv dtype, GPU-addressable (pinned host or device)
     void* tV;

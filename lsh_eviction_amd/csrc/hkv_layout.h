@@ -27,6 +27,7 @@ struct Layout {
     int Smax, chunk, nsplit, max_prompt;
     int pchunk;            // tokens per prefill chunk (HKV_PREFILL_CHUNK), else 0
     size_t nchunk_max;     // prompt chunks per head, padded (HKV_PREFILL_CHUNK)
+    int chist_bins;        // possible chunk scores, C * G * b + 1 (HKV_PREFILL_CHUNK)
     int tcap;              // host tier capacity per head (0: none)
     int tsplit;            // splits per head of the tiered attention over the host tier
     size_t tflag_words;    // words per head of the prompt's held-token bitset
@@ -36,7 +37,7 @@ struct Layout {
     size_t off_R, off_budget, off_plen, off_state, off_K, off_V, off_code, off_tok;
     size_t off_dbg_q, off_dbg_k, off_part, off_frec, off_fscal, off_cand_v, off_ekey;
     size_t off_info, off_count, off_pcode, off_qcode, off_vs, off_csum;
-    size_t off_tcount, off_tpart, off_tflag;
+    size_t off_tcount, off_tpart, off_tflag, off_chist;
     size_t v_bytes;        // bytes of the V region (kv dtype, or int8 codes)
     size_t total;
 };

@@ -85,6 +85,7 @@ hkv_status compute_layout(const hkv_config* cfg, Layout* L, char* err, size_t er
     l.pcode_slots = align_up((size_t)(cfg->max_prompt > 0 ? cfg->max_prompt : 1), 64);
     l.pchunk = chunked ? (cfg->prefill_chunk ? cfg->prefill_chunk : kDefaultPrefillChunk) : 0;
     l.nchunk_max = chunked ? align_up((size_t)((cfg->max_prompt + l.pchunk - 1) / l.pchunk) + 1, 64) : 0;
+    l.chist_bins = chunked ? l.pchunk * G * cfg->n_bits + 1 : 0;
     l.tcap = cfg->tier_capacity;
     if (l.tcap > 0) {
         int ts = kTierBlocks / (l.B * l.Hkv);
@@ -125,6 +126,7 @@ hkv_status compute_layout(const hkv_config* cfg, Layout* L, char* err, size_t er
     l.off_qcode = take(cfg->prefill_policy == HKV_PREFILL_QUERY ? (size_t)l.B * l.Hq * l.pcode_slots * cb : 0);
     // per-chunk scores of the prompt (HKV_PREFILL_CHUNK)
     l.off_csum = take(heads * l.nchunk_max * 4);
+    l.off_chist = take(heads * (size_t)l.chist_bins * 4);
     // host tier: counts, partials of the tiered attention, held-token bitset of the prompt
     l.off_tcount = take(l.tcap > 0 ? heads * 4 : 0);
     l.off_tpart = take(l.tcap > 0 ? (size_t)l.B * l.Hq * l.tsplit * (l.d + 4) * 4 : 0);

@@ -17,8 +17,9 @@
 // layers): the prompt is cut into chunks of C tokens, every chunk is scored
 // by its summed Hamming distance to the observation query codes, and the
 // chunks are evicted in order of (score descending, index ascending) until
-// floor(S / C) remain.  That order is found by a two-level radix histogram
-// over the scores, so the selection is one block per (sequence, KV head).
+// floor(S / C) remain.  Scores are computed one thread per chunk over the
+// whole grid; a histogram of their values gives the threshold, and one block
+// per (sequence, KV head) places the kept chunks.
 #include <type_traits>
 
 #include "hkv.h"
@@ -379,103 +380,167 @@ __device__ __forceinline__ int block_prefix(bool flag, int* s_w, int& total)
     return before + below;
 }
 
-// Chunk-granular selection for one (sequence, KV head); 1024 threads.
-//   1. the G observation queries are hashed (fp32 dot products against R, any
-//      summation order is exact outside the flagged band) and sign-packed;
-//   2. score[i] = sum over the chunk's tokens and the G query codes of the
-//      Hamming distances (integer);
-//   3. E = nch - k evictions: a histogram of score >> 8, then of the low 8
-//      bits inside the bin that holds the E-th largest, gives the threshold T
-//      and how many chunks score above it; of the chunks scoring exactly T
-//      the lowest-indexed ones are evicted;
-//   4. a prefix count in chunk order places the kept chunks in slots
-//      0, 1, ... and writes the kept list.
-// With a reuse list step 3 is replaced by flags set from the list; with
-// N <= S every chunk is kept.  The per-chunk scores live in c.csum (global;
-// a score is read back only by the thread that wrote it, the reuse flags by
-// any thread of the block, through L2).
-template <int BITS>
-__global__ __launch_bounds__(kSelThreads) void k_chunk_select(DevCache c, const float* __restrict__ qobs,
-                                                             const int* __restrict__ reuse, int* __restrict__ kept,
-                                                             int kmax)
+// Exclusive prefix sum of v over the block's threads in thread order, and
+// the block's total.  All threads of the block must call it; two barriers,
+// s_w[kSelWaves] of scratch.
+__device__ __forceinline__ int block_exclusive_sum(int v, int* s_w, int& total)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) s_w[wave] = x;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) {
+        const int t = s_w[w];
+        before += w < wave ? t : 0;
+        all += t;
+    }
+    __syncthreads();
+    total = all;
+    return before + x - v;
+}
+
+// Chunk-granular prefill selection (HKV_PREFILL_CHUNK), three launches:
+//   k_chunk_obs    (one block per head) hashes the G observation queries
+//                  (fp32 dot products against R; any summation order is exact
+//                  outside the flagged band), writes their codes, and clears
+//                  the head's histogram of chunk scores;
+//   k_chunk_score  (one thread per chunk) sums the Hamming distances of the
+//                  chunk's key codes to the G query codes into its score and
+//                  counts the score in the head's histogram (per block in
+//                  LDS, then one global add per bin);
+//   k_chunk_select (one block per head): E = nch - k chunks go, in order of
+//                  (score descending, index ascending).  A suffix sum over the
+//                  histogram finds the score T of the last one and how many
+//                  chunks scoring exactly T go (the lowest-indexed ones); a
+//                  prefix count in chunk order then places the kept chunks
+//                  in slots 0, 1, ... and writes the kept list.
+// With a reuse list the kept chunks are flags set from the list instead;
+// with N <= S every chunk is kept.
+template <int D, int BITS>
+__global__ __launch_bounds__(kSelThreads) void k_chunk_obs(DevCache c, const float* __restrict__ qobs)
 {
     using CT = typename CodeT<BITS>::T;
+    // R and the group's queries go to LDS first, every load in flight at once
+    constexpr int NR4 = D * BITS / 4, RPT = (NR4 + kSelThreads - 1) / kSelThreads;
+    constexpr int NQ4 = kMaxGroup * D / 4, QPT = (NQ4 + kSelThreads - 1) / kSelThreads;
+    __shared__ __align__(16) float sR[D * BITS];
+    __shared__ __align__(16) float sQ[kMaxGroup * D];
     const int h = blockIdx.x, b = blockIdx.y, head = b * c.Hkv + h;
     const int tid = threadIdx.x, lane = tid & 63;
+    const int G = c.G;
+    const int nq4 = G * D / 4;
+    const float4* q4 = reinterpret_cast<const float4*>(qobs + ((size_t)b * c.Hq + (size_t)h * G) * D);
+    float4 rr[RPT], qq[QPT];
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) rr[k] = reinterpret_cast<const float4*>(c.R)[min(tid + k * kSelThreads, NR4 - 1)];
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) qq[k] = q4[min(tid + k * kSelThreads, nq4 - 1)];
+#pragma unroll
+    for (int k = 0; k < RPT; ++k)
+        if (tid + k * kSelThreads < NR4) reinterpret_cast<float4*>(sR)[tid + k * kSelThreads] = rr[k];
+#pragma unroll
+    for (int k = 0; k < QPT; ++k)
+        if (tid + k * kSelThreads < nq4) reinterpret_cast<float4*>(sQ)[tid + k * kSelThreads] = qq[k];
+    int* hist = c.chist + (size_t)head * c.chist_bins;
+    for (int i = tid; i < c.chist_bins; i += kSelThreads) hist[i] = 0;
+    __syncthreads();
+    const int g = tid / BITS, j = tid % BITS;
+    float y = 0.f;
+    if (g < G) {
+#pragma unroll 8
+        for (int i = 0; i < D; ++i) y = fmaf(sQ[g * D + i], sR[i * BITS + j], y);
+    }
+    const unsigned long long m = __ballot(y > 0.f);
+    if (g < G && j == 0) {
+        const CT code = (CT)(m >> (lane & ~(BITS - 1) & 63));
+        store_words(c.dbg_q + ((size_t)b * c.Hq + (size_t)h * G + g) * c.W, c.W, (unsigned long long)code);
+    }
+}
+
+constexpr int kScoreThreads = 256;
+
+template <int BITS>
+__global__ __launch_bounds__(kScoreThreads) void k_chunk_score(DevCache c)
+{
+    using CT = typename CodeT<BITS>::T;
+    extern __shared__ unsigned s_bins[];   // c.chist_bins counters
+    __shared__ CT s_qc[kMaxGroup];
+    const int h = blockIdx.y, b = blockIdx.z, head = b * c.Hkv + h;
+    const int tid = threadIdx.x;
     const int G = c.G, C = c.pchunk;
+    const int N = c.plen[b], S = c.budget[b];
+    const int nch = (N + C - 1) / C;
+    const int i = blockIdx.x * kScoreThreads + tid;
+    if (N <= S || blockIdx.x * kScoreThreads >= nch) return;   // uniform over the block
+    if (tid < G) {
+        const uint32_t* p = c.dbg_q + ((size_t)b * c.Hq + (size_t)h * G + tid) * c.W;
+        unsigned long long v = p[0];
+        if (c.W > 1) v |= (unsigned long long)p[1] << 32;
+        s_qc[tid] = (CT)v;
+    }
+    for (int k = tid; k < c.chist_bins; k += kScoreThreads) s_bins[k] = 0u;
+    __syncthreads();
+    if (i < nch) {
+        const CT* pc = reinterpret_cast<const CT*>(c.pcode) + (size_t)head * c.pcode_slots;
+        const int t1 = min(N, (i + 1) * C);
+        int sum = 0;
+        for (int t = i * C; t < t1; ++t) {
+            const CT kc = pc[t];
+            for (int g = 0; g < G; ++g) sum += popc((CT)(kc ^ s_qc[g]));
+        }
+        c.csum[(size_t)head * c.nchunk_max + i] = sum;
+        atomicAdd(&s_bins[sum], 1u);
+    }
+    __syncthreads();
+    int* hist = c.chist + (size_t)head * c.chist_bins;
+    for (int k = tid; k < c.chist_bins; k += kScoreThreads)
+        if (s_bins[k]) atomicAdd(hist + k, (int)s_bins[k]);
+}
+
+template <int BITS>
+__global__ __launch_bounds__(kSelThreads) void k_chunk_select(DevCache c, const int* __restrict__ reuse,
+                                                             int* __restrict__ kept, int kmax)
+{
+    const int h = blockIdx.x, b = blockIdx.y, head = b * c.Hkv + h;
+    const int tid = threadIdx.x;
+    const int C = c.pchunk;
     const int N = c.plen[b], S = c.budget[b];
     const int nch = (N + C - 1) / C;
     const bool all = N <= S;
     const int k = all ? nch : S / C;
     int* score = c.csum + (size_t)head * c.nchunk_max;
-    const CT* pc = reinterpret_cast<const CT*>(c.pcode) + (size_t)head * c.pcode_slots;
     const size_t rowbase = (size_t)head * c.Smax;
 
-    __shared__ CT s_qc[kMaxGroup];
-    __shared__ unsigned s_hist[256];
     __shared__ int s_w[kSelWaves];
-    __shared__ int s_hb, s_T, s_evict_eq, s_ntok;
-
-    // 1. observation query codes (also exported for inspection)
-    if (qobs) {
-        const int g = tid / BITS, j = tid % BITS;
-        float y = 0.f;
-        if (g < G) {
-            const float* x = qobs + ((size_t)b * c.Hq + (size_t)h * G + g) * c.d;
-            for (int i = 0; i < c.d; ++i) y = fmaf(x[i], c.R[i * BITS + j], y);
-        }
-        const unsigned long long m = __ballot(y > 0.f);
-        if (g < G && j == 0) {
-            const CT code = (CT)(m >> (lane & ~(BITS - 1) & 63));
-            s_qc[g] = code;
-            store_words(c.dbg_q + ((size_t)b * c.Hq + (size_t)h * G + g) * c.W, c.W, (unsigned long long)code);
-        }
-    }
-    if (tid == 0) s_ntok = 0;
-    for (int i = tid; i < 256; i += kSelThreads) s_hist[i] = 0u;
-    __syncthreads();
+    __shared__ int s_T, s_evict_eq, s_short;
+    if (tid == 0) s_short = 0;
 
     const bool scored = !all && !reuse;
     if (scored) {
-        // 2. chunk scores, histogram of their high bits (scores < 2^15)
-        for (int i = tid; i < nch; i += kSelThreads) {
-            int sum = 0;
-            const int t1 = min(N, (i + 1) * C);
-            for (int t = i * C; t < t1; ++t) {
-                const CT kc = pc[t];
-                for (int g = 0; g < G; ++g) sum += popc((CT)(kc ^ s_qc[g]));
-            }
-            score[i] = sum;
-            atomicAdd(&s_hist[sum >> 8], 1u);
-        }
-        __syncthreads();
-        // 3. threshold: the E-th largest score, E = nch - k >= 1
+        // the E-th largest score: thread tid owns a run of bins counted from
+        // the top; a prefix sum over threads gives the chunks above its run
         const int E = nch - k;
-        if (tid == 0) {
-            int cum = 0, hb = 255;
-            for (; hb > 0; --hb) {
-                if (cum + (int)s_hist[hb] >= E) break;
-                cum += (int)s_hist[hb];
+        const int* hist = c.chist + (size_t)head * c.chist_bins;
+        const int nb = c.chist_bins, per = (nb + kSelThreads - 1) / kSelThreads;
+        const int hi = nb - 1 - tid * per, lo = max(hi - per + 1, 0);   // run [lo, hi], top down
+        int local = 0;
+        for (int v = hi; v >= lo; --v) local += hist[v];
+        int total;
+        const int above = block_exclusive_sum(hi >= 0 ? local : 0, s_w, total);
+        if (hi >= 0 && above < E && above + local >= E) {
+            int cum = above, v = hi;
+            for (; v > lo; --v) {
+                if (cum + hist[v] >= E) break;
+                cum += hist[v];
             }
-            s_hb = hb;
-            s_evict_eq = cum;   // chunks above bin hb, for now
-        }
-        __syncthreads();
-        const int hb = s_hb;
-        for (int i = tid; i < 256; i += kSelThreads) s_hist[i] = 0u;
-        __syncthreads();
-        for (int i = tid; i < nch; i += kSelThreads) {
-            const int sc = score[i];
-            if ((sc >> 8) == hb) atomicAdd(&s_hist[sc & 255], 1u);
-        }
-        __syncthreads();
-        if (tid == 0) {
-            int cum = s_evict_eq, lo = 255;
-            for (; lo > 0; --lo) {
-                if (cum + (int)s_hist[lo] >= E) break;
-                cum += (int)s_hist[lo];
-            }
-            s_T = (hb << 8) | lo;
+            s_T = v;
             s_evict_eq = E - cum;   // chunks scoring exactly T that go, lowest first
         }
     } else if (!all) {
@@ -496,35 +561,51 @@ __global__ __launch_bounds__(kSelThreads) void k_chunk_select(DevCache c, const 
     const int T = scored ? s_T : 0, evict_eq = scored ? s_evict_eq : 0;
 
     // 4. kept chunks in chunk order -> slots
+    // scores come from k_chunk_score (an earlier launch), flags from other
+    // threads of this block (through L2); values two tiles ahead are in
+    // flight while a tile is placed
+    auto value = [&](int i) {
+        if (all || i >= nch) return 0;
+        return scored ? score[i] : __hip_atomic_load(score + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    // One block scan per tile counts, for every chunk, the chunks before it
+    // that score below T ("lt") and exactly T ("eq").  Of the eq chunks the
+    // first evict_eq (in chunk order, over the whole head) go, so the kept
+    // eq chunks before a chunk are its eq count minus the evicted ones.
+    auto evicted_eq = [&](int eq_seen) { return min(eq_seen, evict_eq); };
     int base = 0, base_eq = 0;
+    int next1 = value(tid), next2 = value(tid + kSelThreads);
     for (int i0 = 0; i0 < nch; i0 += kSelThreads) {
         const int i = i0 + tid;
         const bool valid = i < nch;
-        int sc = 0;
-        if (valid && scored) sc = score[i];   // written by this thread
-        else if (valid && !all) sc = __hip_atomic_load(score + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        bool keep = valid;
+        const int sc = next1;
+        next1 = next2;
+        next2 = value(i + 2 * kSelThreads);
+        bool lt, eq;
         if (scored) {
-            int neq;
-            const bool eq = valid && sc == T;
-            const int rank = base_eq + block_prefix(eq, s_w, neq);
-            keep = valid && (sc < T || (eq && rank >= evict_eq));
-            base_eq += neq;
-        } else if (!all) {
-            keep = valid && sc != 0;
+            lt = valid && sc < T;
+            eq = valid && sc == T;
+        } else {
+            lt = valid && (all || sc != 0);   // kept chunk
+            eq = false;
         }
-        int nkeep;
-        const int pos = base + block_prefix(keep, s_w, nkeep);
+        int tot;
+        const int ex = block_exclusive_sum((int)lt | ((int)eq << 16), s_w, tot);
+        const int lt_before = ex & 0xFFFF, eq_before = ex >> 16;
+        const bool keep = lt || (eq && base_eq + eq_before >= evict_eq);
+        const int pos = base + lt_before + eq_before - (evicted_eq(base_eq + eq_before) - evicted_eq(base_eq));
         if (keep) {
             if (kept) kept[(size_t)head * kmax + pos] = i;
             const int len = min(C, N - i * C);
             for (int r = 0; r < len; ++r) c.tok[rowbase + (size_t)pos * C + r] = i * C + r;
-            atomicAdd(&s_ntok, len);
+            if (len < C) s_short = C - len;   // only the last chunk can be short; it is placed last
         }
-        base += nkeep;
+        const int tlt = tot & 0xFFFF, teq = tot >> 16;
+        base += tlt + teq - (evicted_eq(base_eq + teq) - evicted_eq(base_eq));
+        base_eq += teq;
     }
     __syncthreads();
-    const int n = s_ntok;
+    const int n = base * C - s_short;   // kept tokens
     for (int s = n + tid; s < min(N, S); s += kSelThreads) c.tok[rowbase + s] = -1;
     if (kept)
         for (int j = base + tid; j < kmax; j += kSelThreads) kept[(size_t)head * kmax + j] = -1;
@@ -744,8 +825,20 @@ hipError_t launch_prefill_chunks(const DevCache& c, const void* K, const void* V
                 hipError_t e = hipGetLastError();
                 if (e != hipSuccess) return e;
             }
-            hipLaunchKernelGGL((k_chunk_select<BITS>), dim3(c.Hkv, c.B), dim3(kSelThreads), 0, st, c, q_obs,
-                               reuse, kept, kmax);
+            if (q_obs) {
+                hipLaunchKernelGGL((k_chunk_obs<D, BITS>), dim3(c.Hkv, c.B), dim3(kSelThreads), 0, st, c, q_obs);
+                if (!reuse && n_max > 0) {
+                    const size_t lds = (size_t)c.chist_bins * 4;
+                    hipError_t ea = hipFuncSetAttribute((const void*)k_chunk_score<BITS>,
+                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                    if (ea != hipSuccess) return ea;
+                    const int nch = (n_max + c.pchunk - 1) / c.pchunk;
+                    hipLaunchKernelGGL((k_chunk_score<BITS>), dim3((nch + kScoreThreads - 1) / kScoreThreads, c.Hkv, c.B),
+                                       dim3(kScoreThreads), lds, st, c);
+                }
+            }
+            hipLaunchKernelGGL((k_chunk_select<BITS>), dim3(c.Hkv, c.B), dim3(kSelThreads), 0, st, c, reuse, kept,
+                               kmax);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess || n_max <= 0) return e;
             hipLaunchKernelGGL((k_prefill_gather<D, BITS, KT>), dim3((c.Smax + 15) / 16, c.Hkv, c.B),
