@@ -248,7 +248,8 @@ const char* hkv_last_error(const hkv_cache* c);
 hkv_status hkv_get_state(const hkv_cache* c, void* K, void* V, uint32_t* codes,
                          int32_t* slot_token, int32_t* head_state, void* stream);
 /* Checkpoint import, same layouts; all five buffers required.  Marks the
- * cache as prefilled. */
+ * cache as prefilled.  A host tier is not part of the checkpoint: its
+ * buffers are the caller's, and its counts are left as they are. */
 hkv_status hkv_set_state(hkv_cache* c, const void* K, const void* V, const uint32_t* codes,
                          const int32_t* slot_token, const int32_t* head_state, void* stream);
 

@@ -155,6 +155,44 @@ def test_host_tier_small(name):
     run_case(shape, steps, schedule=schedule, policy=policy, tier=cap)
 
 
+def test_host_tier_call_errors():
+    """The tier calls check their order and their memory before enqueuing anything."""
+    import torch
+    from lsh_eviction_amd import hkv
+    from lsh_eviction_amd import datagen
+    shape = C.TINY.scaled(prompt=40, budget=16)
+    P = datagen.prompt(shape)
+    plain = hkv.Cache(1, 1, 1, shape.head_dim, shape.n_bits, hkv.HKV_F32, P.budgets, P.R, max_prompt=64)
+    with pytest.raises(hkv.HkvError) as e:
+        plain.attach_tier()                              # created without a tier capacity
+    assert e.value.status == hkv.HKV_ERR_INVALID_ARG
+    with pytest.raises(hkv.HkvError) as e:
+        plain.tier_counts()
+    assert e.value.status == hkv.HKV_ERR_STATE
+    c = hkv.Cache(1, 1, 1, shape.head_dim, shape.n_bits, hkv.HKV_F32, P.budgets, P.R, max_prompt=64,
+                  tier_capacity=64)
+    q = torch.zeros((1, 1, shape.head_dim), device="cuda")
+    with pytest.raises(hkv.HkvError) as e:
+        c.attend_tiered(q)                               # no tier attached yet
+    assert e.value.status == hkv.HKV_ERR_STATE
+    pageable = torch.zeros((1, 1, 64, shape.head_dim))   # not pinned: the GPU cannot address it
+    tok = torch.zeros((1, 1, 64), dtype=torch.int32)
+    with pytest.raises(hkv.HkvError) as e:
+        hkv.hkv_attach_tier(c.h, pageable, pageable.clone(), tok)
+    assert e.value.status == hkv.HKV_ERR_INVALID_ARG
+    c.attach_tier()
+    with pytest.raises(hkv.HkvError) as e:
+        c.attend_tiered(q)                               # before the prefill
+    assert e.value.status == hkv.HKV_ERR_STATE
+    c.prefill(hkv.to_device(P.K), hkv.to_device(P.V), P.prompt_lens)
+    torch.cuda.synchronize()
+    assert int(hkv.to_numpy(c.tier_counts())[0, 0]) == 40 - 16
+    with pytest.raises(hkv.HkvError) as e:
+        c.attach_tier()                                  # after the prefill
+    assert e.value.status == hkv.HKV_ERR_STATE
+    c.close(); plain.close()
+
+
 def test_host_tier_chunk_prefill():
     from hkv_harness import run_case
     run_case(C.LLAMA8B.scaled(prompt=2500, budget=1200), 4, schedule=FUSED, policy=CHUNK, prefill_chunk=10,
