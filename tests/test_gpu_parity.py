@@ -344,6 +344,15 @@ def test_graph_replay_matches_eager(value_bits):
         assert torch.equal(out, o2), step
 
 
+def test_maximum_budget():
+    """One head at the largest supported budget, 2^22 slots: every step scores
+    a 4M-slot code table and one block merges 4096 splits; the 100 prompt
+    tokens past the budget are dropped (TRUNCATE), so the steps evict."""
+    from hkv_harness import run_case
+    run_case(C.TINY.scaled(prompt=(1 << 22) + 100, budget=1 << 22, steps=3), 3, schedule=FUSED, policy=TRUNCATE,
+             check_every=0)
+
+
 FULL = {
     "llama3_8b_layer": (C.LLAMA8B, 6, None),
     "long_128k": (C.LONG128K, 3, [(0, 0), (0, 5)]),
