@@ -104,8 +104,10 @@ typedef struct {
     int32_t decode_schedule; /* HKV_DECODE_* */
     int32_t max_prompt;      /* largest n_max a prefill will be given (>= 0) */
     int32_t chunk;           /* slots per attention split (one workgroup each);
-                                0 selects 1024; otherwise a multiple of 64 in
-                                [64, 65536] */
+                                a multiple of 64 in [64, 65536], or 0: about
+                                one workgroup per compute unit, i.e.
+                                ceil(sum_b S_b * Hkv / 256) rounded up to a
+                                multiple of 64 and clamped to that range */
     int32_t value_bits;      /* 0: values stored in kv_dtype; 8: each value row
                                 stored as d int8 codes and one fp32 scale
                                 (scale = max|v| / 127, code = v / scale rounded

@@ -78,7 +78,18 @@ hkv_status compute_layout(const hkv_config* cfg, Layout* L, char* err, size_t er
     l.schedule = cfg->decode_schedule;
     l.value_bits = cfg->value_bits;
     l.Smax = Smax;
-    l.chunk = cfg->chunk ? cfg->chunk : kDefaultChunk;
+    if (cfg->chunk) {
+        l.chunk = cfg->chunk;
+    } else {
+        // about one block of the decode step per compute unit: the slots of
+        // all eviction domains over kChunkTargetBlocks, a multiple of 64
+        long long slots = 0;
+        for (int b = 0; b < cfg->batch; ++b) slots += cfg->budgets[b];
+        slots *= cfg->n_kv_heads;
+        long long ch = (slots + kChunkTargetBlocks - 1) / kChunkTargetBlocks;
+        ch = (ch + 63) / 64 * 64;
+        l.chunk = (int)(ch < 64 ? 64 : (ch > 65536 ? 65536 : ch));
+    }
     l.nsplit = (Smax + l.chunk - 1) / l.chunk;
     l.max_prompt = cfg->max_prompt;
     l.code_slots = align_up((size_t)Smax, 64);

@@ -239,7 +239,13 @@ def to_numpy(t) -> np.ndarray:
     return t.numpy()
 
 
-DEFAULT_CHUNK = 1024   # what hkv_config.chunk = 0 selects
+def default_chunk(budgets, n_kv_heads: int) -> int:
+    """The split size hkv_config.chunk = 0 selects (include/hkv.h): about one
+    workgroup per compute unit, a multiple of 64 in [64, 65536]."""
+    slots = int(np.asarray(budgets, dtype=np.int64).sum()) * int(n_kv_heads)
+    ch = -(-slots // 256)
+    ch = -(-ch // 64) * 64
+    return min(max(ch, 64), 65536)
 
 
 class Cache:
@@ -266,7 +272,7 @@ class Cache:
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         self.h = hkv_create(self.cfg, R, self.workspace, stream)
         self.n_max = 0
-        self.chunk = int(chunk) or DEFAULT_CHUNK
+        self.chunk = int(chunk) or default_chunk(budgets, n_kv_heads)
 
     def close(self):
         if getattr(self, "h", None):
