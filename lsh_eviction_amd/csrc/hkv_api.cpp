@@ -116,6 +116,8 @@ extern "C" hkv_status hkv_create(const hkv_config* cfg, const float* R_host, voi
     d.vq = L.value_bits == 8;
     d.B = L.B; d.Hq = L.Hq; d.Hkv = L.Hkv; d.G = L.G; d.d = L.d; d.bits = L.bits; d.W = L.W;
     d.Smax = L.Smax; d.chunk = L.chunk; d.nsplit = L.nsplit;
+    d.heads_fastest = 0;
+    for (int b = 1; b < cfg->batch; ++b) d.heads_fastest |= cfg->budgets[b] != cfg->budgets[0];
     d.kv_bf16 = L.kv_dtype == HKV_BF16;
     d.code_slots = (long long)L.code_slots;
     d.pcode_slots = (long long)L.pcode_slots;

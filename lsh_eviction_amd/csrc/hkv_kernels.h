@@ -31,6 +31,7 @@ struct DevCache {
     void* qcode;                    // [B][Hq][pcode_slots] prompt query codes (QUERY prefill)
     float* vs;                      // [B][Hkv][Smax] (+16) value scales when values are int8
     int B, Hq, Hkv, G, d, bits, W, Smax, chunk, nsplit;
+    int heads_fastest;              // fused grid numbering: (sequence, head) fastest when budgets differ
     bool vq;                        // values stored as int8 codes + scales
     int kv_bf16;
     long long code_slots, pcode_slots;

@@ -91,6 +91,8 @@ hkv_status compute_layout(const hkv_config* cfg, Layout* L, char* err, size_t er
         l.chunk = (int)(ch < 64 ? 64 : (ch > 65536 ? 65536 : ch));
     }
     l.nsplit = (Smax + l.chunk - 1) / l.chunk;
+    if (l.nsplit > 65535)
+        FAIL(HKV_ERR_UNSUPPORTED, "chunk %d too small for a budget of %d slots (more than 65535 splits)", l.chunk, Smax);
     l.max_prompt = cfg->max_prompt;
     l.code_slots = align_up((size_t)Smax, 64);
     l.pcode_slots = align_up((size_t)(cfg->max_prompt > 0 ? cfg->max_prompt : 1), 64);

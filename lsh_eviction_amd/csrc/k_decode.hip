@@ -1030,7 +1030,13 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     constexpr int VS = 16 / sizeof(CT);
     constexpr bool kMfma = std::is_same<KT, bf16_t>::value;
     constexpr int TR = tile_rows<GM>();
-    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    // Workgroups go to the XCDs round-robin by number.  With ragged budgets
+    // the blocks are numbered (sequence, KV head) fastest, so every XCD gets
+    // the same mix of sequences; with equal budgets split fastest, which
+    // spreads each head over all XCDs (measured marginally faster there).
+    const int split = c.heads_fastest ? blockIdx.z : blockIdx.x;
+    const int h = c.heads_fastest ? blockIdx.x : blockIdx.y;
+    const int b = c.heads_fastest ? blockIdx.y : blockIdx.z;
     const int G = c.G;
     const int head = b * c.Hkv + h;
     const int s0 = split * c.chunk;
@@ -1647,6 +1653,11 @@ hipError_t with_gm(const DevCache& c, F&& f)
 
 }  // namespace
 
+static dim3 fused_grid(const DevCache& c)
+{
+    return c.heads_fastest ? dim3(c.Hkv, c.B, c.nsplit) : dim3(c.nsplit, c.Hkv, c.B);
+}
+
 hipError_t launch_decode_fused(const DevCache& c, const float* q, const void* k, const void* v, float* out,
                                int* evicted, hipStream_t st)
 {
@@ -1658,12 +1669,12 @@ hipError_t launch_decode_fused(const DevCache& c, const float* q, const void* k,
                     constexpr int D = decltype(dd)::value, BITS = decltype(bb)::value, GM = decltype(gg)::value;
                     if constexpr (std::is_same<KT, bf16_t>::value) {
                         if (c.vq) {
-                            hipLaunchKernelGGL((k_decode_fused<D, BITS, GM, KT, true>), dim3(c.nsplit, c.Hkv, c.B),
+                            hipLaunchKernelGGL((k_decode_fused<D, BITS, GM, KT, true>), fused_grid(c),
                                                dim3(kThreads), 0, st, c, q, (const KT*)k, (const KT*)v, out, evicted);
                             return hipGetLastError();
                         }
                     }
-                    hipLaunchKernelGGL((k_decode_fused<D, BITS, GM, KT>), dim3(c.nsplit, c.Hkv, c.B), dim3(kThreads),
+                    hipLaunchKernelGGL((k_decode_fused<D, BITS, GM, KT>), fused_grid(c), dim3(kThreads),
                                        0, st, c, q, (const KT*)k, (const KT*)v, out, evicted);
                     return hipGetLastError();
                 });
