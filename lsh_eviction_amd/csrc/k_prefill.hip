@@ -212,17 +212,20 @@ __device__ __forceinline__ unsigned wave_max_u32(unsigned v)
 // t >= S, one after the other, evict the occupied slot farthest in summed
 // Hamming distance from their query codes -- their own key code under
 // STREAM, the codes of their G query rows under QUERY -- ties to the lowest
-// slot, and take it.  The code table and a window of the coming tokens' codes
-// stay in LDS.  One barrier per token: the waves' (score, slot) maxima are
-// double-buffered, every wave reduces them to the same winner, and the thread
-// whose scan covers the winning slot updates that table entry itself (it is
-// the entry's only reader).
+// slot, and take it.  The code table lives in registers: thread tid holds
+// the 16-byte groups k * 1024 + tid (VS codes each) in treg[k], so a scan
+// reads no memory; a window of the coming tokens' codes is staged in LDS.
+// One barrier per token: the waves' (score, slot) maxima are double-buffered,
+// every wave reduces them to the same winner, and the thread holding the
+// winning slot updates its register copy (it is the entry's only reader).
 constexpr int kSelTokens = 128;   // tokens whose codes are staged at a time
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+constexpr int kTableRegs = 8;     // 16-byte groups of the table per thread: 1024 x 8 x 16 B = 128 KiB
 
 template <int BITS>
-constexpr size_t select_lds_bytes(int Smax, int nq)
+constexpr size_t select_lds_bytes(int, int nq)
 {
-    return ((size_t)((Smax + 63) & ~63) + (size_t)kSelTokens * (1 + nq)) * (BITS / 8);
+    return (size_t)kSelTokens * (1 + nq) * (BITS / 8);
 }
 
 // GQ = 0: STREAM (the token's key code); GQ > 0: QUERY with G <= GQ query
@@ -240,16 +243,29 @@ __global__ __launch_bounds__(1024) void k_prefill_select(DevCache c)
     const int N = c.plen[b], S = c.budget[b];
     if (N <= S) return;
     const int G = c.G;
-    const int Sp = (S + 63) & ~63;
-    CT* table = reinterpret_cast<CT*>(dyn_lds);
-    CT* skey = table + Sp;                 // [kSelTokens] key codes of the window
-    CT* sq = skey + kSelTokens;            // [kSelTokens][G] query codes of the window (QUERY)
+    CT* skey = reinterpret_cast<CT*>(dyn_lds);   // [kSelTokens] key codes of the window
+    CT* sq = skey + kSelTokens;                   // [kSelTokens][G] query codes of the window (QUERY)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const CT* pc = reinterpret_cast<const CT*>(c.pcode) + (size_t)head * c.pcode_slots;
     constexpr bool QRY = GQ > 0;
     const CT* qc = QRY ? reinterpret_cast<const CT*>(c.qcode) + (size_t)(b * c.Hq + h * G) * c.pcode_slots : nullptr;
     int* tok = c.tok + (size_t)head * c.Smax;
-    for (int s = tid; s < Sp; s += blockDim.x) table[s] = s < S ? pc[s] : (CT)0;
+    // the table: group k of this thread holds slots (k * 1024 + tid) * VS + u
+    uint4 treg[kTableRegs];
+#pragma unroll
+    for (int k = 0; k < kTableRegs; ++k) {
+        const int s = (k * 1024 + tid) * VS;
+        treg[k] = s < S ? *reinterpret_cast<const uint4*>(pc + s) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    const int nfull = S / (VS * 1024);                        // groups with every slot occupied, uniform
+    const bool partial = S % (VS * 1024) != 0;                // one more group, partly occupied
+    // key of slot s: (score << SLOT_BITS) | (SLOT_MASK - s) = (score << SLOT_BITS) + cbase - (k * 1024 * VS + u)
+    const unsigned cbase = SLOT_MASK - (unsigned)(tid * VS);
+    // 16-bit keys of the full groups: local index k * VS + u in LB bits; the
+    // score (at most GQ' * BITS, 1024) shifted by LB stays below 2^15
+    constexpr int LB = VS == 8 ? 6 : (VS == 4 ? 5 : 4);
+    constexpr unsigned LMAX = (1u << LB) - 1u;
+    static_assert(kTableRegs * VS == (1 << LB) && ((16u * BITS) << LB) < 65536u, "16-bit slot keys");
     int par = 0;
     for (int t0 = S; t0 < N; t0 += kSelTokens) {
         const int cnt = min(kSelTokens, N - t0);
@@ -270,24 +286,52 @@ __global__ __launch_bounds__(1024) void k_prefill_select(DevCache c)
             } else {
                 qv[0] = skey[j];
             }
-            unsigned best = 0;
-            for (int s = tid * VS; s < S; s += 1024 * VS) {
-                const uint4 raw = *reinterpret_cast<const uint4*>(table + s);
+            auto score = [&](CT code) {
+                int sc = 0;
+                if constexpr (QRY) {
+#pragma unroll
+                    for (int g = 0; g < GQ; ++g)
+                        if (g < G) sc += popc((CT)(qv[g] ^ code));
+                } else {
+                    sc = popc((CT)(qv[0] ^ code));
+                }
+                return (unsigned)sc;
+            };
+            // Full groups: a 16-bit key per slot, (score << LB) | (last local
+            // index - local index), two slots per packed max; the largest key
+            // is the largest score at the lowest local (hence global) slot.
+            u16x2 best2 = {0, 0};
+#pragma unroll
+            for (int k = 0; k < kTableRegs; ++k) {
                 CT cs[VS];
-                __builtin_memcpy(cs, &raw, 16);
+                __builtin_memcpy(cs, &treg[k], 16);
+                if (k < nfull) {
 #pragma unroll
-                for (int u = 0; u < VS; ++u) {
-                    int sc = 0;
-                    if constexpr (QRY) {
-#pragma unroll
-                        for (int g = 0; g < GQ; ++g)
-                            if (g < G) sc += popc((CT)(qv[g] ^ cs[u]));
-                    } else {
-                        sc = popc((CT)(qv[0] ^ cs[u]));
+                    for (int u = 0; u < VS; u += 2) {
+                        const unsigned li = (unsigned)(k * VS + u);
+                        const u16x2 kk = {(unsigned short)((score(cs[u]) << LB) | (LMAX - li)),
+                                          (unsigned short)((score(cs[u + 1]) << LB) | (LMAX - li - 1))};
+                        best2 = __builtin_elementwise_max(best2, kk);
                     }
-                    const unsigned k = (s + u < S) ? (((unsigned)sc << SLOT_BITS) | (SLOT_MASK - (unsigned)(s + u)))
-                                                   : 0u;
-                    best = k > best ? k : best;
+                }
+            }
+            unsigned best = 0;
+            if (nfull > 0) {
+                const unsigned k16 = max((unsigned)best2.x, (unsigned)best2.y);
+                const unsigned li = LMAX - (k16 & LMAX);
+                const unsigned slot = (li / VS) * (1024u * VS) + (unsigned)(tid * VS) + li % VS;
+                best = ((k16 >> LB) << SLOT_BITS) | (SLOT_MASK - slot);
+            }
+#pragma unroll
+            for (int k = 0; k < kTableRegs; ++k) {
+                CT cs[VS];
+                __builtin_memcpy(cs, &treg[k], 16);
+                if (k == nfull && partial) {
+                    const int s0 = (k * 1024 + tid) * VS;
+#pragma unroll
+                    for (int u = 0; u < VS; ++u)
+                        if (s0 + u < S)
+                            best = max(best, (score(cs[u]) << SLOT_BITS) + (cbase - (unsigned)(k * 1024 * VS + u)));
                 }
             }
             best = wave_max_u32(best);
@@ -297,7 +341,19 @@ __global__ __launch_bounds__(1024) void k_prefill_select(DevCache c)
             v = wave_max_u32(v);
             const int e = (int)(SLOT_MASK - (v & SLOT_MASK));
             if (tid == (e / VS) % 1024) {
-                table[e] = skey[j];
+                const int ke = e / (VS * 1024), ue = e % VS;
+                const CT code = skey[j];
+#pragma unroll
+                for (int k = 0; k < kTableRegs; ++k) {
+                    if (k == ke) {
+                        CT cs[VS];
+                        __builtin_memcpy(cs, &treg[k], 16);
+#pragma unroll
+                        for (int u = 0; u < VS; ++u)
+                            if (u == ue) cs[u] = code;
+                        __builtin_memcpy(&treg[k], cs, 16);
+                    }
+                }
                 tok[e] = t0 + j;
             }
             par ^= 1;
