@@ -842,7 +842,7 @@ constexpr int tile_rows()
 template <int GM>
 constexpr int ring_depth()
 {
-    return 2;
+    return GM >= 16 ? 1 : 2;   // 16 heads: the accumulators take 128 registers a lane
 }
 
 // ---------------------------------------------------------------------------
