@@ -251,6 +251,9 @@ def main():
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.tier and args.prefill not in ("stream", "truncate"):
+        print(json.dumps({"error": "--tier takes --prefill stream or truncate"}))
+        sys.exit(2)
 
     import numpy as np
     import torch
@@ -267,9 +270,6 @@ def main():
     P.prompt_lens, P.budgets = n, budgets
     n_max = int(n.max())
     if args.tier:
-        if args.prefill not in ("stream", "truncate"):
-            print(json.dumps({"error": "--tier takes --prefill stream or truncate"}))
-            sys.exit(2)
         run_tier(args, shape, n, budgets, P, kvd, sched, make_layer_inputs)
         return
 

@@ -1,5 +1,6 @@
-"""bench.py's command-line contract that needs no GPU: more than one GPU is
-refused with a JSON line and exit status 2."""
+"""bench.py's command-line contract that needs no GPU: more than one GPU, and
+the tiered mode with a prefill rule it does not take, are refused with a JSON
+line and exit status 2."""
 import json
 import os
 import subprocess
@@ -24,3 +25,10 @@ def test_step_bytes_of_the_128k_workload():
     # 8 KV heads x 32768 slots x (4 code bytes + 2 x 128 x 2 K/V bytes), plus the new token's
     # K, V, code and position per head, plus q read and out written (fp32)
     assert bench.step_bytes(configs.LONG128K, s) == 8 * 32768 * 516 + 8 * (512 + 4 + 4) + 32 * 128 * 4 * 2
+
+
+def test_tier_mode_refuses_other_prefill_rules():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--tier", "--prefill", "chunk"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "--tier" in json.loads(r.stdout.strip().splitlines()[-1])["error"]

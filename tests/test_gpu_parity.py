@@ -311,18 +311,22 @@ def test_fused_equals_split_bitwise_evictions():
         assert torch.allclose(o1, o2, rtol=1e-4, atol=1e-5)
 
 
-@pytest.mark.parametrize("value_bits", [0, 8])
-def test_graph_replay_matches_eager(value_bits):
-    """A captured decode step replayed several times equals the same steps run eagerly."""
+@pytest.mark.parametrize("value_bits,tier", [(0, 0), (8, 0), (0, 4096)], ids=["plain", "int8", "tier"])
+def test_graph_replay_matches_eager(value_bits, tier):
+    """A captured decode step replayed several times equals the same steps run
+    eagerly (with a host tier: the same tokens spill with the same rows)."""
     import torch
     from lsh_eviction_amd import datagen, hkv
     shape = C.LLAMA8B.scaled(prompt=1500, budget=700)
     wl = datagen.workload(shape, steps=6)
     P, D = wl["prompt"], wl["decode"]
     q, k, v = (hkv.to_device(D.q[0]), hkv.to_device(D.k[0]), hkv.to_device(D.v[0]))
-    caches = [hkv.Cache(1, 32, 8, 128, 32, hkv.HKV_BF16, P.budgets, P.R, max_prompt=P.n_max, value_bits=value_bits)
+    caches = [hkv.Cache(1, 32, 8, 128, 32, hkv.HKV_BF16, P.budgets, P.R, max_prompt=P.n_max, value_bits=value_bits,
+                        tier_capacity=tier)
               for _ in range(2)]
     for c in caches:
+        if tier:
+            c.attach_tier()
         c.prefill(hkv.to_device(P.K), hkv.to_device(P.V), P.prompt_lens)
     torch.cuda.synchronize()
     out = torch.empty((1, 32, 128), device="cuda")
@@ -342,6 +346,11 @@ def test_graph_replay_matches_eager(value_bits):
         torch.cuda.synchronize()
         assert torch.equal(ev, e2), step
         assert torch.equal(out, o2), step
+    if tier:
+        assert torch.equal(caches[0].tier_counts(), caches[1].tier_counts())
+        torch.cuda.synchronize()
+        for key in ("K", "V", "tok"):
+            assert torch.equal(caches[0].tier[key], caches[1].tier[key]), key
 
 
 def test_maximum_budget():
