@@ -247,16 +247,17 @@ extern "C" hkv_status hkv_prefill_chunks(hkv_cache* c, const void* K, const void
     return prefill_impl(c, K, V, q_obs, prompt_lens, n_max, stream, "hkv_prefill_chunks", reuse, kept);
 }
 
-// Device address of a buffer the GPU can reach: device memory as is, pinned
-// host memory through hipHostGetDevicePointer; null for anything else.
-static void* gpu_address(void* p)
+// Device address of a buffer the GPU can reach: device memory of `device` as
+// is, pinned host memory through hipHostGetDevicePointer; null for anything
+// else.
+static void* gpu_address(void* p, int device)
 {
     hipPointerAttribute_t a;
     if (hipPointerGetAttributes(&a, p) != hipSuccess) {
         (void)hipGetLastError();
         return nullptr;
     }
-    if (a.type == hipMemoryTypeDevice) return p;
+    if (a.type == hipMemoryTypeDevice) return a.device == device ? p : nullptr;
     if (a.type == hipMemoryTypeHost) {
         void* d = nullptr;
         if (hipHostGetDevicePointer(&d, p, 0) != hipSuccess) {
@@ -278,12 +279,13 @@ extern "C" hkv_status hkv_attach_tier(hkv_cache* c, void* K, void* V, int32_t* t
     if (!K || !V || !tok) return fail(c, HKV_ERR_INVALID_ARG, "hkv_attach_tier: NULL buffer");
     if (!aligned(K, 16) || !aligned(V, 16) || !aligned(tok, 4))
         return fail(c, HKV_ERR_INVALID_ARG, "hkv_attach_tier: K and V must be 16-byte aligned, tok 4-byte aligned");
-    void* dk = gpu_address(K);
-    void* dv = gpu_address(V);
-    void* dt = gpu_address(tok);
+    void* dk = gpu_address(K, c->device);
+    void* dv = gpu_address(V, c->device);
+    void* dt = gpu_address(tok, c->device);
     if (!dk || !dv || !dt)
         return fail(c, HKV_ERR_INVALID_ARG,
-                    "hkv_attach_tier: tier buffers must be pinned host memory (hipHostMalloc) or device memory");
+                    "hkv_attach_tier: tier buffers must be pinned host memory (hipHostMalloc) or memory of the "
+                    "cache's device");
     hipStream_t st = (hipStream_t)stream;
     hipError_t e = hipMemsetAsync(c->dev.tcount, 0, (size_t)c->lay.B * c->lay.Hkv * 4, st);
     s = check_launch(c, e, st, "hkv_attach_tier");

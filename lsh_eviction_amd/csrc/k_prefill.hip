@@ -576,7 +576,11 @@ __global__ __launch_bounds__(kSelThreads) void k_chunk_select(DevCache c, const 
 
     __shared__ int s_w[kSelWaves];
     __shared__ int s_T, s_evict_eq, s_short;
-    if (tid == 0) s_short = 0;
+    if (tid == 0) {
+        s_short = 0;
+        s_T = 0;
+        s_evict_eq = 0;
+    }
 
     const bool scored = !all && !reuse;
     if (scored) {
@@ -650,7 +654,7 @@ __global__ __launch_bounds__(kSelThreads) void k_chunk_select(DevCache c, const 
         const int lt_before = ex & 0xFFFF, eq_before = ex >> 16;
         const bool keep = lt || (eq && base_eq + eq_before >= evict_eq);
         const int pos = base + lt_before + eq_before - (evicted_eq(base_eq + eq_before) - evicted_eq(base_eq));
-        if (keep) {
+        if (keep && pos < k) {   // exactly k are kept; the bound keeps every write inside the slots regardless
             if (kept) kept[(size_t)head * kmax + pos] = i;
             const int len = min(C, N - i * C);
             for (int r = 0; r < len; ++r) c.tok[rowbase + (size_t)pos * C + r] = i * C + r;
@@ -661,10 +665,11 @@ __global__ __launch_bounds__(kSelThreads) void k_chunk_select(DevCache c, const 
         base_eq += teq;
     }
     __syncthreads();
-    const int n = base * C - s_short;   // kept tokens
+    const int placed = min(base, k);
+    const int n = placed * C - s_short;   // kept tokens
     for (int s = n + tid; s < min(N, S); s += kSelThreads) c.tok[rowbase + s] = -1;
     if (kept)
-        for (int j = base + tid; j < kmax; j += kSelThreads) kept[(size_t)head * kmax + j] = -1;
+        for (int j = placed + tid; j < kmax; j += kSelThreads) kept[(size_t)head * kmax + j] = -1;
     if (tid == 0) c.state[2 * head] = n;
 }
 
