@@ -1004,14 +1004,113 @@ __device__ __forceinline__ int merge_splits(const MergeArgs& a, int e, float4* s
 
 // Shared memory of the last block's merge: one (max, sum) per head and wave
 // and 4 outputs per wave, head and 4-element column, and the (max, sum, logit) records of the
-// batch being folded.
+// batch being folded; with one common maximum per head, the two weights of
+// every record and per head the total weight and the new token's weight.
 template <int D, int GM>
 struct MergeBlockSmem {
     float m[GM][kWaves];
     float l[GM][kWaves];
     float4 a[kWaves][GM][D / 4];
     float4 sc[kThreads];
+    float2 w[kThreads];
+    float L[GM], sn[GM];
 };
+
+// Merge of a head's split records against one common maximum per head, for
+// nsb * G <= kThreads records.  Thread t < nsb * G fetches record t = (split
+// j = t / G, head g = t % G): (max m, sum l, candidate logit z).  M_g is the
+// largest of the maxima of the non-empty partials, of the logits of the
+// candidates that are added back (every split's but the winner's) and of the
+// new token's logit, so every weight exp2(x - M_g) is at most 1.  One wave
+// per head writes each record's weights (exp2(m - M_g) for the partial,
+// exp2(z - M_g) for its candidate) to w, and the head's total weight (the
+// new token's included) to L.  Each thread then folds the acc rows and
+// candidate value rows of splits j = r + RS * jj into At[g] (its 4 columns
+// c4) with plain multiply-adds; the batch's loads are all issued before any
+// is used.  Returns the evicted slot (`e` when the cache is not full).
+template <int D, int GM, int JB>
+__device__ __forceinline__ int merge_scaled(const MergeArgs& a, int e, const float* nlg, MergeBlockSmem<D, GM>& mg,
+                                            float4 (&At)[GM])
+{
+    constexpr int RS = kThreads / (D / 4);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int G = a.G, nrec = a.nsb * G;
+    const float4 scv = ld_sc1_16(a.scal, min(tid, nrec - 1) * 16);
+    float4 av[JB][GM], cv[JB];
+    auto issue = [&](int j0) {
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj) {
+            const int j = min(j0 + a.r + RS * jj, a.nsb - 1);
+            // candidate rows exist only when the cache is full (every split
+            // then writes one); otherwise their weight is 0 and the row is
+            // taken as 0, never read
+            cv[jj] = a.full ? ld_sc1_16(a.cv, (j * D + 4 * a.c4) * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int g = 0; g < GM; ++g)
+                av[jj][g] = ld_sc1_16(a.rec, ((j * G + min(g, G - 1)) * D + 4 * a.c4) * 4);
+        }
+    };
+    issue(0);
+    int js = -1;
+    if (a.full) {
+        e = cand_slot(a.wkey);
+        js = e / a.chunk;
+    }
+    if (tid < nrec) mg.sc[tid] = scv;
+    __syncthreads();
+    for (int g = wave; g < G; g += kWaves) {
+        float mx = nlg[g];
+        for (int j = lane; j < a.nsb; j += 64) {
+            const float4 r = mg.sc[j * G + g];
+            if (r.y > 0.f) mx = fmaxf(mx, r.x);
+            if (a.full && j != js) mx = fmaxf(mx, r.z);
+        }
+        mx = wave_max_f(mx);
+        float ls = 0.f;
+        for (int j = lane; j < a.nsb; j += 64) {
+            const float4 r = mg.sc[j * G + g];
+            const float sp = r.y > 0.f ? exp2_fast(r.x - mx) : 0.f;
+            const float sc = a.full && j != js ? exp2_fast(r.z - mx) : 0.f;
+            ls = fmaf(r.y, sp, ls) + sc;
+            mg.w[j * G + g] = make_float2(sp, sc);
+        }
+        ls = wave_sum_f(ls);
+        if (lane == 0) {
+            const float sn = exp2_fast(nlg[g] - mx);
+            mg.sn[g] = sn;
+            mg.L[g] = ls + sn;
+        }
+    }
+    __syncthreads();
+    for (int j0 = 0; j0 < a.nsb; j0 += RS * JB) {
+        if (j0 > 0) issue(j0);
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj) {
+            const int j = j0 + a.r + RS * jj;
+            if (j < a.nsb) {
+#pragma unroll
+                for (int g = 0; g < GM; ++g) {
+                    if (g < G) {
+                        const float2 w = mg.w[j * G + g];
+                        const float4 x = av[jj][g], y = cv[jj];
+                        At[g] = make_float4(fmaf(y.x, w.y, fmaf(x.x, w.x, At[g].x)), fmaf(y.y, w.y, fmaf(x.y, w.x, At[g].y)),
+                                            fmaf(y.z, w.y, fmaf(x.z, w.x, At[g].z)), fmaf(y.w, w.y, fmaf(x.w, w.x, At[g].w)));
+                    }
+                }
+            }
+        }
+    }
+    return e;
+}
+
+// Sum of v over the lane and its partner lane ^ X (X = 16 or 32); the sum is
+// the same in both lanes.
+template <int X>
+__device__ __forceinline__ float4 pair_sum4(float4 v)
+{
+    const float2 x2 = swap_pair<X>(v.x), y2 = swap_pair<X>(v.y), z2 = swap_pair<X>(v.z), w2 = swap_pair<X>(v.w);
+    return make_float4(x2.x + x2.y, y2.x + y2.y, z2.x + z2.y, w2.x + w2.y);
+}
 
 template <int D, int BITS, int GM>
 union FusedSmem {
@@ -1229,84 +1328,121 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     constexpr int JBMAX = GM <= 4 ? 4 : (GM <= 8 ? 2 : 1);   // register budget
     const int c4 = tid % TPR, r = tid / TPR;
     const unsigned long long wkey = ld_dev(&c.ekey[2 * head + (t & 1)]);
-    float Mt[GM], Lt[GM];
-    float4 At[GM];
-#pragma unroll
-    for (int g = 0; g < GM; ++g) {
-        Mt[g] = -INFINITY;
-        Lt[g] = 0.f;
-        At[g] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
     const size_t hrec = (size_t)head * c.nsplit;
     MergeArgs ma{dev_rsrc(c.frec + hrec * G * D, (size_t)c.nsplit * G * D * 4),
                  dev_rsrc(c.fscal + hrec * G * 4, (size_t)c.nsplit * G * 16),
                  dev_rsrc(c.cand_v + hrec * D, (size_t)c.nsplit * D * 4), G, nsb, r, c4, full, wkey, c.chunk};
     const int per = (nsb + RS - 1) / RS;   // splits per thread
-    int e = n;
-    if (per <= 1 || JBMAX == 1)
-        e = merge_splits<D, GM, 1>(ma, e, u.mg.sc, Mt, Lt, At);
-    else if (per <= 2 || JBMAX == 2)
-        e = merge_splits<D, GM, (JBMAX >= 2 ? 2 : 1)>(ma, e, u.mg.sc, Mt, Lt, At);
-    else
-        e = merge_splits<D, GM, JBMAX>(ma, e, u.mg.sc, Mt, Lt, At);
     MergeBlockSmem<D, GM>& mg = u.mg;
-    // the rows of a wave (its lanes that share c4) join, then one entry per wave
     static_assert(TPR == 16 || TPR == 32, "rows per wave");
-#pragma unroll
-    for (int g = 0; g < GM; ++g) {
-        if (g < G) {
-            if constexpr (TPR == 16) lse_join_swap<16>(Mt[g], Lt[g], At[g]);
-            lse_join_swap<32>(Mt[g], Lt[g], At[g]);
-        }
-    }
-    // merge_splits' barriers already ordered the attention's last use of this
-    // memory before these writes, and its s_sc is a separate member
-    if (lane < TPR) {
-#pragma unroll
-        for (int g = 0; g < GM; ++g) {
-            if (g < G) {
-                mg.a[wave][g][c4] = At[g];
-                if (c4 == 0) {
-                    mg.m[g][wave] = Mt[g];
-                    mg.l[g][wave] = Lt[g];
-                }
-            }
-        }
-    }
-    __syncthreads();
     // Output float4 (head g, columns 4 cc .. 4 cc + 3) is summed by Q adjacent
-    // lanes, lane k taking waves k, k + Q, ..., every entry scaled to the
-    // head's largest max M (the new token's logit included), so each entry
-    // costs one exp2 and the lanes' sums add plainly.
+    // lanes, lane k taking waves k, k + Q, ...
     const int nout = G * TPR;
     int qsh = 0;
     while ((2 << qsh) <= kWaves && (nout << (qsh + 1)) <= kThreads) ++qsh;
     const int Q = 1 << qsh, k = tid & (Q - 1);
     const int oi = min(tid >> qsh, nout - 1);
     const int og = oi / TPR, cc = oi % TPR;
-    float M = s_nlg[og];
+    int e = n;
+    float4 o;
+    if (nsb * G <= kThreads) {
+        // one common maximum per head: plain weighted sums from here on
+        float4 At[GM];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mg.m[og][w]);
-    float L = 0.f;
-    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int w = k; w < kWaves; w += Q) {
-        const float s = exp2_fast(mg.m[og][w] - M);   // 0 for a wave that holds no split
-        const float4 a = mg.a[w][og][cc];
-        L = fmaf(mg.l[og][w], s, L);
-        A = make_float4(fmaf(a.x, s, A.x), fmaf(a.y, s, A.y), fmaf(a.z, s, A.z), fmaf(a.w, s, A.w));
-    }
-    L = lane_group_sum(L, Q);
-    A = make_float4(lane_group_sum(A.x, Q), lane_group_sum(A.y, Q), lane_group_sum(A.z, Q),
-                    lane_group_sum(A.w, Q));
-    if (k == 0 && (tid >> qsh) < nout) {
+        for (int g = 0; g < GM; ++g) At[g] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (per <= 1 || JBMAX == 1)
+            e = merge_scaled<D, GM, 1>(ma, e, s_nlg, mg, At);
+        else if (per <= 2 || JBMAX == 2)
+            e = merge_scaled<D, GM, (JBMAX >= 2 ? 2 : 1)>(ma, e, s_nlg, mg, At);
+        else
+            e = merge_scaled<D, GM, JBMAX>(ma, e, s_nlg, mg, At);
+        // the rows of a wave (its lanes that share c4) add up, then one entry
+        // per wave; merge_scaled's barriers ordered the last reads of the
+        // attention's memory before these writes
+#pragma unroll
+        for (int g = 0; g < GM; ++g) {
+            if (g < G) {
+                if constexpr (TPR == 16) At[g] = pair_sum4<16>(At[g]);
+                At[g] = pair_sum4<32>(At[g]);
+                if (lane < TPR) mg.a[wave][g][c4] = At[g];
+            }
+        }
+        __syncthreads();
+        float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int w = k; w < kWaves; w += Q) {
+            const float4 a = mg.a[w][og][cc];
+            A = make_float4(A.x + a.x, A.y + a.y, A.z + a.z, A.w + a.w);
+        }
+        A = make_float4(lane_group_sum(A.x, Q), lane_group_sum(A.y, Q), lane_group_sum(A.z, Q),
+                        lane_group_sum(A.w, Q));
+        const float4 vn = VQ ? *reinterpret_cast<const float4*>(&s_vdq[VQ ? 4 * cc : 0]) : load4_f32(s_vn + 4 * cc);
+        const float sn = mg.sn[og], inv = 1.f / mg.L[og];
+        o = make_float4(fmaf(vn.x, sn, A.x) * inv, fmaf(vn.y, sn, A.y) * inv, fmaf(vn.z, sn, A.z) * inv,
+                        fmaf(vn.w, sn, A.w) * inv);
+    } else {
+        // more records than threads: running log-sum-exp per thread
+        float Mt[GM], Lt[GM];
+        float4 At[GM];
+#pragma unroll
+        for (int g = 0; g < GM; ++g) {
+            Mt[g] = -INFINITY;
+            Lt[g] = 0.f;
+            At[g] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        if (per <= 1 || JBMAX == 1)
+            e = merge_splits<D, GM, 1>(ma, e, u.mg.sc, Mt, Lt, At);
+        else if (per <= 2 || JBMAX == 2)
+            e = merge_splits<D, GM, (JBMAX >= 2 ? 2 : 1)>(ma, e, u.mg.sc, Mt, Lt, At);
+        else
+            e = merge_splits<D, GM, JBMAX>(ma, e, u.mg.sc, Mt, Lt, At);
+        // the rows of a wave join, then one entry per wave
+#pragma unroll
+        for (int g = 0; g < GM; ++g) {
+            if (g < G) {
+                if constexpr (TPR == 16) lse_join_swap<16>(Mt[g], Lt[g], At[g]);
+                lse_join_swap<32>(Mt[g], Lt[g], At[g]);
+            }
+        }
+        // merge_splits' barriers already ordered the attention's last use of
+        // this memory before these writes, and its s_sc is a separate member
+        if (lane < TPR) {
+#pragma unroll
+            for (int g = 0; g < GM; ++g) {
+                if (g < G) {
+                    mg.a[wave][g][c4] = At[g];
+                    if (c4 == 0) {
+                        mg.m[g][wave] = Mt[g];
+                        mg.l[g][wave] = Lt[g];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        // every wave entry scaled to the head's largest max M (the new
+        // token's logit included), so each entry costs one exp2 and the
+        // lanes' sums add plainly
+        float M = s_nlg[og];
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mg.m[og][w]);
+        float L = 0.f;
+        float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int w = k; w < kWaves; w += Q) {
+            const float s = exp2_fast(mg.m[og][w] - M);   // 0 for a wave that holds no split
+            const float4 a = mg.a[w][og][cc];
+            L = fmaf(mg.l[og][w], s, L);
+            A = make_float4(fmaf(a.x, s, A.x), fmaf(a.y, s, A.y), fmaf(a.z, s, A.z), fmaf(a.w, s, A.w));
+        }
+        L = lane_group_sum(L, Q);
+        A = make_float4(lane_group_sum(A.x, Q), lane_group_sum(A.y, Q), lane_group_sum(A.z, Q),
+                        lane_group_sum(A.w, Q));
         const float sn = exp2_fast(s_nlg[og] - M);
         const float4 vn = VQ ? *reinterpret_cast<const float4*>(&s_vdq[VQ ? 4 * cc : 0]) : load4_f32(s_vn + 4 * cc);
         L += sn;
         const float inv = 1.f / L;
-        reinterpret_cast<float4*>(out + (size_t)(hq0 + og) * D)[cc] =
-            make_float4(fmaf(vn.x, sn, A.x) * inv, fmaf(vn.y, sn, A.y) * inv, fmaf(vn.z, sn, A.z) * inv,
+        o = make_float4(fmaf(vn.x, sn, A.x) * inv, fmaf(vn.y, sn, A.y) * inv, fmaf(vn.z, sn, A.z) * inv,
                         fmaf(vn.w, sn, A.w) * inv);
     }
+    if (k == 0 && (tid >> qsh) < nout) reinterpret_cast<float4*>(out + (size_t)(hq0 + og) * D)[cc] = o;
 
     // a host tier keeps the token that leaves: its rows and position are
     // copied out before the overwrite below (the same thread reads and then

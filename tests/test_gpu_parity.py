@@ -15,6 +15,9 @@ pytestmark = pytest.mark.gpu
 FUSED, SPLIT = 0, 1
 STREAM, TRUNCATE, QUERY, CHUNK = 0, 1, 2, 3
 
+G16 = Shape("g16_b16", 13, batch=1, n_q_heads=16, n_kv_heads=1, head_dim=128, n_bits=16,
+            kv_dtype="bf16", prompt=1100, budget=640, steps=8, key_outliers=True)
+
 SMALL = {
     "tiny": (C.TINY, 64, 0),
     "tiny_chunk64": (C.TINY.scaled(steps=24), 24, 64),
@@ -25,11 +28,17 @@ SMALL = {
                           kv_dtype="bf16", prompt=900, budget=333, steps=12, key_outliers=True), 12, 128),
     "d128_f32_g1": (Shape("d128_f32_g1", 12, batch=1, n_q_heads=2, n_kv_heads=2, head_dim=128, n_bits=64,
                           kv_dtype="f32", prompt=700, budget=256, steps=10, key_outliers=False), 10, 64),
-    "g16_b16": (Shape("g16_b16", 13, batch=1, n_q_heads=16, n_kv_heads=1, head_dim=128, n_bits=16,
-                      kv_dtype="bf16", prompt=1100, budget=640, steps=8, key_outliers=True), 8, 0),
+    "g16_b16": (G16, 8, 0),
     "not_full": (C.LLAMA8B.scaled(prompt=700, budget=1000), 20, 0),
     "fill_then_evict": (C.LLAMA8B.scaled(prompt=990, budget=1000), 20, 0),
     "empty_prompt": (C.TINY.scaled(prompt=0, budget=8), 14, 64),
+    # the fused step's last block merges up to 512 (split, head) records
+    # against one common maximum per head, in one or more batches of splits,
+    # and more records with a running log-sum-exp
+    "g4_two_batches": (C.LLAMA8B.scaled(prompt=8100, budget=8000), 6, 64),
+    "g4_lse_merge": (C.LLAMA8B.scaled(prompt=8700, budget=8600), 6, 64),
+    "g16_two_batches": (G16.scaled(prompt=1600, budget=1500), 6, 64),
+    "g16_lse_merge": (G16.scaled(prompt=2200, budget=2100), 6, 64),
 }
 
 
