@@ -70,6 +70,23 @@ constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within 8
 constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i within 16
 
+// The lane's value and that of lane ^ X (X = 16 or 32), by the lane-swap
+// instructions of gfx950 (VALU, no LDS).  A swap of a register with itself
+// hands each lane its own value and its partner's, in an order that depends
+// on the lane, so callers combine the two symmetrically.
+template <int X>
+__device__ __forceinline__ float2 swap_pair(float v)
+{
+    const unsigned u = __float_as_uint(v);
+    if constexpr (X == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    } else {
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+}
+
 // Sum over aligned groups of N lanes (N = 1 .. 64, power of two); every lane
 // of a group ends with the group's sum.
 template <int N>
@@ -79,8 +96,14 @@ __device__ __forceinline__ float group_sum(float x)
     if constexpr (N >= 4) x += dpp_f<kDppXor2>(x);
     if constexpr (N >= 8) x += dpp_f<kDppHalfMirror>(x);
     if constexpr (N >= 16) x += dpp_f<kDppMirror>(x);
-    if constexpr (N >= 32) x += __shfl_xor(x, 16);
-    if constexpr (N >= 64) x += __shfl_xor(x, 32);
+    if constexpr (N >= 32) {
+        const float2 p = swap_pair<16>(x);
+        x = p.x + p.y;
+    }
+    if constexpr (N >= 64) {
+        const float2 p = swap_pair<32>(x);
+        x = p.x + p.y;
+    }
     return x;
 }
 
@@ -97,28 +120,66 @@ __device__ __forceinline__ uint2 quantize8(const float (&f)[8], float scale)
     return make_uint2(w[0], w[1]);
 }
 
+// 64-bit lane exchanges, as two 32-bit halves moved the same way
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v)
+{
+    const unsigned lo = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)v, CTRL, 0xF, 0xF, false);
+    const unsigned hi = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)(v >> 32), CTRL, 0xF, 0xF, false);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+__device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) { return a > b ? a : b; }
+
+// Largest value over the whole wave (every lane active), joined as in
+// wave_max_f.
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
 {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        unsigned long long o = __shfl_xor(v, m);
-        v = o > v ? o : v;
+    v = umax64(v, dpp_u64<kDppXor1>(v));
+    v = umax64(v, dpp_u64<kDppXor2>(v));
+    v = umax64(v, dpp_u64<kDppHalfMirror>(v));
+    v = umax64(v, dpp_u64<kDppMirror>(v));
+    {
+        const unsigned lo = (unsigned)v, hi = (unsigned)(v >> 32);
+        const auto l = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+        const auto h = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+        v = umax64(((unsigned long long)h[0] << 32) | l[0], ((unsigned long long)h[1] << 32) | l[1]);
+    }
+    {
+        const unsigned lo = (unsigned)v, hi = (unsigned)(v >> 32);
+        const auto l = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+        const auto h = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+        v = umax64(((unsigned long long)h[0] << 32) | l[0], ((unsigned long long)h[1] << 32) | l[1]);
     }
     return v;
 }
 
+// Maximum and sum over the whole wave (every lane active): each step joins a
+// lane with one partner lane -- DPP inside rows of 16, then the 16- and
+// 32-lane swaps -- under a commutative operation, so every lane ends with
+// the same bits.
 __device__ __forceinline__ float wave_max_f(float v)
 {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
-    return v;
+    v = fmaxf(v, dpp_f<kDppXor1>(v));
+    v = fmaxf(v, dpp_f<kDppXor2>(v));
+    v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_f<kDppMirror>(v));
+    float2 p = swap_pair<16>(v);
+    v = fmaxf(p.x, p.y);
+    p = swap_pair<32>(v);
+    return fmaxf(p.x, p.y);
 }
 
 __device__ __forceinline__ float wave_sum_f(float v)
 {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-    return v;
+    v += dpp_f<kDppXor1>(v);
+    v += dpp_f<kDppXor2>(v);
+    v += dpp_f<kDppHalfMirror>(v);
+    v += dpp_f<kDppMirror>(v);
+    float2 p = swap_pair<16>(v);
+    v = p.x + p.y;
+    p = swap_pair<32>(v);
+    return p.x + p.y;
 }
 
 // Ordering key of a candidate slot: larger score first, then lower slot.

@@ -722,23 +722,8 @@ __device__ __forceinline__ void lse_add4(float& m, float& l, float4& a, float mo
     m = mx;
 }
 
-// The lane's (m, l, a) joined with those of lane ^ X (X = 16 or 32), by the
-// lane-swap instructions of gfx950 (VALU, no LDS).  A swap of a register with
-// itself hands each lane its own value and its partner's, in an order that
-// depends on the lane; the join is symmetric, so it takes the two as given.
-template <int X>
-__device__ __forceinline__ float2 swap_pair(float v)
-{
-    const unsigned u = __float_as_uint(v);
-    if constexpr (X == 32) {
-        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-        return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
-    } else {
-        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-        return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
-    }
-}
-
+// The lane's (m, l, a) joined with those of lane ^ X (X = 16 or 32) through
+// swap_pair; the join is symmetric, so it takes the two values as given.
 template <int X>
 __device__ __forceinline__ void lse_join_swap(float& m, float& l, float4& a)
 {
