@@ -69,6 +69,7 @@ constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within 8
 constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i within 16
+constexpr int kDppRor8 = 0x128;       // lane i <- lane (i + 8) mod 16 within 16, i.e. i ^ 8
 
 // The lane's value and that of lane ^ X (X = 16 or 32), by the lane-swap
 // instructions of gfx950 (VALU, no LDS).  A swap of a register with itself

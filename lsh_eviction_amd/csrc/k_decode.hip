@@ -280,7 +280,7 @@ struct Tile {
 template <int D, int GM, typename KT>
 __device__ __forceinline__ void attend_rows(const KT* __restrict__ Kh, const KT* __restrict__ Vh,
                                             const float* __restrict__ qh, int G, int r0, int len, int skip,
-                                            Tile<D, KT> cur, AttnSmem<D, GM>& sm)
+                                            Tile<D, KT> cur, AttnSmem<D, GM>& sm, float* clg)
 {
     using T = Tile<D, KT>;
     constexpr int EPL = T::EPL, LPR = T::LPR, RPW = T::RPW, UNR = T::UNR;
@@ -334,6 +334,10 @@ __device__ __forceinline__ void attend_rows(const KT* __restrict__ Kh, const KT*
             }
             const int row = base + u * RPW + rg;
             const bool isc = (r0 + row) == skip;
+            if (isc && cc == 0) {   // the held-out row's logits
+#pragma unroll
+                for (int g = 0; g < GM; ++g) clg[g] = lg[u][g];
+            }
             if (row >= len || isc) {
 #pragma unroll
                 for (int g = 0; g < GM; ++g) lg[u][g] = -INFINITY;
@@ -502,6 +506,32 @@ struct PSmem {
     float alpha[kWaves][pad_g<GM>()];
 };
 
+// Sums over the four 16-lane rows of a wave of NV values per lane (NV a
+// multiple of 4), transposed on the way: a 32-lane swap of the pair (v[2i],
+// v[2i+1]) and an add leave value 2i summed over lanes l and l ^ 32 in rows
+// 0-1 and value 2i+1 in rows 2-3; a 16-lane swap of two such results and an
+// add complete four sums, one per row.  Afterwards register t[i] of every
+// lane of row r holds the total of value 4 i + kRowOrder[r].
+constexpr int kRowOrder[4] = {0, 2, 1, 3};
+
+template <int NV>
+__device__ __forceinline__ void rows_sum_transposed(const float (&v)[NV], float (&t)[NV / 4])
+{
+    float s[NV / 2];
+#pragma unroll
+    for (int i = 0; i < NV / 2; ++i) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[2 * i]), __float_as_uint(v[2 * i + 1]),
+                                                        false, false);
+        s[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+#pragma unroll
+    for (int i = 0; i < NV / 4; ++i) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(s[2 * i]), __float_as_uint(s[2 * i + 1]),
+                                                        false, false);
+        t[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+}
+
 // Running state of one wave's softmax partial (GM heads, padded heads carry
 // zero queries and are discarded by the caller).
 template <int GM>
@@ -510,10 +540,11 @@ struct MState {
     float acc[GM][8];       // value view: 8 elements of the lane's row segment
 };
 
+// The logits of the held-out row (skip) go to clg[head] as they are computed.
 template <int D, int GM, int TR, bool VQ>
 __device__ __forceinline__ void mfma_tile(const MTile<D, TR, VQ>& tl, int base, int r0, int len, int skip,
                                           const bf16x8 (&qhi)[D / 32], const bf16x8 (&qlo)[D / 32],
-                                          PSmem<GM, TR>& ps, MState<GM>& st)
+                                          PSmem<GM, TR>& ps, MState<GM>& st, float* clg)
 {
     using T = MTile<D, TR, VQ>;
     constexpr int H = T::H, KS = T::KS, LPR = T::LPR, RPW = T::RPW, VU = T::VU;
@@ -541,12 +572,18 @@ __device__ __forceinline__ void mfma_tile(const MTile<D, TR, VQ>& tl, int base, 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = base + 16 * h + 4 * qd + r;
-            const bool ok = row < len && (r0 + row) != skip;
+            const bool held = (r0 + row) == skip;
+            const bool ok = row < len && !held;
+            if (held && n < GM) clg[n] = C[h][r];
             lg[h][r] = ok ? C[h][r] : -INFINITY;
             tmax = fmaxf(tmax, lg[h][r]);
         }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    {
+        float2 t2 = swap_pair<16>(tmax);
+        tmax = fmaxf(t2.x, t2.y);
+        t2 = swap_pair<32>(tmax);
+        tmax = fmaxf(t2.x, t2.y);
+    }
     const float mx = fmaxf(st.m, tmax);
     const float ms = mx == -INFINITY ? 0.f : mx;
     const float alpha = exp2_fast(st.m - ms);
@@ -622,7 +659,7 @@ template <int D, int GM, int TR, int NB, bool VQ = false>
 __device__ __forceinline__ void attend_rows_mfma(const bf16_t* __restrict__ Kh, const void* __restrict__ Vh,
                                                  const float* __restrict__ Vsh, const float* __restrict__ qh, int G,
                                                  int r0, int len, int skip, MTile<D, TR, VQ> (&ring)[NB],
-                                                 AttnSmem<D, GM>& sm, PSmem<GM, TR>& ps)
+                                                 AttnSmem<D, GM>& sm, PSmem<GM, TR>& ps, float* clg)
 {
     constexpr int KS = D / 32, LPR = D / 8;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -665,40 +702,53 @@ __device__ __forceinline__ void attend_rows_mfma(const bf16_t* __restrict__ Kh, 
     for (; k + 2 * NB <= ntile; k += NB) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-            mfma_tile<D, GM, TR>(ring[i], b0 + (k + i) * step, r0, len, skip, qhi, qlo, ps, st);
+            mfma_tile<D, GM, TR>(ring[i], b0 + (k + i) * step, r0, len, skip, qhi, qlo, ps, st, clg);
             ring[i].load(Kh, Vh, Vsh, r0, len, b0 + (k + i + NB) * step);
         }
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
         if (k + i < ntile) {
-            mfma_tile<D, GM, TR>(ring[i], b0 + (k + i) * step, r0, len, skip, qhi, qlo, ps, st);
+            mfma_tile<D, GM, TR>(ring[i], b0 + (k + i) * step, r0, len, skip, qhi, qlo, ps, st, clg);
             if (k + i + NB < ntile) ring[i].load(Kh, Vh, Vsh, r0, len, b0 + (k + i + NB) * step);
         }
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i)
-        if (k + NB + i < ntile) mfma_tile<D, GM, TR>(ring[i], b0 + (k + NB + i) * step, r0, len, skip, qhi, qlo, ps, st);
+        if (k + NB + i < ntile) mfma_tile<D, GM, TR>(ring[i], b0 + (k + NB + i) * step, r0, len, skip, qhi, qlo, ps, st, clg);
 
     // the wave's rows share one running max per head: sums combine directly
     float lsum = st.lsum;
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
-#pragma unroll
-    for (int off = LPR; off < 64; off <<= 1)
-#pragma unroll
-        for (int g = 0; g < GM; ++g)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) st.acc[g][e] += __shfl_xor(st.acc[g][e], off);
+    {
+        float2 t2 = swap_pair<16>(lsum);
+        lsum = t2.x + t2.y;
+        t2 = swap_pair<32>(lsum);
+        lsum = t2.x + t2.y;
+    }
     if (qd == 0 && n < GM) {
         sm.m[wave][n] = st.m;
         sm.l[wave][n] = lsum;
     }
-    if (rg == 0) {
+    // value view: the lanes of a 16-lane row hold 8 columns each of one row
+    // group; with 8-lane groups (D = 64) the two groups of a row add first
+    float v[GM * 8];
 #pragma unroll
-        for (int g = 0; g < GM; ++g)
+    for (int g = 0; g < GM; ++g)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sm.acc[wave][g][cc * 8 + e] = st.acc[g][e];
+        for (int e = 0; e < 8; ++e) v[g * 8 + e] = st.acc[g][e];
+    if constexpr (LPR == 8) {
+#pragma unroll
+        for (int i = 0; i < GM * 8; ++i) v[i] += dpp_f<kDppRor8>(v[i]);
+    }
+    float t[GM * 2];
+    rows_sum_transposed<GM * 8>(v, t);
+    if (LPR == 16 || (lane & 15) < 8) {
+        const int ord = kRowOrder[qd];
+#pragma unroll
+        for (int i = 0; i < GM * 2; ++i) {
+            const int idx = 4 * i + ord;
+            sm.acc[wave][idx / 8][(lane % LPR) * 8 + idx % 8] = t[i];
+        }
     }
     __syncthreads();
 }
@@ -895,12 +945,18 @@ __device__ __forceinline__ void st_sc1_8(__amdgpu_buffer_rsrc_t rs, int off, flo
 // The block's partial of the fused step, write-through: acc [G][D] at `rec`
 // and one (max, sum, candidate logit, 0) per head at `scal` (base 2; the
 // candidate logit is 0 when the chunk has no candidate).
+// Every output float4 (head g, columns i .. i + 3) is summed by P adjacent
+// lanes, lane k taking waves k, k + P, ..., so that all waves share the work.
 template <int D, int GM>
 __device__ __forceinline__ void publish_fused(const AttnSmem<D, GM>& sm, __amdgpu_buffer_rsrc_t rec,
                                               __amdgpu_buffer_rsrc_t scal, int G, const float* clg, bool has_cand)
 {
     constexpr int D4 = D / 4;
-    for (int idx = threadIdx.x; idx < G * D4; idx += kThreads) {
+    const int ne = G * D4;
+    int psh = 0;
+    while ((2 << psh) <= kWaves && (ne << (psh + 1)) <= kThreads) ++psh;
+    const int P = 1 << psh, k = threadIdx.x & (P - 1);
+    for (int idx = threadIdx.x >> psh; idx < ne; idx += kThreads >> psh) {
         const int g = idx / D4, i = (idx % D4) * 4;
         float mx = -INFINITY;
 #pragma unroll
@@ -908,18 +964,19 @@ __device__ __forceinline__ void publish_fused(const AttnSmem<D, GM>& sm, __amdgp
         const float ms = mx == -INFINITY ? 0.f : mx;
         float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
         float ls = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = k; w < kWaves; w += P) {
             const float sc = exp2_fast(sm.m[w][g] - ms);
             const float4 x = *reinterpret_cast<const float4*>(&sm.acc[w][g][i]);
-            a.x += x.x * sc;
-            a.y += x.y * sc;
-            a.z += x.z * sc;
-            a.w += x.w * sc;
-            ls += sm.l[w][g] * sc;
+            a = make_float4(fmaf(x.x, sc, a.x), fmaf(x.y, sc, a.y), fmaf(x.z, sc, a.z), fmaf(x.w, sc, a.w));
+            ls = fmaf(sm.l[w][g], sc, ls);
         }
-        st_sc1_16(rec, (g * D + i) * 4, a);
-        if (i == 0) st_sc1_16(scal, g * 16, make_float4(mx, ls, has_cand ? clg[g] : 0.f, 0.f));
+        a = make_float4(lane_group_sum(a.x, P), lane_group_sum(a.y, P), lane_group_sum(a.z, P),
+                        lane_group_sum(a.w, P));
+        ls = lane_group_sum(ls, P);
+        if (k == 0) {
+            st_sc1_16(rec, (g * D + i) * 4, a);
+            if (i == 0) st_sc1_16(scal, g * 16, make_float4(mx, ls, has_cand ? clg[g] : 0.f, 0.f));
+        }
     }
 }
 
@@ -1244,10 +1301,10 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
         if (tid == 0 && ckey) atomicMax(&c.ekey[2 * head + (t & 1)], ckey);
     }
 
-    // the held-out candidate's K and V rows: fetched now, used after the loop
-    float2 kc2 = make_float2(0.f, 0.f), vc2 = make_float2(0.f, 0.f);
+    // the held-out candidate's value row: fetched now, published after the
+    // loop (the loop takes its logits as it passes its row)
+    float2 vc2 = make_float2(0.f, 0.f);
     if (cand >= 0 && 2 * lane < D) {
-        kc2 = make_float2(to_f32(Kh[(size_t)cand * D + 2 * lane]), to_f32(Kh[(size_t)cand * D + 2 * lane + 1]));
         if constexpr (VQ) {
             const uint16_t w = *reinterpret_cast<const uint16_t*>(Vq8 + (size_t)cand * D + 2 * lane);
             const float sc = Vsh[cand];
@@ -1259,23 +1316,15 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
 
     // attention over the chunk with the candidate held out
     if constexpr (kMfma)
-        attend_rows_mfma<D, GM, TR, NB, VQ>(Kh, Vbase, Vsh, &s_q[0][0], G, s0, len, cand, ring, sm, ps);
+        attend_rows_mfma<D, GM, TR, NB, VQ>(Kh, Vbase, Vsh, &s_q[0][0], G, s0, len, cand, ring, sm, ps, s_clg);
     else
-        attend_rows<D, GM, KT>(Kh, Vh, &s_q[0][0], G, s0, len, cand, first, sm);
+        attend_rows<D, GM, KT>(Kh, Vh, &s_q[0][0], G, s0, len, cand, first, sm, s_clg);
 
     // publish this chunk: partial softmax, candidate logits and value row
-    if (cand >= 0) {
-        const float qs = qscale2<D>();
-        const int i0 = 2 * lane;
-        for (int g = wave; g < G; g += kWaves) {
-            float dot = 0.f;
-            if (i0 < D) dot = fmaf(s_q[g][i0] * qs, kc2.x, s_q[g][i0 + 1] * qs * kc2.y);
-            dot = wave_sum_f(dot);
-            if (lane == 0) s_clg[g] = dot;
-        }
-        if (wave == 0 && i0 < D) st_sc1_8(dev_rsrc(c.cand_v + crec * D, (size_t)D * 4), i0 * 4, vc2);
-    }
-    __syncthreads();
+    // (the attention's closing barrier made its LDS results, the candidate's
+    // logits included, visible to every wave)
+    if (cand >= 0 && wave == 0 && 2 * lane < D)
+        st_sc1_8(dev_rsrc(c.cand_v + crec * D, (size_t)D * 4), 2 * lane * 4, vc2);
     publish_fused<D, GM>(sm, dev_rsrc(c.frec + crec * G * D, (size_t)G * D * 4),
                          dev_rsrc(c.fscal + crec * G * 4, (size_t)G * 16), G, s_clg, cand >= 0);
     own_stores_complete();
@@ -1603,11 +1652,11 @@ __global__ __launch_bounds__(kThreads) void k_attn_split(DevCache c, const float
 #pragma unroll
         for (int i = 0; i < NB; ++i)
             if (i < ntile) ring[i].load(Kh, Vh, nullptr, s0, len, (wave + i * kWaves) * TR);
-        attend_rows_mfma<D, GM, TR, NB>(Kh, Vh, nullptr, q + (size_t)hq0 * D, c.G, s0, len, -1, ring, sm, ps);
+        attend_rows_mfma<D, GM, TR, NB>(Kh, Vh, nullptr, q + (size_t)hq0 * D, c.G, s0, len, -1, ring, sm, ps, nullptr);
     } else {
         Tile<D, KT> first;
         first.load(Kh, Vh, s0, len, wave * Tile<D, KT>::ROWS);
-        attend_rows<D, GM, KT>(Kh, Vh, q + (size_t)hq0 * D, c.G, s0, len, -1, first, sm);
+        attend_rows<D, GM, KT>(Kh, Vh, q + (size_t)hq0 * D, c.G, s0, len, -1, first, sm, nullptr);
     }
     store_partial<D, GM>(sm, c.part, hq0, c.G, c.nsplit, split);
 }
@@ -1669,11 +1718,11 @@ __global__ __launch_bounds__(kThreads) void k_attn_tier(DevCache c, const float*
 #pragma unroll
         for (int i = 0; i < NB; ++i)
             if (i < ntile) ring[i].load(Kh, Vh, nullptr, s0, len, (wave + i * kWaves) * TR);
-        attend_rows_mfma<D, GM, TR, NB>(Kh, Vh, nullptr, q + (size_t)hq0 * D, c.G, s0, len, -1, ring, sm, ps);
+        attend_rows_mfma<D, GM, TR, NB>(Kh, Vh, nullptr, q + (size_t)hq0 * D, c.G, s0, len, -1, ring, sm, ps, nullptr);
     } else {
         Tile<D, KT> first;
         first.load(Kh, Vh, s0, len, wave * Tile<D, KT>::ROWS);
-        attend_rows<D, GM, KT>(Kh, Vh, q + (size_t)hq0 * D, c.G, s0, len, -1, first, sm);
+        attend_rows<D, GM, KT>(Kh, Vh, q + (size_t)hq0 * D, c.G, s0, len, -1, first, sm, nullptr);
     }
     store_partial<D, GM>(sm, c.tpart, hq0, c.G, c.tsplit, split);
 }
