@@ -1196,6 +1196,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     __shared__ float s_nlg[GM];
     __shared__ float s_clg[GM];
     __shared__ int s_last;
+    __shared__ int s_state[3];   // budget, occupancy, step
     AttnSmem<D, GM>& sm = u.at;
 
     const int hq0 = b * c.Hq + h * G;
@@ -1228,19 +1229,28 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     const uint4 kvst = reinterpret_cast<const uint4*>(wave == 0 ? kh : vh)[min(lane, NK4 - 1)];
     const int cvec = min(s0 + tid * VS, (int)c.code_slots - VS);
     const uint4 craw = *reinterpret_cast<const uint4*>(codeh + cvec);
+    // (threads past the end store the last element again, with the value
+    // they loaded from it, so every store is unconditional)
 #pragma unroll
-    for (int j = 0; j < RPT; ++j)
-        if (tid + j * kThreads < NR4) reinterpret_cast<float4*>(u.R)[tid + j * kThreads] = rst[j];
-    if (tid < NQ4) reinterpret_cast<float4*>(&s_q[0][0])[tid] = qst;
-    if (lane < NK4 && wave < 2) reinterpret_cast<uint4*>(wave == 0 ? s_kn : s_vn)[lane] = kvst;
-    // the cache state (its loads overlap the ones above)
-    const int S = c.budget[b];
+    for (int j = 0; j < RPT; ++j) reinterpret_cast<float4*>(u.R)[min(tid + j * kThreads, NR4 - 1)] = rst[j];
+    reinterpret_cast<float4*>(&s_q[0][0])[min(tid, NQ4 - 1)] = qst;
+    reinterpret_cast<uint4*>(wave == 0 ? s_kn : s_vn)[min(lane, NK4 - 1)] = kvst;
+    // The cache state goes through LDS before the barrier, stored by every
+    // thread (the same values), which keeps its loads next to the ones above:
+    // left alone, the compiler issues them after the barrier, and the tile
+    // loads below, which need the chunk's length, would wait for one more
+    // round trip.
+    {
+        const int S0 = c.budget[b], n0 = c.state[2 * head], t0 = c.state[2 * head + 1];
+        s_state[0] = S0;
+        s_state[1] = n0;
+        s_state[2] = t0;
+    }
+    __syncthreads();
+    const int S = s_state[0], n = s_state[1], t = s_state[2];
     const int nsb = (S + c.chunk - 1) / c.chunk;
-    const int n = c.state[2 * head];
-    const int t = c.state[2 * head + 1];
     const bool full = n >= S;
     const int len = max(min(s0 + c.chunk, n) - s0, 0);
-    __syncthreads();
     if (split >= nsb) return;   // ragged batch: this sequence has fewer chunks
 
     // the first tiles of every wave, in flight while the codes are computed
