@@ -26,7 +26,7 @@ struct DevCache {
     float* cand_v;                  // [B][Hkv][nsplit][d] value row of the split's candidate (fp32)
     unsigned long long* ekey;       // [B][Hkv][2] eviction key of the step, by parity of its position
     int* info;                      // [B][Hkv][2] occupancy and position at the start of the step
-    unsigned* count;                // [B][Hkv] blocks of the current step that have published
+    unsigned* count;                // [B][Hkv][kCountStride] blocks of the current step that have published (entry 0)
     void* pcode;                    // [B][Hkv][pcode_slots] prompt key codes
     void* qcode;                    // [B][Hq][pcode_slots] prompt query codes (QUERY prefill)
     float* vs;                      // [B][Hkv][Smax] (+16) value scales when values are int8

@@ -134,7 +134,7 @@ hkv_status compute_layout(const hkv_config* cfg, Layout* L, char* err, size_t er
     l.off_cand_v = take(heads * l.nsplit * l.d * 4);
     l.off_ekey = take(heads * 2 * 8);
     l.off_info = take(heads * 2 * 4);
-    l.off_count = take(heads * 4);
+    l.off_count = take(heads * kCountStride * 4);
     l.off_pcode = take(heads * l.pcode_slots * cb);
     l.off_qcode = take(cfg->prefill_policy == HKV_PREFILL_QUERY ? (size_t)l.B * l.Hq * l.pcode_slots * cb : 0);
     // per-chunk scores of the prompt (HKV_PREFILL_CHUNK)

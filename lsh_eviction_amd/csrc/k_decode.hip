@@ -945,18 +945,16 @@ __device__ __forceinline__ void st_sc1_8(__amdgpu_buffer_rsrc_t rs, int off, flo
 // The block's partial of the fused step, write-through: acc [G][D] at `rec`
 // and one (max, sum, candidate logit, 0) per head at `scal` (base 2; the
 // candidate logit is 0 when the chunk has no candidate).
-// Every output float4 (head g, columns i .. i + 3) is summed by P adjacent
-// lanes, lane k taking waves k, k + P, ..., so that all waves share the work.
+// One thread per output float4 (head g, columns i .. i + 3), summing the
+// waves in order.  (Splitting an entry over several adjacent lanes joined by
+// DPP measured slower: those lanes read rows of different waves that sit in
+// the same LDS banks.)
 template <int D, int GM>
 __device__ __forceinline__ void publish_fused(const AttnSmem<D, GM>& sm, __amdgpu_buffer_rsrc_t rec,
                                               __amdgpu_buffer_rsrc_t scal, int G, const float* clg, bool has_cand)
 {
     constexpr int D4 = D / 4;
-    const int ne = G * D4;
-    int psh = 0;
-    while ((2 << psh) <= kWaves && (ne << (psh + 1)) <= kThreads) ++psh;
-    const int P = 1 << psh, k = threadIdx.x & (P - 1);
-    for (int idx = threadIdx.x >> psh; idx < ne; idx += kThreads >> psh) {
+    for (int idx = threadIdx.x; idx < G * D4; idx += kThreads) {
         const int g = idx / D4, i = (idx % D4) * 4;
         float mx = -INFINITY;
 #pragma unroll
@@ -964,19 +962,15 @@ __device__ __forceinline__ void publish_fused(const AttnSmem<D, GM>& sm, __amdgp
         const float ms = mx == -INFINITY ? 0.f : mx;
         float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
         float ls = 0.f;
-        for (int w = k; w < kWaves; w += P) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
             const float sc = exp2_fast(sm.m[w][g] - ms);
             const float4 x = *reinterpret_cast<const float4*>(&sm.acc[w][g][i]);
             a = make_float4(fmaf(x.x, sc, a.x), fmaf(x.y, sc, a.y), fmaf(x.z, sc, a.z), fmaf(x.w, sc, a.w));
             ls = fmaf(sm.l[w][g], sc, ls);
         }
-        a = make_float4(lane_group_sum(a.x, P), lane_group_sum(a.y, P), lane_group_sum(a.z, P),
-                        lane_group_sum(a.w, P));
-        ls = lane_group_sum(ls, P);
-        if (k == 0) {
-            st_sc1_16(rec, (g * D + i) * 4, a);
-            if (i == 0) st_sc1_16(scal, g * 16, make_float4(mx, ls, has_cand ? clg[g] : 0.f, 0.f));
-        }
+        st_sc1_16(rec, (g * D + i) * 4, a);
+        if (i == 0) st_sc1_16(scal, g * 16, make_float4(mx, ls, has_cand ? clg[g] : 0.f, 0.f));
     }
 }
 
@@ -1339,7 +1333,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
                          dev_rsrc(c.fscal + crec * G * 4, (size_t)G * 16), G, s_clg, cand >= 0);
     own_stores_complete();
     __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&c.count[head], 1u) == (unsigned)(nsb - 1);
+    if (tid == 0) s_last = atomicAdd(&c.count[head * kCountStride], 1u) == (unsigned)(nsb - 1);
     __syncthreads();
     if (!s_last) return;
 
@@ -1347,7 +1341,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     // Every thread owns 4 output columns (c4) of every head for the splits
     // j = r + RS * jj.  All loads of a batch of splits are issued before any
     // of them is used, so the merge costs one round trip to memory per batch.
-    if (tid == 0) c.count[head] = 0u;
+    if (tid == 0) c.count[head * kCountStride] = 0u;
     if constexpr (VQ) {
         // the new token's value row as the cache will hold it: int8 codes
         // (v / scale rounded half to even, clamped to +-127) with scale =

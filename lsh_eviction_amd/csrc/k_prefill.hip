@@ -45,7 +45,7 @@ __global__ void k_prefill_init(DevCache c)
         c.state[2 * head + 1] = N;
         c.ekey[2 * head] = 0ull;
         c.ekey[2 * head + 1] = 0ull;
-        c.count[head] = 0u;
+        c.count[head * kCountStride] = 0u;
     }
 }
 
@@ -60,7 +60,7 @@ __global__ void k_reset(DevCache c)
         c.state[2 * head + 1] = 0;
         c.ekey[2 * head] = 0ull;
         c.ekey[2 * head + 1] = 0ull;
-        c.count[head] = 0u;
+        c.count[head * kCountStride] = 0u;
     }
 }
 
@@ -798,7 +798,7 @@ __global__ void k_clear_step_scratch(DevCache c)
     if (head < c.B * c.Hkv) {
         c.ekey[2 * head] = 0ull;
         c.ekey[2 * head + 1] = 0ull;
-        c.count[head] = 0u;
+        c.count[head * kCountStride] = 0u;
     }
 }
 
