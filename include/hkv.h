@@ -107,7 +107,7 @@ typedef struct {
                                 a multiple of 64 in [64, 65536], or 0: about
                                 one workgroup per compute unit, i.e.
                                 ceil(sum_b S_b * Hkv / 256) rounded up to a
-                                multiple of 64 and clamped to that range */
+                                multiple of 64 and clamped to [256, 65536] */
     int32_t value_bits;      /* 0: values stored in kv_dtype; 8: each value row
                                 stored as d int8 codes and one fp32 scale
                                 (scale = max|v| / 127, code = v / scale rounded

@@ -15,6 +15,7 @@ constexpr int kMaxBudget = 1 << 22;
 constexpr int kMaxBatch = 4096;
 constexpr size_t kLdsTableBytes = 128 * 1024;   // code table of the sequential prefill selection (registers of one block)
 constexpr int kChunkTargetBlocks = 256;   // default split: about one decode block per compute unit of the part
+constexpr int kMinAutoChunk = 256;        // ... but at least this many slots per block
 constexpr int kDefaultPrefillChunk = 10;   // tokens per prefill chunk (HKV_PREFILL_CHUNK)
 constexpr int kMaxPrefillChunk = 32;
 constexpr int kMaxTierCapacity = 1 << 28;

@@ -82,13 +82,15 @@ hkv_status compute_layout(const hkv_config* cfg, Layout* L, char* err, size_t er
         l.chunk = cfg->chunk;
     } else {
         // about one block of the decode step per compute unit: the slots of
-        // all eviction domains over kChunkTargetBlocks, a multiple of 64
+        // all eviction domains over kChunkTargetBlocks, a multiple of 64, and
+        // at least kMinAutoChunk (below that the merge of more, shorter
+        // blocks costs more than the compute units they add)
         long long slots = 0;
         for (int b = 0; b < cfg->batch; ++b) slots += cfg->budgets[b];
         slots *= cfg->n_kv_heads;
         long long ch = (slots + kChunkTargetBlocks - 1) / kChunkTargetBlocks;
         ch = (ch + 63) / 64 * 64;
-        l.chunk = (int)(ch < 64 ? 64 : (ch > 65536 ? 65536 : ch));
+        l.chunk = (int)(ch < kMinAutoChunk ? kMinAutoChunk : (ch > 65536 ? 65536 : ch));
     }
     l.nsplit = (Smax + l.chunk - 1) / l.chunk;
     if (l.nsplit > 65535)

@@ -241,11 +241,11 @@ def to_numpy(t) -> np.ndarray:
 
 def default_chunk(budgets, n_kv_heads: int) -> int:
     """The split size hkv_config.chunk = 0 selects (include/hkv.h): about one
-    workgroup per compute unit, a multiple of 64 in [64, 65536]."""
+    workgroup per compute unit, a multiple of 64 in [256, 65536]."""
     slots = int(np.asarray(budgets, dtype=np.int64).sum()) * int(n_kv_heads)
     ch = -(-slots // 256)
     ch = -(-ch // 64) * 64
-    return min(max(ch, 64), 65536)
+    return min(max(ch, 256), 65536)
 
 
 class Cache:

@@ -93,6 +93,23 @@ def test_query_policy_validates_and_sizes_its_code_buffer(hkv):
     assert extra >= 32 * 8192 * 4
 
 
+@pytest.mark.parametrize("budgets,heads", [([4096], 8), ([32768], 8), ([300], 1), ([1500, 800, 64], 2),
+                                           ([16384] * 8, 8), ([1 << 22], 1)])
+def test_default_chunk_matches_the_library(hkv, budgets, heads):
+    # hkv.Cache sizes its bookkeeping with the rule chunk = 0 selects; the
+    # workspace (which grows with the number of splits) must come out the same
+    from lsh_eviction_amd.hkv import default_chunk
+    ch = default_chunk(budgets, heads)
+    assert ch % 64 == 0 and 256 <= ch <= 65536
+    kw = dict(batch=len(budgets), n_q_heads=4 * heads, n_kv_heads=heads, budgets=budgets,
+              prefill_policy=hkv.HKV_PREFILL_TRUNCATE)
+    auto, fixed = _cfg(hkv, **kw), _cfg(hkv, chunk=ch, **kw)
+    assert hkv.hkv_workspace_bytes(auto) == hkv.hkv_workspace_bytes(fixed)
+    # and the comparison can tell split counts apart: half the chunk, more splits
+    other = _cfg(hkv, chunk=ch // 2 // 64 * 64, **kw)
+    assert hkv.hkv_workspace_bytes(auto) != hkv.hkv_workspace_bytes(other)
+
+
 def test_chunk_policy_validates_and_sizes_its_score_buffer(hkv):
     a = _cfg(hkv, prefill_policy=hkv.HKV_PREFILL_CHUNK)
     assert hkv.hkv_validate_config(a) == hkv.HKV_OK
