@@ -224,6 +224,9 @@ INT8_VALUES = {
     "not_full": (C.LLAMA8B.scaled(prompt=700, budget=1000), 8, 0),
     "fill_then_evict": (C.LLAMA8B.scaled(prompt=990, budget=1000), 16, 0),
     "empty_prompt": (C.TINY.scaled(prompt=0, budget=8, kv_dtype="bf16"), 10, 64),
+    # both merges of the fused step's last block (common maximum; running log-sum-exp above 512 records)
+    "g4_two_batches": (SMALL["g4_two_batches"][0], 4, 64),
+    "g16_lse_merge": (SMALL["g16_lse_merge"][0], 4, 64),
 }
 
 
