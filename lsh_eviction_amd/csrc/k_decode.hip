@@ -17,7 +17,8 @@
 //   ticket; the head's last block reads the winner from the eviction key
 //   (the global argmax with lowest-index ties is always its own chunk's
 //   candidate), adds back the held-out candidates of the other chunks and the
-//   new token, merges by log-sum-exp and writes the new token into the
+//   new token, merges the partials against one common maximum per head
+//   (a running log-sum-exp when there are very many) and writes the new token into the
 //   winner's slot.  The result equals "evict, write, then attend" with every
 //   K/V byte read once and no grid-wide barrier or L2-wide fence.
 //

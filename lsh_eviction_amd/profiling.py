@@ -29,13 +29,37 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and with runs of whitespace collapsed, so that
+    an edit of a comment does not count as a change of the kernel."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif text[i] in "\"'":
+            q, j = text[i], i + 1
+            while j < n and text[j] != q:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(text[i])
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
-    """Hash of the sources of the decode kernels; counter readings taken on other
-    sources are stale."""
+    """Hash of the code (comments and whitespace aside) of the decode kernels;
+    counter readings taken on other code are stale."""
     h = hashlib.sha256()
     for f in ("k_decode.hip", "hkv_device.h"):
-        with open(os.path.join(ROOT, "lsh_eviction_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "lsh_eviction_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -160,8 +184,8 @@ def write_traffic_md(args, rec):
     if args.alg_bytes:
         lines += ["", f"Algorithmic bytes per launch: {args.alg_bytes:,}; measured traffic is "
                   f"{rec['bytes_per_launch'] / args.alg_bytes:.3f}x that."]
-    lines += ["", f"Kernel source hash when measured: `{rec['kernel_hash']}` (bench.py reports this traffic only "
-              "while the source still has that hash)."]
+    lines += ["", f"Kernel source hash when measured (of the code with comments and whitespace set aside): "
+              f"`{rec['kernel_hash']}` (bench.py reports this traffic only while the code still has that hash)."]
     with open(args.md, "w") as fh:
         fh.write("\n".join(lines) + "\n")
 
