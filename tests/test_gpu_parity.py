@@ -32,6 +32,13 @@ SMALL = {
     "not_full": (C.LLAMA8B.scaled(prompt=700, budget=1000), 20, 0),
     "fill_then_evict": (C.LLAMA8B.scaled(prompt=990, budget=1000), 20, 0),
     "empty_prompt": (C.TINY.scaled(prompt=0, budget=8), 14, 64),
+    # group sizes that are not powers of two (padded MFMA columns, uneven records)
+    "g3_d128": (Shape("g3_d128", 14, batch=2, n_q_heads=6, n_kv_heads=2, head_dim=128, n_bits=32,
+                      kv_dtype="bf16", prompt=900, budget=500, steps=8, key_outliers=True), 8, 64),
+    "g6_d64": (Shape("g6_d64", 15, batch=1, n_q_heads=12, n_kv_heads=2, head_dim=64, n_bits=16,
+                     kv_dtype="bf16", prompt=700, budget=400, steps=8, key_outliers=False), 8, 0),
+    "g12_f32": (Shape("g12_f32", 16, batch=1, n_q_heads=12, n_kv_heads=1, head_dim=128, n_bits=64,
+                      kv_dtype="f32", prompt=600, budget=300, steps=6, key_outliers=False), 6, 64),
     # the fused step's last block merges up to 512 (split, head) records
     # against one common maximum per head, in one or more batches of splits,
     # and more records with a running log-sum-exp
@@ -66,6 +73,8 @@ QUERY_SMALL = {
     "d64_bf16_g2": (SMALL["d64_bf16_g2"][0], 4, 128),
     "not_full": (C.LLAMA8B.scaled(prompt=700, budget=1000), 4, 0),
     "empty_prompt": (C.TINY.scaled(prompt=0, budget=8), 4, 64),
+    "g3_d128": (SMALL["g3_d128"][0], 4, 64),
+    "g12_f32": (SMALL["g12_f32"][0], 3, 64),
 }
 
 
@@ -227,6 +236,7 @@ INT8_VALUES = {
     # both merges of the fused step's last block (common maximum; running log-sum-exp above 512 records)
     "g4_two_batches": (SMALL["g4_two_batches"][0], 4, 64),
     "g16_lse_merge": (SMALL["g16_lse_merge"][0], 4, 64),
+    "g6_d64": (SMALL["g6_d64"][0], 6, 0),
 }
 
 
