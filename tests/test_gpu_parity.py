@@ -39,6 +39,8 @@ SMALL = {
                      kv_dtype="bf16", prompt=700, budget=400, steps=8, key_outliers=False), 8, 0),
     "g12_f32": (Shape("g12_f32", 16, batch=1, n_q_heads=12, n_kv_heads=1, head_dim=128, n_bits=64,
                       kv_dtype="f32", prompt=600, budget=300, steps=6, key_outliers=False), 6, 64),
+    # many sequences of short, uneven budgets (KV-head-fastest grid numbering)
+    "many_sequences": (C.RAGGED.scaled(batch=40, prompt_range=(300, 900)), 6, 0),
     # the fused step's last block merges up to 512 (split, head) records
     # against one common maximum per head, in one or more batches of splits,
     # and more records with a running log-sum-exp
