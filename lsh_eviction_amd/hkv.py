@@ -103,6 +103,23 @@ def make_config(batch, n_q_heads, n_kv_heads, head_dim, n_bits, kv_dtype, budget
     return cfg
 
 
+def _require(t, name: str, shape, dtype, device: str = "cuda"):
+    """The boundary takes plain pointers, so a tensor of the wrong shape, type,
+    layout or device would be read out of bounds by a kernel: refuse it here
+    with a Python error instead."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(int(x) for x in shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.device.type != device:
+        raise ValueError(f"{name}: on {t.device}, expected a {device} tensor")
+
+
 def _ptr(t) -> Optional[int]:
     if t is None:
         return None
@@ -295,7 +312,19 @@ class Cache:
         HKV_PREFILL_CHUNK: Q [B][Hq][d] fp32 observation queries (may be None with
         reuse), reuse [B][Hkv][kept_len] int32 or None; returns the kept chunk
         lists [B][Hkv][kept_len] int32 (device)."""
-        self.n_max = int(K.shape[2])
+        import torch
+        kvt = kv_torch_dtype(self.kv_dtype)
+        n_max = int(K.shape[2]) if isinstance(K, torch.Tensor) and K.dim() == 4 else -1
+        _require(K, "K", (self.B, self.Hkv, n_max, self.d), kvt)
+        _require(V, "V", (self.B, self.Hkv, n_max, self.d), kvt)
+        self.n_max = n_max
+        if self.prefill_policy == HKV_PREFILL_QUERY:
+            _require(Q, "Q", (self.B, self.Hq, n_max, self.d), torch.float32)
+        elif self.prefill_policy == HKV_PREFILL_CHUNK:
+            if Q is not None:
+                _require(Q, "Q", (self.B, self.Hq, self.d), torch.float32)
+            if reuse is not None:
+                _require(reuse, "reuse", (self.B, self.Hkv, max(self.kept_len, 1)), torch.int32)
         if self.prefill_policy == HKV_PREFILL_CHUNK:
             import torch
             kept = torch.empty((self.B, self.Hkv, max(self.kept_len, 1)), dtype=torch.int32, device="cuda")
@@ -326,19 +355,38 @@ class Cache:
         hkv_tier_counts(self.h, cnt, stream)
         return cnt
 
-    def attend_tiered(self, q, out=None, stream=None):
+    def attend_tiered(self, q, out=None, stream=None, check=True):
         import torch
         if out is None:
             out = torch.empty((self.B, self.Hq, self.d), dtype=torch.float32, device="cuda")
+        if check:
+            _require(q, "q", (self.B, self.Hq, self.d), torch.float32)
+            _require(out, "out", (self.B, self.Hq, self.d), torch.float32)
         hkv_attend_tiered(self.h, q, out, stream)
         return out
 
-    def decode_step(self, q, k, v, out=None, evicted=None, stream=None):
+    def check_step_args(self, q, k, v, out, evicted):
+        """Raise unless q, k, v, out, evicted have the shapes, types and layout
+        hkv_decode_step reads and writes."""
+        import torch
+        kvt = kv_torch_dtype(self.kv_dtype)
+        _require(q, "q", (self.B, self.Hq, self.d), torch.float32)
+        _require(k, "k", (self.B, self.Hkv, self.d), kvt)
+        _require(v, "v", (self.B, self.Hkv, self.d), kvt)
+        _require(out, "out", (self.B, self.Hq, self.d), torch.float32)
+        _require(evicted, "evicted", (self.B, self.Hkv), torch.int32)
+
+    def decode_step(self, q, k, v, out=None, evicted=None, stream=None, check=True):
+        """One decode step.  check=False skips the argument checks (several
+        microseconds of host time per call): for loops over tensors already
+        passed through check_step_args."""
         import torch
         if out is None:
             out = torch.empty((self.B, self.Hq, self.d), dtype=torch.float32, device="cuda")
         if evicted is None:
             evicted = torch.empty((self.B, self.Hkv), dtype=torch.int32, device="cuda")
+        if check:
+            self.check_step_args(q, k, v, out, evicted)
         hkv_decode_step(self.h, q, k, v, out, evicted, stream)
         return out, evicted
 
@@ -363,6 +411,17 @@ class Cache:
         return out
 
     def set_state(self, s, stream=None):
+        import torch
+        kvt = kv_torch_dtype(self.kv_dtype)
+        rows = self.B * self.Hkv * self.Smax
+        _require(s["K"], "K", (self.B, self.Hkv, self.Smax, self.d), kvt)
+        if self.value_bits == 8:
+            _require(s["V"], "V", (rows * (self.d + 4),), torch.uint8)
+        else:
+            _require(s["V"], "V", (self.B, self.Hkv, self.Smax, self.d), kvt)
+        _require(s["codes"], "codes", (self.B, self.Hkv, self.Smax, self.W), torch.int32)
+        _require(s["tok"], "tok", (self.B, self.Hkv, self.Smax), torch.int32)
+        _require(s["state"], "state", (self.B, self.Hkv, 2), torch.int32)
         hkv_set_state(self.h, s["K"], s["V"], s["codes"], s["tok"], s["state"], stream)
 
     def last_codes(self, stream=None):

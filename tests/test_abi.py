@@ -196,3 +196,21 @@ def test_int8_values_shrink_the_workspace(hkv):
     v8 = hkv.hkv_workspace_bytes(_cfg(hkv, value_bits=8))
     # V: 8 heads x 4096 slots x 128 values go from 2 bytes to 1 byte (+ a 4-byte scale per slot)
     assert full - v8 >= 8 * 4096 * (128 - 4) - 4096
+
+
+def test_binding_refuses_tensors_a_kernel_would_misread():
+    # the C ABI sees plain pointers; the binding checks what it hands over
+    import torch
+    from lsh_eviction_amd.hkv import _require
+    ok = torch.zeros(2, 4, 8)
+    _require(ok, "q", (2, 4, 8), torch.float32, device="cpu")
+    with pytest.raises(ValueError, match="shape"):
+        _require(ok, "q", (2, 4, 16), torch.float32, device="cpu")
+    with pytest.raises(TypeError, match="dtype"):
+        _require(ok.to(torch.bfloat16), "q", (2, 4, 8), torch.float32, device="cpu")
+    with pytest.raises(ValueError, match="contiguous"):
+        _require(torch.zeros(2, 8, 4).transpose(1, 2), "q", (2, 4, 8), torch.float32, device="cpu")
+    with pytest.raises(ValueError, match="cuda"):
+        _require(ok, "q", (2, 4, 8), torch.float32)
+    with pytest.raises(TypeError, match="torch.Tensor"):
+        _require(ok.numpy(), "q", (2, 4, 8), torch.float32)
