@@ -170,7 +170,11 @@ __global__ __launch_bounds__(256) void k_project_mfma(DevCache c, const KT* __re
             unsigned long long cde = 0;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                const unsigned long long m = r == 0 ? mk[nt][0] : r == 1 ? mk[nt][1] : r == 2 ? mk[nt][2] : mk[nt][3];
+                // the lane's ballot by masks (a select chain over the four
+                // became a private array indexed at run time, i.e. scratch)
+                unsigned long long m = 0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) m |= mk[nt][q] & (0ull - (unsigned long long)(r == q));
                 cde |= ((m >> (16 * a)) & 0xFFFFull) << (16 * nt);
             }
             const int t = t0 + wave * 16 + lane;
