@@ -890,10 +890,6 @@ constexpr int ring_depth()
 // other; agent-scope atomic loads and stores (the sc1 cache policy) write
 // through and re-fetch past them, so the data never sits stale in a writer's
 // or a reader's L2, and no L2-wide writeback fence is needed.
-__device__ __forceinline__ unsigned long long ld_dev(const unsigned long long* p)
-{
-    return __hip_atomic_load(const_cast<unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // Every memory operation this thread issued has completed -- its write-through
 // stores have reached the coherence point -- before anything after it is
@@ -982,7 +978,7 @@ struct MergeArgs {
     __amdgpu_buffer_rsrc_t rec, scal, cv;
     int G, nsb, r, c4;
     bool full;
-    unsigned long long wkey;
+    unsigned wkey0;   // low half of the head's eviction key (its slot), valid in lane 0 of each wave
     int chunk;
 };
 
@@ -1016,7 +1012,7 @@ __device__ __forceinline__ int merge_splits(const MergeArgs& a, int e, float4* s
             }
         }
         if (a.full) {
-            e = cand_slot(a.wkey);
+            e = cand_slot(__builtin_amdgcn_readlane(a.wkey0, 0));
             js = e / a.chunk;
         }
         __syncthreads();   // readers of the previous batch are done
@@ -1088,9 +1084,10 @@ __device__ __forceinline__ int merge_scaled(const MergeArgs& a, int e, const flo
         }
     };
     issue(0);
+    __builtin_amdgcn_sched_barrier(0);   // the key is read after the record loads are issued
     int js = -1;
     if (a.full) {
-        e = cand_slot(a.wkey);
+        e = cand_slot(__builtin_amdgcn_readlane(a.wkey0, 0));
         js = e / a.chunk;
     }
     if (tid < nrec) mg.sc[tid] = scv;
@@ -1366,11 +1363,18 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     constexpr int RS = kThreads / TPR;
     constexpr int JBMAX = GM <= 4 ? 4 : (GM <= 8 ? 2 : 1);   // register budget
     const int c4 = tid % TPR, r = tid / TPR;
-    const unsigned long long wkey = ld_dev(&c.ekey[2 * head + (t & 1)]);
+    // The winner's slot is the low half of the eviction key.  One lane per
+    // wave loads it: a load by all lanes of this uniform address becomes a
+    // scalar at once, and its wait would hold back the record loads issued
+    // after it; the merge reads it (readlane) once those are on their way.
+    unsigned wkey0 = 0u;
+    if (lane == 0)
+        wkey0 = __hip_atomic_load(reinterpret_cast<unsigned*>(&c.ekey[2 * head + (t & 1)]), __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
     const size_t hrec = (size_t)head * c.nsplit;
     MergeArgs ma{dev_rsrc(c.frec + hrec * G * D, (size_t)c.nsplit * G * D * 4),
                  dev_rsrc(c.fscal + hrec * G * 4, (size_t)c.nsplit * G * 16),
-                 dev_rsrc(c.cand_v + hrec * D, (size_t)c.nsplit * D * 4), G, nsb, r, c4, full, wkey, c.chunk};
+                 dev_rsrc(c.cand_v + hrec * D, (size_t)c.nsplit * D * 4), G, nsb, r, c4, full, wkey0, c.chunk};
     const int per = (nsb + RS - 1) / RS;   // splits per thread
     MergeBlockSmem<D, GM>& mg = u.mg;
     static_assert(TPR == 16 || TPR == 32, "rows per wave");
