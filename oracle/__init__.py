@@ -244,6 +244,14 @@ class OracleHead:
         lib().orc_get_value_codes(self._h, _p(q), _p(sc))
         return q, sc
 
+    def set_value_codes(self, q: np.ndarray, scale: np.ndarray):
+        """Import int8 codes [budget][d] and fp32 scales [budget] of an int8-value
+        cache; the held values become code * scale."""
+        S = max(self.budget, 0)
+        q = np.ascontiguousarray(q, np.int8).reshape(S, self.d)
+        sc = np.ascontiguousarray(scale, np.float32).reshape(S)
+        lib().orc_set_value_codes(self._h, _p(q), _p(sc))
+
     def state(self) -> dict:
         S = max(self.budget, 0)
         K = np.zeros((S, self.d)); V = np.zeros((S, self.d))
@@ -278,12 +286,27 @@ class OracleCache:
     Query head hq belongs to KV head hq // G (contiguous groups)."""
 
     def __init__(self, R, budgets, n_q_heads: int, n_kv_heads: int, heads=None, value_bits: int = 0,
-                 tier: int = -1):
+                 tier: int = -1, workers: int = 1):
         self.B = len(budgets)
         self.Hq, self.Hkv = int(n_q_heads), int(n_kv_heads)
         self.G = self.Hq // self.Hkv
         self.sel = heads if heads is not None else [(b, h) for b in range(self.B) for h in range(self.Hkv)]
         self.heads = {(b, h): OracleHead(R, int(budgets[b]), self.G, value_bits, tier) for (b, h) in self.sel}
+        # Heads are independent eviction domains and the C oracle keeps no
+        # global state, so with workers > 1 the calls of different heads run in
+        # host threads side by side (each head's own work stays one plain,
+        # single-threaded C call; ctypes releases the interpreter lock).
+        self.workers = max(1, int(workers))
+
+    def map_heads(self, fn):
+        """{(b, h): fn((b, h), head)} over the selected heads, in threads when workers > 1."""
+        items = list(self.heads.items())
+        if self.workers == 1 or len(items) == 1:
+            return {key: fn(key, o) for key, o in items}
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=min(self.workers, len(items))) as ex:
+            outs = list(ex.map(lambda kv: fn(kv[0], kv[1]), items))
+        return {key: r for (key, _), r in zip(items, outs)}
 
     def prefill(self, K, V, prompt_lens, policy=STREAM, inj_codes=None, Q=None, inj_qcodes=None,
                 chunk=DEFAULT_CHUNK_TOKENS, reuse=None):
@@ -292,36 +315,41 @@ class OracleCache:
         observation queries, inj_qcodes [B][Hq][W] and reuse [B][Hkv][k] kept lists.
         Under CHUNK returns the kept lists {(b, h): [ceil(S_b / chunk)] int32}."""
         G = self.G
-        kept = {}
-        for (b, h), o in self.heads.items():
+
+        def one(key, o):
+            b, h = key
             n = int(prompt_lens[b])
             inj = None if inj_codes is None else inj_codes[b, h, :n]
             if policy == CHUNK:
                 q = None if Q is None else widen(Q[b, h * G:(h + 1) * G])
                 iq = None if inj_qcodes is None else inj_qcodes[b, h * G:(h + 1) * G]
                 ru = None if reuse is None else reuse[b, h]
-                kept[(b, h)] = o.prefill_chunks(widen(K[b, h, :n]), widen(V[b, h, :n]), q, chunk, inj, iq, ru)
-            elif policy == QUERY:
+                return o.prefill_chunks(widen(K[b, h, :n]), widen(V[b, h, :n]), q, chunk, inj, iq, ru)
+            if policy == QUERY:
                 q = widen(Q[b, h * G:(h + 1) * G, :n]).transpose(1, 0, 2)
                 iq = None if inj_qcodes is None else np.ascontiguousarray(
                     inj_qcodes[b, h * G:(h + 1) * G, :n].transpose(1, 0, 2))
                 o.prefill_query(widen(K[b, h, :n]), widen(V[b, h, :n]), q, inj, iq)
             else:
                 o.prefill(widen(K[b, h, :n]), widen(V[b, h, :n]), policy, inj)
+            return None
+
+        kept = self.map_heads(one)
         return kept if policy == CHUNK else None
 
     def attend_tiered(self, q):
         """q [B][Hq][d]; attention over cache and host tier per head, keyed (b, h)."""
         G = self.G
-        return {(b, h): o.attend_tiered(widen(q[b, h * G:(h + 1) * G])) for (b, h), o in self.heads.items()}
+        return self.map_heads(lambda key, o: o.attend_tiered(widen(q[key[0], key[1] * G:(key[1] + 1) * G])))
 
     def decode_step(self, q, k, v, inj_qcodes=None, inj_kcodes=None):
         """q [B][Hq][d] fp32; k, v [B][Hkv][d]; returns per-head dicts keyed (b, h)."""
-        res = {}
         G = self.G
-        for (b, h), o in self.heads.items():
+
+        def one(key, o):
+            b, h = key
             iq = None if inj_qcodes is None else inj_qcodes[b, h * G:(h + 1) * G]
             ik = None if inj_kcodes is None else inj_kcodes[b, h]
-            res[(b, h)] = o.decode_step(widen(q[b, h * G:(h + 1) * G]), widen(k[b, h]),
-                                        widen(v[b, h]), iq, ik)
-        return res
+            return o.decode_step(widen(q[b, h * G:(h + 1) * G]), widen(k[b, h]), widen(v[b, h]), iq, ik)
+
+        return self.map_heads(one)

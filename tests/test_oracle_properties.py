@@ -206,3 +206,30 @@ def test_snapshot_restore(oracle_mod):
         assert ra["evicted"] == rc["evicted"]
         np.testing.assert_array_equal(ra["out"], rc["out"])
     np.testing.assert_array_equal(a.state()["tok"], c.state()["tok"])
+
+
+def test_threaded_heads_equal_sequential(oracle_mod):
+    """Driving independent heads from several host threads gives exactly the
+    results of driving them one after another."""
+    rng = np.random.default_rng(9)
+    B, Hq, Hkv, d, b, N = 2, 8, 4, 32, 32, 60
+    R = rng.standard_normal((d, b)).astype(np.float32)
+    budgets = np.array([20, 33], np.int32)
+    K = rng.standard_normal((B, Hkv, N, d)).astype(np.float32)
+    V = rng.standard_normal((B, Hkv, N, d)).astype(np.float32)
+    lens = np.array([N, 45], np.int32)
+    caches = [oracle_mod.OracleCache(R, budgets, Hq, Hkv, workers=w) for w in (1, 4)]
+    for c in caches:
+        c.prefill(K, V, lens, oracle_mod.STREAM)
+    for _ in range(8):
+        q = rng.standard_normal((B, Hq, d)).astype(np.float32)
+        k = rng.standard_normal((B, Hkv, d)).astype(np.float32)
+        v = rng.standard_normal((B, Hkv, d)).astype(np.float32)
+        r1, r4 = (c.decode_step(q, k, v) for c in caches)
+        assert list(r1) == list(r4)
+        for key in r1:
+            assert r1[key]["evicted"] == r4[key]["evicted"]
+            np.testing.assert_array_equal(r1[key]["out"], r4[key]["out"])
+    for key in caches[0].heads:
+        s1, s4 = caches[0].heads[key].state(), caches[1].heads[key].state()
+        np.testing.assert_array_equal(s1["tok"], s4["tok"])

@@ -79,3 +79,35 @@ def test_eviction_does_not_depend_on_value_storage(oracle_mod):
         q = rng.standard_normal((G, d)); k = rng.standard_normal(d); v = rng.standard_normal(d)
         assert a.decode_step(q, k, v)["evicted"] == c.decode_step(q, k, v)["evicted"]
     assert list(a.state()["tok"]) == list(c.state()["tok"])
+
+
+def test_int8_snapshot_restore(oracle_mod):
+    """A checkpoint of an int8-value cache (state plus value codes and scales)
+    restored into a fresh cache continues identically; the import makes the
+    held values code * scale."""
+    rng = np.random.default_rng(44)
+    d, b, S, N, G = 32, 16, 14, 40, 2
+    R = rng.standard_normal((d, b))
+    a = oracle_mod.OracleHead(R, S, G, value_bits=8)
+    a.prefill(rng.standard_normal((N, d)), rng.standard_normal((N, d)).astype(np.float32))
+    qs = rng.standard_normal((16, G, d)); ks = rng.standard_normal((16, d))
+    vs = rng.standard_normal((16, d)).astype(np.float32)
+    for i in range(6):
+        a.decode_step(qs[i], ks[i], vs[i])
+    snap = a.state()
+    codes, scales = a.value_codes()
+    c = oracle_mod.OracleHead(R, S, G, value_bits=8)
+    c.set_state(dict(snap, V=np.zeros_like(snap["V"])))   # values come from the codes alone
+    c.set_value_codes(codes, scales)
+    held = codes.astype(np.float64) * scales[:, None].astype(np.float64)
+    np.testing.assert_array_equal(c.state()["V"], held)
+    np.testing.assert_array_equal(c.state()["V"], snap["V"])
+    for i in range(6, 16):
+        ra = a.decode_step(qs[i], ks[i], vs[i])
+        rc = c.decode_step(qs[i], ks[i], vs[i])
+        assert ra["evicted"] == rc["evicted"]
+        np.testing.assert_array_equal(ra["out"], rc["out"])
+    ca, sa = a.value_codes()
+    cc, sc = c.value_codes()
+    np.testing.assert_array_equal(ca, cc)
+    np.testing.assert_array_equal(sa.view(np.uint32), sc.view(np.uint32))
