@@ -64,7 +64,8 @@
  *     n_q_heads % n_kv_heads == 0 with G = n_q_heads / n_kv_heads <= 16;
  *     kv dtype fp32 or bf16; 1 <= budget <= 2^22 per sequence (a prefill
  *     with HKV_PREFILL_STREAM or HKV_PREFILL_QUERY needs
- *     budget * ceil(b/8) <= 128 KiB, its code table lives in on-chip LDS);
+ *     budget * ceil(b/8) <= 128 KiB: one workgroup holds the head's code
+ *     table in its registers);
  *     1 <= batch <= 4096; 1 <= prefill chunk <= 32 tokens.
  */
 #ifndef HKV_H
@@ -250,8 +251,11 @@ const char* hkv_last_error(const hkv_cache* c);
 hkv_status hkv_get_state(const hkv_cache* c, void* K, void* V, uint32_t* codes,
                          int32_t* slot_token, int32_t* head_state, void* stream);
 /* Checkpoint import, same layouts; all five buffers required.  Marks the
- * cache as prefilled.  A host tier is not part of the checkpoint: its
- * buffers are the caller's, and its counts are left as they are. */
+ * cache as prefilled.  head_state is read back first (the call synchronises
+ * `stream` once): HKV_ERR_INVALID_ARG, with nothing enqueued, unless every
+ * head has 0 <= occupancy <= its budget and occupancy <= next position.  A
+ * host tier is not part of the checkpoint: its buffers are the caller's, and
+ * its counts are left as they are. */
 hkv_status hkv_set_state(hkv_cache* c, const void* K, const void* V, const uint32_t* codes,
                          const int32_t* slot_token, const int32_t* head_state, void* stream);
 

@@ -377,7 +377,23 @@ extern "C" hkv_status hkv_set_state(hkv_cache* c, const void* K, const void* V, 
     hipStream_t st = (hipStream_t)stream;
     const size_t heads = (size_t)L.B * L.Hkv;
     const size_t kv = heads * L.Smax * L.d * L.es;
-    hipError_t e = hipMemcpyAsync(c->dev.K, K, kv, hipMemcpyDeviceToDevice, st);
+    // The occupancy and position of every head decide which slots the kernels
+    // read and write, so they are checked on the host before anything is
+    // enqueued: 0 <= occupancy <= budget and occupancy <= position.
+    std::vector<int32_t> hs(heads * 2);
+    hipError_t e = hipMemcpyAsync(hs.data(), head_state, heads * 8, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return check_launch(c, e, st, "hkv_set_state");
+    for (size_t i = 0; i < heads; ++i) {
+        const int32_t n = hs[2 * i], t = hs[2 * i + 1], S = c->budgets[i / L.Hkv];
+        if (n < 0 || n > S || t < n) {
+            char msg[160];
+            snprintf(msg, sizeof(msg), "hkv_set_state: head_state of sequence %zu, KV head %zu is (%d, %d); needs "
+                     "0 <= occupancy <= budget %d and occupancy <= position", i / L.Hkv, i % L.Hkv, n, t, S);
+            return fail(c, HKV_ERR_INVALID_ARG, msg);
+        }
+    }
+    e = hipMemcpyAsync(c->dev.K, K, kv, hipMemcpyDeviceToDevice, st);
     if (e == hipSuccess) e = hipMemcpyAsync(c->dev.V, V, L.v_bytes, hipMemcpyDeviceToDevice, st);
     if (e == hipSuccess && L.value_bits == 8)
         e = hipMemcpyAsync(c->dev.vs, (const char*)V + L.v_bytes, heads * L.Smax * 4, hipMemcpyDeviceToDevice, st);

@@ -12,6 +12,8 @@ Rules (the readings are the same on both sides):
 """
 from __future__ import annotations
 
+import json
+import os
 import sys
 import time
 from typing import Iterable, Optional, Sequence, Tuple
@@ -43,7 +45,7 @@ def check_codes(gpu: np.ndarray, ref: np.ndarray, flags: np.ndarray, what: str) 
         idx = np.argwhere(bad)[:5]
         raise AssertionError(f"{what}: {int(np.count_nonzero(bad))} unflagged code words differ, "
                              f"first at {idx.tolist()}")
-    return int(sum(bin(int(x)).count("1") for x in diff.ravel() if x))
+    return int(np.unpackbits(np.ascontiguousarray(diff).view(np.uint8)).sum())
 
 
 def rel_err_rows(out: np.ndarray, ref: np.ndarray) -> float:
@@ -62,7 +64,7 @@ def run_case(shape: Shape, steps: int, schedule: int = 0, policy: int = 0, chunk
              heads: Optional[Sequence[Tuple[int, int]]] = None, seed: Optional[int] = None,
              check_every: int = 1, stats: Optional[dict] = None, value_bits: int = 0,
              prefill_chunk: int = 0, reuse: Optional[np.ndarray] = None, observe: bool = True,
-             tier: int = 0):
+             tier: int = 0, workers: int = 8, label: Optional[str] = None):
     """Prefill + `steps` decode steps on the GPU, replayed on the oracle for `heads`
     (all heads if None).  Raises AssertionError on any parity failure.
 
@@ -70,6 +72,11 @@ def run_case(shape: Shape, steps: int, schedule: int = 0, policy: int = 0, chunk
     (their codes are checked and injected), `reuse` [B][Hkv][k] is passed as
     the kept list, and the GPU's kept lists are compared with the oracle's and
     returned in stats["kept"].
+
+    The oracle drives up to `workers` heads at once from host threads.  When the
+    environment names a file in HKV_PARITY_LOG, one JSON line per case is
+    appended to it: worst attention error, flagged bits that differed, steps and
+    heads compared.
 
     With tier > 0 a host tier of that capacity (pinned host memory) is attached
     before the prefill; its counts, token positions and rows are compared with
@@ -116,21 +123,26 @@ def run_case(shape: Shape, steps: int, schedule: int = 0, policy: int = 0, chunk
     del Kt, Vt, Qt
 
     sel = list(heads) if heads is not None else [(b, h) for b in range(B) for h in range(Hkv)]
-    orc = oracle.OracleCache(P.R, P.budgets, Hq, Hkv, heads=sel, value_bits=value_bits, tier=tier if tier else -1)
-    flagged = 0
-    for (b, h) in sel:
+    orc = oracle.OracleCache(P.R, P.budgets, Hq, Hkv, heads=sel, value_bits=value_bits, tier=tier if tier else -1,
+                             workers=workers)
+
+    def prefill_codes_ok(key, o):
+        b, h = key
         n = int(P.prompt_lens[b])
         if n == 0:
-            continue
-        codes_o, flags_o = orc.heads[(b, h)].encode(oracle.widen(P.K[b, h, :n]))
-        flagged += check_codes(pcodes[b, h, :n], codes_o, flags_o, f"prefill codes b={b} h={h}")
+            return 0
+        codes_o, flags_o = o.encode(oracle.widen(P.K[b, h, :n]))
+        fl = check_codes(pcodes[b, h, :n], codes_o, flags_o, f"prefill codes b={b} h={h}")
         if query:
             for g in range(G):
-                qo, qf = orc.heads[(b, h)].encode(oracle.widen(Qp[b, h * G + g, :n]))
-                flagged += check_codes(qpcodes[b, h * G + g, :n], qo, qf, f"prefill query codes b={b} hq={h * G + g}")
+                qo, qf = o.encode(oracle.widen(Qp[b, h * G + g, :n]))
+                fl += check_codes(qpcodes[b, h * G + g, :n], qo, qf, f"prefill query codes b={b} hq={h * G + g}")
         if chunked and Qp is not None:
-            qo, qf = orc.heads[(b, h)].encode(oracle.widen(Qp[b, h * G:(h + 1) * G]))
-            flagged += check_codes(qpcodes[b, h * G:(h + 1) * G], qo, qf, f"observation codes b={b} h={h}")
+            qo, qf = o.encode(oracle.widen(Qp[b, h * G:(h + 1) * G]))
+            fl += check_codes(qpcodes[b, h * G:(h + 1) * G], qo, qf, f"observation codes b={b} h={h}")
+        return fl
+
+    flagged = sum(orc.map_heads(prefill_codes_ok).values())
     # replay the oracle's prefill with the GPU codes
     kept_o = orc.prefill(P.K, P.V, P.prompt_lens, policy, inj_codes=pcodes, Q=Qp, inj_qcodes=qpcodes,
                          chunk=cache.prefill_chunk or oracle.DEFAULT_CHUNK_TOKENS, reuse=reuse)
@@ -151,6 +163,8 @@ def run_case(shape: Shape, steps: int, schedule: int = 0, policy: int = 0, chunk
         log(f"  prefill tier ok, tiered attention rel err {tworst:.2e}, {time.time()-t0:.1f}s")
 
     worst = 0.0
+    dflagged = 0
+    states_compared = 0
     for s in range(steps):
         q = hkv.to_device(Dd.q[s]); k = hkv.to_device(Dd.k[s]); v = hkv.to_device(Dd.v[s])
         out, ev = cache.decode_step(q, k, v)
@@ -161,14 +175,15 @@ def run_case(shape: Shape, steps: int, schedule: int = 0, policy: int = 0, chunk
         for (b, h), r in res.items():
             qo, qf = orc.heads[(b, h)].encode(oracle.widen(Dd.q[s, b, h * G:(h + 1) * G]))
             ko, kf = orc.heads[(b, h)].encode(oracle.widen(Dd.k[s, b, h]))
-            check_codes(qc[b, h * G:(h + 1) * G], qo, qf, f"step {s} qcodes b={b} h={h}")
-            check_codes(kc[b, h], ko, kf, f"step {s} kcode b={b} h={h}")
+            dflagged += check_codes(qc[b, h * G:(h + 1) * G], qo, qf, f"step {s} qcodes b={b} h={h}")
+            dflagged += check_codes(kc[b, h], ko, kf, f"step {s} kcode b={b} h={h}")
             assert ev[b, h] == r["evicted"], f"step {s} b={b} h={h}: evicted {ev[b, h]} != {r['evicted']}"
             err = rel_err_rows(out[b, h * G:(h + 1) * G].astype(np.float64), r["out"])
             worst = max(worst, err)
             assert err <= ATTN_TOL, f"step {s} b={b} h={h}: attention rel err {err:.3e} > {ATTN_TOL}"
         if check_every and (s + 1) % check_every == 0 or s == steps - 1:
             compare_state(cache, orc, sel, shape, f"after step {s}")
+            states_compared += 1
             if tier:
                 compare_tier(cache, orc, sel, shape, f"after step {s}")
         if tier:
@@ -177,6 +192,16 @@ def run_case(shape: Shape, steps: int, schedule: int = 0, policy: int = 0, chunk
         + (f", tiered {tworst:.2e}" if tier else "") + f", {time.time()-t0:.1f}s")
     if stats is not None:
         stats.update(worst=worst, flagged=flagged, tiered_worst=tworst)
+    logp = os.environ.get("HKV_PARITY_LOG")
+    if logp:
+        rec = {"case": label or shape.name, "workload": shape.name, "schedule": "split" if schedule else "fused",
+               "policy": policy, "value_bits": value_bits, "tier": tier, "chunk": cache.chunk,
+               "heads": len(sel), "decode_steps": steps, "states_compared": states_compared + 1,
+               "worst_attention_rel_err": worst, "tiered_worst": tworst,
+               "prefill_flagged_bits_differing": flagged, "decode_flagged_bits_differing": dflagged,
+               "seconds": round(time.time() - t0, 1)}
+        with open(logp, "a") as fh:
+            fh.write(json.dumps(rec) + "\n")
     cache.close()
     return worst
 

@@ -1,8 +1,10 @@
 """GPU parity of the HIP path (through the C ABI) against the fp64 CPU oracle.
 
-Small shapes are checked on every head and every step; the full workload
-shapes are checked in the launch configuration the benchmark times, on
-sampled (sequence, KV head) pairs the oracle replays one by one.
+Small shapes are checked on every head and every step.  The full workload
+shapes run in the launch configuration the benchmark times, over their whole
+decode sequences: on every KV head of the single-sequence workloads, and on
+many (sequence, KV head) pairs of the batched ones, which the oracle replays
+head by head.
 """
 import numpy as np
 import pytest
@@ -386,16 +388,69 @@ def test_maximum_budget():
              check_every=0)
 
 
+def _ragged_pairs():
+    """(sequence, KV head) pairs of the ragged batch: every head of the sequence
+    with the smallest budget and of the one with the largest, and one head of
+    every fourth other sequence."""
+    from lsh_eviction_amd import datagen
+    _, budgets = datagen.lengths(C.RAGGED)
+    lo, hi = int(np.argmin(budgets)), int(np.argmax(budgets))
+    pairs = [(lo, h) for h in range(8)] + [(hi, h) for h in range(8)]
+    pairs += [(b, b % 8) for b in range(1, C.RAGGED.batch, 4) if b not in (lo, hi)]
+    return pairs
+
+
+# (shape, decode steps, heads (None: all), state compared every n steps, schedule)
 FULL = {
-    "llama3_8b_layer": (C.LLAMA8B, 6, None),
-    "long_128k": (C.LONG128K, 3, [(0, 0), (0, 5)]),
-    "ragged_b32": (C.RAGGED, 3, [(0, 0), (13, 3), (31, 7)]),
-    "llama3_70b_layer": (C.LLAMA70B, 3, [(0, 0), (5, 6)]),
+    "llama3_8b_layer": (C.LLAMA8B, 256, None, 16, FUSED),
+    "long_128k": (C.LONG128K, 128, None, 16, FUSED),
+    "ragged_b32": (C.RAGGED, 64, "ragged", 16, FUSED),
+    "llama3_70b_layer": (C.LLAMA70B, 128, [(0, h) for h in range(8)] + [(b, b) for b in range(1, 8)], 16, FUSED),
+    # the five-launch schedule at full size
+    "llama3_8b_layer_split": (C.LLAMA8B, 64, None, 16, SPLIT),
+    "long_128k_split": (C.LONG128K, 16, [(0, 2), (0, 7)], 8, SPLIT),
 }
 
 
 @pytest.mark.parametrize("name", list(FULL))
-def test_full_size_sampled(name):
+def test_full_size_whole_decode(name):
+    """Each workload at its full size, in the launch configuration the benchmark
+    times, over its whole decode sequence: every decode step's codes, evicted
+    slots and attention are compared, and the whole cache state (slot -> token
+    map, code table, K/V rows, occupancy and position) every few steps."""
     from hkv_harness import run_case
-    shape, steps, heads = FULL[name]
-    run_case(shape, steps, schedule=FUSED, policy=STREAM, heads=heads, check_every=0)
+    shape, steps, heads, every, schedule = FULL[name]
+    if heads == "ragged":
+        heads = _ragged_pairs()
+    run_case(shape, steps, schedule=schedule, policy=STREAM, heads=heads, check_every=every, workers=16,
+             label=name)
+
+
+def test_set_state_rejects_bad_head_state():
+    """A checkpoint whose occupancy or position would send the kernels outside
+    the head's slots is refused before anything is enqueued, and the cache keeps
+    working from its previous state."""
+    import torch
+    from lsh_eviction_amd import datagen, hkv
+    shape = C.LLAMA8B.scaled(batch=2, prompt=900, budget=400)
+    wl = datagen.workload(shape, steps=2)
+    P, D = wl["prompt"], wl["decode"]
+    c = hkv.Cache(2, 32, 8, 128, 32, hkv.HKV_BF16, P.budgets, P.R, max_prompt=P.n_max)
+    c.prefill(hkv.to_device(P.K), hkv.to_device(P.V), P.prompt_lens)
+    good = {k: v.clone() for k, v in c.get_state().items()}
+    torch.cuda.synchronize()
+    for (b, h, n, t) in [(0, 0, -1, 900), (1, 3, 401, 900), (1, 7, 400, 399)]:
+        bad = {k: v.clone() for k, v in good.items()}
+        bad["state"][b, h, 0] = n
+        bad["state"][b, h, 1] = t
+        with pytest.raises(hkv.HkvError) as e:
+            c.set_state(bad)
+        assert e.value.status == hkv.HKV_ERR_INVALID_ARG
+        assert "head_state" in str(e.value)
+    after = c.get_state()
+    for k in good:
+        assert torch.equal(after[k], good[k]), k
+    out, ev = c.decode_step(hkv.to_device(D.q[0]), hkv.to_device(D.k[0]), hkv.to_device(D.v[0]))
+    torch.cuda.synchronize()
+    c.set_state(good)          # a valid checkpoint is still taken
+    c.close()
