@@ -26,6 +26,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, AMD public spec
 MALL_BYTES = 256 << 20
+HOLD_CYCLES = 1_000_000     # spin of torch.cuda._sleep before a timed region (well under 1 ms)
 DEFAULT_WORKLOAD = "long_128k"
 
 
@@ -100,11 +101,24 @@ def copy_bandwidth(mib: int = 1024, reps: int = 10) -> float:
     return gbs
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (as lscpu reports it), from /proc/cpuinfo."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(shape, budget_s: float = 15.0):
     """The oracle's decode step timed on one host core on a bounded sample: the
     first sequence of the workload with all its KV heads, its cache filled with
     the first `budget` prompt tokens (the same slot count the GPU cache holds;
-    the time of a decode step does not depend on which tokens the slots hold)."""
+    the time of a decode step does not depend on which tokens the slots hold).
+    The timing thread is pinned to one core of the process's CPU set for the
+    timed loop (the oracle itself is single-threaded), then unpinned."""
     import oracle
     from lsh_eviction_amd import datagen
     oracle.lib()
@@ -115,20 +129,27 @@ def cpu_baseline(shape, budget_s: float = 15.0):
     D = datagen.decode(one, steps=256, key_scale=P.key_scale if one.key_outliers else None)
     orc = oracle.OracleCache(P.R, P.budgets, one.n_q_heads, one.n_kv_heads)
     orc.prefill(P.K, P.V, P.prompt_lens, oracle.TRUNCATE)
-    t0 = time.perf_counter()
-    steps = 0
-    while steps < 256:
-        orc.decode_step(D.q[steps], D.k[steps], D.v[steps])
-        steps += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
+    allowed = sorted(os.sched_getaffinity(0))
+    core = allowed[-1]
+    os.sched_setaffinity(0, {core})   # pid 0: this (the calling) thread
+    try:
+        t0 = time.perf_counter()
+        steps = 0
+        while steps < 256:
+            orc.decode_step(D.q[steps], D.k[steps], D.v[steps])
+            steps += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+    finally:
+        os.sched_setaffinity(0, set(allowed))
     per_seq_step = dt / steps
     rate = 1.0 / (per_seq_step * shape.batch)   # a workload step covers `batch` sequences
     return {"value": round(rate, 4), "unit": "decode steps/s", "cores": 1, "kind": "oracle",
+            "pinned_core": core, "nproc": os.cpu_count(), "cpus_allowed": len(allowed), "cpu_model": cpu_model(),
             "sample": f"1 sequence x {one.n_kv_heads} KV heads x {S1} slots (G={one.group}, d={one.head_dim}), "
-                      f"{steps} decode steps in {dt:.1f} s on one thread, scaled to {shape.batch} "
-                      f"sequence(s) per workload step"}
+                      f"{steps} decode steps in {dt:.1f} s on one thread pinned to core {core}, scaled to "
+                      f"{shape.batch} sequence(s) per workload step"}
 
 
 def host_link_bandwidth(mib: int = 512, reps: int = 5) -> float:
@@ -250,6 +271,9 @@ def main():
     ap.add_argument("--tier", action="store_true",
                     help="tiered decode: evictions kept in a pinned host tier, attention over both tiers")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--only-timed", action="store_true",
+                    help="launch only the warm-up and timed steps (no 50-step blocks, no warm single-cache run): "
+                         "for counter runs")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -352,6 +376,10 @@ def main():
     K_ = args.steps
     t_wall = time.perf_counter()
     e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # A bounded spin kernel ahead of the start event holds the stream while the
+    # host enqueues the timed launches, so the region measures the GPU's steps
+    # back to back and not the host's first launch latency.
+    torch.cuda._sleep(HOLD_CYCLES)
     if graph is not None:
         reps = max(1, K_ // L)
         K_ = reps * L
@@ -375,7 +403,7 @@ def main():
         kern_ms = total_ms / K_
     # spread: the same steps in blocks of 50, each block bracketed by events
     blocks = []
-    for j in range(0, min(K_, 1000) - 49, 50):
+    for j in range(0, 0 if args.only_timed else min(K_, 1000) - 49, 50):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         for i in range(j, j + 50):
@@ -384,14 +412,14 @@ def main():
         blocks.append((a, b))
     # warm: one layer cache only, so the step's bytes may stay in the 256 MB MALL
     w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    KW = min(K_, 500)
+    KW = 0 if args.only_timed else min(K_, 500)
     w0.record(stream)
     for i in range(KW):
         caches[0].decode_step(qs[i % POOL], ks[i % POOL], vs[i % POOL], outs[0], evs[0], stream, check=False)
     w1.record(stream)
     torch.cuda.synchronize()
     block_us = sorted(a.elapsed_time(b) * 1e3 / 50 for a, b in blocks)
-    warm_us = w0.elapsed_time(w1) * 1e3 / KW
+    warm_us = w0.elapsed_time(w1) * 1e3 / KW if KW else None
     wall = time.perf_counter() - t_wall
     copy_gbs = copy_bandwidth()
 
@@ -410,7 +438,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": shape.kv_dtype if args.value_bits == 0 else shape.kv_dtype + "+i8",
         "data": "synthetic",
         "config": {"workload": shape.name, "batch": shape.batch, "n_q_heads": shape.n_q_heads,
                    "n_kv_heads": shape.n_kv_heads, "head_dim": shape.head_dim, "n_bits": shape.n_bits,
@@ -424,7 +452,7 @@ def main():
         "kernel": "k_decode_fused" if args.schedule == "fused" else "all kernels of the split step",
         "hbm_frac_of_step": round(per_step / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "us_per_step_median_of_50_step_blocks": round(float(np.median(block_us)), 3) if block_us else None,
-        "warm_us_per_step_one_cache": round(warm_us, 3),
+        "warm_us_per_step_one_cache": round(warm_us, 3) if warm_us else None,
         "copy_gbs": round(copy_gbs, 1),
         "frac_of_copy": round(achieved / copy_gbs, 4),
         "prefill_ms_per_layer": round(float(np.mean(prefill_ms)), 2),

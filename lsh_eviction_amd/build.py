@@ -28,8 +28,20 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}",
           f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
-def _compile(src: str, verbose: bool) -> str:
+def _stale(src: str, obj: str) -> bool:
+    """The object is older than its source or any header it may include."""
+    if not os.path.exists(obj):
+        return True
+    t = os.path.getmtime(obj)
+    deps = [os.path.join(CSRC, src)] + [os.path.join(d, f) for d in (CSRC, INCLUDE) for f in os.listdir(d)
+                                        if f.endswith(".h")]
+    return any(os.path.getmtime(p) > t for p in deps)
+
+
+def _compile(src: str, verbose: bool, incremental: bool = False) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
+    if incremental and not _stale(src, obj):
+        return obj
     cmd = [HIPCC] + COMMON + DEVICE_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC, "-x", "hip"] + COMMON[0:] + DEVICE_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
@@ -44,12 +56,14 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
+def build(verbose: bool = False, jobs: int = 4, incremental: bool = False) -> str:
+    """Compile every source (incremental: only those older than their object)
+    and link libhkv.so."""
     if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     os.makedirs(OBJDIR, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, verbose, incremental), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
@@ -60,4 +74,4 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, incremental="--incremental" in sys.argv))

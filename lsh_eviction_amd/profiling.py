@@ -190,6 +190,56 @@ def write_traffic_md(args, rec):
         fh.write("\n".join(lines) + "\n")
 
 
+def all_counters(path: str):
+    """{counter: {kernel name: [value per dispatch]}} of a counter-collection csv."""
+    acc = collections.defaultdict(lambda: collections.defaultdict(lambda: collections.defaultdict(float)))
+    with open(path, newline="") as fh:
+        for row in csv.DictReader(fh):
+            disp = row.get("Dispatch_Id") or row.get("Correlation_Id")
+            acc[row["Counter_Name"]][row["Kernel_Name"]][disp] += float(row["Counter_Value"])
+    return {c: {k: list(v.values()) for k, v in per.items()} for c, per in acc.items()}
+
+
+def cmd_counters(args):
+    """Mean per dispatch of every counter in the given csv files, for each
+    kernel matching one of the needles; one markdown table."""
+    needles = args.kernels.split(",")
+    table = collections.OrderedDict()   # counter -> {needle: (mean, dispatches)}
+    names = {}
+    for path in args.csv:
+        for ctr, per in all_counters(path).items():
+            for nd in needles:
+                hits = [(k, v) for k, v in per.items() if nd in k]
+                if not hits:
+                    continue
+                k, v = max(hits, key=lambda kv: len(kv[1]))
+                names[nd] = _short(k)
+                table.setdefault(ctr, {})[nd] = (_mean(v), len(v))
+    lines = [f"# {args.title}", "", "Commands (each a run of its own, the counters of one pass after --pmc):", ""]
+    lines += [f"    {c}" for c in args.cmd]
+    lines += ["", "Mean per dispatch (rocprofv3 sums a counter over its hardware instances unless its name says "
+              "otherwise; derived counters are rocprofv3's own expressions).", ""]
+    lines.append("| counter | " + " | ".join(f"`{names.get(nd, nd)}`" for nd in needles) + " |")
+    lines.append("|---|" + "---:|" * len(needles))
+    for ctr, per in table.items():
+        cells = []
+        for nd in needles:
+            if nd in per:
+                m, n = per[nd]
+                cells.append(f"{m:,.4g} ({n})" if abs(m) < 1e4 else f"{m:,.0f} ({n})")
+            else:
+                cells.append("")
+        lines.append(f"| {ctr} | " + " | ".join(cells) + " |")
+    lines += ["", "(n) = dispatches averaged."]
+    if args.note:
+        lines += ["", args.note]
+    text = "\n".join(lines) + "\n"
+    if args.out:
+        with open(args.out, "w") as fh:
+            fh.write(text)
+    print(text)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -208,8 +258,15 @@ def main(argv=None):
     a.add_argument("--md", default="")
     a.add_argument("--alg-bytes", type=int, default=0)
     a.add_argument("--bench-args", default="--steps 20 --warmup 2 --no-cpu")
+    a = sub.add_parser("counters")
+    a.add_argument("--csv", nargs="+", required=True)
+    a.add_argument("--kernels", required=True, help="comma-separated substrings of kernel names")
+    a.add_argument("--cmd", nargs="+", default=[])
+    a.add_argument("--title", default="rocprofv3 counters")
+    a.add_argument("--out", default="")
+    a.add_argument("--note", default="")
     args = ap.parse_args(argv)
-    {"copy": cmd_copy, "stats": cmd_stats, "traffic": cmd_traffic}[args.mode](args)
+    {"copy": cmd_copy, "stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters}[args.mode](args)
 
 
 if __name__ == "__main__":
