@@ -39,6 +39,10 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
+// Buffer resources: word 3 = 32-bit data format, no swizzle.  Cache policy
+// sc1 = the agent-scope policy of a load or store (see the fused schedule).
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kCpolSC1 = 16;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int D>
@@ -191,19 +195,20 @@ __device__ __forceinline__ unsigned long long join16(const uint32_t (*c16)[16], 
 // ---------------------------------------------------------------------------
 // Hamming candidate of a slot range
 // ---------------------------------------------------------------------------
-template <int BITS, int GM>
+// Best (score, lowest slot) key of the thread's codes in [s0, s1): group j
+// is the 16 bytes at slot s0 + (j * kThreads + tid) * VS.  The first NPRE
+// groups were loaded by the caller before the tile ring (pre); later groups
+// (chunks longer than NPRE * kThreads * VS slots) are loaded here, and a wait
+// for one of those is a wait for every tile issued before it.
+template <int BITS, int GM, int NPRE>
 __device__ __forceinline__ unsigned long long thread_candidate(const typename CodeT<BITS>::T* __restrict__ code,
                                                                const typename CodeT<BITS>::T (&qc)[GM], int G,
-                                                               int s0, int s1, uint4 first)
+                                                               int s0, int s1, const uint4 (&pre)[NPRE])
 {
     using CT = typename CodeT<BITS>::T;
     constexpr int VS = 16 / sizeof(CT);
     unsigned long long best = 0;
-    uint4 raw = first;
-    for (int s = s0 + (int)threadIdx.x * VS; s < s1; s += kThreads * VS) {
-        const int sn = s + kThreads * VS;
-        uint4 nxt = make_uint4(0, 0, 0, 0);
-        if (sn < s1) nxt = *reinterpret_cast<const uint4*>(code + sn);
+    auto fold = [&](uint4 raw, int s) {
         CT cs[VS];
         __builtin_memcpy(cs, &raw, 16);
 #pragma unroll
@@ -215,8 +220,11 @@ __device__ __forceinline__ unsigned long long thread_candidate(const typename Co
             const unsigned long long k = (s + u < s1) ? cand_key(sc, s + u) : 0ull;
             best = k > best ? k : best;
         }
-        raw = nxt;
-    }
+    };
+#pragma unroll
+    for (int j = 0; j < NPRE; ++j) fold(pre[j], s0 + (j * kThreads + (int)threadIdx.x) * VS);
+    for (int s = s0 + (NPRE * kThreads + (int)threadIdx.x) * VS; s < s1; s += kThreads * VS)
+        fold(*reinterpret_cast<const uint4*>(code + s), s);
     return best;
 }
 
@@ -445,6 +453,14 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // (l / 16) of the head dimension, 16 bytes per k-step), V in coalesced
 // 16-byte row segments (lane l: row group l / (D/8), segment l % (D/8)).
 // Rows at or beyond `len` are not loaded and read as zero.
+// P.V runs on the matrix cores for d = 128 with values stored as given (see
+// mfma_tile_pv); int8 values and d = 64 accumulate P.V on the VALU.
+template <int D, bool VQ>
+constexpr bool pv_on_mfma()
+{
+    return D == 128 && !VQ;
+}
+
 template <int D, int TR, bool VQ = false>
 struct MTile {
     static constexpr int H = TR / 16;          // 16-row halves
@@ -467,6 +483,30 @@ struct MTile {
     {
         const int lane = threadIdx.x & 63;
         const int i = lane & 15, qd = lane >> 4;
+        if constexpr (pv_on_mfma<D, VQ>()) {
+            // MFMA row i of the block holds physical row i / 4 + 4 (i % 4) (see
+            // mfma_tile_pv).  Buffer loads over the range's len rows: 32-bit
+            // offsets, and rows at or beyond len read as zero (the caller masks
+            // them).
+            static_assert(H == 1, "one 16-row block per tile");
+            const int nb = len * D * 2;
+            const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(Kh + (size_t)r0 * D), 0, nb, kRsrcWord3);
+            const auto rv = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<bf16_t*>(reinterpret_cast<const bf16_t*>(Vh) + (size_t)r0 * D), 0, nb, kRsrcWord3);
+            const int ko = (base + (i >> 2) + 4 * (i & 3)) * (D * 2) + qd * (D / 2);
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const auto w = __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 16 * s, 0, 0);
+                __builtin_memcpy(&k[0][s], &w, 16);
+            }
+            const int rg = lane / LPR, cc = lane % LPR;
+#pragma unroll
+            for (int u = 0; u < VU; ++u) {
+                const auto w = __builtin_amdgcn_raw_buffer_load_b128(rv, (base + u * RPW + rg) * (D * 2) + cc * 16, 0, 0);
+                __builtin_memcpy(&v[u], &w, 16);
+            }
+            return;
+        }
         const int last = len > 0 ? len - 1 : 0;
 #pragma unroll
         for (int h = 0; h < H; ++h) {
@@ -650,6 +690,131 @@ __device__ __forceinline__ void mfma_tile(const MTile<D, TR, VQ>& tl, int base, 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// A wave's running partial when P.V runs on the matrix cores: the running
+// max and sum of head n = lane % 16 (the logits' layout; the sum over the
+// wave's rows of quarter lane / 16), and in register r of acc[blk] the
+// accumulator of head 4 (lane / 16) + r, column 8 (lane % 16) + blk.
+struct MStatePV {
+    float m, lsum;
+    f32x4 acc[8];
+};
+
+// Rescale factor of head 4 (lane / 16) + r, from the lane of the logits
+// layout that holds it (alpha: head lane % 16).  Heads beyond the group are
+// padding whatever they get.
+template <int GM>
+__device__ __forceinline__ float head_alpha(float alpha, int qd, int r)
+{
+    const int ai = __float_as_int(alpha);
+    if constexpr (GM <= 4) {
+        return __int_as_float(__builtin_amdgcn_readlane(ai, r));
+    } else if constexpr (GM <= 8) {
+        const int a0 = __builtin_amdgcn_readlane(ai, r), a1 = __builtin_amdgcn_readlane(ai, 4 + r);
+        return __int_as_float((qd & 1) ? a1 : a0);
+    } else {
+        return __int_as_float(__builtin_amdgcn_ds_bpermute((4 * qd + r) * 4, __float_as_int(alpha)));
+    }
+}
+
+// One 16-row tile with both products on the matrix cores (d = 128, values as
+// given).  The K tile's rows enter the logits MFMA in the order
+// pi(i) = i / 4 + 4 (i % 4) (MTile::load), so register r of the lanes of
+// quarter qd holds the logit of physical row qd + 4 r for head n = lane % 16.
+// That is the A-operand layout of a 16 x 16 x 16 MFMA with the heads as its M
+// dimension and the tile's rows, in the order pi, as its K dimension.  The
+// coalesced value loads hold row qd + 4 u, columns 8 n .. 8 n + 7 in v[u]
+// (lane n of quarter qd), so element blk of v[0..3] is that MFMA's B operand
+// for output column 8 n + blk: P.V is eight MFMAs, one per column block, with
+// no exchange between lanes.  The probabilities enter as a bf16 high part and
+// a bf16 remainder (two MFMAs into one fp32 accumulator), as the queries do
+// in the logits; the values are bf16, so every product is exact.
+template <int GM>
+__device__ __forceinline__ void mfma_tile_pv(const MTile<128, 16, false>& tl, int base, int r0, int len, int skip,
+                                             const bf16x8 (&qhi)[4], const bf16x8 (&qlo)[4], MStatePV& st,
+                                             float* clg)
+{
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, qd = lane >> 4;
+
+    f32x4 C = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, tl.k[0][s]);
+        C = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qhi[s], C, 0, 0, 0);
+        C = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo[s], C, 0, 0, 0);
+    }
+    // logits of physical rows qd + 4 r for head n; masked rows get -inf
+    float lg[4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int row = base + qd + 4 * r;
+        const bool held = (r0 + row) == skip;
+        if (held && n < GM) clg[n] = C[r];
+        lg[r] = (row < len && !held) ? C[r] : -INFINITY;
+        tmax = fmaxf(tmax, lg[r]);
+    }
+    {
+        float2 t2 = swap_pair<16>(tmax);
+        tmax = fmaxf(t2.x, t2.y);
+        t2 = swap_pair<32>(tmax);
+        tmax = fmaxf(t2.x, t2.y);
+    }
+    const float mold = st.m;
+    const float mx = fmaxf(mold, tmax);
+    const float ms = mx == -INFINITY ? 0.f : mx;
+    const float alpha = exp2_fast(mold - ms);
+    st.m = mx;
+    float p[4], psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        p[r] = exp2_fast(lg[r] - ms);
+        psum += p[r];
+    }
+    st.lsum = st.lsum * alpha + psum;
+    // the accumulators are rescaled only when some head's maximum moved
+    // (a wave-uniform branch; alpha is exactly 1 for the others)
+    if (__builtin_amdgcn_ballot_w64(mx != mold) != 0ull) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float ah = head_alpha<GM>(alpha, qd, r);
+#pragma unroll
+            for (int blk = 0; blk < 8; ++blk) st.acc[blk][r] *= ah;
+        }
+    }
+    bf16x4 ph, pl;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        ph[r] = (__bf16)p[r];
+        pl[r] = (__bf16)(p[r] - (float)ph[r]);
+    }
+    const s16x4 aph = __builtin_bit_cast(s16x4, ph), apl = __builtin_bit_cast(s16x4, pl);
+    // Value rows at or past len read as zero (the buffer's range ends at
+    // len), so masked rows add exactly 0 * 0.
+    const uint4 (&vr)[4] = tl.v;
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) {
+        const int w = blk >> 1;
+        uint32_t x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint4 vv = vr[u];
+            x[u] = w == 0 ? vv.x : w == 1 ? vv.y : w == 2 ? vv.z : vv.w;
+        }
+        // v_perm_b32: bytes 0-3 of the selection are the second operand's,
+        // 4-7 the first's; take the low (even blk) or high (odd blk) halves
+        const uint32_t sel = (blk & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t b0 = __builtin_amdgcn_perm(x[1], x[0], sel);
+        const uint32_t b1 = __builtin_amdgcn_perm(x[3], x[2], sel);
+        const s16x4 bv = __builtin_bit_cast(s16x4, make_uint2(b0, b1));
+        st.acc[blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aph, bv, st.acc[blk], 0, 0, 0);
+        st.acc[blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(apl, bv, st.acc[blk], 0, 0, 0);
+    }
+}
+
 // Same contract as attend_rows, for bf16 K/V.  Logits come from MFMA: the
 // query of head n is column n of the B operand, split into a bf16 high part
 // and a bf16 remainder (two MFMAs into one fp32 accumulator), so the products
@@ -683,6 +848,62 @@ __device__ __forceinline__ void attend_rows_mfma(const bf16_t* __restrict__ Kh, 
         }
     }
 
+    const int step = kWaves * TR;
+    const int b0 = wave * TR;
+    const int ntile = len > b0 ? (len - b0 + step - 1) / step : 0;
+    if constexpr (pv_on_mfma<D, VQ>()) {
+        static_assert(TR == 16, "one 16-row block per tile");
+        MStatePV st;
+        st.m = -INFINITY;
+        st.lsum = 0.f;
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk) st.acc[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // the ring as below
+        int k = 0;
+        for (; k + 2 * NB <= ntile; k += NB) {
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                mfma_tile_pv<GM>(ring[i], b0 + (k + i) * step, r0, len, skip, qhi, qlo, st, clg);
+                ring[i].load(Kh, Vh, Vsh, r0, len, b0 + (k + i + NB) * step);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            if (k + i < ntile) {
+                mfma_tile_pv<GM>(ring[i], b0 + (k + i) * step, r0, len, skip, qhi, qlo, st, clg);
+                if (k + i + NB < ntile) ring[i].load(Kh, Vh, Vsh, r0, len, b0 + (k + i + NB) * step);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+            if (k + NB + i < ntile)
+                mfma_tile_pv<GM>(ring[i], b0 + (k + NB + i) * step, r0, len, skip, qhi, qlo, st, clg);
+
+        float lsum = st.lsum;
+        {
+            float2 t2 = swap_pair<16>(lsum);
+            lsum = t2.x + t2.y;
+            t2 = swap_pair<32>(lsum);
+            lsum = t2.x + t2.y;
+        }
+        if (qd == 0 && n < GM) {
+            sm.m[wave][n] = st.m;
+            sm.l[wave][n] = lsum;
+        }
+        // head 4 qd + r, columns 8 n .. 8 n + 7: the eight blocks' register r
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int g = 4 * qd + r;
+            if (g < GM) {
+                float4* dst = reinterpret_cast<float4*>(&sm.acc[wave][g < GM ? g : 0][8 * n]);
+                dst[0] = make_float4(st.acc[0][r], st.acc[1][r], st.acc[2][r], st.acc[3][r]);
+                dst[1] = make_float4(st.acc[4][r], st.acc[5][r], st.acc[6][r], st.acc[7][r]);
+            }
+        }
+        __syncthreads();
+        return;
+    }
+
     MState<GM> st;
     st.m = -INFINITY;
     st.lsum = 0.f;
@@ -696,9 +917,6 @@ __device__ __forceinline__ void attend_rows_mfma(const bf16_t* __restrict__ Kh, 
     // as soon as it has been computed.  In the main loop every reload is
     // valid, so no load sits in a branch there and the wait counters stay
     // exact; the last 2 NB tiles form the tail.
-    const int step = kWaves * TR;
-    const int b0 = wave * TR;
-    const int ntile = len > b0 ? (len - b0 + step - 1) / step : 0;
     int k = 0;
     for (; k + 2 * NB <= ntile; k += NB) {
 #pragma unroll
@@ -875,10 +1093,12 @@ constexpr int tile_rows()
 }
 
 // tiles of a wave in flight at once in the bf16 path
-template <int GM>
+template <int GM, int D, bool VQ>
 constexpr int ring_depth()
 {
-    return GM >= 16 ? 1 : 2;   // 16 heads: the accumulators take 128 registers a lane
+    // with P.V on the VALU, 16 heads' accumulators take 128 registers a lane;
+    // on the matrix cores they take 32 whatever the group size
+    return pv_on_mfma<D, VQ>() || GM < 16 ? 2 : 1;
 }
 
 // ---------------------------------------------------------------------------
@@ -905,8 +1125,6 @@ __device__ __forceinline__ void own_stores_complete()
 // policy of an agent-scope load (sc1: a line this XCD's L2 may hold stale is
 // fetched again), 16 bytes at byte offset `off` of a buffer resource.
 // Out-of-range offsets read zero.
-constexpr int kCpolSC1 = 16;
-constexpr int kRsrcWord3 = 0x00020000;   // 32-bit data format, no swizzle
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const float* base, size_t bytes)
 {
@@ -1153,6 +1371,9 @@ union FusedSmem {
     MergeBlockSmem<D, GM> mg;
 };
 
+// 16-byte code groups per thread the fused step loads before its tiles
+constexpr int kCodePre = 4;
+
 // VQ: values are int8 codes with a per-row scale (bf16 keys only).
 template <int D, int BITS, int GM, typename KT, bool VQ = false>
 __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const float* __restrict__ q,
@@ -1219,8 +1440,14 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     const int NQ4 = G * D / 4;
     const float4 qst = reinterpret_cast<const float4*>(qh)[min(tid, NQ4 - 1)];
     const uint4 kvst = reinterpret_cast<const uint4*>(wave == 0 ? kh : vh)[min(lane, NK4 - 1)];
-    const int cvec = min(s0 + tid * VS, (int)c.code_slots - VS);
-    const uint4 craw = *reinterpret_cast<const uint4*>(codeh + cvec);
+    // the chunk's codes, up to kCodePre 16-byte groups per thread (every
+    // workload's chunk; longer chunks load the rest while scoring)
+    // (groups past the chunk read its last group again, one cached line)
+    const int clast = max(min(s0 + c.chunk, (int)c.code_slots) - VS, 0);
+    uint4 craw[kCodePre];
+#pragma unroll
+    for (int j = 0; j < kCodePre; ++j)
+        craw[j] = *reinterpret_cast<const uint4*>(codeh + min(s0 + (j * kThreads + tid) * VS, clast));
     // (threads past the end store the last element again, with the value
     // they loaded from it, so every store is unconditional)
 #pragma unroll
@@ -1246,7 +1473,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     if (split >= nsb) return;   // ragged batch: this sequence has fewer chunks
 
     // the first tiles of every wave, in flight while the codes are computed
-    constexpr int NB = ring_depth<GM>();
+    constexpr int NB = ring_depth<GM, D, VQ>();
     MTile<D, TR, VQ> ring[kMfma ? NB : 1];
     Tile<D, KT> first;
     if constexpr (kMfma) {
@@ -1297,23 +1524,27 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
         CT qc[GM];
 #pragma unroll
         for (int g = 0; g < GM; ++g) qc[g] = g < G ? (CT)join16<BITS>(s_q16, g) : (CT)0;
-        ckey = thread_candidate<BITS, GM>(codeh, qc, G, s0, s0 + len, craw);
+        ckey = thread_candidate<BITS, GM, kCodePre>(codeh, qc, G, s0, s0 + len, craw);
         ckey = block_max_u64(ckey, s_red);
         cand = ckey ? cand_slot(ckey) : -1;
         if (tid == 0 && ckey) atomicMax(&c.ekey[2 * head + (t & 1)], ckey);
     }
 
-    // the held-out candidate's value row: fetched now, published after the
-    // loop (the loop takes its logits as it passes its row)
-    float2 vc2 = make_float2(0.f, 0.f);
-    if (cand >= 0 && 2 * lane < D) {
-        if constexpr (VQ) {
-            const uint16_t w = *reinterpret_cast<const uint16_t*>(Vq8 + (size_t)cand * D + 2 * lane);
-            const float sc = Vsh[cand];
-            vc2 = make_float2((float)(int8_t)(w & 0xFFu) * sc, (float)(int8_t)(w >> 8) * sc);
-        } else {
-            vc2 = make_float2(to_f32(Vh[(size_t)cand * D + 2 * lane]), to_f32(Vh[(size_t)cand * D + 2 * lane + 1]));
-        }
+    // The held-out candidate's value row: fetched now, converted and published
+    // after the loop (the loop takes its logits as it passes its row).  The
+    // load is unconditional (row 0 when there is no candidate) and its bits
+    // stay raw until then: a conversion here would wait for the load, and so
+    // for the whole tile ring issued before it, ahead of the loop.
+    const size_t crow = (size_t)(cand >= 0 ? cand : 0);
+    const int ce = 2 * (lane % (D / 2));
+    using VRaw = typename std::conditional<VQ, uint16_t, typename std::conditional<kMfma, uint32_t, float2>::type>::type;
+    VRaw vraw;
+    float vcsc = 0.f;
+    if constexpr (VQ) {
+        vraw = *reinterpret_cast<const uint16_t*>(Vq8 + crow * D + ce);
+        vcsc = Vsh[crow];
+    } else {
+        vraw = *reinterpret_cast<const VRaw*>(Vh + crow * D + ce);
     }
 
     // attention over the chunk with the candidate held out
@@ -1325,8 +1556,16 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     // publish this chunk: partial softmax, candidate logits and value row
     // (the attention's closing barrier made its LDS results, the candidate's
     // logits included, visible to every wave)
-    if (cand >= 0 && wave == 0 && 2 * lane < D)
+    if (cand >= 0 && wave == 0 && 2 * lane < D) {
+        float2 vc2;
+        if constexpr (VQ)
+            vc2 = make_float2((float)(int8_t)(vraw & 0xFFu) * vcsc, (float)(int8_t)(vraw >> 8) * vcsc);
+        else if constexpr (kMfma)
+            vc2 = make_float2(__uint_as_float(vraw << 16), __uint_as_float(vraw & 0xFFFF0000u));
+        else
+            vc2 = vraw;
         st_sc1_8(dev_rsrc(c.cand_v + crec * D, (size_t)D * 4), 2 * lane * 4, vc2);
+    }
     publish_fused<D, GM>(sm, dev_rsrc(c.frec + crec * G * D, (size_t)G * D * 4),
                          dev_rsrc(c.fscal + crec * G * 4, (size_t)G * 16), G, s_clg, cand >= 0);
     own_stores_complete();
@@ -1585,9 +1824,9 @@ __global__ __launch_bounds__(kThreads) void k_hamming_argmax(DevCache c)
     for (int g = 0; g < GM; ++g)
         qc[g] = g < G ? (CT)load_code_words(c.dbg_q + ((size_t)b * c.Hq + h * G + g) * c.W, c.W) : (CT)0;
     const CT* codeh = reinterpret_cast<const CT*>(c.code) + (size_t)head * c.code_slots;
-    uint4 first = make_uint4(0, 0, 0, 0);
-    if (s0 + (int)threadIdx.x * VS < s1) first = *reinterpret_cast<const uint4*>(codeh + s0 + threadIdx.x * VS);
-    unsigned long long key = thread_candidate<BITS, GM>(codeh, qc, G, s0, s1, first);
+    uint4 first[1] = {make_uint4(0, 0, 0, 0)};
+    if (s0 + (int)threadIdx.x * VS < s1) first[0] = *reinterpret_cast<const uint4*>(codeh + s0 + threadIdx.x * VS);
+    unsigned long long key = thread_candidate<BITS, GM, 1>(codeh, qc, G, s0, s1, first);
     key = block_max_u64(key, s_red);
     if (threadIdx.x == 0 && key) atomicMax(&c.ekey[2 * head], key);
 }
@@ -1655,7 +1894,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_split(DevCache c, const float
     const int len = max(min(s0 + c.chunk, n) - s0, 0);
     const int wave = threadIdx.x >> 6;
     if constexpr (kMfma) {
-        constexpr int TR = tile_rows<GM>(), NB = ring_depth<GM>();
+        constexpr int TR = tile_rows<GM>(), NB = ring_depth<GM, D, false>();
         MTile<D, TR> ring[NB];
         const int ntile = len > wave * TR ? (len - wave * TR + kWaves * TR - 1) / (kWaves * TR) : 0;
 #pragma unroll
@@ -1721,7 +1960,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_tier(DevCache c, const float*
     const int len = min(s0 + rps, m) - s0;
     const int wave = threadIdx.x >> 6;
     if constexpr (kMfma) {
-        constexpr int TR = tile_rows<GM>(), NB = ring_depth<GM>();
+        constexpr int TR = tile_rows<GM>(), NB = ring_depth<GM, D, false>();
         MTile<D, TR> ring[NB];
         const int ntile = len > wave * TR ? (len - wave * TR + kWaves * TR - 1) / (kWaves * TR) : 0;
 #pragma unroll
