@@ -209,6 +209,25 @@ hkv_status hkv_prefill_chunks(hkv_cache* c, const void* K, const void* V, const 
 hkv_status hkv_decode_step(hkv_cache* c, const float* q, const void* k, const void* v,
                            float* out, int32_t* evicted_slot, void* stream);
 
+/* hkv_decode_step for callers that cannot allocate or pass scratch memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same step, with the same results, but its per-step
+ * scratch -- the split records, held-out candidate rows, eviction keys and
+ * ticket counters (fused schedule) or split partials (split schedule) --
+ * lives in a static device array of the library, 8 MiB per GPU, held until
+ * the process ends, instead of the cache's workspace.  Makes no allocation.
+ * The array is shared by every call on a GPU and keeps the last call's
+ * contents; each call first clears what must start at zero (with a kernel,
+ * so the call can be captured in a graph).  Calls that overlap on one GPU
+ * (other streams, other host threads, other caches) race on the array and
+ * must be serialised by the caller.  HKV_ERR_UNSUPPORTED, with nothing
+ * enqueued, when the step would need more than 8 MiB (about
+ * B * Hkv * nsplit * (G * d * 4 + G * 16 + d * 4) + B * Hq * nsplit *
+ * (d + 4) * 4 bytes, nsplit = ceil(Smax / chunk)).  Otherwise as
+ * hkv_decode_step. */
+hkv_status hkv_decode_step_static(hkv_cache* c, const float* q, const void* k, const void* v,
+                                  float* out, int32_t* evicted_slot, void* stream);
+
 /* Attach the host tier (a cache created with tier_capacity > 0, before its
  * prefill; HKV_ERR_STATE after it, HKV_ERR_INVALID_ARG without a capacity).
  * K, V: [B][Hkv][tier_capacity][d] kv dtype; tok: [B][Hkv][tier_capacity]

@@ -5,6 +5,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -66,6 +67,77 @@ hkv_status usable(hkv_cache* c)
 
 extern "C" const char* hkv_last_error(const hkv_cache* c) { return c ? c->err.c_str() : g_err.c_str(); }
 
+// ---------------------------------------------------------------------------
+// Per-step scratch of hkv_decode_step_static, for callers that cannot
+// allocate: a file-scope device array, one copy per GPU, alive until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is a stand-in, not a device address): hkv_create resolves its
+// device address once per device, with that device current, and the entry
+// point uses only that address.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kStaticScratchBytes = 8u << 20;
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device `dev` (resolved once).
+hipError_t resolve_static_scratch(int dev)
+{
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[dev]) return hipSuccess;
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+    return hipSuccess;
+}
+
+void* static_scratch(int dev)
+{
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    return g_scratch_ptr[dev];
+}
+
+// The per-step scratch of a decode step carved from `base` (256-byte
+// aligned pieces, as in the workspace): the fused step's records, candidate
+// rows, eviction keys and ticket counters, and the split schedule's
+// partials.  Returns the bytes used.
+size_t carve_step_scratch(const hkv::Layout& L, char* base, hkv::DevCache* d)
+{
+    const size_t heads = (size_t)L.B * L.Hkv;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = (off + bytes + hkv::kAlign - 1) / hkv::kAlign * hkv::kAlign;
+        return o;
+    };
+    const size_t frec = take(heads * L.nsplit * L.G * L.d * 4);
+    const size_t fscal = take(heads * L.nsplit * L.G * 16);
+    const size_t cand_v = take(heads * L.nsplit * L.d * 4);
+    const size_t part = take((size_t)L.B * L.Hq * L.nsplit * (L.d + 4) * 4);
+    const size_t ekey = take(heads * 2 * 8);
+    const size_t count = take(heads * hkv::kCountStride * 4);
+    if (d && base) {
+        d->frec = (float*)(base + frec);
+        d->fscal = (float*)(base + fscal);
+        d->cand_v = (float*)(base + cand_v);
+        d->part = (float*)(base + part);
+        d->ekey = (unsigned long long*)(base + ekey);
+        d->count = (unsigned*)(base + count);
+    }
+    return off;
+}
+
+}  // namespace
+
 extern "C" hkv_status hkv_create(const hkv_config* cfg, const float* R_host, void* workspace,
                                  size_t ws_bytes, void* stream, hkv_cache** out)
 {
@@ -83,6 +155,14 @@ extern "C" hkv_status hkv_create(const hkv_config* cfg, const float* R_host, voi
         return fail(nullptr, HKV_ERR_INVALID_ARG, msg);
     }
     hipStream_t st = (hipStream_t)stream;
+    int dev = 0;
+    hipError_t ge = hipGetDevice(&dev);
+    if (ge == hipSuccess) ge = resolve_static_scratch(dev);
+    if (ge != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(nullptr, HKV_ERR_DEVICE, std::string("hkv_create: device address of the static scratch: ") +
+                                                 hipGetErrorString(ge));
+    }
     hkv_cache* c = new hkv_cache();
     c->lay = L;
     c->budgets.assign(cfg->budgets, cfg->budgets + cfg->batch);
@@ -336,6 +416,45 @@ extern "C" hkv_status hkv_decode_step(hkv_cache* c, const float* q, const void* 
                        ? hkv::launch_decode_fused(c->dev, q, k, v, out, evicted_slot, st)
                        : hkv::launch_decode_split(c->dev, q, k, v, out, evicted_slot, st);
     s = check_launch(c, e, st, "hkv_decode_step");
+    if (s == HKV_OK) {
+        c->stepped = true;
+        c->obs_codes = false;
+    }
+    return s;
+}
+
+extern "C" hkv_status hkv_decode_step_static(hkv_cache* c, const float* q, const void* k, const void* v,
+                                             float* out, int32_t* evicted_slot, void* stream)
+{
+    hkv_status s = usable(c);
+    if (s != HKV_OK) return s;
+    if (!c->prefilled)
+        return fail(c, HKV_ERR_STATE, "hkv_decode_step_static: call hkv_prefill or hkv_set_state first");
+    if (!q || !k || !v || !out || !evicted_slot)
+        return fail(c, HKV_ERR_INVALID_ARG, "hkv_decode_step_static: NULL buffer");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+        return fail(c, HKV_ERR_INVALID_ARG, "hkv_decode_step_static: q, k, v must be 16-byte aligned");
+    const size_t need = carve_step_scratch(c->lay, nullptr, nullptr);
+    if (need > kStaticScratchBytes) {
+        char msg[200];
+        snprintf(msg, sizeof(msg),
+                 "hkv_decode_step_static: this cache's step needs %zu bytes of scratch, more than the %zu of the "
+                 "static scratch (fewer splits, i.e. a larger chunk, or hkv_decode_step)", need, kStaticScratchBytes);
+        return fail(c, HKV_ERR_UNSUPPORTED, msg);
+    }
+    char* base = (char*)static_scratch(c->device);
+    if (!base) return fail(c, HKV_ERR_STATE, "hkv_decode_step_static: no static scratch on this device");
+    hkv::DevCache d = c->dev;
+    carve_step_scratch(c->lay, base, &d);
+    hipStream_t st = (hipStream_t)stream;
+    // the array keeps the last call's contents: the eviction keys and ticket
+    // counters must start at zero (a kernel, not a memset, so the step can be
+    // captured in a graph)
+    hipError_t e = hkv::launch_clear_step_scratch(d, st);
+    if (e == hipSuccess)
+        e = c->lay.schedule == HKV_DECODE_FUSED ? hkv::launch_decode_fused(d, q, k, v, out, evicted_slot, st)
+                                                : hkv::launch_decode_split(d, q, k, v, out, evicted_slot, st);
+    s = check_launch(c, e, st, "hkv_decode_step_static");
     if (s == HKV_OK) {
         c->stepped = true;
         c->obs_codes = false;

@@ -24,7 +24,7 @@ HKV_DECODE_FUSED, HKV_DECODE_SPLIT = 0, 1
 
 # every symbol include/hkv.h declares
 EXPORTS = ("hkv_validate_config", "hkv_workspace_bytes", "hkv_create", "hkv_prefill",
-           "hkv_prefill_queries", "hkv_prefill_chunks", "hkv_decode_step", "hkv_destroy", "hkv_status_str", "hkv_last_error",
+           "hkv_prefill_queries", "hkv_prefill_chunks", "hkv_decode_step", "hkv_decode_step_static", "hkv_destroy", "hkv_status_str", "hkv_last_error",
            "hkv_get_state", "hkv_set_state", "hkv_debug_last_codes", "hkv_debug_prefill_codes",
            "hkv_debug_prefill_query_codes", "hkv_debug_scores", "hkv_encode", "hkv_attach_tier",
            "hkv_tier_counts", "hkv_attend_tiered")
@@ -69,6 +69,7 @@ def load():
         "hkv_tier_counts": (I, [P, P, P]),
         "hkv_attend_tiered": (I, [P, P, P, P]),
         "hkv_decode_step": (I, [P, P, P, P, P, P, P]),
+        "hkv_decode_step_static": (I, [P, P, P, P, P, P, P]),
         "hkv_destroy": (I, [P]),
         "hkv_status_str": (C.c_char_p, [I]),
         "hkv_last_error": (C.c_char_p, [P]),
@@ -167,6 +168,11 @@ def hkv_prefill(h, K, V, prompt_lens, n_max: int, stream=None):
 def hkv_decode_step(h, q, k, v, out, evicted_slot, stream=None):
     _check(load().hkv_decode_step(h, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(evicted_slot),
                                   _stream(stream)), h)
+
+
+def hkv_decode_step_static(h, q, k, v, out, evicted_slot, stream=None):
+    _check(load().hkv_decode_step_static(h, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(evicted_slot),
+                                         _stream(stream)), h)
 
 
 def hkv_destroy(h):
@@ -388,6 +394,20 @@ class Cache:
         if check:
             self.check_step_args(q, k, v, out, evicted)
         hkv_decode_step(self.h, q, k, v, out, evicted, stream)
+        return out, evicted
+
+    def decode_step_static(self, q, k, v, out=None, evicted=None, stream=None, check=True):
+        """decode_step with its per-step scratch in the library's static
+        device array (hkv_decode_step_static): for callers that cannot
+        allocate.  Calls that overlap on one GPU race."""
+        import torch
+        if out is None:
+            out = torch.empty((self.B, self.Hq, self.d), dtype=torch.float32, device="cuda")
+        if evicted is None:
+            evicted = torch.empty((self.B, self.Hkv), dtype=torch.int32, device="cuda")
+        if check:
+            self.check_step_args(q, k, v, out, evicted)
+        hkv_decode_step_static(self.h, q, k, v, out, evicted, stream)
         return out, evicted
 
     def get_state(self, stream=None):
