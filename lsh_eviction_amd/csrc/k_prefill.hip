@@ -10,7 +10,7 @@
 // the STREAM policy the prompt enters the cache one token at a time by the
 // decode rule, each token scored against its own key code; TRUNCATE keeps
 // the first `budget` tokens.  The sequential selection keeps the whole code
-// table of one (sequence, KV head) in LDS.
+// table of one (sequence, KV head) in the registers of one workgroup.
 //
 // Chunk-granular prefill (a reading of the ChunkKV summary page: tokens kept
 // or dropped in groups of consecutive tokens, kept indices reusable across
