@@ -108,7 +108,15 @@ typedef struct {
                                 a multiple of 64 in [64, 65536], or 0: about
                                 one workgroup per compute unit, i.e.
                                 ceil(sum_b S_b * Hkv / 256) rounded up to a
-                                multiple of 64 and clamped to [256, 65536] */
+                                multiple of 64 and clamped to [256, 65536].
+                                When budgets differ, the fused step cuts
+                                sequence b into ceil(S_b / chunk) splits of
+                                one length (a multiple of 64, at most chunk)
+                                and runs them longest first, and chunk 0
+                                picks, from a quarter of that value up to
+                                the largest budget, the chunk whose blocks a
+                                model of the dispatch (8 XCDs of 32 compute
+                                units) finishes first */
     int32_t value_bits;      /* 0: values stored in kv_dtype; 8: each value row
                                 stored as d int8 codes and one fp32 scale
                                 (scale = max|v| / 127, code = v / scale rounded
@@ -134,6 +142,11 @@ hkv_status hkv_validate_config(const hkv_config* cfg);
  * Sizes: K and V caches [B][Hkv][Smax][d] of kv dtype, code table, slot->token
  * map, per-split partial results and the prefill code buffer; Smax = max_b S_b. */
 hkv_status hkv_workspace_bytes(const hkv_config* cfg, size_t* bytes);
+
+/* Slots per attention split a cache with this configuration uses: cfg.chunk
+ * when it is set, else the default the chunk field describes (host-only).
+ * Same status as hkv_validate_config; *chunk is written on HKV_OK. */
+hkv_status hkv_config_chunk(const hkv_config* cfg, int32_t* chunk);
 
 /* Create a cache in `workspace` (device, 256-byte aligned, >= the bytes
  * hkv_workspace_bytes reported; owned by the caller and not touched by

@@ -196,8 +196,9 @@ extern "C" hkv_status hkv_create(const hkv_config* cfg, const float* R_host, voi
     d.vq = L.value_bits == 8;
     d.B = L.B; d.Hq = L.Hq; d.Hkv = L.Hkv; d.G = L.G; d.d = L.d; d.bits = L.bits; d.W = L.W;
     d.Smax = L.Smax; d.chunk = L.chunk; d.nsplit = L.nsplit;
-    d.heads_fastest = 0;
-    for (int b = 1; b < cfg->batch; ++b) d.heads_fastest |= cfg->budgets[b] != cfg->budgets[0];
+    d.ragged = L.nblk > 0;
+    d.blk = (const uint2*)(ws + L.off_blk);
+    d.nblk = L.nblk;
     d.kv_bf16 = L.kv_dtype == HKV_BF16;
     d.code_slots = (long long)L.code_slots;
     d.pcode_slots = (long long)L.pcode_slots;
@@ -220,6 +221,11 @@ extern "C" hkv_status hkv_create(const hkv_config* cfg, const float* R_host, voi
     if (e == hipSuccess)
         e = hipMemcpyAsync((void*)d.budget, cfg->budgets, (size_t)L.B * sizeof(int32_t),
                            hipMemcpyHostToDevice, st);
+    if (e == hipSuccess && L.nblk > 0) {
+        std::vector<uint32_t> blk((size_t)L.nblk * 2);
+        hkv::fused_block_order(cfg->budgets, cfg->batch, L.chunk, blk.data());
+        e = hipMemcpy((void*)d.blk, blk.data(), blk.size() * 4, hipMemcpyHostToDevice);
+    }
     if (e == hipSuccess) e = hkv::launch_reset(d, st);
     // value scales start at zero (the attention tile reads the scales of 16 rows at once)
     if (e == hipSuccess && L.value_bits == 8)

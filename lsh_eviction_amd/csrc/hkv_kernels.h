@@ -31,7 +31,9 @@ struct DevCache {
     void* qcode;                    // [B][Hq][pcode_slots] prompt query codes (QUERY prefill)
     float* vs;                      // [B][Hkv][Smax] (+16) value scales when values are int8
     int B, Hq, Hkv, G, d, bits, W, Smax, chunk, nsplit;
-    int heads_fastest;              // fused grid numbering: (sequence, head) fastest when budgets differ
+    int ragged;                     // budgets differ: the fused step runs the block list `blk`
+    const uint2* blk;               // [nblk] (b | split << 16, split length) of each fused block, longest first
+    int nblk;
     bool vq;                        // values stored as int8 codes + scales
     int kv_bf16;
     long long code_slots, pcode_slots;

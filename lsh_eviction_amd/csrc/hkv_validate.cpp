@@ -1,6 +1,10 @@
 // hkv_validate.cpp -- host-only configuration checks and workspace layout.
+#include <algorithm>
+#include <climits>
+#include <functional>
 #include <cstdio>
 #include <cstring>
+#include <vector>
 
 #include "hkv_layout.h"
 
@@ -78,6 +82,8 @@ hkv_status compute_layout(const hkv_config* cfg, Layout* L, char* err, size_t er
     l.schedule = cfg->decode_schedule;
     l.value_bits = cfg->value_bits;
     l.Smax = Smax;
+    bool ragged = false;
+    for (int b = 1; b < cfg->batch; ++b) ragged = ragged || cfg->budgets[b] != cfg->budgets[0];
     if (cfg->chunk) {
         l.chunk = cfg->chunk;
     } else {
@@ -91,10 +97,15 @@ hkv_status compute_layout(const hkv_config* cfg, Layout* L, char* err, size_t er
         long long ch = (slots + kChunkTargetBlocks - 1) / kChunkTargetBlocks;
         ch = (ch + 63) / 64 * 64;
         l.chunk = (int)(ch < kMinAutoChunk ? kMinAutoChunk : (ch > 65536 ? 65536 : ch));
+        // ragged budgets: the chunk whose longest-first block list ends first
+        if (ragged) l.chunk = ragged_auto_chunk(cfg->budgets, cfg->batch, cfg->n_kv_heads, l.chunk);
     }
     l.nsplit = (Smax + l.chunk - 1) / l.chunk;
     if (l.nsplit > 65535)
         FAIL(HKV_ERR_UNSUPPORTED, "chunk %d too small for a budget of %d slots (more than 65535 splits)", l.chunk, Smax);
+    l.nblk = ragged ? fused_block_order(cfg->budgets, cfg->batch, l.chunk, nullptr) : 0;
+    if ((long long)l.nblk * l.Hkv > INT_MAX)
+        FAIL(HKV_ERR_UNSUPPORTED, "chunk %d too small: more than 2^31 - 1 decode blocks", l.chunk);
     l.max_prompt = cfg->max_prompt;
     l.code_slots = align_up((size_t)Smax, 64);
     l.pcode_slots = align_up((size_t)(cfg->max_prompt > 0 ? cfg->max_prompt : 1), 64);
@@ -137,6 +148,7 @@ hkv_status compute_layout(const hkv_config* cfg, Layout* L, char* err, size_t er
     l.off_ekey = take(heads * 2 * 8);
     l.off_info = take(heads * 2 * 4);
     l.off_count = take(heads * kCountStride * 4);
+    l.off_blk = take((size_t)l.nblk * 8);
     l.off_pcode = take(heads * l.pcode_slots * cb);
     l.off_qcode = take(cfg->prefill_policy == HKV_PREFILL_QUERY ? (size_t)l.B * l.Hq * l.pcode_slots * cb : 0);
     // per-chunk scores of the prompt (HKV_PREFILL_CHUNK)
@@ -149,6 +161,77 @@ hkv_status compute_layout(const hkv_config* cfg, Layout* L, char* err, size_t er
     l.total = off;
     return HKV_OK;
 #undef FAIL
+}
+
+int fused_block_order(const int32_t* budgets, int B, int chunk, uint32_t* out)
+{
+    struct Blk {
+        int rows, b, split, len;   // rows: slots of this split, len: the sequence's split length
+    };
+    std::vector<Blk> v;
+    for (int b = 0; b < B; ++b) {
+        const int S = budgets[b];
+        const int k0 = (S + chunk - 1) / chunk;
+        const int len = (int)align_up((size_t)((S + k0 - 1) / k0), 64);
+        const int k = (S + len - 1) / len;
+        for (int j = 0; j < k; ++j) v.push_back({std::min(len, S - j * len), b, j, len});
+    }
+    if (out) {
+        std::stable_sort(v.begin(), v.end(), [](const Blk& x, const Blk& y) { return x.rows > y.rows; });
+        for (size_t i = 0; i < v.size(); ++i) {
+            out[2 * i] = (uint32_t)v[i].b | (uint32_t)v[i].split << 16;
+            out[2 * i + 1] = (uint32_t)v[i].len;
+        }
+    }
+    return (int)v.size();
+}
+
+long long fused_makespan(const int32_t* budgets, int B, int Hkv, int chunk)
+{
+    const int n = fused_block_order(budgets, B, chunk, nullptr);
+    std::vector<uint32_t> list((size_t)n * 2);
+    fused_block_order(budgets, B, chunk, list.data());
+    // per XCD, the time each of its compute units is next free (min-heaps)
+    std::vector<std::vector<long long>> free(kXcds, std::vector<long long>(kCusPerXcd, 0));
+    long long id = 0, end = 0;
+    for (int i = 0; i < n; ++i) {
+        const int b = (int)(list[2 * i] & 0xFFFFu), j = (int)(list[2 * i] >> 16), len = (int)list[2 * i + 1];
+        const long long rows = std::min(len, budgets[b] - j * len);
+        for (int h = 0; h < Hkv; ++h, ++id) {
+            std::vector<long long>& x = free[id % kXcds];
+            std::pop_heap(x.begin(), x.end(), std::greater<long long>());
+            x.back() += rows + kBlockFixedSlots;
+            end = std::max(end, x.back());
+            std::push_heap(x.begin(), x.end(), std::greater<long long>());
+        }
+    }
+    return end;
+}
+
+int ragged_auto_chunk(const int32_t* budgets, int B, int Hkv, int base)
+{
+    int Smax = 0;
+    long long slots = 0;
+    for (int b = 0; b < B; ++b) {
+        Smax = std::max(Smax, (int)budgets[b]);
+        slots += budgets[b];
+    }
+    const int lo = std::max(kMinAutoChunk, (int)align_up((size_t)(base / 4), 64));
+    const int hi = std::min(65536, (int)align_up((size_t)Smax, 64));
+    if (lo >= hi) return base;
+    const int step = (int)align_up((size_t)((hi - lo) / kAutoChunkCandidates + 1), 64);
+    int best = base;
+    long long best_t = fused_makespan(budgets, B, Hkv, base);
+    for (int T = hi; T >= lo; T -= step) {
+        // blocks of this chunk: at most sum_b ceil(S_b / T) per head
+        if ((slots / T + B) * Hkv > kAutoChunkMaxBlocks) continue;
+        const long long t = fused_makespan(budgets, B, Hkv, T);
+        if (t < best_t || (t == best_t && T > best)) {
+            best = T;
+            best_t = t;
+        }
+    }
+    return best;
 }
 
 }  // namespace hkv
@@ -165,6 +248,15 @@ extern "C" hkv_status hkv_workspace_bytes(const hkv_config* cfg, size_t* bytes)
     hkv::Layout l;
     hkv_status s = hkv::compute_layout(cfg, &l, nullptr, 0);
     if (s == HKV_OK) *bytes = l.total;
+    return s;
+}
+
+extern "C" hkv_status hkv_config_chunk(const hkv_config* cfg, int32_t* chunk)
+{
+    if (!chunk) return HKV_ERR_INVALID_ARG;
+    hkv::Layout l;
+    hkv_status s = hkv::compute_layout(cfg, &l, nullptr, 0);
+    if (s == HKV_OK) *chunk = l.chunk;
     return s;
 }
 

@@ -1384,16 +1384,29 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     constexpr int VS = 16 / sizeof(CT);
     constexpr bool kMfma = std::is_same<KT, bf16_t>::value;
     constexpr int TR = tile_rows<GM>();
-    // Workgroups go to the XCDs round-robin by number.  With ragged budgets
-    // the blocks are numbered (sequence, KV head) fastest, so every XCD gets
-    // the same mix of sequences; with equal budgets split fastest, which
-    // spreads each head over all XCDs (measured marginally faster there).
-    const int split = c.heads_fastest ? blockIdx.z : blockIdx.x;
-    const int h = c.heads_fastest ? blockIdx.x : blockIdx.y;
-    const int b = c.heads_fastest ? blockIdx.y : blockIdx.z;
+    // Workgroups go to the XCDs round-robin by number.  With equal budgets
+    // the split is fastest, which spreads each head over all XCDs (measured
+    // marginally faster there).  With ragged budgets the KV head is fastest
+    // and the rest follows the block list (equal splits per sequence,
+    // longest first): each XCD gets the same mix of work, and its compute
+    // units that finish early take the short blocks.
+    int split, h, b, chunk;
+    if (c.ragged) {
+        const int i = blockIdx.x / c.Hkv;
+        h = blockIdx.x - i * c.Hkv;
+        const uint2 e = c.blk[i];
+        b = (int)(e.x & 0xFFFFu);
+        split = (int)(e.x >> 16);
+        chunk = (int)e.y;
+    } else {
+        split = blockIdx.x;
+        h = blockIdx.y;
+        b = blockIdx.z;
+        chunk = c.chunk;
+    }
     const int G = c.G;
     const int head = b * c.Hkv + h;
-    const int s0 = split * c.chunk;
+    const int s0 = split * chunk;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
     __shared__ FusedSmem<D, BITS, GM> u;
@@ -1443,7 +1456,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     // the chunk's codes, up to kCodePre 16-byte groups per thread (every
     // workload's chunk; longer chunks load the rest while scoring)
     // (groups past the chunk read its last group again, one cached line)
-    const int clast = max(min(s0 + c.chunk, (int)c.code_slots) - VS, 0);
+    const int clast = max(min(s0 + chunk, (int)c.code_slots) - VS, 0);
     uint4 craw[kCodePre];
 #pragma unroll
     for (int j = 0; j < kCodePre; ++j)
@@ -1467,10 +1480,10 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     }
     __syncthreads();
     const int S = s_state[0], n = s_state[1], t = s_state[2];
-    const int nsb = (S + c.chunk - 1) / c.chunk;
+    const int nsb = (S + chunk - 1) / chunk;
     const bool full = n >= S;
-    const int len = max(min(s0 + c.chunk, n) - s0, 0);
-    if (split >= nsb) return;   // ragged batch: this sequence has fewer chunks
+    const int len = max(min(s0 + chunk, n) - s0, 0);
+    if (split >= nsb) return;   // (no block lies past its sequence's splits; kept as a guard)
 
     // the first tiles of every wave, in flight while the codes are computed
     constexpr int NB = ring_depth<GM, D, VQ>();
@@ -1613,7 +1626,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     const size_t hrec = (size_t)head * c.nsplit;
     MergeArgs ma{dev_rsrc(c.frec + hrec * G * D, (size_t)c.nsplit * G * D * 4),
                  dev_rsrc(c.fscal + hrec * G * 4, (size_t)c.nsplit * G * 16),
-                 dev_rsrc(c.cand_v + hrec * D, (size_t)c.nsplit * D * 4), G, nsb, r, c4, full, wkey0, c.chunk};
+                 dev_rsrc(c.cand_v + hrec * D, (size_t)c.nsplit * D * 4), G, nsb, r, c4, full, wkey0, chunk};
     const int per = (nsb + RS - 1) / RS;   // splits per thread
     MergeBlockSmem<D, GM>& mg = u.mg;
     static_assert(TPR == 16 || TPR == 32, "rows per wave");
@@ -2073,7 +2086,7 @@ hipError_t with_gm(const DevCache& c, F&& f)
 
 static dim3 fused_grid(const DevCache& c)
 {
-    return c.heads_fastest ? dim3(c.Hkv, c.B, c.nsplit) : dim3(c.nsplit, c.Hkv, c.B);
+    return c.ragged ? dim3(c.nblk * c.Hkv) : dim3(c.nsplit, c.Hkv, c.B);
 }
 
 hipError_t launch_decode_fused(const DevCache& c, const float* q, const void* k, const void* v, float* out,

@@ -24,7 +24,8 @@ HKV_DECODE_FUSED, HKV_DECODE_SPLIT = 0, 1
 
 # every symbol include/hkv.h declares
 EXPORTS = ("hkv_validate_config", "hkv_workspace_bytes", "hkv_create", "hkv_prefill",
-           "hkv_prefill_queries", "hkv_prefill_chunks", "hkv_decode_step", "hkv_decode_step_static", "hkv_destroy", "hkv_status_str", "hkv_last_error",
+           "hkv_prefill_queries", "hkv_prefill_chunks", "hkv_decode_step", "hkv_decode_step_static", "hkv_destroy",
+           "hkv_status_str", "hkv_last_error", "hkv_config_chunk",
            "hkv_get_state", "hkv_set_state", "hkv_debug_last_codes", "hkv_debug_prefill_codes",
            "hkv_debug_prefill_query_codes", "hkv_debug_scores", "hkv_encode", "hkv_attach_tier",
            "hkv_tier_counts", "hkv_attend_tiered")
@@ -61,6 +62,7 @@ def load():
     sig = {
         "hkv_validate_config": (I, [cfgp]),
         "hkv_workspace_bytes": (I, [cfgp, C.POINTER(Z)]),
+        "hkv_config_chunk": (I, [cfgp, C.POINTER(I)]),
         "hkv_create": (I, [cfgp, P, P, Z, P, C.POINTER(P)]),
         "hkv_prefill": (I, [P, P, P, P, I, P]),
         "hkv_prefill_queries": (I, [P, P, P, P, P, I, P]),
@@ -262,13 +264,13 @@ def to_numpy(t) -> np.ndarray:
     return t.numpy()
 
 
-def default_chunk(budgets, n_kv_heads: int) -> int:
-    """The split size hkv_config.chunk = 0 selects (include/hkv.h): about one
-    workgroup per compute unit, a multiple of 64 in [256, 65536]."""
-    slots = int(np.asarray(budgets, dtype=np.int64).sum()) * int(n_kv_heads)
-    ch = -(-slots // 256)
-    ch = -(-ch // 64) * 64
-    return min(max(ch, 256), 65536)
+def hkv_config_chunk(cfg) -> int:
+    """Slots per attention split the library uses for this configuration."""
+    out = C.c_int32(0)
+    s = load().hkv_config_chunk(C.byref(cfg), C.byref(out))
+    if s != HKV_OK:
+        raise HkvError(s, "hkv_config_chunk: invalid configuration")
+    return out.value
 
 
 class Cache:
@@ -295,7 +297,7 @@ class Cache:
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         self.h = hkv_create(self.cfg, R, self.workspace, stream)
         self.n_max = 0
-        self.chunk = int(chunk) or default_chunk(budgets, n_kv_heads)
+        self.chunk = hkv_config_chunk(self.cfg)
 
     def close(self):
         if getattr(self, "h", None):

@@ -94,16 +94,27 @@ def test_query_policy_validates_and_sizes_its_code_buffer(hkv):
 
 
 @pytest.mark.parametrize("budgets,heads", [([4096], 8), ([32768], 8), ([300], 1), ([1500, 800, 64], 2),
-                                           ([16384] * 8, 8), ([1 << 22], 1)])
-def test_default_chunk_matches_the_library(hkv, budgets, heads):
-    # hkv.Cache sizes its bookkeeping with the rule chunk = 0 selects; the
-    # workspace (which grows with the number of splits) must come out the same
-    from lsh_eviction_amd.hkv import default_chunk
-    ch = default_chunk(budgets, heads)
-    assert ch % 64 == 0 and 256 <= ch <= 65536
+                                           ([16384] * 8, 8), ([1 << 22], 1),
+                                           ([7854, 2092, 4800, 4801, 9600, 3000, 6100, 2500], 8)])
+def test_default_chunk(hkv, budgets, heads):
+    # chunk = 0: with equal budgets about one workgroup per compute unit,
+    # ceil(sum_b S_b * Hkv / 256) rounded up to 64 in [256, 65536]; with
+    # ragged ones a multiple of 64 from a quarter of that to the largest
+    # budget.  The workspace (which grows with the number of splits) comes
+    # out as with that chunk given explicitly.
+    slots = sum(budgets) * heads
+    plain = min(max(-(-(-(-slots // 256)) // 64) * 64, 256), 65536)
     kw = dict(batch=len(budgets), n_q_heads=4 * heads, n_kv_heads=heads, budgets=budgets,
               prefill_policy=hkv.HKV_PREFILL_TRUNCATE)
-    auto, fixed = _cfg(hkv, **kw), _cfg(hkv, chunk=ch, **kw)
+    auto = _cfg(hkv, **kw)
+    ch = hkv.hkv_config_chunk(auto)
+    assert ch % 64 == 0 and 256 <= ch <= 65536
+    if len(set(budgets)) == 1:
+        assert ch == plain
+    else:
+        assert max(256, -(-(plain // 4) // 64) * 64) <= ch <= max(plain, -(-max(budgets) // 64) * 64)
+    fixed = _cfg(hkv, chunk=ch, **kw)
+    assert hkv.hkv_config_chunk(fixed) == ch
     assert hkv.hkv_workspace_bytes(auto) == hkv.hkv_workspace_bytes(fixed)
     # and the comparison can tell split counts apart: half the chunk, more splits
     other = _cfg(hkv, chunk=ch // 2 // 64 * 64, **kw)
