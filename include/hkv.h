@@ -50,6 +50,12 @@
  *     anything is enqueued, so a call that fails validation has no effect.  A
  *     launch failure poisons the handle: every later call returns
  *     HKV_ERR_STATE.  hkv_last_error() gives a one-line reason.
+ *   - debugging (environment, read at hkv_create): HKV_DEBUG=1 synchronises
+ *     the stream after every call and reports a device error there;
+ *     HKV_DEBUG_NAN=1 fills the per-step partial results (split records,
+ *     candidate rows, tier partials) with NaN before every decode step and
+ *     tiered attention, so a read of one that the step did not write shows
+ *     as NaN in its output.
  *   - host tier (tier_capacity > 0, a reading of the TTKV page's slow DRAM
  *     tier): every token that leaves the cache -- the prompt tokens a prefill
  *     rule does not keep, in position order, then the token each full decode

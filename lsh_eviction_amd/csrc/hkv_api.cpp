@@ -26,6 +26,7 @@ struct hkv_cache {
     bool obs_codes = false;    // dbg_q holds a CHUNK prefill's observation codes
     bool poisoned = false;
     bool debug_sync = false;
+    bool debug_nan = false;    // HKV_DEBUG_NAN=1: partial results poisoned with NaN before each step
     std::string err;
 };
 
@@ -169,6 +170,8 @@ extern "C" hkv_status hkv_create(const hkv_config* cfg, const float* R_host, voi
     c->plens.assign(cfg->batch, 0);
     const char* dbg = getenv("HKV_DEBUG");
     c->debug_sync = dbg && dbg[0] == '1';
+    const char* dnan = getenv("HKV_DEBUG_NAN");
+    c->debug_nan = dnan && dnan[0] == '1';
     if (hipGetDevice(&c->device) != hipSuccess) c->device = 0;
 
     char* ws = (char*)workspace;
@@ -404,7 +407,9 @@ extern "C" hkv_status hkv_attend_tiered(hkv_cache* c, const float* q, float* out
     if (!aligned(q, 16) || !aligned(out, 16))
         return fail(c, HKV_ERR_INVALID_ARG, "hkv_attend_tiered: q and out must be 16-byte aligned");
     hipStream_t st = (hipStream_t)stream;
-    return check_launch(c, hkv::launch_attend_tiered(c->dev, q, out, st), st, "hkv_attend_tiered");
+    hipError_t e = c->debug_nan ? hkv::launch_poison_partials(c->dev, st) : hipSuccess;
+    if (e == hipSuccess) e = hkv::launch_attend_tiered(c->dev, q, out, st);
+    return check_launch(c, e, st, "hkv_attend_tiered");
 }
 
 extern "C" hkv_status hkv_decode_step(hkv_cache* c, const float* q, const void* k, const void* v,
@@ -418,9 +423,10 @@ extern "C" hkv_status hkv_decode_step(hkv_cache* c, const float* q, const void* 
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
         return fail(c, HKV_ERR_INVALID_ARG, "hkv_decode_step: q, k, v must be 16-byte aligned");
     hipStream_t st = (hipStream_t)stream;
-    hipError_t e = c->lay.schedule == HKV_DECODE_FUSED
-                       ? hkv::launch_decode_fused(c->dev, q, k, v, out, evicted_slot, st)
-                       : hkv::launch_decode_split(c->dev, q, k, v, out, evicted_slot, st);
+    hipError_t e = c->debug_nan ? hkv::launch_poison_partials(c->dev, st) : hipSuccess;
+    if (e == hipSuccess)
+        e = c->lay.schedule == HKV_DECODE_FUSED ? hkv::launch_decode_fused(c->dev, q, k, v, out, evicted_slot, st)
+                                                : hkv::launch_decode_split(c->dev, q, k, v, out, evicted_slot, st);
     s = check_launch(c, e, st, "hkv_decode_step");
     if (s == HKV_OK) {
         c->stepped = true;
@@ -457,6 +463,7 @@ extern "C" hkv_status hkv_decode_step_static(hkv_cache* c, const float* q, const
     // counters must start at zero (a kernel, not a memset, so the step can be
     // captured in a graph)
     hipError_t e = hkv::launch_clear_step_scratch(d, st);
+    if (e == hipSuccess && c->debug_nan) e = hkv::launch_poison_partials(d, st);
     if (e == hipSuccess)
         e = c->lay.schedule == HKV_DECODE_FUSED ? hkv::launch_decode_fused(d, q, k, v, out, evicted_slot, st)
                                                 : hkv::launch_decode_split(d, q, k, v, out, evicted_slot, st);

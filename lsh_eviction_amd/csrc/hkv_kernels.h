@@ -79,5 +79,9 @@ hipError_t launch_import_codes(const DevCache& c, const uint32_t* codes, hipStre
 hipError_t launch_export_pcodes(const DevCache& c, uint32_t* codes, int n_max, bool queries, hipStream_t st);
 // clears the per-step scratch (eviction keys) after a state import
 hipError_t launch_clear_step_scratch(const DevCache& c, hipStream_t st);
+// debug: fills the per-step partial results (fused records, split and tier
+// partials, candidate rows) with NaN, so a read of one not written by the
+// step that follows shows in its output
+hipError_t launch_poison_partials(const DevCache& c, hipStream_t st);
 
 }  // namespace hkv

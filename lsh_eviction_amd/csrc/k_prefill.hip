@@ -812,6 +812,33 @@ hipError_t launch_clear_step_scratch(const DevCache& c, hipStream_t st)
     return hipGetLastError();
 }
 
+// Fills n words with a quiet NaN (debug poisoning of per-step partial results).
+__global__ void k_fill_nan(uint32_t* __restrict__ p, size_t n)
+{
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0x7FC00000u;
+}
+
+static hipError_t fill_nan(float* p, size_t n, hipStream_t st)
+{
+    if (!p || n == 0) return hipSuccess;
+    const size_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(k_fill_nan, dim3((unsigned)(blocks < 2048 ? blocks : 2048)), dim3(256), 0, st,
+                       reinterpret_cast<uint32_t*>(p), n);
+    return hipGetLastError();
+}
+
+hipError_t launch_poison_partials(const DevCache& c, hipStream_t st)
+{
+    const size_t heads = (size_t)c.B * c.Hkv, qheads = (size_t)c.B * c.Hq;
+    hipError_t e = fill_nan(c.frec, heads * c.nsplit * c.G * c.d, st);
+    if (e == hipSuccess) e = fill_nan(c.fscal, heads * c.nsplit * c.G * 4, st);
+    if (e == hipSuccess) e = fill_nan(c.cand_v, heads * c.nsplit * c.d, st);
+    if (e == hipSuccess) e = fill_nan(c.part, qheads * c.nsplit * (c.d + 4), st);
+    if (e == hipSuccess && c.tpart) e = fill_nan(c.tpart, qheads * c.tsplit * (c.d + 4), st);
+    return e;
+}
+
 hipError_t launch_reset(const DevCache& c, hipStream_t st)
 {
     hipLaunchKernelGGL(k_reset, dim3((c.Smax + 255) / 256, c.Hkv, c.B), dim3(256), 0, st, c);

@@ -454,3 +454,55 @@ def test_set_state_rejects_bad_head_state():
     torch.cuda.synchronize()
     c.set_state(good)          # a valid checkpoint is still taken
     c.close()
+
+
+# Cases for the NaN-poisoned run: (shape, steps, schedule, chunk, value_bits, tier)
+POISON = {
+    "tiny_fused": (C.TINY, 24, FUSED, 0, 0, 0),
+    "tiny_split": (C.TINY, 24, SPLIT, 0, 0, 0),
+    "ragged_small_fused": (SMALL["ragged_small"][0], 6, FUSED, 0, 0, 0),
+    "ragged_small_split": (SMALL["ragged_small"][0], 6, SPLIT, 0, 0, 0),
+    "many_sequences": (SMALL["many_sequences"][0], 4, FUSED, 0, 0, 0),
+    "not_full_fused": (SMALL["not_full"][0], 8, FUSED, 0, 0, 0),
+    "not_full_split": (SMALL["not_full"][0], 8, SPLIT, 0, 0, 0),
+    "empty_prompt": (SMALL["empty_prompt"][0], 10, FUSED, 64, 0, 0),
+    "g4_lse_merge": (SMALL["g4_lse_merge"][0], 3, FUSED, 64, 0, 0),
+    "g16_two_batches": (SMALL["g16_two_batches"][0], 3, FUSED, 64, 0, 0),
+    "int8_ragged_small": (SMALL["ragged_small"][0], 4, FUSED, 0, 8, 0),
+    "int8_g16_lse_merge": (SMALL["g16_lse_merge"][0], 3, FUSED, 64, 8, 0),
+    "tier_llama8b_small": (C.LLAMA8B.scaled(prompt=3000, budget=1500), 4, FUSED, 0, 0, 8192),
+    "tier_tiny_split": (C.TINY, 8, SPLIT, 0, 0, 4096),
+}
+
+
+@pytest.mark.parametrize("name", list(POISON))
+def test_nan_poisoned_partials(name, monkeypatch):
+    """With HKV_DEBUG_NAN=1 every per-step partial result (fused records and
+    candidate rows, split partials, tier partials) holds NaN before each step;
+    parity still holds, so no step reads a partial it did not write."""
+    from hkv_harness import run_case
+    monkeypatch.setenv("HKV_DEBUG_NAN", "1")
+    shape, steps, schedule, chunk, value_bits, tier = POISON[name]
+    run_case(shape, steps, schedule=schedule, policy=STREAM, chunk=chunk, value_bits=value_bits, tier=tier)
+
+
+def test_nan_poison_reaches_the_workspace(monkeypatch):
+    """The switch above does poison: after a fused step the split partials,
+    which that schedule does not write, still hold the NaN pattern."""
+    import torch
+    from lsh_eviction_amd import datagen, hkv
+    monkeypatch.setenv("HKV_DEBUG_NAN", "1")
+    shape = C.TINY
+    wl = datagen.workload(shape, steps=1)
+    P, D = wl["prompt"], wl["decode"]
+    kvd = hkv.HKV_BF16 if shape.kv_dtype == "bf16" else hkv.HKV_F32
+    c = hkv.Cache(shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.n_bits, kvd,
+                  P.budgets, P.R, max_prompt=P.n_max)
+    c.prefill(hkv.to_device(P.K), hkv.to_device(P.V), P.prompt_lens)
+    c.decode_step(hkv.to_device(D.q[0]), hkv.to_device(D.k[0]), hkv.to_device(D.v[0]))
+    torch.cuda.synchronize()
+    words = c.workspace[: c.workspace.numel() // 4 * 4].view(torch.int32)
+    nan_words = int((words == 0x7FC00000).sum().item())
+    nsplit = -(-int(np.max(P.budgets)) // c.chunk)
+    assert nan_words >= shape.batch * shape.n_q_heads * nsplit * (shape.head_dim + 4)
+    c.close()
