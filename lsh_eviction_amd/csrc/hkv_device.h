@@ -12,6 +12,9 @@ namespace hkv {
 typedef uint16_t bf16_t;   // raw bf16 bits
 
 constexpr float kLog2e = 1.4426950408889634f;
+// Buffer resources: word 3 = 32-bit data format, no swizzle.  Reads past
+// num_records return zero.
+constexpr int kRsrcWord3 = 0x00020000;
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }

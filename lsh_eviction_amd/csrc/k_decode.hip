@@ -39,9 +39,8 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-// Buffer resources: word 3 = 32-bit data format, no swizzle.  Cache policy
-// sc1 = the agent-scope policy of a load or store (see the fused schedule).
-constexpr int kRsrcWord3 = 0x00020000;
+// Cache policy sc1 of a buffer load or store = the agent-scope policy (see
+// the fused schedule).
 constexpr int kCpolSC1 = 16;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 

@@ -6,6 +6,13 @@
 // matrix cores (fp32 MFMA 16x16x4: fp32 semantics, so the signs agree with an
 // fp64 reference outside the flagged band).
 //
+// bf16 keys take a second form of the same contraction on the bf16 matrix
+// cores: R is split by truncation into three bf16 parts, hi + mid + lo == R
+// exactly (the bf16x3 scheme of Henry, Tang and Heinecke, "Leveraging the
+// bfloat16 artificial intelligence datatype for higher-precision
+// computations", 2019), and each bf16 x bf16 product is exact in fp32, so
+// only the fp32 summation order differs from the fp32 kernel.
+//
 // Prefill rule (the page does not describe prefill; reading used here): with
 // the STREAM policy the prompt enters the cache one token at a time by the
 // decode rule, each token scored against its own key code; TRUNCATE keeps
@@ -185,11 +192,194 @@ __global__ __launch_bounds__(256) void k_project_mfma(DevCache c, const KT* __re
     }
 }
 
-// Blocks per head of the projection of n_max rows.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Codes of bf16 prompt rows on the bf16 matrix cores (MFMA 16x16x32): X is
+// [B][nh][n_max][D] bf16, codes go to dst[(b * nh + h) * pcode_slots + t].
+// R is split into bf16 parts hi + mid + lo == R (truncation: hi keeps the
+// top 8 significant bits of R, mid the top 8 of R - hi, lo the rest, at
+// most 8 bits), so x * part is exact in fp32.  The hi products and the
+// mid + lo products go to separate accumulators: the first carries the
+// rounding of an fp32 dot product of length D, the second is below 2^-7 of
+// the projection's magnitude, so the result stays within the error of an
+// fp32 dot product in any summation order, and its signs agree with an
+// exact projection outside the flagged band.
+//
+// The work is a stream of key rows, so the kernel is built to keep memory
+// busy: a persistent grid of as many blocks as the compute units hold, each
+// wave holding all of R's parts in registers and a ring of NB tiles in
+// flight.  Block k takes a contiguous run of the 64-row tiles of all heads
+// (tiles_per_head per head); wave w takes rows 16 w .. 16 w + 15 of a tile.
+// Lane l feeds row l % 16 and dimensions 32 s + 8 (l / 16) .. + 7 of MFMA
+// step s, and holds the same dimensions of R's column (tile * 16 + l % 16).
+// Rows past the prompt (and tiles past the last) read as zero through the
+// buffer resource, so every load is issued and the ring's waits are exact.
+template <int D, int BITS>
+__global__ __launch_bounds__(256, 1) void k_project_bf16x3(DevCache c, const bf16_t* __restrict__ Kp, int n_max,
+                                                           int nh, int tiles_per_head, int total_tiles,
+                                                           void* __restrict__ dst)
+{
+    using CT = typename CodeT<BITS>::T;
+    constexpr int NT = BITS / 16;            // bit tiles
+    constexpr int KS = D / 32;               // MFMA steps over the head dimension
+    constexpr int NB = BITS > 32 ? 4 : 6;    // tiles in flight per wave (register budget)
+    constexpr int LDR = D + 8;               // R^T row in LDS, padded by 16 bytes
+    constexpr int NR4 = D * BITS / 4, RPT = NR4 / 256;
+    static_assert(NR4 % 256 == 0 && BITS % 4 == 0, "R staging shape");
+    __shared__ __align__(16) uint16_t sRT[3][BITS][LDR];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int qd = lane >> 4, col = lane & 15;
+    const int lane_off = (wave * 16 + col) * (D * 2) + qd * 16;   // byte offset in a tile
+
+    // block k takes the contiguous tiles [t_begin, t_end) of the stream of
+    // all heads' tiles, so each block reads one run of memory
+    const int t_begin = (int)((long long)total_tiles * blockIdx.x / gridDim.x);
+    const int t_end = (int)((long long)total_tiles * (blockIdx.x + 1) / gridDim.x);
+    auto issue = [&](int tau, uint4 (&r)[KS]) {
+        const bf16_t* base = Kp;
+        int bytes = 0;
+        if (tau < t_end) {
+            const int head = tau / tiles_per_head, t0 = (tau - head * tiles_per_head) * 64;
+            base = Kp + ((size_t)head * n_max + t0) * D;
+            bytes = max(min(c.plen[head / nh] - t0, 64), 0) * D * 2;
+        }
+        // uniform, but computed by a vector instruction (v_med3): kept in a
+        // scalar register so the resource is scalar and no load is waterfalled
+        bytes = __builtin_amdgcn_readfirstlane(bytes);
+        const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(base), 0, bytes, kRsrcWord3);
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            r[s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane_off + 64 * s, 0, 0));
+    };
+    // R is requested first (waits are in order of issue: a wait for R issued
+    // after the ring would drain the ring), then the first tiles, which are
+    // in flight while R is split
+    float4 rr[RPT];
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) rr[j] = reinterpret_cast<const float4*>(c.R)[threadIdx.x + j * 256];
+    uint4 ring[NB][KS];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) issue(t_begin + k, ring[k]);
+    {
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) {
+            const int i = 4 * ((int)threadIdx.x + j * 256), dim = i / BITS, bit0 = i % BITS;
+            const float v[4] = {rr[j].x, rr[j].y, rr[j].z, rr[j].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t hb = __float_as_uint(v[e]) & 0xFFFF0000u;
+                const float r1 = v[e] - __uint_as_float(hb);   // exact: the low 16 bits
+                const uint32_t mb = __float_as_uint(r1) & 0xFFFF0000u;
+                const float r2 = r1 - __uint_as_float(mb);     // exact, at most 8 significant bits
+                sRT[0][bit0 + e][dim] = (uint16_t)(hb >> 16);
+                sRT[1][bit0 + e][dim] = (uint16_t)(mb >> 16);
+                sRT[2][bit0 + e][dim] = (uint16_t)(__float_as_uint(r2) >> 16);
+            }
+        }
+    }
+    __syncthreads();
+    bf16x8 Rf[NT][KS][3];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+                Rf[nt][s][p] = *reinterpret_cast<const bf16x8*>(&sRT[p][nt * 16 + col][32 * s + 8 * qd]);
+
+    // Whole rounds of the ring: the block's tile count is rounded up to a
+    // multiple of NB, and the tiles past the last read nothing (a resource
+    // of size 0) and store nothing.  No exit inside a round: with one, the
+    // compiler sinks each prefetch down to its use and the ring is lost.
+    for (int i0 = t_begin; i0 < t_end; i0 += NB) {
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const int tau = i0 + k;
+            const bool valid = tau < t_end;
+            const int head = valid ? tau / tiles_per_head : 0;
+            const int t0 = valid ? (tau - head * tiles_per_head) * 64 : 0;
+            const int N = valid ? c.plen[head / nh] : 0;
+            f32x4 ah[NT], am[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) ah[nt] = am[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const bf16x8 a = __builtin_bit_cast(bf16x8, ring[k][s]);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    ah[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, Rf[nt][s][0], ah[nt], 0, 0, 0);
+                    am[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, Rf[nt][s][1], am[nt], 0, 0, 0);
+                    am[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, Rf[nt][s][2], am[nt], 0, 0, 0);
+                }
+            }
+            // the ring slot is free once the products have read it
+            issue(tau + NB, ring[k]);
+            unsigned long long mk[NT][4];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const f32x4 y = ah[nt] + am[nt];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) mk[nt][r] = __ballot(y[r] > 0.f);
+            }
+            // result row i = 4 * (lane / 16) + r sits in register r of lanes 16 * (i / 4) + col
+            if (lane < 16) {
+                const int a = lane >> 2, r = lane & 3;
+                unsigned long long cde = 0;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    unsigned long long m = 0;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) m |= mk[nt][q] & (0ull - (unsigned long long)(r == q));
+                    cde |= ((m >> (16 * a)) & 0xFFFFull) << (16 * nt);
+                }
+                const int t = t0 + wave * 16 + lane;
+                if (t < N) reinterpret_cast<CT*>(dst)[(size_t)head * c.pcode_slots + t] = (CT)cde;
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // the last round's prefetches (of nothing) land before the wave ends
+}
+
+// Resident workgroups of a 256-thread kernel on the current device (every
+// compute unit times the blocks one holds), the size of a persistent grid.
+static int resident_blocks(const void* kernel)
+{
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    return cus * (per_cu > 0 ? per_cu : 1);
+}
+
+// Blocks per head of the fp32 projection of n_max rows.
 static int proj_blocks(int n_max)
 {
     const int tiles = (n_max + 63) / 64;
     return tiles < kProjMaxBlocks ? tiles : kProjMaxBlocks;
+}
+
+// Prompt key codes: bf16 keys on the bf16 matrix cores (bf16x3), fp32 keys
+// on the fp32 ones.
+template <int D, int BITS, typename KT>
+hipError_t launch_project_keys(const DevCache& c, const void* K, int n_max, hipStream_t st)
+{
+    if constexpr (std::is_same<KT, bf16_t>::value) {
+        const int per_head = (n_max + 63) / 64;
+        const long long total = (long long)per_head * c.B * c.Hkv;
+        if (total <= 0) return hipSuccess;
+        if (total > INT32_MAX) return hipErrorInvalidValue;
+        static const int resident = resident_blocks((const void*)k_project_bf16x3<D, BITS>);
+        const int grid = total < resident ? (int)total : resident;
+        hipLaunchKernelGGL((k_project_bf16x3<D, BITS>), dim3(grid), dim3(256), 0, st, c, (const bf16_t*)K, n_max,
+                           c.Hkv, per_head, (int)total, c.pcode);
+    } else {
+        hipLaunchKernelGGL((k_project_mfma<D, BITS, KT>), dim3(proj_blocks(n_max), c.Hkv, c.B), dim3(256), 0, st,
+                           c, (const KT*)K, n_max, c.Hkv, c.pcode);
+    }
+    return hipGetLastError();
 }
 
 template <int CTRL>
@@ -878,9 +1068,7 @@ hipError_t launch_prefill(const DevCache& c, const void* K, const void* V, const
         return with_d_kv(c, [&](auto dd, auto kt) {
             constexpr int D = decltype(dd)::value;
             using KT = decltype(kt);
-            hipLaunchKernelGGL((k_project_mfma<D, BITS, KT>), dim3(proj_blocks(n_max), c.Hkv, c.B),
-                               dim3(256), 0, st, c, (const KT*)K, n_max, c.Hkv, c.pcode);
-            hipError_t e = hipGetLastError();
+            hipError_t e = launch_project_keys<D, BITS, KT>(c, K, n_max, st);
             if (e != hipSuccess) return e;
             if (policy == HKV_PREFILL_STREAM) {
                 e = launch_select<BITS, 0>(c, st);
@@ -912,9 +1100,7 @@ hipError_t launch_prefill_chunks(const DevCache& c, const void* K, const void* V
             constexpr int D = decltype(dd)::value;
             using KT = decltype(kt);
             if (n_max > 0) {
-                hipLaunchKernelGGL((k_project_mfma<D, BITS, KT>), dim3(proj_blocks(n_max), c.Hkv, c.B),
-                                   dim3(256), 0, st, c, (const KT*)K, n_max, c.Hkv, c.pcode);
-                hipError_t e = hipGetLastError();
+                hipError_t e = launch_project_keys<D, BITS, KT>(c, K, n_max, st);
                 if (e != hipSuccess) return e;
             }
             if (q_obs) {
