@@ -43,6 +43,8 @@ SMALL = {
                       kv_dtype="f32", prompt=600, budget=300, steps=6, key_outliers=False), 6, 64),
     # many sequences of short, uneven budgets (KV-head-fastest grid numbering)
     "many_sequences": (C.RAGGED.scaled(batch=40, prompt_range=(300, 900)), 6, 0),
+    # ragged budgets cut into several equal splits each, run longest first
+    "ragged_equal_splits": (C.RAGGED.scaled(batch=6, prompt_range=(700, 2600)), 6, 448),
     # the fused step's last block merges up to 512 (split, head) records
     # against one common maximum per head, in one or more batches of splits,
     # and more records with a running log-sum-exp
