@@ -369,17 +369,17 @@ def main():
                     caches[i].decode_step(qs[i % POOL], ks[i % POOL], vs[i % POOL], outs[i], evs[i], s, check=False)
         torch.cuda.synchronize()
 
-    for i in range(args.warmup):
-        one(i)
-    torch.cuda.synchronize()
-
     K_ = args.steps
     t_wall = time.perf_counter()
     e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    # A bounded spin kernel ahead of the start event holds the stream while the
-    # host enqueues the timed launches, so the region measures the GPU's steps
+    # A bounded spin kernel holds the stream while the host enqueues the
+    # warm-up and the timed launches; the warm-up steps then run back to back
+    # right before the start event, so the region measures the GPU's steps
     # back to back and not the host's first launch latency.
+    torch.cuda.synchronize()
     torch.cuda._sleep(HOLD_CYCLES)
+    for i in range(args.warmup):
+        one(i)
     if graph is not None:
         reps = max(1, K_ // L)
         K_ = reps * L
