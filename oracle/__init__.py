@@ -60,7 +60,7 @@ def lib():
         L.orc_prefill_query.argtypes = [P, C.c_int, P, P, P, P, P]
         L.orc_set_value_bits.argtypes = [P, C.c_int]
         L.orc_set_value_bits.restype = C.c_int
-        L.orc_quantize_row.argtypes = [P, C.c_int, P, P]
+        L.orc_quantize_row.argtypes = [P, C.c_int, C.c_int, P, P]
         L.orc_get_value_codes.argtypes = [P, P, P]
         L.orc_set_value_codes.argtypes = [P, P, P]
         L.orc_prefill_query.restype = C.c_int
@@ -122,7 +122,7 @@ class OracleHead:
             raise ValueError("orc_create rejected its arguments")
         self.value_bits = int(value_bits)
         if lib().orc_set_value_bits(self._h, self.value_bits) != 0:
-            raise ValueError("value_bits must be 0 or 8")
+            raise ValueError("value_bits must be 0, 4 or 8")
         self.tier_cap = int(tier)
         if self.tier_cap >= 0 and lib().orc_set_tier(self._h, self.tier_cap) != 0:
             raise ValueError("a host tier needs values stored as given")
@@ -237,7 +237,8 @@ class OracleHead:
         return {"K": K[:k], "V": V[:k], "tok": tok[:k], "count": count}
 
     def value_codes(self):
-        """int8 codes [budget][d] and fp32 scales [budget] of an int8-value cache."""
+        """Codes [budget][d] (one int8 per element) and fp32 scales [budget] of a
+        cache with quantized values."""
         S = max(self.budget, 0)
         q = np.zeros((S, self.d), np.int8)
         sc = np.zeros(S, np.float32)
@@ -245,8 +246,9 @@ class OracleHead:
         return q, sc
 
     def set_value_codes(self, q: np.ndarray, scale: np.ndarray):
-        """Import int8 codes [budget][d] and fp32 scales [budget] of an int8-value
-        cache; the held values become code * scale."""
+        """Import codes [budget][d] (one int8 per element) and fp32 scales
+        [budget] of a cache with quantized values; the held values become
+        code * scale."""
         S = max(self.budget, 0)
         q = np.ascontiguousarray(q, np.int8).reshape(S, self.d)
         sc = np.ascontiguousarray(scale, np.float32).reshape(S)
@@ -268,15 +270,16 @@ class OracleHead:
         lib().orc_set_state(self._h, _p(K), _p(V), _p(code), _p(tok), int(st["n"]), int(st["t"]))
 
 
-def quantize_rows(V: np.ndarray):
-    """The value-compression rule applied to rows V[..][d]: int8 codes, fp32 scales."""
+def quantize_rows(V: np.ndarray, bits: int = 8):
+    """The value-compression rule at `bits` (8 or 4) applied to rows V[..][d]:
+    codes (one int8 per element), fp32 scales."""
     V = _f64(V)
     d = V.shape[-1]
     flat = V.reshape(-1, d)
     q = np.zeros(flat.shape, np.int8)
     sc = np.zeros(flat.shape[0], np.float32)
     for i in range(flat.shape[0]):
-        lib().orc_quantize_row(_p(flat[i]), d, _p(q[i]), _p(sc[i:i + 1]))
+        lib().orc_quantize_row(_p(flat[i]), d, int(bits), _p(q[i]), _p(sc[i:i + 1]))
     return q.reshape(V.shape), sc.reshape(V.shape[:-1])
 
 

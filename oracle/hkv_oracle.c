@@ -28,9 +28,9 @@ struct orc_head {
     int64_t* tok;     /* [budget]  token position held by the slot, -1 if empty */
     int n;            /* occupancy: slots 0 .. n-1 hold tokens */
     int64_t t;        /* position of the next token */
-    int vbits;        /* 0: values kept as given; 8: int8 codes with a per-row scale */
-    int8_t* vq;       /* [budget][d] value codes (vbits == 8) */
-    float* vs;        /* [budget]    value scales (vbits == 8) */
+    int vbits;        /* 0: values kept as given; 8 or 4: codes of that width with a per-row scale */
+    int8_t* vq;       /* [budget][d] value codes, one per element (vbits != 0) */
+    float* vs;        /* [budget]    value scales (vbits != 0) */
     int tcap;         /* host tier: capacity in tokens, -1 when there is no tier */
     int64_t tcount;   /* tokens sent to the tier (may exceed tcap; the excess is not kept) */
     double* tK;       /* [tcap][d] */
@@ -139,26 +139,29 @@ static int pick_victim(const orc_head* h, const uint32_t* qcodes, int ngroup)
 
 /* READING of the value compression (the DASH-KV summary page, "Value
  * compression strategy": values tolerate a coarser quantization than keys
- * because the output is their weighted average; it gives no rule).  One row
- * of d values (exact fp32 / bf16 numbers) becomes d int8 codes and one fp32
- * scale, all in fp32 arithmetic: scale = max_i |v_i| / 127; code_i = v_i /
- * scale rounded to nearest, ties to even, clamped to [-127, 127]; a zero row
- * has scale 0 and codes 0.  The value the cache holds is code_i * scale. */
-void orc_quantize_row(const double* v, int d, int8_t* q, float* scale)
+ * because the output is their weighted average; it gives no rule, and its
+ * introduction names INT8 "or lower").  One row of d values (exact fp32 /
+ * bf16 numbers) becomes d signed codes of `bits` bits (8 or 4) and one fp32
+ * scale, all in fp32 arithmetic, with Q = 2^(bits-1) - 1 (127 or 7):
+ * scale = max_i |v_i| / Q; code_i = v_i / scale rounded to nearest, ties to
+ * even, clamped to [-Q, Q]; a zero row has scale 0 and codes 0.  The value
+ * the cache holds is code_i * scale. */
+void orc_quantize_row(const double* v, int d, int bits, int8_t* q, float* scale)
 {
+    const float Q = (float)((1 << (bits - 1)) - 1);
     float amax = 0.0f;
     for (int i = 0; i < d; ++i) {
         const float a = fabsf((float)v[i]);
         if (a > amax) amax = a;
     }
-    const float sc = amax / 127.0f;
+    const float sc = amax / Q;
     for (int i = 0; i < d; ++i) {
         float c = 0.0f;
         if (sc > 0.0f) {
             const float x = (float)v[i] / sc;
             c = rintf(x);
-            if (c > 127.0f) c = 127.0f;
-            if (c < -127.0f) c = -127.0f;
+            if (c > Q) c = Q;
+            if (c < -Q) c = -Q;
         }
         q[i] = (int8_t)c;
     }
@@ -170,9 +173,9 @@ static void write_slot(orc_head* h, int e, const double* k, const double* v, con
                        int64_t pos)
 {
     memcpy(h->K + (size_t)e * h->d, k, sizeof(double) * h->d);
-    if (h->vbits == 8) {
+    if (h->vbits != 0) {
         int8_t* q = h->vq + (size_t)e * h->d;
-        orc_quantize_row(v, h->d, q, &h->vs[e]);
+        orc_quantize_row(v, h->d, h->vbits, q, &h->vs[e]);
         for (int i = 0; i < h->d; ++i) h->V[(size_t)e * h->d + i] = (double)q[i] * (double)h->vs[e];
     } else {
         memcpy(h->V + (size_t)e * h->d, v, sizeof(double) * h->d);
@@ -523,13 +526,13 @@ void orc_scores(const orc_head* h, const uint32_t* qcodes, int32_t* scores)
         scores[s] = s < h->n ? gqa_score(h, qcodes, h->group, s) : -1;
 }
 
-/* Store values as int8 codes with a per-row scale (bits = 8) or as given
- * (bits = 0).  Only on an empty cache; returns 0, or -1. */
+/* Store values as 8- or 4-bit codes with a per-row scale (bits = 8 or 4)
+ * or as given (bits = 0).  Only on an empty cache; returns 0, or -1. */
 int orc_set_value_bits(orc_head* h, int bits)
 {
-    if (h->n != 0 || (bits != 0 && bits != 8) || (bits == 8 && h->tcap >= 0)) return -1;
+    if (h->n != 0 || (bits != 0 && bits != 8 && bits != 4) || (bits != 0 && h->tcap >= 0)) return -1;
     h->vbits = bits;
-    if (bits == 8 && !h->vq) {
+    if (bits != 0 && !h->vq) {
         size_t slots = h->budget > 0 ? (size_t)h->budget : 1;
         h->vq = (int8_t*)calloc(slots * h->d, 1);
         h->vs = (float*)calloc(slots, sizeof(float));
@@ -537,10 +540,11 @@ int orc_set_value_bits(orc_head* h, int bits)
     return 0;
 }
 
-/* Value codes [budget][d] and scales [budget] of an int8-value cache. */
+/* Value codes [budget][d] (one per element, whatever their width) and
+ * scales [budget] of a cache with quantized values. */
 void orc_get_value_codes(const orc_head* h, int8_t* q, float* scale)
 {
-    if (h->vbits != 8) return;
+    if (h->vbits == 0) return;
     size_t S = (size_t)h->budget;
     if (q) memcpy(q, h->vq, S * h->d);
     if (scale) memcpy(scale, h->vs, S * sizeof(float));
@@ -549,7 +553,7 @@ void orc_get_value_codes(const orc_head* h, int8_t* q, float* scale)
 /* Restore value codes and scales (the held values become code * scale). */
 void orc_set_value_codes(orc_head* h, const int8_t* q, const float* scale)
 {
-    if (h->vbits != 8) return;
+    if (h->vbits == 0) return;
     size_t S = (size_t)h->budget;
     memcpy(h->vq, q, S * h->d);
     memcpy(h->vs, scale, S * sizeof(float));

@@ -86,16 +86,17 @@ int64_t orc_get_tier(const orc_head* h, double* K, double* V, int64_t* tok);
 /* Attention over the cache and the tier's kept tokens: out [group][d]. */
 void orc_attend_tiered(const orc_head* h, const double* q, double* out);
 
-/* Value compression (a reading; see the .c file): bits = 8 stores every
- * value row as int8 codes with one fp32 scale (fp32 arithmetic: scale =
- * max|v| / 127, code = round-half-even(v / scale) clamped to +-127) and the
- * cache then holds code * scale; bits = 0 stores values as given.  Only on an
- * empty cache; returns 0, or -1. */
+/* Value compression (a reading; see the .c file): bits = 8 or 4 stores every
+ * value row as signed codes of that width with one fp32 scale (fp32
+ * arithmetic, Q = 127 or 7: scale = max|v| / Q, code = round-half-even(v /
+ * scale) clamped to +-Q) and the cache then holds code * scale; bits = 0
+ * stores values as given.  Only on an empty cache; returns 0, or -1. */
 int orc_set_value_bits(orc_head* h, int bits);
-/* The rule on one row: q [d] codes, *scale. */
-void orc_quantize_row(const double* v, int d, int8_t* q, float* scale);
-/* Codes [budget][d] and scales [budget] of an int8-value cache (export,
- * import; import sets the held values to code * scale). */
+/* The rule on one row at the given width: q [d] codes, *scale. */
+void orc_quantize_row(const double* v, int d, int bits, int8_t* q, float* scale);
+/* Codes [budget][d] (one int8 per element) and scales [budget] of a cache
+ * with quantized values (export, import; import sets the held values to
+ * code * scale). */
 void orc_get_value_codes(const orc_head* h, int8_t* q, float* scale);
 void orc_set_value_codes(orc_head* h, const int8_t* q, const float* scale);
 

@@ -145,17 +145,21 @@ int main(void)
     run_case(32, 32, 25, 3, 70, ORC_PREFILL_CHUNK, 0, 100, 8);
     run_case(128, 64, 12, 16, 30, ORC_PREFILL_STREAM, 0, 8, 6);   /* tier overflows */
     run_case(64, 16, 40, 2, 10, ORC_PREFILL_STREAM, 8, -1, 35);    /* fills, then evicts */
+    run_case(64, 32, 21, 4, 60, ORC_PREFILL_CHUNK, 4, -1, 10);     /* 4-bit values */
     run_case(32, 16, 8, 1, 0, ORC_PREFILL_STREAM, 0, -1, 12);      /* empty prompt */
     /* quantisation of single rows, zero row included */
     {
         double v[16] = {0};
         int8_t q[16];
         float s = -1.f;
-        orc_quantize_row(v, 16, q, &s);
+        orc_quantize_row(v, 16, 8, q, &s);
         CHECK(s == 0.f);
         for (int i = 0; i < 16; ++i) v[i] = nrand();
-        orc_quantize_row(v, 16, q, &s);
+        orc_quantize_row(v, 16, 8, q, &s);
         CHECK(s > 0.f);
+        orc_quantize_row(v, 16, 4, q, &s);
+        CHECK(s > 0.f);
+        for (int i = 0; i < 16; ++i) CHECK(q[i] >= -7 && q[i] <= 7);
     }
     /* rejected arguments */
     {
