@@ -33,13 +33,13 @@ DEFAULT_WORKLOAD = "long_128k"
 def step_bytes(shape, budgets, value_bits: int = 0) -> int:
     """Algorithmic HBM bytes of one decode step: per cached slot and KV head the
     code (b/8 bytes), the K row (d * kv bytes) and the V row (d * kv bytes, or
-    d int8 codes and a 4-byte scale) are read; per KV head the new k, v, code
+    d codes of value_bits bits and a 4-byte scale) are read; per KV head the new k, v, code
     and position are written; q is read and out written (fp32)."""
     es = 2 if shape.kv_dtype == "bf16" else 4
     cb = shape.n_bits // 8
     H, d = shape.n_kv_heads, shape.head_dim
     slots = int(sum(int(s) for s in budgets)) * H
-    vrow = d + 4 if value_bits == 8 else d * es
+    vrow = d * value_bits // 8 + 4 if value_bits else d * es
     per_slot = cb + d * es + vrow
     writes = shape.batch * H * (d * es + vrow + cb + 4)
     qo = shape.batch * shape.n_q_heads * d * 4 * 2
@@ -261,8 +261,8 @@ def main():
     ap.add_argument("--config", default=DEFAULT_WORKLOAD)
     ap.add_argument("--schedule", default="fused", choices=["fused", "split"])
     ap.add_argument("--chunk", type=int, default=0)
-    ap.add_argument("--value-bits", type=int, default=0, choices=[0, 8],
-                    help="8: values kept as int8 codes with a per-row scale (a different workload)")
+    ap.add_argument("--value-bits", type=int, default=0, choices=[0, 4, 8],
+                    help="8 or 4: values kept as codes of that width with a per-row scale (a different workload)")
     ap.add_argument("--prefill", default="stream", choices=["stream", "truncate", "query", "chunk"],
                     help="prefill rule of the layer caches (timed per layer, not part of a step)")
     ap.add_argument("--layers", type=int, default=0, help="layer caches rotated (0 = enough to exceed the MALL twice)")
@@ -426,7 +426,7 @@ def main():
     ms_per_step = total_ms / K_
     value = 1000.0 / ms_per_step
     achieved = per_step / (kern_ms * 1e-3) / 1e9
-    traffic = load_traffic(args.config, args.schedule + ("/v8" if args.value_bits == 8 else ""))
+    traffic = load_traffic(args.config, args.schedule + (f"/v{args.value_bits}" if args.value_bits else ""))
     rec = {
         "metric": "decode steps/s (LSH score+evict+attend) & % HBM peak, 8B-shape 128K ctx",
         "value": round(value, 1),
@@ -438,7 +438,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": shape.kv_dtype if args.value_bits == 0 else shape.kv_dtype + "+i8",
+        "dtype": shape.kv_dtype if args.value_bits == 0 else f"{shape.kv_dtype}+i{args.value_bits}",
         "data": "synthetic",
         "config": {"workload": shape.name, "batch": shape.batch, "n_q_heads": shape.n_q_heads,
                    "n_kv_heads": shape.n_kv_heads, "head_dim": shape.head_dim, "n_bits": shape.n_bits,

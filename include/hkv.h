@@ -62,9 +62,9 @@
  *     step evicts, in step order -- is appended to caller-owned tier buffers
  *     (normally pinned host memory) instead of being dropped, and
  *     hkv_attend_tiered attends over the cache and the tier together.
- *   - values (value_bits = 8, a reading of the DASH-KV page's value
- *     compression): V rows are kept as int8 codes with a per-row fp32 scale;
- *     keys, codes and eviction are unchanged.  Inputs stay kv dtype; the
+ *   - values (value_bits = 8 or 4, a reading of the DASH-KV page's value
+ *     compression): V rows are kept as int8 or 4-bit codes with a per-row
+ *     fp32 scale; keys, codes and eviction are unchanged.  Inputs stay kv dtype; the
  *     library quantizes when it stores a row.
  *   - supported: n_bits in {16, 32, 64}; head_dim in {64, 128};
  *     n_q_heads % n_kv_heads == 0 with G = n_q_heads / n_kv_heads <= 16;
@@ -123,12 +123,14 @@ typedef struct {
                                 the largest budget, the chunk whose blocks a
                                 model of the dispatch (8 XCDs of 32 compute
                                 units) finishes first */
-    int32_t value_bits;      /* 0: values stored in kv_dtype; 8: each value row
-                                stored as d int8 codes and one fp32 scale
-                                (scale = max|v| / 127, code = v / scale rounded
-                                half to even, clamped to +-127, in fp32; the
-                                cache holds code * scale).  8 needs kv_dtype
-                                HKV_BF16 and HKV_DECODE_FUSED */
+    int32_t value_bits;      /* 0: values stored in kv_dtype; 8 or 4: each
+                                value row stored as d signed codes of that
+                                width and one fp32 scale (Q = 127 or 7:
+                                scale = max|v| / Q, code = v / scale rounded
+                                half to even, clamped to +-Q, in fp32; the
+                                cache holds code * scale; 4-bit codes two a
+                                byte, element 2i in the low half of byte i).
+                                Needs kv_dtype HKV_BF16 and HKV_DECODE_FUSED */
     int32_t prefill_chunk;   /* tokens per chunk under HKV_PREFILL_CHUNK: 0
                                 selects 10, else 1 .. 32; must be 0 under the
                                 other policies */
@@ -284,8 +286,9 @@ const char* hkv_last_error(const hkv_cache* c);
  * K, V [B][Hkv][Smax][d] kv dtype; codes [B][Hkv][Smax][W] uint32 with
  * W = ceil(b/32) (unused high bits zero); slot_token [B][Hkv][Smax] int32
  * (-1 = empty slot); head_state [B][Hkv][2] int32 = (occupancy, next position).
- * With value_bits = 8, V is [B][Hkv][Smax][d] int8 codes followed by
- * [B][Hkv][Smax] fp32 scales (B*Hkv*Smax*(d + 4) bytes). */
+ * With value_bits = 8 or 4, V is [B][Hkv][Smax][d * value_bits / 8] bytes of
+ * codes (int8, or two 4-bit codes a byte as stored) followed by
+ * [B][Hkv][Smax] fp32 scales (B*Hkv*Smax*(d * value_bits / 8 + 4) bytes). */
 hkv_status hkv_get_state(const hkv_cache* c, void* K, void* V, uint32_t* codes,
                          int32_t* slot_token, int32_t* head_state, void* stream);
 /* Checkpoint import, same layouts; all five buffers required.  Marks the

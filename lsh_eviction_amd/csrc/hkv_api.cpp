@@ -196,7 +196,7 @@ extern "C" hkv_status hkv_create(const hkv_config* cfg, const float* R_host, voi
     d.pcode = ws + L.off_pcode;
     d.qcode = ws + L.off_qcode;
     d.vs = (float*)(ws + L.off_vs);
-    d.vq = L.value_bits == 8;
+    d.vbits = L.value_bits;
     d.B = L.B; d.Hq = L.Hq; d.Hkv = L.Hkv; d.G = L.G; d.d = L.d; d.bits = L.bits; d.W = L.W;
     d.Smax = L.Smax; d.chunk = L.chunk; d.nsplit = L.nsplit;
     d.ragged = L.nblk > 0;
@@ -231,7 +231,7 @@ extern "C" hkv_status hkv_create(const hkv_config* cfg, const float* R_host, voi
     }
     if (e == hipSuccess) e = hkv::launch_reset(d, st);
     // value scales start at zero (the attention tile reads the scales of 16 rows at once)
-    if (e == hipSuccess && L.value_bits == 8)
+    if (e == hipSuccess && L.value_bits != 0)
         e = hipMemsetAsync(d.vs, 0, ((size_t)L.B * L.Hkv * L.Smax + 16) * 4, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     if (e != hipSuccess) {
@@ -488,7 +488,7 @@ extern "C" hkv_status hkv_get_state(const hkv_cache* cc, void* K, void* V, uint3
     hipError_t e = hipSuccess;
     if (K) e = hipMemcpyAsync(K, c->dev.K, kv, hipMemcpyDeviceToDevice, st);
     if (e == hipSuccess && V) e = hipMemcpyAsync(V, c->dev.V, L.v_bytes, hipMemcpyDeviceToDevice, st);
-    if (e == hipSuccess && V && L.value_bits == 8)
+    if (e == hipSuccess && V && L.value_bits != 0)
         e = hipMemcpyAsync((char*)V + L.v_bytes, c->dev.vs, heads * L.Smax * 4, hipMemcpyDeviceToDevice, st);
     if (e == hipSuccess && codes) e = hkv::launch_export_codes(c->dev, codes, st);
     if (e == hipSuccess && slot_token)
@@ -527,7 +527,7 @@ extern "C" hkv_status hkv_set_state(hkv_cache* c, const void* K, const void* V, 
     }
     e = hipMemcpyAsync(c->dev.K, K, kv, hipMemcpyDeviceToDevice, st);
     if (e == hipSuccess) e = hipMemcpyAsync(c->dev.V, V, L.v_bytes, hipMemcpyDeviceToDevice, st);
-    if (e == hipSuccess && L.value_bits == 8)
+    if (e == hipSuccess && L.value_bits != 0)
         e = hipMemcpyAsync(c->dev.vs, (const char*)V + L.v_bytes, heads * L.Smax * 4, hipMemcpyDeviceToDevice, st);
     if (e == hipSuccess) e = hkv::launch_import_codes(c->dev, codes, st);
     if (e == hipSuccess) e = hipMemcpyAsync(c->dev.tok, slot_token, heads * L.Smax * 4, hipMemcpyDeviceToDevice, st);

@@ -124,6 +124,20 @@ __device__ __forceinline__ uint2 quantize8(const float (&f)[8], float scale)
     return make_uint2(w[0], w[1]);
 }
 
+// Eight values -> eight 4-bit codes v / scale, rounded half to even, clamped
+// to +-7, packed two per byte (element 2i in the low half of byte i); all
+// zero when scale is 0.
+__device__ __forceinline__ uint32_t quantize4(const float (&f)[8], float scale)
+{
+    uint32_t w = 0u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float cq = scale > 0.f ? fminf(fmaxf(rintf(f[e] / scale), -7.f), 7.f) : 0.f;
+        w |= ((uint32_t)(int32_t)cq & 0xFu) << (4 * e);
+    }
+    return w;
+}
+
 // 64-bit lane exchanges, as two 32-bit halves moved the same way
 template <int CTRL>
 __device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v)

@@ -34,7 +34,7 @@ struct DevCache {
     int ragged;                     // budgets differ: the fused step runs the block list `blk`
     const uint2* blk;               // [nblk] (b | split << 16, split length) of each fused block, longest first
     int nblk;
-    bool vq;                        // values stored as int8 codes + scales
+    int vbits;                      // values stored as given (0), or as 8- or 4-bit codes + scales
     int kv_bf16;
     long long code_slots, pcode_slots;
     int* csum;                      // [B][Hkv][nchunk_max] per-chunk scores or flags (CHUNK prefill)

@@ -44,10 +44,10 @@ hkv_status compute_layout(const hkv_config* cfg, Layout* L, char* err, size_t er
         FAIL(HKV_ERR_UNSUPPORTED, "prefill_chunk %d set without HKV_PREFILL_CHUNK", cfg->prefill_chunk);
     if (chunked && (cfg->prefill_chunk < 0 || cfg->prefill_chunk > kMaxPrefillChunk))
         FAIL(HKV_ERR_UNSUPPORTED, "prefill_chunk %d outside [0, %d]", cfg->prefill_chunk, kMaxPrefillChunk);
-    if (cfg->value_bits != 0 && cfg->value_bits != 8)
-        FAIL(HKV_ERR_UNSUPPORTED, "value_bits %d not in {0, 8}", cfg->value_bits);
-    if (cfg->value_bits == 8 && (cfg->kv_dtype != HKV_BF16 || cfg->decode_schedule != HKV_DECODE_FUSED))
-        FAIL(HKV_ERR_UNSUPPORTED, "value_bits 8 needs kv_dtype HKV_BF16 and HKV_DECODE_FUSED");
+    if (cfg->value_bits != 0 && cfg->value_bits != 8 && cfg->value_bits != 4)
+        FAIL(HKV_ERR_UNSUPPORTED, "value_bits %d not in {0, 4, 8}", cfg->value_bits);
+    if (cfg->value_bits != 0 && (cfg->kv_dtype != HKV_BF16 || cfg->decode_schedule != HKV_DECODE_FUSED))
+        FAIL(HKV_ERR_UNSUPPORTED, "value_bits %d needs kv_dtype HKV_BF16 and HKV_DECODE_FUSED", cfg->value_bits);
     if (cfg->tier_capacity < 0 || cfg->tier_capacity > kMaxTierCapacity)
         FAIL(HKV_ERR_UNSUPPORTED, "tier_capacity %d outside [0, %d]", cfg->tier_capacity, kMaxTierCapacity);
     if (cfg->tier_capacity > 0 && cfg->value_bits != 0)
@@ -133,10 +133,11 @@ hkv_status compute_layout(const hkv_config* cfg, Layout* L, char* err, size_t er
     l.off_plen = take((size_t)l.B * 4);
     l.off_state = take(heads * 2 * 4);
     l.off_K = take(heads * Smax * l.d * l.es);
-    l.v_bytes = heads * Smax * l.d * (l.value_bits == 8 ? 1 : l.es);
+    // value rows: d elements of the kv dtype, or d codes of value_bits bits
+    l.v_bytes = l.value_bits ? heads * Smax * l.d * l.value_bits / 8 : heads * Smax * l.d * l.es;
     l.off_V = take(l.v_bytes);
     // value scales, padded by 16 entries: the attention tile reads 16 rows' scales at once
-    l.off_vs = take(l.value_bits == 8 ? (heads * Smax + 16) * 4 : 0);
+    l.off_vs = take(l.value_bits ? (heads * Smax + 16) * 4 : 0);
     l.off_code = take(heads * l.code_slots * cb);
     l.off_tok = take(heads * Smax * 4);
     l.off_dbg_q = take((size_t)l.B * l.Hq * l.W * 4);

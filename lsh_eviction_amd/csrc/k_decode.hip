@@ -453,30 +453,32 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // 16-byte row segments (lane l: row group l / (D/8), segment l % (D/8)).
 // Rows at or beyond `len` are not loaded and read as zero.
 // P.V runs on the matrix cores for d = 128 with values stored as given (see
-// mfma_tile_pv); int8 values and d = 64 accumulate P.V on the VALU.
-template <int D, bool VQ>
+// mfma_tile_pv); quantized values and d = 64 accumulate P.V on the VALU.
+// VQ: the width of the stored value codes, 0 (values as given), 8 or 4.
+template <int D, int VQ>
 constexpr bool pv_on_mfma()
 {
-    return D == 128 && !VQ;
+    return D == 128 && VQ == 0;
 }
 
-template <int D, int TR, bool VQ = false>
+template <int D, int TR, int VQ = 0>
 struct MTile {
     static constexpr int H = TR / 16;          // 16-row halves
     static constexpr int KS = D / 32;          // k-steps of 32 per half
     static constexpr int LPR = D / 8;          // V lanes per row (8 values each)
     static constexpr int RPW = 64 / LPR;       // V rows per wave load
     static constexpr int VU = TR / RPW;        // V loads per lane
-    using VW = typename std::conditional<VQ, uint2, uint4>::type;   // 8 bf16 values or 8 int8 codes
+    // 8 bf16 values, 8 int8 codes or 8 4-bit codes
+    using VW = typename std::conditional<VQ == 8, uint2, typename std::conditional<VQ == 4, uint32_t, uint4>::type>::type;
     uint4 k[H][KS];
     VW v[VU];
-    float vs[VQ ? H : 1][4];   // int8 values: scales of rows 16h + 4(l/16) + r (MFMA layout)
+    float vs[VQ ? H : 1][4];   // quantized values: scales of rows 16h + 4(l/16) + r (MFMA layout)
 
     // Rows beyond the range are clamped to its last row (loaded, then masked by
     // the caller); len == 0 clamps to row 0 of the range, which is in bounds.
     // No load sits in a branch, so the wait counters stay exact and the tile
     // in flight is never waited for early.
-    // Vh: bf16 rows, or int8 code rows with their scales at Vsh (VQ).
+    // Vh: bf16 rows, or code rows (VQ bits a code) with their scales at Vsh.
     __device__ __forceinline__ void load(const bf16_t* __restrict__ Kh, const void* __restrict__ Vh,
                                          const float* __restrict__ Vsh, int r0, int len, int base)
     {
@@ -518,8 +520,11 @@ struct MTile {
 #pragma unroll
         for (int u = 0; u < VU; ++u) {
             const int row = min(base + u * RPW + rg, last);
-            if constexpr (VQ)
+            if constexpr (VQ == 8)
                 v[u] = *reinterpret_cast<const uint2*>(reinterpret_cast<const int8_t*>(Vh) + (size_t)(r0 + row) * D + cc * 8);
+            else if constexpr (VQ == 4)
+                v[u] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(Vh) + (size_t)(r0 + row) * (D / 2) +
+                                                          cc * 4);
             else
                 v[u] = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(Vh) + (size_t)(r0 + row) * D + cc * 8);
         }
@@ -581,7 +586,7 @@ struct MState {
 };
 
 // The logits of the held-out row (skip) go to clg[head] as they are computed.
-template <int D, int GM, int TR, bool VQ>
+template <int D, int GM, int TR, int VQ>
 __device__ __forceinline__ void mfma_tile(const MTile<D, TR, VQ>& tl, int base, int r0, int len, int skip,
                                           const bf16x8 (&qhi)[D / 32], const bf16x8 (&qlo)[D / 32],
                                           PSmem<GM, TR>& ps, MState<GM>& st, float* clg)
@@ -635,7 +640,7 @@ __device__ __forceinline__ void mfma_tile(const MTile<D, TR, VQ>& tl, int base, 
         for (int r = 0; r < 4; ++r) {
             const float p = exp2_fast(lg[h][r] - ms);
             psum += p;
-            // int8 values: the row's scale rides on its probability
+            // quantized values: the row's scale rides on its probability
             const float pv = VQ ? p * tl.vs[VQ ? h : 0][r] : p;
             if (n < GM) ps.p[wave][16 * h + 4 * qd + r][n] = pv;
         }
@@ -672,10 +677,14 @@ __device__ __forceinline__ void mfma_tile(const MTile<D, TR, VQ>& tl, int base, 
             pg[4 * g4 + 3] = p4.w;
         }
         float vf[8];
-        if constexpr (VQ) {
+        if constexpr (VQ == 8) {
             const uint32_t w[2] = {tl.v[u].x, tl.v[u].y};
 #pragma unroll
             for (int e = 0; e < 8; ++e) vf[e] = (float)(int8_t)((w[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+        } else if constexpr (VQ == 4) {
+            // code e in bits 4e .. 4e + 3, sign-extended by an arithmetic shift
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vf[e] = (float)((int32_t)(tl.v[u] << (28 - 4 * e)) >> 28);
         } else {
             Vec16<bf16_t>::cvt(tl.v[u], vf);
         }
@@ -820,7 +829,7 @@ __device__ __forceinline__ void mfma_tile_pv(const MTile<128, 16, false>& tl, in
 // keep fp32 accuracy while K stays exact.  Probabilities go through LDS to the
 // lanes that hold the value rows; P.V is accumulated in fp32 on the VALU.
 // Two tiles alternate: one is computed while the other is in flight.
-template <int D, int GM, int TR, int NB, bool VQ = false>
+template <int D, int GM, int TR, int NB, int VQ = 0>
 __device__ __forceinline__ void attend_rows_mfma(const bf16_t* __restrict__ Kh, const void* __restrict__ Vh,
                                                  const float* __restrict__ Vsh, const float* __restrict__ qh, int G,
                                                  int r0, int len, int skip, MTile<D, TR, VQ> (&ring)[NB],
@@ -1092,7 +1101,7 @@ constexpr int tile_rows()
 }
 
 // tiles of a wave in flight at once in the bf16 path
-template <int GM, int D, bool VQ>
+template <int GM, int D, int VQ>
 constexpr int ring_depth()
 {
     // with P.V on the VALU, 16 heads' accumulators take 128 registers a lane;
@@ -1373,8 +1382,9 @@ union FusedSmem {
 // 16-byte code groups per thread the fused step loads before its tiles
 constexpr int kCodePre = 4;
 
-// VQ: values are int8 codes with a per-row scale (bf16 keys only).
-template <int D, int BITS, int GM, typename KT, bool VQ = false>
+// VQ: values are stored as codes of VQ bits (8 or 4) with a per-row scale
+// (bf16 keys only), or as given (0).
+template <int D, int BITS, int GM, typename KT, int VQ = 0>
 __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const float* __restrict__ q,
                                                            const KT* __restrict__ knew, const KT* __restrict__ vnew,
                                                            float* __restrict__ out, int* __restrict__ evicted)
@@ -1412,8 +1422,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     __shared__ PSmem<GM, TR> ps;
     __shared__ __align__(16) float s_q[GM][D];     // the group's queries (fp32)
     __shared__ __align__(16) KT s_kn[D], s_vn[D];  // the new token's key and value
-    __shared__ __align__(16) float s_vdq[VQ ? D : 1];   // int8 values: the new value as the cache holds it
-    __shared__ uint16_t s_vq2[VQ ? D / 2 : 1];          // ... its codes, two per entry
+    __shared__ __align__(16) float s_vdq[VQ ? D : 1];   // quantized values: the new value as the cache holds it
+    __shared__ uint16_t s_vq2[VQ ? D / 2 : 1];          // ... its codes, two per entry (in the low byte at 4 bits)
     __shared__ float s_vsc;                              // ... and its scale
     __shared__ uint32_t s_q16[BITS / 16][16];
     __shared__ uint32_t s_k16[BITS / 16];
@@ -1429,9 +1439,10 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     const size_t rowbase = (size_t)head * c.Smax;
     KT* Kh = reinterpret_cast<KT*>(c.K) + rowbase * D;
     KT* Vh = reinterpret_cast<KT*>(c.V) + rowbase * D;
-    int8_t* Vq8 = reinterpret_cast<int8_t*>(c.V) + rowbase * D;   // int8 values (VQ)
+    constexpr int VROW = VQ ? D * VQ / 8 : 1;                      // bytes of a row of value codes
+    uint8_t* Vq = reinterpret_cast<uint8_t*>(c.V) + rowbase * VROW;  // value codes (VQ)
     float* Vsh = VQ ? c.vs + rowbase : nullptr;
-    const void* Vbase = VQ ? (const void*)Vq8 : (const void*)Vh;
+    const void* Vbase = VQ ? (const void*)Vq : (const void*)Vh;
     const CT* codeh = reinterpret_cast<const CT*>(c.code) + (size_t)head * c.code_slots;
     const size_t crec = (size_t)head * c.nsplit + split;
     const KT* kh = knew + (size_t)head * D;
@@ -1549,11 +1560,14 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     // for the whole tile ring issued before it, ahead of the loop.
     const size_t crow = (size_t)(cand >= 0 ? cand : 0);
     const int ce = 2 * (lane % (D / 2));
-    using VRaw = typename std::conditional<VQ, uint16_t, typename std::conditional<kMfma, uint32_t, float2>::type>::type;
+    using VRaw = typename std::conditional<VQ != 0, uint16_t, typename std::conditional<kMfma, uint32_t, float2>::type>::type;
     VRaw vraw;
     float vcsc = 0.f;
-    if constexpr (VQ) {
-        vraw = *reinterpret_cast<const uint16_t*>(Vq8 + crow * D + ce);
+    if constexpr (VQ == 8) {
+        vraw = *reinterpret_cast<const uint16_t*>(Vq + crow * VROW + ce);
+        vcsc = Vsh[crow];
+    } else if constexpr (VQ == 4) {
+        vraw = Vq[crow * VROW + ce / 2];   // the two codes of elements ce, ce + 1
         vcsc = Vsh[crow];
     } else {
         vraw = *reinterpret_cast<const VRaw*>(Vh + crow * D + ce);
@@ -1570,8 +1584,11 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     // logits included, visible to every wave)
     if (cand >= 0 && wave == 0 && 2 * lane < D) {
         float2 vc2;
-        if constexpr (VQ)
+        if constexpr (VQ == 8)
             vc2 = make_float2((float)(int8_t)(vraw & 0xFFu) * vcsc, (float)(int8_t)(vraw >> 8) * vcsc);
+        else if constexpr (VQ == 4)
+            vc2 = make_float2((float)((int32_t)((uint32_t)vraw << 28) >> 28) * vcsc,
+                              (float)((int32_t)((uint32_t)vraw << 24) >> 28) * vcsc);
         else if constexpr (kMfma)
             vc2 = make_float2(__uint_as_float(vraw << 16), __uint_as_float(vraw & 0xFFFF0000u));
         else
@@ -1592,18 +1609,20 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     // of them is used, so the merge costs one round trip to memory per batch.
     if (tid == 0) c.count[head * kCountStride] = 0u;
     if constexpr (VQ) {
-        // the new token's value row as the cache will hold it: int8 codes
-        // (v / scale rounded half to even, clamped to +-127) with scale =
-        // max|v| / 127, all in fp32; every later use of the value is
-        // code * scale
+        // the new token's value row as the cache will hold it: codes of VQ
+        // bits (v / scale rounded half to even, clamped to +-Q) with scale =
+        // max|v| / Q, Q = 127 or 7, all in fp32; every later use of the value
+        // is code * scale
         if (wave == 0) {
+            constexpr float Q = VQ == 8 ? 127.0f : 7.0f;
             const int i0 = 2 * lane;
             const float f0 = i0 < D ? to_f32(s_vn[i0]) : 0.f, f1 = i0 < D ? to_f32(s_vn[i0 + 1]) : 0.f;
-            const float sc = wave_max_f(fmaxf(fabsf(f0), fabsf(f1))) / 127.0f;
-            const float c0 = sc > 0.f ? fminf(fmaxf(rintf(f0 / sc), -127.f), 127.f) : 0.f;
-            const float c1 = sc > 0.f ? fminf(fmaxf(rintf(f1 / sc), -127.f), 127.f) : 0.f;
+            const float sc = wave_max_f(fmaxf(fabsf(f0), fabsf(f1))) / Q;
+            const float c0 = sc > 0.f ? fminf(fmaxf(rintf(f0 / sc), -Q), Q) : 0.f;
+            const float c1 = sc > 0.f ? fminf(fmaxf(rintf(f1 / sc), -Q), Q) : 0.f;
             if (i0 < D) {
-                s_vq2[lane] = (uint16_t)(((uint32_t)(int32_t)c0 & 0xFFu) | (((uint32_t)(int32_t)c1 & 0xFFu) << 8));
+                constexpr uint32_t M = (1u << VQ) - 1u;
+                s_vq2[lane] = (uint16_t)(((uint32_t)(int32_t)c0 & M) | (((uint32_t)(int32_t)c1 & M) << VQ));
                 s_vdq[i0] = c0 * sc;
                 s_vdq[i0 + 1] = c1 * sc;
             }
@@ -1759,8 +1778,10 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     // stage 5: the new token takes slot e
     for (int i = tid; i < D; i += kThreads) {
         Kh[(size_t)e * D + i] = s_kn[i];
-        if constexpr (VQ) {
-            if (i < D / 2) reinterpret_cast<uint16_t*>(Vq8 + (size_t)e * D)[i] = s_vq2[i];
+        if constexpr (VQ == 8) {
+            if (i < D / 2) reinterpret_cast<uint16_t*>(Vq + (size_t)e * VROW)[i] = s_vq2[i];
+        } else if constexpr (VQ == 4) {
+            if (i < D / 2) Vq[(size_t)e * VROW + i] = (uint8_t)s_vq2[i];
         } else {
             Vh[(size_t)e * D + i] = s_vn[i];
         }
@@ -2098,8 +2119,13 @@ hipError_t launch_decode_fused(const DevCache& c, const float* q, const void* k,
                 return with_gm(c, [&](auto gg) {
                     constexpr int D = decltype(dd)::value, BITS = decltype(bb)::value, GM = decltype(gg)::value;
                     if constexpr (std::is_same<KT, bf16_t>::value) {
-                        if (c.vq) {
-                            hipLaunchKernelGGL((k_decode_fused<D, BITS, GM, KT, true>), fused_grid(c),
+                        if (c.vbits == 8) {
+                            hipLaunchKernelGGL((k_decode_fused<D, BITS, GM, KT, 8>), fused_grid(c),
+                                               dim3(kThreads), 0, st, c, q, (const KT*)k, (const KT*)v, out, evicted);
+                            return hipGetLastError();
+                        }
+                        if (c.vbits == 4) {
+                            hipLaunchKernelGGL((k_decode_fused<D, BITS, GM, KT, 4>), fused_grid(c),
                                                dim3(kThreads), 0, st, c, q, (const KT*)k, (const KT*)v, out, evicted);
                             return hipGetLastError();
                         }

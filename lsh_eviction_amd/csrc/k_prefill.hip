@@ -576,10 +576,11 @@ __global__ __launch_bounds__(256) void k_prefill_gather(DevCache c, const KT* __
     for (int q = j; q < CH; q += 16) kd[q] = ks[q];
     bool quantized = false;
     if constexpr (std::is_same<KT, bf16_t>::value) {
-        if (c.vq) {
-            // value row -> int8 codes and one scale (scale = max|v| / 127,
-            // code = v / scale rounded half to even, clamped to +-127, fp32);
-            // the 16 lanes of the row each take 8 values (D / 8 <= 16)
+        if (c.vbits) {
+            // value row -> codes of vbits bits and one scale (Q = 127 or 7:
+            // scale = max|v| / Q, code = v / scale rounded half to even,
+            // clamped to +-Q, fp32); the 16 lanes of the row each take 8
+            // values (D / 8 <= 16)
             float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             const int nchunk = D / 8;
             if (j < nchunk) Vec16<bf16_t>::cvt(vs[j], f);
@@ -590,11 +591,18 @@ __global__ __launch_bounds__(256) void k_prefill_gather(DevCache c, const KT* __
             amax = fmaxf(amax, dpp_f<kDppXor2>(amax));
             amax = fmaxf(amax, dpp_f<kDppHalfMirror>(amax));
             amax = fmaxf(amax, dpp_f<kDppMirror>(amax));
-            const float sc = amax / 127.0f;
-            if (j < nchunk) {
-                reinterpret_cast<uint2*>(reinterpret_cast<int8_t*>(c.V) + (rowbase + s) * D)[j] = quantize8(f, sc);
+            if (c.vbits == 8) {
+                const float sc = amax / 127.0f;
+                if (j < nchunk)
+                    reinterpret_cast<uint2*>(reinterpret_cast<int8_t*>(c.V) + (rowbase + s) * D)[j] = quantize8(f, sc);
+                if (j == 0) c.vs[rowbase + s] = sc;
+            } else {
+                const float sc = amax / 7.0f;
+                if (j < nchunk)
+                    reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(c.V) + (rowbase + s) * (D / 2))[j] =
+                        quantize4(f, sc);
+                if (j == 0) c.vs[rowbase + s] = sc;
             }
-            if (j == 0) c.vs[rowbase + s] = sc;
             quantized = true;
         }
     }

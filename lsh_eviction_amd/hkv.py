@@ -417,8 +417,9 @@ class Cache:
         dt = kv_torch_dtype(self.kv_dtype)
         K = torch.empty((self.B, self.Hkv, self.Smax, self.d), dtype=dt, device="cuda")
         rows = self.B * self.Hkv * self.Smax
-        if self.value_bits == 8:
-            V = torch.empty(rows * (self.d + 4), dtype=torch.uint8, device="cuda")
+        vrow = self.d * self.value_bits // 8   # bytes of a row of value codes
+        if self.value_bits:
+            V = torch.empty(rows * (vrow + 4), dtype=torch.uint8, device="cuda")
         else:
             V = torch.empty_like(K)
         codes = torch.empty((self.B, self.Hkv, self.Smax, self.W), dtype=torch.int32, device="cuda")
@@ -426,10 +427,13 @@ class Cache:
         st = torch.empty((self.B, self.Hkv, 2), dtype=torch.int32, device="cuda")
         hkv_get_state(self.h, K, V, codes, tok, st, stream)
         out = {"K": K, "V": V, "codes": codes, "tok": tok, "state": st}
-        if self.value_bits == 8:
-            # int8 codes [B][Hkv][Smax][d], then fp32 scales [B][Hkv][Smax]
-            out["Vq"] = V[:rows * self.d].view(torch.int8).view(self.B, self.Hkv, self.Smax, self.d)
-            out["Vs"] = V[rows * self.d:].view(torch.float32).view(self.B, self.Hkv, self.Smax)
+        if self.value_bits:
+            # codes [B][Hkv][Smax][d * bits / 8] (int8, or two 4-bit codes a
+            # byte, element 2i in the low half of byte i), then fp32 scales
+            # [B][Hkv][Smax]
+            q = V[:rows * vrow].view(self.B, self.Hkv, self.Smax, vrow)
+            out["Vq"] = q.view(torch.int8) if self.value_bits == 8 else q
+            out["Vs"] = V[rows * vrow:].view(torch.float32).view(self.B, self.Hkv, self.Smax)
         return out
 
     def set_state(self, s, stream=None):
@@ -437,8 +441,8 @@ class Cache:
         kvt = kv_torch_dtype(self.kv_dtype)
         rows = self.B * self.Hkv * self.Smax
         _require(s["K"], "K", (self.B, self.Hkv, self.Smax, self.d), kvt)
-        if self.value_bits == 8:
-            _require(s["V"], "V", (rows * (self.d + 4),), torch.uint8)
+        if self.value_bits:
+            _require(s["V"], "V", (rows * (self.d * self.value_bits // 8 + 4),), torch.uint8)
         else:
             _require(s["V"], "V", (self.B, self.Hkv, self.Smax, self.d), kvt)
         _require(s["codes"], "codes", (self.B, self.Hkv, self.Smax, self.W), torch.int32)

@@ -235,6 +235,18 @@ def compare_tier(cache, orc, sel, shape: Shape, when: str):
         assert kv_bytes_equal(hkv.to_numpy(tv[b, h, :m]), o["V"], shape.kv_dtype), f"{when} b={b} h={h}: tier V"
 
 
+def unpack_int4(packed: np.ndarray) -> np.ndarray:
+    """Two signed 4-bit codes a byte (element 2i in the low half of byte i) ->
+    one int8 per element."""
+    p = packed.astype(np.uint8)
+    lo = ((p & 0x0F).astype(np.int8) << 4) >> 4
+    hi = (p.astype(np.int8) >> 4)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), np.int8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
 def compare_state(cache, orc, sel, shape: Shape, when: str):
     from lsh_eviction_amd import hkv
     st = cache.get_state()
@@ -242,9 +254,12 @@ def compare_state(cache, orc, sel, shape: Shape, when: str):
     codes = words_u32(st["codes"])
     hs = hkv.to_numpy(st["state"])
     K = hkv.to_numpy(st["K"])
-    vq = getattr(cache, "value_bits", 0) == 8
+    vbits = getattr(cache, "value_bits", 0)
+    vq = vbits != 0
     if vq:
         Vq = st["Vq"].cpu().numpy(); Vs = st["Vs"].cpu().numpy()
+        if vbits == 4:
+            Vq = unpack_int4(Vq)
     else:
         V = hkv.to_numpy(st["V"])
     for (b, h) in sel:

@@ -70,9 +70,12 @@ def test_named_shapes_validate(hkv):
     (dict(prefill_chunk=5), "UNSUPPORTED"),                 # chunk size without the CHUNK policy
     (dict(prefill_policy=3, prefill_chunk=33), "UNSUPPORTED"),
     (dict(prefill_policy=3, prefill_chunk=-1), "UNSUPPORTED"),
-    (dict(value_bits=4), "UNSUPPORTED"),
+    (dict(value_bits=2), "UNSUPPORTED"),
     (dict(value_bits=8, kv_dtype=0), "UNSUPPORTED"),        # int8 values need bf16 keys
     (dict(value_bits=8, decode_schedule=1), "UNSUPPORTED"), # and the fused schedule
+    (dict(value_bits=4, kv_dtype=0), "UNSUPPORTED"),        # so do 4-bit values
+    (dict(value_bits=4, decode_schedule=1), "UNSUPPORTED"),
+    (dict(tier_capacity=1000, value_bits=4), "UNSUPPORTED"),
     (dict(budgets=[40000], prefill_policy=2), "UNSUPPORTED"),   # QUERY keeps its table on chip too
     (dict(chunk=100), "UNSUPPORTED"),
     (dict(chunk=32), "UNSUPPORTED"),
@@ -202,11 +205,15 @@ def test_status_strings(hkv):
     assert hkv.status_str(99) == "HKV_UNKNOWN_STATUS"
 
 
-def test_int8_values_shrink_the_workspace(hkv):
+def test_quantized_values_shrink_the_workspace(hkv):
     full = hkv.hkv_workspace_bytes(_cfg(hkv))
     v8 = hkv.hkv_workspace_bytes(_cfg(hkv, value_bits=8))
+    v4 = hkv.hkv_workspace_bytes(_cfg(hkv, value_bits=4))
     # V: 8 heads x 4096 slots x 128 values go from 2 bytes to 1 byte (+ a 4-byte scale per slot)
     assert full - v8 >= 8 * 4096 * (128 - 4) - 4096
+    # ... and to half a byte
+    assert v8 - v4 >= 8 * 4096 * 64 - 4096
+    assert hkv.hkv_validate_config(_cfg(hkv, value_bits=4)) == hkv.HKV_OK
 
 
 def test_binding_refuses_tensors_a_kernel_would_misread():

@@ -140,10 +140,11 @@ def test_chunk_prefill_reuse_across_layers():
     np.testing.assert_array_equal(st2["kept"], st["kept"])
 
 
-def test_chunk_prefill_int8_values():
+@pytest.mark.parametrize("value_bits", [8, 4], ids=["int8", "int4"])
+def test_chunk_prefill_quantized_values(value_bits):
     from hkv_harness import run_case
     run_case(C.LLAMA8B.scaled(prompt=2500, budget=1200), 4, schedule=FUSED, policy=CHUNK, prefill_chunk=10,
-             value_bits=8)
+             value_bits=value_bits)
 
 
 def test_chunk_prefill_full_long_128k():
@@ -246,23 +247,27 @@ INT8_VALUES = {
 }
 
 
+@pytest.mark.parametrize("value_bits", [8, 4], ids=["int8", "int4"])
 @pytest.mark.parametrize("name", list(INT8_VALUES))
-def test_int8_values_small(name):
-    """Values kept as int8 codes with per-row scales: codes and scales bit-exact,
-    evictions exact, attention within tolerance of the oracle over code * scale."""
+def test_quantized_values_small(name, value_bits):
+    """Values kept as int8 or 4-bit codes with per-row scales: codes and scales
+    bit-exact, evictions exact, attention within tolerance of the oracle over
+    code * scale."""
     from hkv_harness import run_case
     shape, steps, chunk = INT8_VALUES[name]
-    run_case(shape, steps, schedule=FUSED, policy=STREAM, chunk=chunk, value_bits=8)
+    run_case(shape, steps, schedule=FUSED, policy=STREAM, chunk=chunk, value_bits=value_bits)
 
 
-def test_int8_values_query_prefill():
+@pytest.mark.parametrize("value_bits", [8, 4], ids=["int8", "int4"])
+def test_quantized_values_query_prefill(value_bits):
     from hkv_harness import run_case
-    run_case(C.LLAMA8B.scaled(prompt=2500, budget=1200), 4, schedule=FUSED, policy=QUERY, value_bits=8)
+    run_case(C.LLAMA8B.scaled(prompt=2500, budget=1200), 4, schedule=FUSED, policy=QUERY, value_bits=value_bits)
 
 
-def test_int8_values_full_long_128k():
+@pytest.mark.parametrize("value_bits", [8, 4], ids=["int8", "int4"])
+def test_quantized_values_full_long_128k(value_bits):
     from hkv_harness import run_case
-    run_case(C.LONG128K, 3, schedule=FUSED, policy=STREAM, heads=[(0, 2)], check_every=0, value_bits=8)
+    run_case(C.LONG128K, 3, schedule=FUSED, policy=STREAM, heads=[(0, 2)], check_every=0, value_bits=value_bits)
 
 
 def test_scores_and_encoder():
@@ -295,7 +300,7 @@ def test_scores_and_encoder():
     cache.close()
 
 
-@pytest.mark.parametrize("value_bits", [0, 8])
+@pytest.mark.parametrize("value_bits", [0, 8, 4])
 def test_snapshot_restore_continues_identically(value_bits):
     import torch
     from lsh_eviction_amd import datagen, hkv
@@ -339,7 +344,7 @@ def test_fused_equals_split_bitwise_evictions():
         assert torch.allclose(o1, o2, rtol=1e-4, atol=1e-5)
 
 
-@pytest.mark.parametrize("value_bits,tier", [(0, 0), (8, 0), (0, 4096)], ids=["plain", "int8", "tier"])
+@pytest.mark.parametrize("value_bits,tier", [(0, 0), (8, 0), (4, 0), (0, 4096)], ids=["plain", "int8", "int4", "tier"])
 def test_graph_replay_matches_eager(value_bits, tier):
     """A captured decode step replayed several times equals the same steps run
     eagerly (with a host tier: the same tokens spill with the same rows)."""
@@ -472,6 +477,7 @@ POISON = {
     "g16_two_batches": (SMALL["g16_two_batches"][0], 3, FUSED, 64, 0, 0),
     "int8_ragged_small": (SMALL["ragged_small"][0], 4, FUSED, 0, 8, 0),
     "int8_g16_lse_merge": (SMALL["g16_lse_merge"][0], 3, FUSED, 64, 8, 0),
+    "int4_ragged_small": (SMALL["ragged_small"][0], 4, FUSED, 0, 4, 0),
     "tier_llama8b_small": (C.LLAMA8B.scaled(prompt=3000, budget=1500), 4, FUSED, 0, 0, 8192),
     "tier_tiny_split": (C.TINY, 8, SPLIT, 0, 0, 4096),
 }

@@ -43,7 +43,8 @@ def _same_state(caches):
         assert torch.equal(s1[key], s2[key]), key
 
 
-@pytest.mark.parametrize("schedule,value_bits", [(0, 0), (1, 0), (0, 8)], ids=["fused", "split", "fused_int8"])
+@pytest.mark.parametrize("schedule,value_bits", [(0, 0), (1, 0), (0, 8), (0, 4)],
+                         ids=["fused", "split", "fused_int8", "fused_int4"])
 def test_static_scratch_matches_workspace_scratch(schedule, value_bits):
     big = C.LLAMA8B.scaled(batch=2, prompt=6000, budget=4000)
     small = C.LLAMA8B.scaled(batch=1, prompt=900, budget=500)
