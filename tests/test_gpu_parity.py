@@ -45,6 +45,8 @@ SMALL = {
     "many_sequences": (C.RAGGED.scaled(batch=40, prompt_range=(300, 900)), 6, 0),
     # ragged budgets cut into several equal splits each, run longest first
     "ragged_equal_splits": (C.RAGGED.scaled(batch=6, prompt_range=(700, 2600)), 6, 448),
+    # 512 sequences of 32-150 slots, 1-3 splits of 64 each: a block list of ~1200 entries
+    "many_sequences_512": (C.RAGGED.scaled(batch=512, prompt_range=(64, 300)), 3, 64),
     # the fused step's last block merges up to 512 (split, head) records
     # against one common maximum per head, in one or more batches of splits,
     # and more records with a running log-sum-exp
@@ -393,6 +395,17 @@ def test_maximum_budget():
     from hkv_harness import run_case
     run_case(C.TINY.scaled(prompt=(1 << 22) + 100, budget=1 << 22, steps=3), 3, schedule=FUSED, policy=TRUNCATE,
              check_every=0)
+
+
+def test_maximum_batch():
+    """The largest supported batch, 4096 sequences of 8-40 slots (2 KV heads
+    each): the block list's sequence field reaches 4095 and the grid has
+    8192 blocks.  The oracle replays a spread of heads, the last sequence's
+    included."""
+    from hkv_harness import run_case
+    shape = C.RAGGED.scaled(batch=4096, n_q_heads=8, n_kv_heads=2, prompt_range=(16, 80))
+    heads = [(b, b % 2) for b in range(0, 4096, 97)] + [(4095, 0), (4095, 1), (0, 1)]
+    run_case(shape, 3, schedule=FUSED, policy=STREAM, heads=heads, check_every=1)
 
 
 def _ragged_pairs():
