@@ -452,13 +452,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // (l / 16) of the head dimension, 16 bytes per k-step), V in coalesced
 // 16-byte row segments (lane l: row group l / (D/8), segment l % (D/8)).
 // Rows at or beyond `len` are not loaded and read as zero.
-// P.V runs on the matrix cores for d = 128 with values stored as given (see
-// mfma_tile_pv); quantized values and d = 64 accumulate P.V on the VALU.
+// P.V runs on the matrix cores for d = 128 (see mfma_tile_pv), with values
+// as given or quantized; d = 64 accumulates P.V on the VALU.
 // VQ: the width of the stored value codes, 0 (values as given), 8 or 4.
 template <int D, int VQ>
 constexpr bool pv_on_mfma()
 {
-    return D == 128 && VQ == 0;
+    return D == 128;
 }
 
 template <int D, int TR, int VQ = 0>
@@ -501,10 +501,33 @@ struct MTile {
                 __builtin_memcpy(&k[0][s], &w, 16);
             }
             const int rg = lane / LPR, cc = lane % LPR;
+            if constexpr (VQ == 0) {
 #pragma unroll
-            for (int u = 0; u < VU; ++u) {
-                const auto w = __builtin_amdgcn_raw_buffer_load_b128(rv, (base + u * RPW + rg) * (D * 2) + cc * 16, 0, 0);
-                __builtin_memcpy(&v[u], &w, 16);
+                for (int u = 0; u < VU; ++u) {
+                    const auto w =
+                        __builtin_amdgcn_raw_buffer_load_b128(rv, (base + u * RPW + rg) * (D * 2) + cc * 16, 0, 0);
+                    __builtin_memcpy(&v[u], &w, 16);
+                }
+            } else {
+                // the same rows and columns as codes (VB bytes a row), then
+                // the scales of rows qd + 4 r: the rows of this lane's logits
+                constexpr int VB = D * VQ / 8;
+                const auto rq = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(Vh) + (size_t)r0 * VB), 0, len * VB,
+                    kRsrcWord3);
+#pragma unroll
+                for (int u = 0; u < VU; ++u) {
+                    const int off = (base + u * RPW + rg) * VB + cc * VQ;   // 8 codes of VQ bits
+                    if constexpr (VQ == 8) {
+                        const auto w = __builtin_amdgcn_raw_buffer_load_b64(rq, off, 0, 0);
+                        __builtin_memcpy(&v[u], &w, 8);
+                    } else {
+                        v[u] = __builtin_amdgcn_raw_buffer_load_b32(rq, off, 0, 0);
+                    }
+                }
+                const int last = len > 0 ? len - 1 : 0;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) vs[0][r] = Vsh[r0 + min(base + qd + 4 * r, last)];
             }
             return;
         }
@@ -727,8 +750,8 @@ __device__ __forceinline__ float head_alpha(float alpha, int qd, int r)
     }
 }
 
-// One 16-row tile with both products on the matrix cores (d = 128, values as
-// given).  The K tile's rows enter the logits MFMA in the order
+// One 16-row tile with both products on the matrix cores (d = 128).  The K
+// tile's rows enter the logits MFMA in the order
 // pi(i) = i / 4 + 4 (i % 4) (MTile::load), so register r of the lanes of
 // quarter qd holds the logit of physical row qd + 4 r for head n = lane % 16.
 // That is the A-operand layout of a 16 x 16 x 16 MFMA with the heads as its M
@@ -738,9 +761,18 @@ __device__ __forceinline__ float head_alpha(float alpha, int qd, int r)
 // for output column 8 n + blk: P.V is eight MFMAs, one per column block, with
 // no exchange between lanes.  The probabilities enter as a bf16 high part and
 // a bf16 remainder (two MFMAs into one fp32 accumulator), as the queries do
-// in the logits; the values are bf16, so every product is exact.
-template <int GM>
-__device__ __forceinline__ void mfma_tile_pv(const MTile<128, 16, false>& tl, int base, int r0, int len, int skip,
+// in the logits; the values are bf16, or integer codes converted exactly to
+// bf16 with each row's scale folded into its probability, so every product
+// is exact.
+// Two small integers as a pair of bf16 (a in the low half): their fp32
+// forms are exact in bf16 (|code| <= 127 needs 7 bits), i.e. the high halves.
+__device__ __forceinline__ uint32_t bf16_pair_of_ints(int a, int b)
+{
+    return __builtin_amdgcn_perm(__float_as_uint((float)b), __float_as_uint((float)a), 0x07060302u);
+}
+
+template <int GM, int VQ = 0>
+__device__ __forceinline__ void mfma_tile_pv(const MTile<128, 16, VQ>& tl, int base, int r0, int len, int skip,
                                              const bf16x8 (&qhi)[4], const bf16x8 (&qlo)[4], MStatePV& st,
                                              float* clg)
 {
@@ -793,16 +825,36 @@ __device__ __forceinline__ void mfma_tile_pv(const MTile<128, 16, false>& tl, in
             for (int blk = 0; blk < 8; ++blk) st.acc[blk][r] *= ah;
         }
     }
+    // quantized values: each row's scale rides on its probability in the A
+    // operand (the sum above is of the unscaled ones), and P.V runs on the
+    // raw codes, converted exactly to bf16
     bf16x4 ph, pl;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        ph[r] = (__bf16)p[r];
-        pl[r] = (__bf16)(p[r] - (float)ph[r]);
+        const float pa = VQ ? p[r] * tl.vs[0][r] : p[r];
+        ph[r] = (__bf16)pa;
+        pl[r] = (__bf16)(pa - (float)ph[r]);
     }
     const s16x4 aph = __builtin_bit_cast(s16x4, ph), apl = __builtin_bit_cast(s16x4, pl);
     // Value rows at or past len read as zero (the buffer's range ends at
     // len), so masked rows add exactly 0 * 0.
-    const uint4 (&vr)[4] = tl.v;
+    uint4 vr[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        if constexpr (VQ == 8) {
+            const uint32_t x = tl.v[u].x, y = tl.v[u].y;
+            auto c8 = [](uint32_t w, int k) { return (int)(int8_t)(w >> (8 * k)); };
+            vr[u] = make_uint4(bf16_pair_of_ints(c8(x, 0), c8(x, 1)), bf16_pair_of_ints(c8(x, 2), c8(x, 3)),
+                               bf16_pair_of_ints(c8(y, 0), c8(y, 1)), bf16_pair_of_ints(c8(y, 2), c8(y, 3)));
+        } else if constexpr (VQ == 4) {
+            const uint32_t w = tl.v[u];
+            auto c4 = [](uint32_t x, int e) { return (int32_t)(x << (28 - 4 * e)) >> 28; };
+            vr[u] = make_uint4(bf16_pair_of_ints(c4(w, 0), c4(w, 1)), bf16_pair_of_ints(c4(w, 2), c4(w, 3)),
+                               bf16_pair_of_ints(c4(w, 4), c4(w, 5)), bf16_pair_of_ints(c4(w, 6), c4(w, 7)));
+        } else {
+            vr[u] = tl.v[u];
+        }
+    }
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) {
         const int w = blk >> 1;
@@ -871,21 +923,21 @@ __device__ __forceinline__ void attend_rows_mfma(const bf16_t* __restrict__ Kh, 
         for (; k + 2 * NB <= ntile; k += NB) {
 #pragma unroll
             for (int i = 0; i < NB; ++i) {
-                mfma_tile_pv<GM>(ring[i], b0 + (k + i) * step, r0, len, skip, qhi, qlo, st, clg);
+                mfma_tile_pv<GM, VQ>(ring[i], b0 + (k + i) * step, r0, len, skip, qhi, qlo, st, clg);
                 ring[i].load(Kh, Vh, Vsh, r0, len, b0 + (k + i + NB) * step);
             }
         }
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             if (k + i < ntile) {
-                mfma_tile_pv<GM>(ring[i], b0 + (k + i) * step, r0, len, skip, qhi, qlo, st, clg);
+                mfma_tile_pv<GM, VQ>(ring[i], b0 + (k + i) * step, r0, len, skip, qhi, qlo, st, clg);
                 if (k + i + NB < ntile) ring[i].load(Kh, Vh, Vsh, r0, len, b0 + (k + i + NB) * step);
             }
         }
 #pragma unroll
         for (int i = 0; i < NB; ++i)
             if (k + NB + i < ntile)
-                mfma_tile_pv<GM>(ring[i], b0 + (k + NB + i) * step, r0, len, skip, qhi, qlo, st, clg);
+                mfma_tile_pv<GM, VQ>(ring[i], b0 + (k + NB + i) * step, r0, len, skip, qhi, qlo, st, clg);
 
         float lsum = st.lsum;
         {
