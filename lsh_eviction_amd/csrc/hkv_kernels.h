@@ -29,7 +29,7 @@ struct DevCache {
     unsigned* count;                // [B][Hkv][kCountStride] blocks of the current step that have published (entry 0)
     void* pcode;                    // [B][Hkv][pcode_slots] prompt key codes
     void* qcode;                    // [B][Hq][pcode_slots] prompt query codes (QUERY prefill)
-    float* vs;                      // [B][Hkv][Smax] (+16) value scales when values are int8
+    float* vs;                      // [B][Hkv][Smax] (+16) value scales when values are stored as codes
     int B, Hq, Hkv, G, d, bits, W, Smax, chunk, nsplit;
     int ragged;                     // budgets differ: the fused step runs the block list `blk`
     const uint2* blk;               // [nblk] (b | split << 16, split length) of each fused block, longest first

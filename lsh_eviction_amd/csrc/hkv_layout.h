@@ -49,7 +49,7 @@ struct Layout {
     size_t off_dbg_q, off_dbg_k, off_part, off_frec, off_fscal, off_cand_v, off_ekey;
     size_t off_info, off_count, off_pcode, off_qcode, off_vs, off_csum;
     size_t off_tcount, off_tpart, off_tflag, off_chist, off_blk;
-    size_t v_bytes;        // bytes of the V region (kv dtype, or int8 codes)
+    size_t v_bytes;        // bytes of the V region (kv dtype, or codes of value_bits bits)
     size_t total;
 };
 
