@@ -277,7 +277,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+        print(json.dumps({"error": "the decode step runs on one GPU (it has no cross-GPU path); --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     if args.tier and args.prefill not in ("stream", "truncate"):
