@@ -157,7 +157,10 @@ __device__ __forceinline__ uint32_t enc_lds(const float* Xq, int nq, const KT* x
     const float* xr = Xq + (size_t)(m < nq ? m : 0) * D + qd * DQ;
     const KT* kr = xk + qd * DQ;
     const float* rc = Rs + (size_t)(qd * DQ) * BITS + nt * 16 + m;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // Every operand is read from LDS before the first product, so the reads
+    // overlap; a product that waits for its own read would make the encoder
+    // a chain of LDS round trips.
+    float xs[DQ], rs[DQ];
 #pragma unroll
     for (int v = 0; v < DQ / EPL; ++v) {
         float kf[EPL];
@@ -167,16 +170,23 @@ __device__ __forceinline__ uint32_t enc_lds(const float* Xq, int nq, const KT* x
             const float4 q4 = *reinterpret_cast<const float4*>(xr + v * EPL + 4 * e4);
             const float qv[4] = {q4.x, q4.y, q4.z, q4.w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int s = v * EPL + 4 * e4 + e;
-                const float x = m < nq ? qv[e] : (m == nq ? kf[4 * e4 + e] : 0.f);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x, rc[s * BITS], acc, 0, 0, 0);
-            }
+            for (int e = 0; e < 4; ++e)
+                xs[v * EPL + 4 * e4 + e] = m < nq ? qv[e] : (m == nq ? kf[4 * e4 + e] : 0.f);
         }
     }
+#pragma unroll
+    for (int s = 0; s < DQ; ++s) rs[s] = rc[s * BITS];
+    __builtin_amdgcn_sched_barrier(0);
+    // four independent accumulation chains, added at the end (any fp32
+    // summation order gives the exact sign outside the flagged band)
+    f32x4 acc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < DQ; ++s) acc[s & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(xs[s], rs[s], acc[s & 3], 0, 0, 0);
     unsigned long long mk[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) mk[r] = __ballot(acc[r] > 0.f);
+    for (int r = 0; r < 4; ++r) mk[r] = __ballot((acc[0][r] + acc[1][r]) + (acc[2][r] + acc[3][r]) > 0.f);
     const int a = (lane & 15) >> 2, r = lane & 3;
     const unsigned long long mm = r == 0 ? mk[0] : r == 1 ? mk[1] : r == 2 ? mk[2] : mk[3];
     return (uint32_t)((mm >> (16 * a)) & 0xFFFFull);
@@ -220,8 +230,13 @@ __device__ __forceinline__ unsigned long long thread_candidate(const typename Co
             best = k > best ? k : best;
         }
     };
+    // (a wave whose preloaded groups all lie past the range skips them: its
+    // first lane holds the lowest slot)
 #pragma unroll
-    for (int j = 0; j < NPRE; ++j) fold(pre[j], s0 + (j * kThreads + (int)threadIdx.x) * VS);
+    for (int j = 0; j < NPRE; ++j) {
+        const int sj = s0 + (j * kThreads + (int)threadIdx.x) * VS;
+        if (__builtin_amdgcn_readfirstlane(sj) < s1) fold(pre[j], sj);
+    }
     for (int s = s0 + (NPRE * kThreads + (int)threadIdx.x) * VS; s < s1; s += kThreads * VS)
         fold(*reinterpret_cast<const uint4*>(code + s), s);
     return best;
@@ -1547,13 +1562,16 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     const int len = max(min(s0 + chunk, n) - s0, 0);
     if (split >= nsb) return;   // (no block lies past its sequence's splits; kept as a guard)
 
-    // the first tiles of every wave, in flight while the codes are computed
+    // The first tile of every wave is in flight while the codes are computed;
+    // the rest of the ring is requested once the chunk's candidate is known.
+    // (Requested all at once here, the ring fills the memory pipeline's queue,
+    // and every wave waits at issue until most of it has drained, which holds
+    // back the codes and the start of the loop.)
     constexpr int NB = ring_depth<GM, D, VQ>();
     MTile<D, TR, VQ> ring[kMfma ? NB : 1];
     Tile<D, KT> first;
     if constexpr (kMfma) {
-#pragma unroll
-        for (int i = 0; i < NB; ++i) ring[i].load(Kh, Vbase, Vsh, s0, len, (wave + i * kWaves) * TR);
+        ring[0].load(Kh, Vbase, Vsh, s0, len, wave * TR);
     } else {
         first.load(Kh, Vh, s0, len, wave * Tile<D, KT>::ROWS);
     }
@@ -1625,6 +1643,11 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
         vraw = *reinterpret_cast<const VRaw*>(Vh + crow * D + ce);
     }
 
+    // the rest of the ring
+    if constexpr (kMfma) {
+#pragma unroll
+        for (int i = 1; i < NB; ++i) ring[i].load(Kh, Vbase, Vsh, s0, len, (wave + i * kWaves) * TR);
+    }
     // attention over the chunk with the candidate held out
     if constexpr (kMfma)
         attend_rows_mfma<D, GM, TR, NB, VQ>(Kh, Vbase, Vsh, &s_q[0][0], G, s0, len, cand, ring, sm, ps, s_clg);
