@@ -144,19 +144,23 @@ __device__ __forceinline__ void encode_block16(const XT* __restrict__ X, int nve
 }
 
 // Wave-level encoder over operands staged in LDS: rows 0 .. nq-1 of X are
-// the fp32 rows of Xq, row nq is the vector xk (stored as KT), rows above are
-// zero; Rs is R (d x b fp32, row-major).  Lane i returns the 16-bit chunk nt
-// of the code of row i (as encode16_mfma).
-template <int D, int BITS, typename KT>
-__device__ __forceinline__ uint32_t enc_lds(const float* Xq, int nq, const KT* xk, const float* Rs, int nt)
+// the fp32 rows of Xq (row stride XS), row nq is the vector xk (stored as
+// KT), rows above are zero; Rt is R transposed, b rows of d entries with row
+// stride D + 4.  Lane i returns the 16-bit chunk nt of the code of row i (as
+// encode16_mfma).  Lane (m, qd) = (l % 16, l / 16) feeds row m of X and
+// column 16 nt + m of R over k = qd d/4 + s at product s; it reads both
+// operands as 16-byte runs, and the row padding puts the 16 lanes of a
+// quarter-wave on distinct banks.
+template <int D, int BITS, typename KT, int XS>
+__device__ __forceinline__ uint32_t enc_lds(const float* Xq, int nq, const KT* xk, const float* Rt, int nt)
 {
     constexpr int DQ = D / 4;
     constexpr int EPL = Vec16<KT>::EPL;
     const int lane = threadIdx.x & 63;
     const int m = lane & 15, qd = lane >> 4;
-    const float* xr = Xq + (size_t)(m < nq ? m : 0) * D + qd * DQ;
+    const float* xr = Xq + (size_t)(m < nq ? m : 0) * XS + qd * DQ;
     const KT* kr = xk + qd * DQ;
-    const float* rc = Rs + (size_t)(qd * DQ) * BITS + nt * 16 + m;
+    const float* rr = Rt + (size_t)(nt * 16 + m) * (D + 4) + qd * DQ;
     // Every operand is read from LDS before the first product, so the reads
     // overlap; a product that waits for its own read would make the encoder
     // a chain of LDS round trips.
@@ -175,7 +179,13 @@ __device__ __forceinline__ uint32_t enc_lds(const float* Xq, int nq, const KT* x
         }
     }
 #pragma unroll
-    for (int s = 0; s < DQ; ++s) rs[s] = rc[s * BITS];
+    for (int v = 0; v < DQ / 4; ++v) {
+        const float4 r4 = *reinterpret_cast<const float4*>(rr + 4 * v);
+        rs[4 * v] = r4.x;
+        rs[4 * v + 1] = r4.y;
+        rs[4 * v + 2] = r4.z;
+        rs[4 * v + 3] = r4.w;
+    }
     __builtin_amdgcn_sched_barrier(0);
     // four independent accumulation chains, added at the end (any fp32
     // summation order gives the exact sign outside the flagged band)
@@ -300,7 +310,7 @@ struct Tile {
 // sm.candlg.  `first` is the wave's first tile, already in flight.  The next
 // tile is loaded while the current one is computed.  On return (after a block
 // barrier) sm.m, sm.l, sm.acc hold one (max, sum, acc) per wave.
-template <int D, int GM, typename KT>
+template <int D, int GM, typename KT, int QS = D>
 __device__ __forceinline__ void attend_rows(const KT* __restrict__ Kh, const KT* __restrict__ Vh,
                                             const float* __restrict__ qh, int G, int r0, int len, int skip,
                                             Tile<D, KT> cur, AttnSmem<D, GM>& sm, float* clg)
@@ -315,7 +325,7 @@ __device__ __forceinline__ void attend_rows(const KT* __restrict__ Kh, const KT*
 #pragma unroll
     for (int g = 0; g < GM; ++g) {
         if (g < G) {
-            const float4* qp = reinterpret_cast<const float4*>(qh + g * D + cc * EPL);
+            const float4* qp = reinterpret_cast<const float4*>(qh + g * QS + cc * EPL);
 #pragma unroll
             for (int e4 = 0; e4 < EPL / 4; ++e4) {
                 const float4 f = qp[e4];
@@ -896,7 +906,7 @@ __device__ __forceinline__ void mfma_tile_pv(const MTile<128, 16, VQ>& tl, int b
 // keep fp32 accuracy while K stays exact.  Probabilities go through LDS to the
 // lanes that hold the value rows; P.V is accumulated in fp32 on the VALU.
 // Two tiles alternate: one is computed while the other is in flight.
-template <int D, int GM, int TR, int NB, int VQ = 0>
+template <int D, int GM, int TR, int NB, int VQ = 0, int QS = D>
 __device__ __forceinline__ void attend_rows_mfma(const bf16_t* __restrict__ Kh, const void* __restrict__ Vh,
                                                  const float* __restrict__ Vsh, const float* __restrict__ qh, int G,
                                                  int r0, int len, int skip, MTile<D, TR, VQ> (&ring)[NB],
@@ -910,7 +920,7 @@ __device__ __forceinline__ void attend_rows_mfma(const bf16_t* __restrict__ Kh, 
     bf16x8 qhi[KS], qlo[KS];
     {
         const float qs = qscale2<D>();
-        const float* qp = qh + (size_t)(n < G ? n : 0) * D + qd * (D / 4);
+        const float* qp = qh + (size_t)(n < G ? n : 0) * QS + qd * (D / 4);
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
 #pragma unroll
@@ -1441,7 +1451,7 @@ __device__ __forceinline__ float4 pair_sum4(float4 v)
 
 template <int D, int BITS, int GM>
 union FusedSmem {
-    float R[D * BITS];          // encoder operand, dead once the codes are known
+    float R[BITS * (D + 4)];    // encoder operand (R transposed, rows padded), dead once the codes are known
     AttnSmem<D, GM> at;
     MergeBlockSmem<D, GM> mg;
 };
@@ -1487,7 +1497,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
 
     __shared__ FusedSmem<D, BITS, GM> u;
     __shared__ PSmem<GM, TR> ps;
-    __shared__ __align__(16) float s_q[GM][D];     // the group's queries (fp32)
+    constexpr int QS = D + 4;                      // row stride of s_q (padded: see enc_lds)
+    __shared__ __align__(16) float s_q[GM][QS];    // the group's queries (fp32)
     __shared__ __align__(16) KT s_kn[D], s_vn[D];  // the new token's key and value
     __shared__ __align__(16) float s_vdq[VQ ? D : 1];   // quantized values: the new value as the cache holds it
     __shared__ uint16_t s_vq2[VQ ? D / 2 : 1];          // ... its codes, two per entry (in the low byte at 4 bits)
@@ -1540,9 +1551,20 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
         craw[j] = *reinterpret_cast<const uint4*>(codeh + min(s0 + (j * kThreads + tid) * VS, clast));
     // (threads past the end store the last element again, with the value
     // they loaded from it, so every store is unconditional)
+    // R goes in transposed (b rows of d entries, padded), q with padded rows
 #pragma unroll
-    for (int j = 0; j < RPT; ++j) reinterpret_cast<float4*>(u.R)[min(tid + j * kThreads, NR4 - 1)] = rst[j];
-    reinterpret_cast<float4*>(&s_q[0][0])[min(tid, NQ4 - 1)] = qst;
+    for (int j = 0; j < RPT; ++j) {
+        const int i4 = min(tid + j * kThreads, NR4 - 1);
+        const int k = i4 / (BITS / 4), c = 4 * (i4 % (BITS / 4));
+        u.R[(c + 0) * (D + 4) + k] = rst[j].x;
+        u.R[(c + 1) * (D + 4) + k] = rst[j].y;
+        u.R[(c + 2) * (D + 4) + k] = rst[j].z;
+        u.R[(c + 3) * (D + 4) + k] = rst[j].w;
+    }
+    {
+        const int i4 = min(tid, NQ4 - 1);
+        *reinterpret_cast<float4*>(&s_q[i4 / (D / 4)][4 * (i4 % (D / 4))]) = qst;
+    }
     reinterpret_cast<uint4*>(wave == 0 ? s_kn : s_vn)[min(lane, NK4 - 1)] = kvst;
     // The cache state goes through LDS before the barrier, stored by every
     // thread (the same values), which keeps its loads next to the ones above:
@@ -1580,11 +1602,11 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     // key (row G, or a pass of its own when the group fills all 16 rows)
     constexpr int NT = BITS / 16;
     if (wave < NT) {
-        const uint32_t c16 = enc_lds<D, BITS, KT>(&s_q[0][0], G, s_kn, u.R, wave);
+        const uint32_t c16 = enc_lds<D, BITS, KT, QS>(&s_q[0][0], G, s_kn, u.R, wave);
         if (lane < G) s_q16[wave][lane] = c16;
         if (lane == G && G < 16) s_k16[wave] = c16;
     } else if (G == 16 && wave < 2 * NT) {
-        const uint32_t c16 = enc_lds<D, BITS, KT>(&s_q[0][0], 0, s_kn, u.R, wave - NT);
+        const uint32_t c16 = enc_lds<D, BITS, KT, QS>(&s_q[0][0], 0, s_kn, u.R, wave - NT);
         if (lane == 0) s_k16[wave - NT] = c16;
     }
     // base-2 logit of the new token for each head (only the head's last block
@@ -1650,9 +1672,9 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     }
     // attention over the chunk with the candidate held out
     if constexpr (kMfma)
-        attend_rows_mfma<D, GM, TR, NB, VQ>(Kh, Vbase, Vsh, &s_q[0][0], G, s0, len, cand, ring, sm, ps, s_clg);
+        attend_rows_mfma<D, GM, TR, NB, VQ, QS>(Kh, Vbase, Vsh, &s_q[0][0], G, s0, len, cand, ring, sm, ps, s_clg);
     else
-        attend_rows<D, GM, KT>(Kh, Vh, &s_q[0][0], G, s0, len, cand, first, sm, s_clg);
+        attend_rows<D, GM, KT, QS>(Kh, Vh, &s_q[0][0], G, s0, len, cand, first, sm, s_clg);
 
     // publish this chunk: partial softmax, candidate logits and value row
     // (the attention's closing barrier made its LDS results, the candidate's
