@@ -1698,13 +1698,19 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     __syncthreads();
     if (tid == 0) s_last = atomicAdd(&c.count[head * kCountStride], 1u) == (unsigned)(nsb - 1);
     __syncthreads();
-    if (!s_last) return;
+    // The other blocks run the merge below dry: over empty record buffers
+    // (their loads read zero and touch no memory) and with every global
+    // store skipped.  Which compute unit merges a head changes from step to
+    // step; without this, the merge's instructions reach the instruction
+    // caches only as each unit happens to merge, and the first few hundred
+    // steps of a run merge from cold caches.
+    const bool dry = !s_last;
 
     // ---- the last block of the head: winner, merge, write ----
     // Every thread owns 4 output columns (c4) of every head for the splits
     // j = r + RS * jj.  All loads of a batch of splits are issued before any
     // of them is used, so the merge costs one round trip to memory per batch.
-    if (tid == 0) c.count[head * kCountStride] = 0u;
+    if (tid == 0 && !dry) c.count[head * kCountStride] = 0u;
     if constexpr (VQ) {
         // the new token's value row as the cache will hold it: codes of VQ
         // bits (v / scale rounded half to even, clamped to +-Q) with scale =
@@ -1735,13 +1741,14 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     // scalar at once, and its wait would hold back the record loads issued
     // after it; the merge reads it (readlane) once those are on their way.
     unsigned wkey0 = 0u;
-    if (lane == 0)
+    if (lane == 0 && !dry)
         wkey0 = __hip_atomic_load(reinterpret_cast<unsigned*>(&c.ekey[2 * head + (t & 1)]), __ATOMIC_RELAXED,
                                   __HIP_MEMORY_SCOPE_AGENT);
     const size_t hrec = (size_t)head * c.nsplit;
-    MergeArgs ma{dev_rsrc(c.frec + hrec * G * D, (size_t)c.nsplit * G * D * 4),
-                 dev_rsrc(c.fscal + hrec * G * 4, (size_t)c.nsplit * G * 16),
-                 dev_rsrc(c.cand_v + hrec * D, (size_t)c.nsplit * D * 4), G, nsb, r, c4, full, wkey0, chunk};
+    const size_t live = dry ? 0 : 1;
+    MergeArgs ma{dev_rsrc(c.frec + hrec * G * D, live * c.nsplit * G * D * 4),
+                 dev_rsrc(c.fscal + hrec * G * 4, live * c.nsplit * G * 16),
+                 dev_rsrc(c.cand_v + hrec * D, live * c.nsplit * D * 4), G, nsb, r, c4, full, wkey0, chunk};
     const int per = (nsb + RS - 1) / RS;   // splits per thread
     MergeBlockSmem<D, GM>& mg = u.mg;
     static_assert(TPR == 16 || TPR == 32, "rows per wave");
@@ -1852,6 +1859,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
         o = make_float4(fmaf(vn.x, sn, A.x) * inv, fmaf(vn.y, sn, A.y) * inv, fmaf(vn.z, sn, A.z) * inv,
                         fmaf(vn.w, sn, A.w) * inv);
     }
+    if (dry) return;
     if (k == 0 && (tid >> qsh) < nout) reinterpret_cast<float4*>(out + (size_t)(hq0 + og) * D)[cc] = o;
 
     // a host tier keeps the token that leaves: its rows and position are
