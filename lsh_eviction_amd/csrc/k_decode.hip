@@ -20,7 +20,9 @@
 //   new token, merges the partials against one common maximum per head
 //   (a running log-sum-exp when there are very many) and writes the new token into the
 //   winner's slot.  The result equals "evict, write, then attend" with every
-//   K/V byte read once and no grid-wide barrier or L2-wide fence.
+//   K/V byte read once and no grid-wide barrier or L2-wide fence.  The other
+//   blocks run the same merge dry (empty record buffers, no stores), which
+//   keeps its code in every compute unit's instruction cache.
 //
 //   SPLIT (five launches): lsh_encode, hamming_argmax, evict_write, split-K
 //   attention, LSE merge.
