@@ -1705,8 +1705,12 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(DevCache c, const flo
     // store skipped.  Which compute unit merges a head changes from step to
     // step; without this, the merge's instructions reach the instruction
     // caches only as each unit happens to merge, and the first few hundred
-    // steps of a run merge from cold caches.
+    // steps of a run merge from cold caches.  Only the merge against one
+    // common maximum (at most kThreads records, one batch of loads) is run
+    // dry: the running log-sum-exp over very many splits would cost every
+    // block a loop over all of them.
     const bool dry = !s_last;
+    if (dry && nsb * G > kThreads) return;
 
     // ---- the last block of the head: winner, merge, write ----
     // Every thread owns 4 output columns (c4) of every head for the splits
